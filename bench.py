@@ -1,0 +1,293 @@
+"""Benchmark of the fused vocabulary cross-entropy hot path on one MI355X.
+
+One step = one pass of the logits cross-entropy hot path over one batch:
+ce_forward (online-softmax row sweep + deterministic mean when reduced) then
+ce_backward (gradient rebuilt from the saved statistics into a separate
+buffer).  The headline workload is (SQ,B,V) = (2048, 2, 128256) BF16 logits,
+4096 tokens, the shape of the TransformerEngine PR's validation comment.
+Inputs are synthetic and resident in HBM before the timed region.
+
+Printed: ONE JSON line with throughput (tokens/s), the roofline of the
+dominant kernel (the backward sweep, HBM bound) measured with HIP events on
+the stream the kernels run on, the FP64 CPU oracle timed on a bounded sample
+of the same workload, and the fused linear cross-entropy (M=4096, H=4096,
+V=131072) timed the same way against the BF16 matrix-core peak.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "CE fwd+bwd tokens/s (N=4096,V=128256 bf16); % of HBM / MFMA roofline"
+
+
+def _bf16_dev(bits: np.ndarray, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def _event_pairs(n):
+    import torch
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n)]
+
+
+def bench_logits(case, steps: int, warmup: int):
+    import torch
+    import vocabulary_cross_entropy_amd as vce
+    from vocabulary_cross_entropy_amd import accounting
+
+    dev = torch.device("cuda:0")
+    z = _bf16_dev(case.logits, dev)
+    t = torch.from_numpy(case.targets).to(dev)
+    go = torch.from_numpy(case.grad_output).to(dev)
+    if case.reduce_loss:
+        go = go.reshape(-1)
+    N, V = case.N, case.V
+    loss = torch.empty((case.d0, case.d1), device=dev)
+    mean = torch.empty((), device=dev)
+    stats = torch.empty((case.d0, case.d1, 4), device=dev)
+    nv = torch.empty((), dtype=torch.int32, device=dev)
+    grad = torch.empty_like(z)
+    out = (loss, mean if case.reduce_loss else None, stats, nv if case.reduce_loss else None)
+    eps, red = case.label_smoothing, case.reduce_loss
+
+    def step(ev_f=None, ev_b=None):
+        if ev_f: ev_f[0].record()
+        vce.ce_forward(z, t, eps, red, out=out)
+        if ev_f: ev_f[1].record()
+        if ev_b: ev_b[0].record()
+        vce.ce_backward(z, t, stats, out[3], go, eps, red, grad=grad)
+        if ev_b: ev_b[1].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # timed region: K whole steps, bracketed by synchronisation
+    ev_f, ev_b = _event_pairs(steps), _event_pairs(steps)
+    whole = _event_pairs(1)[0]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    whole[0].record()
+    for i in range(steps):
+        step(ev_f[i], ev_b[i])
+    whole[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = whole[0].elapsed_time(whole[1])
+    fwd_ms = [a.elapsed_time(b) for a, b in ev_f]
+    bwd_ms = [a.elapsed_time(b) for a, b in ev_b]
+
+    # in-place backward: logits restored before each launch, outside its events
+    zin = torch.empty_like(z)
+    ip_ms = []
+    for i in range(max(3, min(steps, 10))):
+        zin.copy_(z)
+        vce.ce_forward(zin, t, eps, red, out=out)
+        e = _event_pairs(1)[0]
+        e[0].record()
+        vce.ce_backward(zin, t, stats, out[3], go, eps, red, overwrite_input=True)
+        e[1].record()
+        torch.cuda.synchronize()
+        ip_ms.append(e[0].elapsed_time(e[1]))
+
+    n_ign = int(case.meta["n_ignored"])
+    es = case.elem_bytes
+    b_fwd = accounting.ce_bytes(N, V, es, n_ign, "fwd")
+    b_bwd = accounting.ce_bytes(N, V, es, n_ign, "bwd")
+    avg_f, avg_b = sum(fwd_ms) / steps, sum(bwd_ms) / steps
+    ms_step = total_ms / steps
+    return dict(
+        ms_per_step=ms_step, wall_s=wall, tokens_per_s=N * steps / (total_ms * 1e-3),
+        fwd_ms_avg=avg_f, bwd_ms_avg=avg_b, fwd_ms_median=statistics.median(fwd_ms),
+        bwd_ms_median=statistics.median(bwd_ms), bwd_inplace_ms_median=statistics.median(ip_ms),
+        fwd_GBs=b_fwd / (avg_f * 1e-3) / 1e9, bwd_GBs=b_bwd / (avg_b * 1e-3) / 1e9,
+        fb_GBs=(b_fwd + b_bwd) / (ms_step * 1e-3) / 1e9,
+        bytes_fwd=b_fwd, bytes_bwd=b_bwd,
+        bytes_fb_nominal=accounting.ce_bytes_nominal(N, V, es, "fb"),
+    )
+
+
+def bench_linear(case, steps: int, warmup: int):
+    import torch
+    import vocabulary_cross_entropy_amd as vce
+    from vocabulary_cross_entropy_amd import accounting
+
+    dev = torch.device("cuda:0")
+    X, W = _bf16_dev(case.X, dev), _bf16_dev(case.W, dev)
+    t = torch.from_numpy(case.targets).to(dev)
+    go = torch.ones(1, device=dev)
+    M, H, V = case.M, case.H, case.V
+    ws = vce.lce_workspace(M, H, V, dev)
+    loss = torch.empty(M, device=dev)
+    mean = torch.empty((), device=dev)
+    stats = torch.empty((M, 4), device=dev)
+    nv = torch.empty((), dtype=torch.int32, device=dev)
+    dX, dW = torch.empty_like(X), torch.empty_like(W)
+    out = (loss, mean, stats, nv)
+    eps = case.label_smoothing
+
+    def step(ev_f=None, ev_b=None):
+        if ev_f: ev_f[0].record()
+        vce.lce_forward(X, W, t, eps, True, workspace=ws, out=out)
+        if ev_f: ev_f[1].record()
+        if ev_b: ev_b[0].record()
+        vce.lce_backward(X, W, t, stats, nv, go, eps, True, workspace=ws, dX=dX, dW=dW)
+        if ev_b: ev_b[1].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev_f, ev_b = _event_pairs(steps), _event_pairs(steps)
+    whole = _event_pairs(1)[0]
+    whole[0].record()
+    for i in range(steps):
+        step(ev_f[i], ev_b[i])
+    whole[1].record()
+    torch.cuda.synchronize()
+    total_ms = whole[0].elapsed_time(whole[1])
+    fwd_ms = [a.elapsed_time(b) for a, b in ev_f]
+    bwd_ms = [a.elapsed_time(b) for a, b in ev_b]
+    f_fwd = accounting.linear_flops(M, H, V, "fwd")
+    f_fb = accounting.linear_flops(M, H, V, "fb")
+    f_bwd = accounting.linear_flops(M, H, V, "bwd")
+    ms_step = total_ms / steps
+    avg_f, avg_b = sum(fwd_ms) / steps, sum(bwd_ms) / steps
+    peak = accounting.BF16_MFMA_PEAK_TFLOPS
+    return dict(
+        workload=case.name, M=M, H=H, V=V, ms_per_step=ms_step,
+        tokens_per_s=M * steps / (total_ms * 1e-3),
+        fwd_ms_median=statistics.median(fwd_ms), bwd_ms_median=statistics.median(bwd_ms),
+        fb_tflops=f_fb / (ms_step * 1e-3) / 1e12,
+        roofline={"bound": "mfma", "achieved": round(f_fwd / (avg_f * 1e-3) / 1e12, 2),
+                  "peak": peak, "unit": "TFLOP/s",
+                  "frac": round(f_fwd / (avg_f * 1e-3) / 1e12 / peak, 4),
+                  "traffic": None, "kernel": "lce_forward (GEMM + online-LSE epilogue, merge)"},
+        bwd_tflops=f_bwd / (avg_b * 1e-3) / 1e12,
+        fb_frac_of_peak=f_fb / (ms_step * 1e-3) / 1e12 / peak,
+        workspace_MiB=ws.numel() / 2 ** 20,
+    )
+
+
+def cpu_baseline(case, budget_s: float = 10.0):
+    """The FP64 oracle (C core, OpenMP over rows) on a bounded sample of the
+    workload: 64-row batches of randomly chosen rows, forward (loss and
+    statistics) then backward (gradient rows), until the time budget is spent
+    (passes over all rows repeat if the budget allows)."""
+    import oracle
+    g = oracle.row_scale(case.grad_output, case.targets, case.reduce_loss, case.ignore_idx)
+    N = case.N
+    rng = np.random.default_rng(0)
+    order = rng.permutation(N)
+    done, chunk = 0, 64
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        s = done % N
+        rows = np.sort(order[s:s + chunk])
+        oracle.ce_forward(case.logits, case.targets, case.label_smoothing, case.ignore_idx, rows=rows)
+        oracle.ce_backward(case.logits, case.targets, g, case.label_smoothing, case.ignore_idx,
+                           rows=rows)
+        done += rows.size
+    el = time.perf_counter() - t0
+    return {"value": round(done / el, 1), "unit": "tokens/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{done} row passes over random rows of the {N}-row workload "
+                      f"(forward + backward, FP64), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-linear", action="store_true", help="skip the fused linear form")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", choices=["logits", "linear"], default=None,
+                    help="run one form only (for profiling)")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 1 GiB device copy (scale for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus "
+              f"{args.gpus}", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from vocabulary_cross_entropy_amd import accounting
+    from vocabulary_cross_entropy_amd import workloads as wl
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calib:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        print("[bench] copy calibration: 5 copies of 1 GiB done", file=sys.stderr, flush=True)
+    print("[bench] generating the (SQ,B,V) = (2048, 2, 128256) BF16 workload", file=sys.stderr,
+          flush=True)
+    case = wl.headline_logits()
+    res = None
+    if args.only in (None, "logits"):
+        res = bench_logits(case, args.steps, args.warmup)
+        print(f"[bench] logits CE: {res['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
+    lin = None
+    if not args.no_linear and args.only in (None, "linear"):
+        print("[bench] generating the linear workload M=4096 H=4096 V=131072", file=sys.stderr,
+              flush=True)
+        lcase = wl.linear_4k()
+        lin = bench_linear(lcase, max(3, min(args.steps, 10)), min(args.warmup, 3))
+        print(f"[bench] linear CE: {lin['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
+    if res is None:
+        print(json.dumps({"linear_ce": lin}))
+        return
+    cpu = None if args.no_cpu else cpu_baseline(case)
+    peak = accounting.HBM_PEAK_GBS
+    achieved = res["bwd_GBs"]
+    line = {
+        "metric": METRIC,
+        "value": round(res["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "logits_ce_fwd_bwd_sqbv_2048x2_v128256", "tokens": case.N,
+                   "V": case.V, "layout": "SQ,B,V", "storage": "bf16",
+                   "label_smoothing": case.label_smoothing, "reduce_loss": case.reduce_loss,
+                   "ignored_rows": case.meta["n_ignored"], "grad": "separate buffer"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": peak, "unit": "GB/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "ce_bwd (ce_backward row sweep)",
+                     "bytes_per_launch": res["bytes_bwd"]},
+        "cpu_baseline": cpu,
+        "phases": {"fwd_ms_median": round(res["fwd_ms_median"], 4),
+                   "bwd_ms_median": round(res["bwd_ms_median"], 4),
+                   "bwd_inplace_ms_median": round(res["bwd_inplace_ms_median"], 4),
+                   "fwd_GBs": round(res["fwd_GBs"], 1), "bwd_GBs": round(res["bwd_GBs"], 1),
+                   "fb_GBs": round(res["fb_GBs"], 1),
+                   "fb_frac_of_hbm_peak": round(res["fb_GBs"] / peak, 4)},
+        "linear_ce": lin,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

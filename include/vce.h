@@ -1,0 +1,179 @@
+/*
+ * libvce: fused cross-entropy over a large vocabulary for AMD MI355X (gfx950).
+ *
+ * Two forms of the same loss are exported.
+ *
+ *  1. Logits cross-entropy (ce_forward / ce_backward).  The operation is the
+ *     one of the TransformerEngine cross-entropy API page (Signature and I/O
+ *     Contract): logits of shape (B,SQ,V) or (SQ,B,V), integer targets of
+ *     shape (B,SQ) or (SQ,B), label smoothing, an optional averaged scalar
+ *     loss, an ignore index (default -100), loss in FP32 computed in FP32
+ *     whatever the input dtype (Description).  As in the TransformerEngine
+ *     PR "Minimize the memory usage of the fused cross entropy kernel"
+ *     (Changes; Sequence Diagram), the forward saves per-row statistics only,
+ *     the backward rebuilds the gradient from them, and the backward may write
+ *     the gradient over the logits ("overwrite_input", destructive reuse).
+ *
+ *  2. Fused linear cross-entropy (lce_forward / lce_backward).  The loss of
+ *     logits = X W^T computed tile by tile without storing the (M, V) logit
+ *     matrix: the cut-cross-entropy package description (linear_cross_entropy
+ *     of embeddings, classifier and labels) and the Liger-Kernel PR "Add SM100
+ *     tensor-parallel fused scaled cross entropy" (Summary: classifier GEMM
+ *     fused with NLL/LSE; Backward: dZ from recomputed logits, then dX and dW;
+ *     a caller-owned reusable workspace with a size query).
+ *
+ * Definitions (per row r with logits z, target t, smoothing eps, vocabulary V):
+ *     m = max_v z_v,  d = sum_v exp(z_v - m),  lse = m + ln d
+ *     q_v = (1 - eps) [v = t] + eps / V        (eps/V on every class)
+ *     loss_r = -sum_v q_v (z_v - lse) = (1-eps)(lse - z_t) + eps (lse - mean_v z_v)
+ *     grad[r, v] = g_r (exp(z_v - lse) - q_v)
+ *   g_r = grad_output[r] for per-token loss, grad_output[0] / n_valid for the
+ *   averaged loss.  Rows whose target equals ignore_idx have loss 0 and
+ *   gradient 0 and are excluded from the average (numerator and count).  With
+ *   no valid row the average is 0 (count taken as 1).  A target that is
+ *   neither ignore_idx nor in [0, V) yields NaN loss and NaN gradient for that
+ *   row (it cannot be reported without a device synchronisation).
+ *
+ * Saved statistics: stats is (N, 4) FP32 per row = (m, d, z_t, mean_v z_v),
+ * 16 bytes per row.  Rows that are ignored hold zeros there.
+ *
+ * Conventions for every entry point:
+ *  - All pointers are DEVICE pointers on the current HIP device, owned by
+ *    the caller.  The library never allocates, frees or synchronises and
+ *    keeps no state between calls.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  All work
+ *    is enqueued on it in order, so a call is safe inside HIP graph capture.
+ *  - Return value 0 means every kernel was enqueued.  A nonzero VCE_E* code
+ *    means the arguments were rejected and nothing was launched (VCE_EHIP: a
+ *    launch failed).  vce_strerror() names a code.
+ *  - N = d0 * d1 rows; N = 0 is a successful no-op (with reduce_loss the
+ *    averaged loss 0 and count 0 are still written).
+ */
+#ifndef VCE_H
+#define VCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum vce_status {
+  VCE_OK = 0,
+  VCE_EINVAL = 1,       /* null pointer, bad size, eps outside [0,1], negative stride */
+  VCE_EDTYPE = 2,       /* dtype not VCE_DTYPE_FP32 / VCE_DTYPE_BF16 */
+  VCE_EALIGN = 3,       /* pointer or stride not aligned as required */
+  VCE_EALIAS = 4,       /* overwrite_input set but grad != logits, or buffers overlap */
+  VCE_EWORKSPACE = 5,   /* workspace too small (see lce_workspace_size) */
+  VCE_EHIP = 6,         /* a kernel launch failed */
+  VCE_EUNSUPPORTED = 7  /* a size this build does not handle (see the entry point) */
+};
+
+enum vce_dtype { VCE_DTYPE_FP32 = 0, VCE_DTYPE_BF16 = 1 };
+
+/* Text for a status code (static storage). */
+const char* vce_strerror(int status);
+
+/*
+ * ce_forward: single-pass online-softmax forward of logits cross-entropy.
+ *
+ *  logits   (d0, d1, V) elements of `dtype` (FP32 or BF16).  Row (i0, i1)
+ *           starts at element i0*ls0 + i1*ls1; the V elements of a row are
+ *           contiguous.  (B,SQ,V) storage: d0=B, d1=SQ; (SQ,B,V): d0=SQ, d1=B;
+ *           any permuted view works through the two strides.  Must be aligned
+ *           to the element size.
+ *  targets  int64, element (i0, i1) at i0*ts0 + i1*ts1.
+ *  label_smoothing  eps in [0, 1].   reduce_loss  0 or 1.
+ *  ignore_idx       rows with this target are ignored (may lie in [0, V)).
+ *  loss_tok (N) FP32, always written, flattened row order r = i0*d1 + i1.
+ *  loss_mean  1 FP32: written iff reduce_loss (may be NULL otherwise).
+ *  stats    (N, 4) FP32 saved statistics (see above), always written.
+ *  n_valid  1 int32: count of non-ignored rows; required iff reduce_loss
+ *           (the backward of the averaged loss reads it), else may be NULL.
+ *  Kernels: one row sweep (one 256-thread workgroup per row), plus one
+ *  single-workgroup deterministic mean when reduce_loss or n_valid is given.
+ */
+int ce_forward(const void* logits, int dtype, int64_t d0, int64_t d1, int64_t V,
+               int64_t ls0, int64_t ls1, const int64_t* targets, int64_t ts0, int64_t ts1,
+               float label_smoothing, int reduce_loss, int64_t ignore_idx,
+               float* loss_tok, float* loss_mean, float* stats, int32_t* n_valid,
+               void* stream);
+
+/*
+ * ce_backward: rebuild the logits gradient from the saved statistics.
+ *
+ *  logits, dtype, d0, d1, V, ls0, ls1, targets, ts0, ts1, label_smoothing,
+ *  reduce_loss, ignore_idx: exactly as given to ce_forward.
+ *  grad     gradient, same dtype, shape and strides as logits (FP32 math,
+ *           stored rounded to nearest even for BF16).  Every element of every
+ *           row is written (ignored rows: zeros).
+ *  stats    (N, 4) from ce_forward.   n_valid: from ce_forward; read iff
+ *           reduce_loss.
+ *  grad_output  FP32: 1 element if reduce_loss, else (N) in flattened row
+ *           order.
+ *  overwrite_input  nonzero: grad must equal logits, and the logits are
+ *           replaced by the gradient (no extra buffer).  Zero: grad and
+ *           logits must not overlap (VCE_EALIAS otherwise).
+ */
+int ce_backward(const void* logits, void* grad, int dtype, int64_t d0, int64_t d1, int64_t V,
+                int64_t ls0, int64_t ls1, const int64_t* targets, int64_t ts0, int64_t ts1,
+                const float* stats, const int32_t* n_valid, const float* grad_output,
+                float label_smoothing, int reduce_loss, int64_t ignore_idx, int overwrite_input,
+                void* stream);
+
+/*
+ * lce_workspace_size: bytes of device workspace lce_forward and lce_backward
+ * need for an (M, H, V) problem (one buffer serves both; its contents need
+ * not survive between calls).  Analogue of the workspace query API of the
+ * Liger-Kernel PR (Summary).  Returns 0 for invalid sizes.
+ */
+size_t lce_workspace_size(int64_t M, int64_t H, int64_t V);
+
+/*
+ * lce_forward: loss of logits = X W^T without storing the logits.
+ *
+ *  X (M, H) and W (V, H): BF16, row-major, contiguous, 16-byte aligned;
+ *  H must be a multiple of 8 (VCE_EUNSUPPORTED otherwise).  FP32
+ *  accumulation on the matrix cores.
+ *  targets (M) int64 contiguous.   Outputs as ce_forward with N = M:
+ *  loss_tok (M), loss_mean (iff reduce_loss), stats (M, 4), n_valid.
+ *  workspace: at least lce_workspace_size(M, H, V) bytes, 256-byte aligned.
+ */
+int lce_forward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
+                const int64_t* targets, float label_smoothing, int reduce_loss,
+                int64_t ignore_idx, float* loss_tok, float* loss_mean, float* stats,
+                int32_t* n_valid, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * lce_backward: dX (M, H) and dW (V, H), BF16, overwritten (not accumulated).
+ *
+ *  X, W, M, H, V, targets, label_smoothing, reduce_loss, ignore_idx: as given
+ *  to lce_forward.  stats, n_valid: from lce_forward.  grad_output: FP32, 1
+ *  element if reduce_loss else (M).  The logits are recomputed chunk by chunk
+ *  over the vocabulary; the gradient of each chunk is held in the workspace.
+ */
+int lce_backward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
+                 const int64_t* targets, const float* stats, const int32_t* n_valid,
+                 const float* grad_output, float label_smoothing, int reduce_loss,
+                 int64_t ignore_idx, void* dX, void* dW, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/*
+ * vce_gemm_bf16: the matrix-core building block of the linear form, exported
+ * so it can be checked and timed on its own.  C (rows, cols) FP32 row-major
+ * with leading dimension ldc:  C[i][j] = sum_k P(i, k) Q(j, k).
+ *  p_kmajor = 1: P(i, k) = P[i*ldp + k]  (row-major rows x K)
+ *  p_kmajor = 0: P(i, k) = P[k*ldp + i]  (row-major K x rows)
+ *  likewise for Q.  BF16 operands, FP32 accumulation.  rows and cols any
+ *  size; K a multiple of 8; ldp, ldq multiples of 8; 16-byte aligned.
+ */
+int vce_gemm_bf16(const void* P, int p_kmajor, int64_t ldp, const void* Q, int q_kmajor,
+                  int64_t ldq, int64_t rows, int64_t cols, int64_t K, float* C, int64_t ldc,
+                  void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VCE_H */

@@ -271,7 +271,9 @@ def test_round_bf16_against_torch():
     got = oracle.round_bf16(x.astype(np.float64))
     np.testing.assert_array_equal(got, ref)
     # and the input generator's FP32 -> BF16 rounding agrees with torch too
-    np.testing.assert_array_equal(wl.f32_to_bf16_bits(x), ref)
+    np.testing.assert_array_equal(wl.f32_to_bf16_bits_np(x), ref)
+    big = np.tile(x, 25)  # large enough for the torch path
+    np.testing.assert_array_equal(wl.f32_to_bf16_bits(big), wl.f32_to_bf16_bits_np(big))
 
 
 def test_layouts_and_strides():

@@ -1,0 +1,255 @@
+"""Parity of the HIP logits cross-entropy (ce_forward / ce_backward) with the
+FP64 oracle, element by element, through the C-ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import vocabulary_cross_entropy_amd as vce
+from vocabulary_cross_entropy_amd import workloads as wl
+from vce_testutil import (assert_grad_bf16, assert_grad_fp32, assert_loss_close, grad_terms,
+                          to_device, to_host_bits)
+
+pytestmark = pytest.mark.gpu
+IGN = wl.IGNORE_INDEX
+
+
+def _say(msg):
+    print(f"[parity-ce] {msg}", flush=True)
+
+
+def run_case(case: wl.LogitsCase, overwrite: bool = False, logits_dev=None):
+    """Forward and backward on the GPU; returns host copies of everything."""
+    z = to_device(case.logits, case.dtype) if logits_dev is None else logits_dev
+    t = torch.from_numpy(case.targets).cuda()
+    go = torch.from_numpy(case.grad_output).cuda()
+    loss, loss_mean, stats, n_valid = vce.ce_forward(z, t, case.label_smoothing, case.reduce_loss,
+                                                     case.ignore_idx)
+    grad = vce.ce_backward(z, t, stats, n_valid, go.reshape(-1) if case.reduce_loss else go,
+                           case.label_smoothing, case.reduce_loss, case.ignore_idx,
+                           overwrite_input=overwrite)
+    torch.cuda.synchronize()
+    out = dict(loss=loss.cpu().numpy(), stats=stats.cpu().numpy().reshape(-1, 4),
+               grad=to_host_bits(grad))
+    if case.reduce_loss:
+        out["loss_mean"] = float(loss_mean.item())
+        out["n_valid"] = int(n_valid.item())
+    return out
+
+
+def check_forward(case, out):
+    ref_loss, ref_stats, _ = oracle.ce_forward(case.logits, case.targets, case.label_smoothing,
+                                               case.ignore_idx)
+    err = assert_loss_close(out["loss"], ref_loss)
+    valid = (case.targets.reshape(-1) != case.ignore_idx) & np.isfinite(ref_loss)
+    st = out["stats"][valid]
+    rs = ref_stats[valid]
+    # row max and target logit are exact input values: bitwise equal
+    np.testing.assert_array_equal(st[:, 0], rs[:, 0].astype(np.float32))
+    np.testing.assert_array_equal(st[:, 2], rs[:, 2].astype(np.float32))
+    np.testing.assert_allclose(st[:, 1], rs[:, 1], rtol=2e-5)
+    np.testing.assert_allclose(st[:, 3], rs[:, 3], rtol=0, atol=1e-5)
+    if case.reduce_loss:
+        ref_mean = oracle.mean_loss(ref_loss, case.targets, case.ignore_idx)
+        assert abs(out["loss_mean"] - ref_mean) <= 1e-4 + 1e-5 * abs(ref_mean)
+        assert out["n_valid"] == oracle.n_valid(case.targets, case.ignore_idx)
+    return err
+
+
+def check_backward(case, out, chunk=256):
+    g = oracle.row_scale(case.grad_output, case.targets, case.reduce_loss, case.ignore_idx)
+    N, V = case.N, case.V
+    gpu = out["grad"].reshape(N, V)
+    tflat = case.targets.reshape(-1)
+    worst = 0
+    band = {}
+    for s in range(0, N, chunk):
+        rows = np.arange(s, min(N, s + chunk))
+        ref = oracle.ce_backward(case.logits, case.targets, g, case.label_smoothing,
+                                 case.ignore_idx, rows=rows)
+        if case.dtype == wl.DTYPE_BF16:
+            T = grad_terms(ref, g[rows], tflat[rows], case.label_smoothing, case.ignore_idx)
+            worst = max(worst, assert_grad_bf16(gpu[rows], ref, T, f"grad rows {s}..", band))
+        else:
+            worst = max(worst, assert_grad_fp32(gpu[rows], ref, f"grad rows {s}.."))
+    if band:
+        _say(f"grad: {band['elements']} elements, worst {band['worst_ulp']} ulp outside the "
+             f"cancellation band; band {band['band']} elements ({band['band_beyond_1ulp']} beyond "
+             f"1 ulp, worst err/T {band['worst_band_err_over_T']:.2e})")
+    return worst
+
+
+@pytest.mark.parametrize("eps", [0.0, 0.1])
+@pytest.mark.parametrize("reduce_loss", [False, True])
+def test_tiny_fp32(eps, reduce_loss):
+    case = wl.tiny_logits(eps, reduce_loss)
+    _say(case.name)
+    out = run_case(case)
+    check_forward(case, out)
+    check_backward(case, out)
+
+
+def test_bsqv_v32000_bf16_full():
+    case = wl.medium_logits()
+    _say(case.name)
+    out = run_case(case)
+    err = check_forward(case, out)
+    worst = check_backward(case, out, chunk=512)
+    _say(f"max loss err {err:.2e}, worst grad ulp {worst}")
+
+
+@pytest.fixture(scope="module")
+def headline():
+    _say("generating the (SQ,B,V) = (2048, 2, 128256) workload")
+    return wl.headline_logits()
+
+
+def test_sqbv_v128256_bf16_separate(headline):
+    _say(headline.name + " separate gradient buffer")
+    out = run_case(headline)
+    err = check_forward(headline, out)
+    worst = check_backward(headline, out, chunk=512)
+    _say(f"max loss err {err:.2e}, worst grad ulp {worst}")
+
+
+def test_sqbv_v128256_bf16_in_place_equals_separate(headline):
+    _say(headline.name + " in place vs separate")
+    sep = run_case(headline)
+    inp = run_case(headline, overwrite=True)
+    np.testing.assert_array_equal(inp["grad"], sep["grad"])
+    np.testing.assert_array_equal(inp["loss"], sep["loss"])
+
+
+@pytest.mark.parametrize("V,dtype", [(1, "fp32"), (7, "bf16"), (9, "fp32"), (1001, "bf16"),
+                                     (1003, "fp32"), (4099, "bf16"), (33333, "bf16")])
+def test_ragged_vocab(V, dtype):
+    # V not a multiple of the vector width: rows start at every 16-byte phase.
+    case = wl.make_logits(2000 + V, 3, 5, V, dtype=dtype, sigma=3.0, ignore_count=2,
+                          label_smoothing=0.05, reduce_loss=False, grad_output="random")
+    _say(f"ragged V={V} {dtype}")
+    out = run_case(case)
+    check_forward(case, out)
+    check_backward(case, out)
+
+
+def test_fp32_large_vocab():
+    case = wl.make_logits(2101, 8, 8, 128256, dtype="fp32", sigma=4.0, ignore_count=3,
+                          target_boost=8.0, label_smoothing=0.1, reduce_loss=True)
+    _say("fp32 V=128256")
+    out = run_case(case)
+    check_forward(case, out)
+    check_backward(case, out)
+
+
+def test_many_short_rows():
+    case = wl.make_logits(2102, 70, 1000, 64, dtype="bf16", sigma=2.0, ignore_frac=0.1,
+                          label_smoothing=0.2, reduce_loss=True)
+    _say("70000 rows of V=64")
+    out = run_case(case)
+    check_forward(case, out)
+    check_backward(case, out, chunk=8192)
+
+
+def test_strided_layout_view():
+    # (SQ,B,V) storage passed as a (B,SQ,V) view: the strides carry the layout.
+    case = wl.make_logits(2103, 64, 4, 5000, dtype="bf16", sigma=3.0, ignore_count=5,
+                          label_smoothing=0.1, reduce_loss=True, layout="SQ,B")
+    _say("transposed (B,SQ,V) view of (SQ,B,V) storage")
+    z_sb = to_device(case.logits, "bf16")
+    t_sb = torch.from_numpy(case.targets).cuda()
+    zv, tv = z_sb.transpose(0, 1), t_sb.transpose(0, 1)
+    go = torch.ones(1, device="cuda")
+    loss, mean, stats, nv = vce.ce_forward(zv, tv, 0.1, True)
+    grad = vce.ce_backward(zv, tv, stats, nv, go, 0.1, True)
+    torch.cuda.synchronize()
+    ref_loss, _, _ = oracle.ce_forward(case.logits.transpose(1, 0, 2), case.targets.T, 0.1)
+    assert_loss_close(loss.cpu().numpy(), ref_loss)
+    g = oracle.row_scale(np.ones(1), case.targets, True)
+    ref_grad = oracle.ce_backward(case.logits.transpose(1, 0, 2), case.targets.T, g, 0.1)
+    gb = to_host_bits(grad.contiguous()).reshape(-1, 5000)
+    T = grad_terms(ref_grad, g.reshape(64, 4).T.reshape(-1), case.targets.T.reshape(-1), 0.1, IGN)
+    assert_grad_bf16(gb, ref_grad, T)
+    assert grad.stride() == zv.stride()
+
+
+def test_all_rows_ignored():
+    case = wl.make_logits(2104, 2, 16, 300, dtype="bf16", sigma=1.0, ignore_count=32,
+                          reduce_loss=True)
+    out = run_case(case)
+    assert out["loss_mean"] == 0.0 and out["n_valid"] == 0
+    assert np.all(out["loss"] == 0.0)
+    assert np.all((out["grad"] & 0x7FFF) == 0)
+
+
+def test_target_out_of_range_and_ignore_inside_vocab():
+    case = wl.make_logits(2105, 1, 6, 500, dtype="fp32", sigma=2.0, reduce_loss=False)
+    case.targets[0, :] = [3, 500, -1, 7, 42, 7]
+    case.ignore_idx = 7
+    out = run_case(case)
+    ref_loss, _, _ = oracle.ce_forward(case.logits, case.targets, 0.0, ignore_idx=7)
+    assert_loss_close(out["loss"], ref_loss)
+    flat = out["loss"].reshape(-1)
+    assert np.isnan(flat[1]) and np.isnan(flat[2])
+    assert flat[3] == 0.0 and flat[5] == 0.0
+    check_backward(case, out)
+
+
+def test_negative_infinity_columns():
+    case = wl.make_logits(2106, 2, 4, 2000, dtype="fp32", sigma=2.0, reduce_loss=False)
+    case.logits[:, :, 1990:] = -np.inf
+    case.targets[case.targets >= 1990] = 5
+    out = run_case(case)
+    check_forward(case, out)
+    check_backward(case, out)
+
+
+def test_deterministic():
+    case = wl.make_logits(2107, 8, 64, 32000, dtype="bf16", sigma=3.0, ignore_frac=0.05,
+                          label_smoothing=0.1, reduce_loss=True)
+    a = run_case(case)
+    b = run_case(case)
+    for k in ("loss", "stats", "grad"):
+        np.testing.assert_array_equal(a[k], b[k])
+    assert a["loss_mean"] == b["loss_mean"]
+
+
+def test_empty_batch():
+    z = torch.empty((0, 4, 100), dtype=torch.bfloat16, device="cuda")
+    t = torch.empty((0, 4), dtype=torch.int64, device="cuda")
+    loss, mean, stats, nv = vce.ce_forward(z, t, 0.0, True)
+    torch.cuda.synchronize()
+    assert mean.item() == 0.0 and nv.item() == 0 and loss.numel() == 0
+
+
+def test_graph_capture_replay():
+    # Every call only enqueues kernels on the given stream, so forward and
+    # backward can be captured and replayed.
+    case = wl.make_logits(2108, 4, 256, 8000, dtype="bf16", sigma=3.0, ignore_frac=0.05,
+                          label_smoothing=0.1, reduce_loss=True)
+    z = to_device(case.logits, "bf16")
+    t = torch.from_numpy(case.targets).cuda()
+    go = torch.ones(1, device="cuda")
+    loss = torch.empty((4, 256), device="cuda")
+    mean = torch.empty((), device="cuda")
+    stats = torch.empty((4, 256, 4), device="cuda")
+    nv = torch.empty((), dtype=torch.int32, device="cuda")
+    grad = torch.empty_like(z)
+    out = (loss, mean, stats, nv)
+    vce.ce_forward(z, t, 0.1, True, out=out)
+    vce.ce_backward(z, t, stats, nv, go, 0.1, True, grad=grad)
+    torch.cuda.synchronize()
+    ref = (loss.clone(), mean.clone(), grad.clone())
+    s = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        loss.zero_(); grad.zero_()
+        with torch.cuda.graph(graph, stream=s):
+            vce.ce_forward(z, t, 0.1, True, out=out, stream=s)
+            vce.ce_backward(z, t, stats, nv, go, 0.1, True, grad=grad, stream=s)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        loss.zero_(); mean.zero_(); grad.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(loss, ref[0]) and torch.equal(mean, ref[1]) and torch.equal(grad, ref[2])

@@ -1,0 +1,238 @@
+"""Thin Python binding of libvce (include/vce.h) over ctypes.
+
+Argument marshalling only: torch tensors supply device memory and the HIP
+stream, every step of the computation runs in the library's HIP kernels.
+There is no fallback: if ``libvce.so`` is missing or the device is not a GPU,
+the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvce.so")
+
+DTYPE_FP32 = 0
+DTYPE_BF16 = 1
+
+STATUS = {0: "VCE_OK", 1: "VCE_EINVAL", 2: "VCE_EDTYPE", 3: "VCE_EALIGN", 4: "VCE_EALIAS",
+          5: "VCE_EWORKSPACE", 6: "VCE_EHIP", 7: "VCE_EUNSUPPORTED"}
+
+# (name, restype, argtypes) for every symbol include/vce.h declares.
+_I64, _I32, _F32, _VP, _SZ = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+SIGNATURES = {
+    "vce_strerror": (ctypes.c_char_p, [_I32]),
+    "ce_forward": (_I32, [_VP, _I32, _I64, _I64, _I64, _I64, _I64, _VP, _I64, _I64, _F32, _I32, _I64,
+                          _VP, _VP, _VP, _VP, _VP]),
+    "ce_backward": (_I32, [_VP, _VP, _I32, _I64, _I64, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _VP,
+                           _VP, _F32, _I32, _I64, _I32, _VP]),
+    "lce_workspace_size": (_SZ, [_I64, _I64, _I64]),
+    "lce_forward": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _F32, _I32, _I64, _VP, _VP, _VP, _VP,
+                           _VP, _SZ, _VP]),
+    "lce_backward": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _F32, _I32, _I64, _VP,
+                            _VP, _VP, _SZ, _VP]),
+    "vce_gemm_bf16": (_I32, [_VP, _I32, _I64, _VP, _I32, _I64, _I64, _I64, _I64, _VP, _I64, _VP]),
+}
+
+_lib = None
+
+
+class VceError(RuntimeError):
+    def __init__(self, name: str, code: int, text: str):
+        super().__init__(f"{name} failed: {STATUS.get(code, code)} ({text})")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """Load libvce.so (built in-tree by ``python -m vocabulary_cross_entropy_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m vocabulary_cross_entropy_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().vce_strerror(code).decode()
+
+
+def _check(name: str, code: int):
+    if code != 0:
+        raise VceError(name, code, strerror(code))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DTYPE_FP32
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise RuntimeError("libvce runs on the GPU only: tensors must be on a HIP device")
+
+
+def _logits3d(logits: torch.Tensor, targets: torch.Tensor):
+    if logits.dim() == 2:
+        logits = logits.unsqueeze(0)
+        targets = targets.unsqueeze(0)
+    if logits.dim() != 3 or tuple(targets.shape) != tuple(logits.shape[:2]):
+        raise ValueError("logits must be (d0, d1, V) with targets (d0, d1)")
+    if logits.stride(2) != 1:
+        raise ValueError("the vocabulary dimension of logits must be contiguous")
+    if targets.dtype != torch.int64:
+        raise TypeError("targets must be int64")
+    return logits, targets
+
+
+def ce_forward(logits: torch.Tensor, targets: torch.Tensor, label_smoothing: float = 0.0,
+               reduce_loss: bool = False, ignore_idx: int = -100, *, stream=None, out=None):
+    """Forward of logits cross-entropy.  Returns (loss_tok, loss_mean, stats, n_valid);
+    loss_mean and n_valid are None unless reduce_loss."""
+    logits, targets = _logits3d(logits, targets)
+    _need_cuda(logits, targets)
+    d0, d1, V = logits.shape
+    dev = logits.device
+    if out is None:
+        loss_tok = torch.empty((d0, d1), dtype=torch.float32, device=dev)
+        stats = torch.empty((d0, d1, 4), dtype=torch.float32, device=dev)
+        loss_mean = torch.empty((), dtype=torch.float32, device=dev) if reduce_loss else None
+        n_valid = torch.empty((), dtype=torch.int32, device=dev) if reduce_loss else None
+    else:
+        loss_tok, loss_mean, stats, n_valid = out
+    rc = lib().ce_forward(_ptr(logits), _dtype_code(logits), d0, d1, V, logits.stride(0),
+                          logits.stride(1), _ptr(targets), targets.stride(0), targets.stride(1),
+                          float(label_smoothing), int(bool(reduce_loss)), int(ignore_idx),
+                          _ptr(loss_tok), _ptr(loss_mean), _ptr(stats), _ptr(n_valid),
+                          _stream(stream))
+    _check("ce_forward", rc)
+    return loss_tok, loss_mean, stats, n_valid
+
+
+def ce_backward(logits: torch.Tensor, targets: torch.Tensor, stats: torch.Tensor,
+                n_valid: torch.Tensor | None, grad_output: torch.Tensor,
+                label_smoothing: float = 0.0, reduce_loss: bool = False, ignore_idx: int = -100,
+                overwrite_input: bool = False, *, grad: torch.Tensor | None = None, stream=None):
+    """Gradient of logits cross-entropy rebuilt from ``stats``.  With
+    ``overwrite_input`` the logits tensor itself receives the gradient."""
+    logits, targets = _logits3d(logits, targets)
+    _need_cuda(logits, targets, stats, grad_output)
+    d0, d1, V = logits.shape
+    if overwrite_input:
+        grad = logits
+    elif grad is None:
+        grad = torch.empty_strided(logits.shape, logits.stride(), dtype=logits.dtype,
+                                   device=logits.device)
+    elif grad.dim() == 2:
+        grad = grad.unsqueeze(0)
+    if tuple(grad.stride()) != tuple(logits.stride()) or grad.dtype != logits.dtype:
+        raise ValueError("grad must have the dtype and strides of logits")
+    rc = lib().ce_backward(_ptr(logits), _ptr(grad), _dtype_code(logits), d0, d1, V,
+                           logits.stride(0), logits.stride(1), _ptr(targets), targets.stride(0),
+                           targets.stride(1), _ptr(stats), _ptr(n_valid), _ptr(grad_output),
+                           float(label_smoothing), int(bool(reduce_loss)), int(ignore_idx),
+                           int(bool(overwrite_input)), _stream(stream))
+    _check("ce_backward", rc)
+    return grad
+
+
+def lce_workspace_size(M: int, H: int, V: int) -> int:
+    return int(lib().lce_workspace_size(M, H, V))
+
+
+def lce_workspace(M: int, H: int, V: int, device="cuda") -> torch.Tensor:
+    n = lce_workspace_size(M, H, V)
+    if n == 0:
+        raise ValueError(f"no workspace plan for M={M}, H={H}, V={V}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _check_linear(X, W, targets):
+    if X.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
+        raise TypeError("X and W must be bfloat16")
+    if not (X.is_contiguous() and W.is_contiguous() and targets.is_contiguous()):
+        raise ValueError("X, W and targets must be contiguous")
+    if X.dim() != 2 or W.dim() != 2 or X.shape[1] != W.shape[1] or targets.numel() != X.shape[0]:
+        raise ValueError("X (M,H), W (V,H), targets (M)")
+    if targets.dtype != torch.int64:
+        raise TypeError("targets must be int64")
+    _need_cuda(X, W, targets)
+
+
+def lce_forward(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
+                label_smoothing: float = 0.0, reduce_loss: bool = True, ignore_idx: int = -100,
+                *, workspace: torch.Tensor | None = None, stream=None, out=None):
+    """Fused linear cross-entropy forward.  Returns (loss_tok, loss_mean, stats, n_valid)."""
+    _check_linear(X, W, targets)
+    M, H = X.shape
+    V = W.shape[0]
+    dev = X.device
+    if workspace is None:
+        workspace = lce_workspace(M, H, V, dev)
+    if out is None:
+        loss_tok = torch.empty(M, dtype=torch.float32, device=dev)
+        stats = torch.empty((M, 4), dtype=torch.float32, device=dev)
+        loss_mean = torch.empty((), dtype=torch.float32, device=dev) if reduce_loss else None
+        n_valid = torch.empty((), dtype=torch.int32, device=dev) if reduce_loss else None
+    else:
+        loss_tok, loss_mean, stats, n_valid = out
+    rc = lib().lce_forward(_ptr(X), _ptr(W), M, H, V, _ptr(targets), float(label_smoothing),
+                           int(bool(reduce_loss)), int(ignore_idx), _ptr(loss_tok),
+                           _ptr(loss_mean), _ptr(stats), _ptr(n_valid), _ptr(workspace),
+                           workspace.numel(), _stream(stream))
+    _check("lce_forward", rc)
+    return loss_tok, loss_mean, stats, n_valid
+
+
+def lce_backward(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, stats: torch.Tensor,
+                 n_valid: torch.Tensor | None, grad_output: torch.Tensor,
+                 label_smoothing: float = 0.0, reduce_loss: bool = True, ignore_idx: int = -100,
+                 *, workspace: torch.Tensor | None = None, dX: torch.Tensor | None = None,
+                 dW: torch.Tensor | None = None, stream=None):
+    """Fused linear cross-entropy backward.  Returns (dX, dW), BF16."""
+    _check_linear(X, W, targets)
+    M, H = X.shape
+    V = W.shape[0]
+    if workspace is None:
+        workspace = lce_workspace(M, H, V, X.device)
+    dX = torch.empty_like(X) if dX is None else dX
+    dW = torch.empty_like(W) if dW is None else dW
+    rc = lib().lce_backward(_ptr(X), _ptr(W), M, H, V, _ptr(targets), _ptr(stats), _ptr(n_valid),
+                            _ptr(grad_output), float(label_smoothing), int(bool(reduce_loss)),
+                            int(ignore_idx), _ptr(dX), _ptr(dW), _ptr(workspace),
+                            workspace.numel(), _stream(stream))
+    _check("lce_backward", rc)
+    return dX, dW
+
+
+def gemm_bf16(P: torch.Tensor, p_kmajor: bool, Q: torch.Tensor, q_kmajor: bool, rows: int,
+              cols: int, K: int, *, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """C[i, j] = sum_k P(i, k) Q(j, k) with the library's matrix-core GEMM."""
+    _need_cuda(P, Q)
+    C = torch.empty((rows, cols), dtype=torch.float32, device=P.device) if out is None else out
+    rc = lib().vce_gemm_bf16(_ptr(P), int(p_kmajor), P.stride(0), _ptr(Q), int(q_kmajor),
+                             Q.stride(0), rows, cols, K, _ptr(C), C.stride(0), _stream(stream))
+    _check("vce_gemm_bf16", rc)
+    return C

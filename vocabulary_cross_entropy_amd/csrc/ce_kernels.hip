@@ -1,0 +1,367 @@
+// Logits cross-entropy kernels for gfx950: the statistics-saving forward row
+// sweep, the deterministic mean, and the gradient-rebuilding backward sweep.
+//
+// What they compute follows the TransformerEngine cross-entropy API page
+// (Description: fused online-softmax, FP32 math for BF16/FP32 input; I/O
+// Contract) and the TransformerEngine PR that saves statistics instead of the
+// derivative (Changes; Sequence Diagram: one forward kernel on a single GPU,
+// backward rebuilds the gradient from input, targets, stats and grad_output).
+//
+// Design for CDNA4: one 256-thread workgroup (4 wavefronts) per row; every
+// lane streams 16-byte vectors (8 BF16 or 4 FP32) with four loads in flight
+// before any arithmetic; one exponential per logit (the running max is
+// updated once per 4-vector chunk, not per element); the row state is merged
+// across the wavefront with butterfly shuffles and across wavefronts in LDS.
+#include "vce_device.h"
+#include "vce_internal.h"
+
+namespace vce {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kUnroll = 4;
+
+template <int DT>
+struct Elem;
+template <>
+struct Elem<0> {  // FP32
+  using T = float;
+  static constexpr int kVec = 4;
+  __device__ static float load(const float* p) { return *p; }
+};
+template <>
+struct Elem<1> {  // BF16
+  using T = uint16_t;
+  static constexpr int kVec = 8;
+  __device__ static float load(const uint16_t* p) { return from_bf16(*p); }
+};
+
+// Row geometry: elements [0, head) and [tail0, V) are handled one by one, the
+// 16-byte aligned body [head, tail0) as vectors.
+struct RowSplit {
+  int64_t head, nvec, tail0;
+};
+
+template <int DT>
+__device__ __forceinline__ RowSplit split_row(const void* row, int64_t V) {
+  constexpr int es = sizeof(typename Elem<DT>::T);
+  constexpr int vec = Elem<DT>::kVec;
+  uintptr_t a = reinterpret_cast<uintptr_t>(row);
+  int64_t head = (int64_t)(((16u - (a & 15u)) & 15u) / es);
+  if (head > V) head = V;
+  RowSplit s;
+  s.head = head;
+  s.nvec = (V - head) / vec;
+  s.tail0 = head + s.nvec * vec;
+  return s;
+}
+
+// Values of one 16-byte vector as floats.
+template <int DT>
+__device__ __forceinline__ void unpack(const u32x4_t& w, float* z);
+template <>
+__device__ __forceinline__ void unpack<0>(const u32x4_t& w, float* z) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) z[i] = __uint_as_float(w[i]);
+}
+template <>
+__device__ __forceinline__ void unpack<1>(const u32x4_t& w, float* z) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    z[2 * i] = bf16_lo(w[i]);
+    z[2 * i + 1] = bf16_hi(w[i]);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float vec_sum(const u32x4_t& w, const float* z, float acc);
+template <>
+__device__ __forceinline__ float vec_sum<0>(const u32x4_t&, const float* z, float acc) {
+  return acc + ((z[0] + z[1]) + (z[2] + z[3]));
+}
+template <>
+__device__ __forceinline__ float vec_sum<1>(const u32x4_t& w, const float*, float acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc = bf16_pair_sum(w[i], acc);
+  return acc;
+}
+
+// Fold n vectors (already loaded) into the running state.
+template <int DT, int N>
+__device__ __forceinline__ void fold(LseState& st, const u32x4_t* w) {
+  constexpr int vec = Elem<DT>::kVec;
+  float z[N][vec];
+#pragma unroll
+  for (int u = 0; u < N; ++u) unpack<DT>(w[u], z[u]);
+  float cm = z[0][0];
+#pragma unroll
+  for (int u = 0; u < N; ++u)
+#pragma unroll
+    for (int i = 0; i < vec; ++i) cm = fmaxf(cm, z[u][i]);
+  const float m_new = fmaxf(st.m, cm);
+  const float mref = (m_new == kNegInf) ? 0.0f : m_new;
+  const float mL = mref * kLog2e;
+  float dpart[N];
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < vec; ++i) acc += exp2_hw(__builtin_fmaf(z[u][i], kLog2e, -mL));
+    dpart[u] = acc;
+  }
+  float dsum = dpart[0];
+#pragma unroll
+  for (int u = 1; u < N; ++u) dsum += dpart[u];
+  st.d = st.d * exp2_hw((st.m - mref) * kLog2e) + dsum;
+#pragma unroll
+  for (int u = 0; u < N; ++u) st.s = vec_sum<DT>(w[u], z[u], st.s);
+  st.m = m_new;
+}
+
+__device__ __forceinline__ LseState block_reduce(LseState st, LseState* sh) {
+  lse_wave_reduce(st);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) sh[wave] = st;
+  __syncthreads();
+  LseState r = sh[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) lse_merge(r, sh[w]);
+  return r;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void ce_fwd_kernel(CeFwdParams p) {
+  using T = typename Elem<DT>::T;
+  __shared__ LseState sh[kWaves];
+  const int64_t r = blockIdx.x;
+  const int64_t i0 = r / p.d1, i1 = r - i0 * p.d1;
+  const int64_t t = p.targets[i0 * p.ts0 + i1 * p.ts1];
+  const int tid = threadIdx.x;
+  if (t == p.ignore_idx) {
+    if (tid == 0) {
+      p.loss_tok[r] = 0.0f;
+      *reinterpret_cast<f32x4_t*>(p.stats + 4 * r) = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    return;
+  }
+  const int64_t V = p.V;
+  const T* row = static_cast<const T*>(p.logits) + i0 * p.ls0 + i1 * p.ls1;
+  const bool t_ok = (t >= 0 && t < V);
+  float zt = __builtin_nanf("");
+  if (tid == 0 && t_ok) zt = Elem<DT>::load(row + t);
+
+  const RowSplit rs = split_row<DT>(row, V);
+  LseState st = {kNegInf, 0.0f, 0.0f};
+  {
+    const int64_t nscal = rs.head + (V - rs.tail0);
+    if (tid < nscal) {
+      const int64_t idx = tid < rs.head ? tid : rs.tail0 + (tid - rs.head);
+      const float z = Elem<DT>::load(row + idx);
+      st.m = z;
+      st.d = (z == kNegInf) ? 0.0f : 1.0f;
+      st.s = z;
+    }
+  }
+  const u32x4_t* vrow = reinterpret_cast<const u32x4_t*>(row + rs.head);
+  int64_t j = tid;
+  for (; j + (kUnroll - 1) * kThreads < rs.nvec; j += kUnroll * kThreads) {
+    u32x4_t w[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) w[u] = __builtin_nontemporal_load(vrow + j + u * kThreads);
+    fold<DT, kUnroll>(st, w);
+  }
+  for (; j < rs.nvec; j += kThreads) {
+    u32x4_t w[1] = {__builtin_nontemporal_load(vrow + j)};
+    fold<DT, 1>(st, w);
+  }
+  const LseState tot = block_reduce(st, sh);
+  if (tid == 0) {
+    const float eps = p.eps;
+    const float lse_shift = log2_hw(tot.d) * kLn2;  // lse - m
+    const float mean = tot.s / (float)V;
+    float loss = lse_shift - (1.0f - eps) * (zt - tot.m);
+    if (eps != 0.0f) loss -= eps * (mean - tot.m);
+    p.loss_tok[r] = t_ok ? loss : __builtin_nanf("");
+    *reinterpret_cast<f32x4_t*>(p.stats + 4 * r) = f32x4_t{tot.m, tot.d, zt, mean};
+  }
+}
+
+// Averaged loss over non-ignored rows and their count, one workgroup, fixed
+// summation order (bitwise reproducible).
+__global__ __launch_bounds__(1024) void ce_mean_kernel(CeMeanParams p) {
+  __shared__ double ssum[1024];
+  __shared__ int64_t scnt[1024];
+  double sum = 0.0;
+  int64_t cnt = 0;
+  for (int64_t r = threadIdx.x; r < p.N; r += 1024) {
+    const int64_t i0 = r / p.d1, i1 = r - i0 * p.d1;
+    if (p.targets[i0 * p.ts0 + i1 * p.ts1] != p.ignore_idx) {
+      sum += (double)p.loss_tok[r];
+      ++cnt;
+    }
+  }
+  ssum[threadIdx.x] = sum;
+  scnt[threadIdx.x] = cnt;
+  __syncthreads();
+  for (int s = 512; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) {
+      ssum[threadIdx.x] += ssum[threadIdx.x + s];
+      scnt[threadIdx.x] += scnt[threadIdx.x + s];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int64_t c = scnt[0];
+    if (p.loss_mean) p.loss_mean[0] = (float)(ssum[0] / (double)(c > 0 ? c : 1));
+    if (p.n_valid) p.n_valid[0] = (int32_t)c;
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void store_vec(void* dst, const float* g);
+template <>
+__device__ __forceinline__ void store_vec<0>(void* dst, const float* g) {
+  u32x4_t w = {__float_as_uint(g[0]), __float_as_uint(g[1]), __float_as_uint(g[2]),
+               __float_as_uint(g[3])};
+  __builtin_nontemporal_store(w, static_cast<u32x4_t*>(dst));
+}
+template <>
+__device__ __forceinline__ void store_vec<1>(void* dst, const float* g) {
+  u32x4_t w = {pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]), pack_bf16x2(g[4], g[5]),
+               pack_bf16x2(g[6], g[7])};
+  __builtin_nontemporal_store(w, static_cast<u32x4_t*>(dst));
+}
+
+template <int DT>
+__device__ __forceinline__ void store_one(typename Elem<DT>::T* dst, float g);
+template <>
+__device__ __forceinline__ void store_one<0>(float* dst, float g) { *dst = g; }
+template <>
+__device__ __forceinline__ void store_one<1>(uint16_t* dst, float g) { *dst = to_bf16(g); }
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void ce_bwd_kernel(CeBwdParams p) {
+  using T = typename Elem<DT>::T;
+  constexpr int vec = Elem<DT>::kVec;
+  const int64_t r = blockIdx.x;
+  const int64_t i0 = r / p.d1, i1 = r - i0 * p.d1;
+  const int64_t t = p.targets[i0 * p.ts0 + i1 * p.ts1];
+  const int tid = threadIdx.x;
+  const int64_t V = p.V;
+  const int64_t off = i0 * p.ls0 + i1 * p.ls1;
+  const T* row = static_cast<const T*>(p.logits) + off;
+  T* grow = static_cast<T*>(p.grad) + off;
+  const RowSplit rs = split_row<DT>(grow, V);
+  u32x4_t* gvec = reinterpret_cast<u32x4_t*>(grow + rs.head);
+
+  if (t == p.ignore_idx || !(t >= 0 && t < V)) {
+    // Ignored row: zero gradient.  Target out of range: NaN gradient.
+    const float fill = (t == p.ignore_idx) ? 0.0f : __builtin_nanf("");
+    float f[vec];
+#pragma unroll
+    for (int i = 0; i < vec; ++i) f[i] = fill;
+    const int64_t nscal = rs.head + (V - rs.tail0);
+    if (tid < nscal) {
+      const int64_t idx = tid < rs.head ? tid : rs.tail0 + (tid - rs.head);
+      store_one<DT>(grow + idx, fill);
+    }
+    for (int64_t j = tid; j < rs.nvec; j += kThreads) store_vec<DT>(gvec + j, f);
+    return;
+  }
+
+  float g;
+  if (p.reduce_loss) {
+    const int32_t nv = p.n_valid[0];
+    g = p.grad_output[0] / (float)(nv > 0 ? nv : 1);
+  } else {
+    g = p.grad_output[r];
+  }
+  const f32x4_t sv = *reinterpret_cast<const f32x4_t*>(p.stats + 4 * r);
+  const float m = sv[0], d = sv[1];
+  const float mref = (m == kNegInf) ? 0.0f : m;
+  const float mL = mref * kLog2e;
+  const float gs = g / d;
+  const float goff = g * (p.eps / (float)V);
+  const float gt = g * (1.0f - p.eps);
+
+  {
+    const int64_t nscal = rs.head + (V - rs.tail0);
+    if (tid < nscal) {
+      const int64_t idx = tid < rs.head ? tid : rs.tail0 + (tid - rs.head);
+      const float z = Elem<DT>::load(row + idx);
+      float gv = exp2_hw(__builtin_fmaf(z, kLog2e, -mL)) * gs - goff;
+      if (idx == t) gv -= gt;
+      store_one<DT>(grow + idx, gv);
+    }
+  }
+  // The logits row and the gradient row share their alignment within 16 bytes
+  // only if their base offsets agree; the host guarantees it (same strides and
+  // equal base alignment), so the same split serves both.
+  const u32x4_t* vrow = reinterpret_cast<const u32x4_t*>(row + rs.head);
+  const int64_t tv = t - rs.head;  // target position inside the vector body
+  int64_t j = tid;
+  for (; j + (kUnroll - 1) * kThreads < rs.nvec; j += kUnroll * kThreads) {
+    u32x4_t w[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) w[u] = __builtin_nontemporal_load(vrow + j + u * kThreads);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      float z[vec];
+      unpack<DT>(w[u], z);
+      float gv[vec];
+#pragma unroll
+      for (int i = 0; i < vec; ++i) gv[i] = exp2_hw(__builtin_fmaf(z[i], kLog2e, -mL)) * gs - goff;
+      const int64_t base = (j + u * kThreads) * vec;
+      if (tv >= base && tv < base + vec) {
+#pragma unroll
+        for (int i = 0; i < vec; ++i)
+          if (base + i == tv) gv[i] -= gt;
+      }
+      store_vec<DT>(gvec + j + u * kThreads, gv);
+    }
+  }
+  for (; j < rs.nvec; j += kThreads) {
+    const u32x4_t w = __builtin_nontemporal_load(vrow + j);
+    float z[vec];
+    unpack<DT>(w, z);
+    float gv[vec];
+#pragma unroll
+    for (int i = 0; i < vec; ++i) gv[i] = exp2_hw(__builtin_fmaf(z[i], kLog2e, -mL)) * gs - goff;
+    const int64_t base = j * vec;
+    if (tv >= base && tv < base + vec) {
+#pragma unroll
+      for (int i = 0; i < vec; ++i)
+        if (base + i == tv) gv[i] -= gt;
+    }
+    store_vec<DT>(gvec + j, gv);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_ce_forward(const CeFwdParams& p, int dtype, int64_t N, hipStream_t stream) {
+  if (N <= 0) return hipSuccess;
+  if (dtype == 0)
+    hipLaunchKernelGGL(ce_fwd_kernel<0>, dim3((unsigned)N), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(ce_fwd_kernel<1>, dim3((unsigned)N), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_mean(const CeMeanParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(ce_mean_kernel, dim3(1), dim3(1024), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_backward(const CeBwdParams& p, int dtype, int64_t N, hipStream_t stream) {
+  if (N <= 0) return hipSuccess;
+  if (dtype == 0)
+    hipLaunchKernelGGL(ce_bwd_kernel<0>, dim3((unsigned)N), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(ce_bwd_kernel<1>, dim3((unsigned)N), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace vce

@@ -1,0 +1,290 @@
+// C-ABI of libvce: argument validation and kernel dispatch.  Declarations and
+// the contract of every entry point are in include/vce.h.
+//
+// Nothing here allocates, frees or synchronises: each entry point checks its
+// arguments on the host, then enqueues its kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "vce.h"
+#include "vce_internal.h"
+
+namespace {
+
+inline bool aligned(const void* p, size_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+inline bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+inline int launch_status(hipError_t e) { return e == hipSuccess ? VCE_OK : VCE_EHIP; }
+
+// Byte extent [lo, hi) touched by a (d0, d1, V) strided tensor.
+inline void extent(const void* base, int64_t d0, int64_t d1, int64_t V, int64_t s0, int64_t s1,
+                   int64_t es, uintptr_t* lo, uintptr_t* hi) {
+  const int64_t last = (d0 - 1) * s0 + (d1 - 1) * s1 + V;
+  *lo = reinterpret_cast<uintptr_t>(base);
+  *hi = *lo + (uintptr_t)(last * es);
+}
+
+struct CeShape {
+  int64_t N;
+  int64_t es;
+};
+
+int check_ce_common(const void* logits, int dtype, int64_t d0, int64_t d1, int64_t V, int64_t ls0,
+                    int64_t ls1, const int64_t* targets, int64_t ts0, int64_t ts1, float eps,
+                    int reduce_loss, CeShape* sh) {
+  if (dtype != VCE_DTYPE_FP32 && dtype != VCE_DTYPE_BF16) return VCE_EDTYPE;
+  if (d0 < 0 || d1 < 0 || V <= 0) return VCE_EINVAL;
+  if (ls0 < 0 || ls1 < 0 || ts0 < 0 || ts1 < 0) return VCE_EINVAL;
+  if (!(eps >= 0.0f && eps <= 1.0f)) return VCE_EINVAL;  // also rejects NaN
+  if (reduce_loss != 0 && reduce_loss != 1) return VCE_EINVAL;
+  int64_t N;
+  if (!mul_ok(d0, d1, &N) || N > (int64_t)INT32_MAX) return VCE_EINVAL;
+  const int64_t es = dtype == VCE_DTYPE_FP32 ? 4 : 2;
+  if (N > 0) {
+    if (!logits || !targets) return VCE_EINVAL;
+    int64_t span0, span1, tmp;
+    if (!mul_ok(d0 - 1, ls0, &span0) || !mul_ok(d1 - 1, ls1, &span1)) return VCE_EINVAL;
+    if (span0 > INT64_MAX / 8 - span1 - V || !mul_ok(span0 + span1 + V, es, &tmp))
+      return VCE_EINVAL;
+    if (!aligned(logits, (size_t)es) || !aligned(targets, 8)) return VCE_EALIGN;
+  }
+  sh->N = N;
+  sh->es = es;
+  return VCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vce_strerror(int status) {
+  switch (status) {
+    case VCE_OK: return "success";
+    case VCE_EINVAL: return "invalid argument (null pointer, size, stride or label_smoothing)";
+    case VCE_EDTYPE: return "unsupported dtype (expected FP32 or BF16)";
+    case VCE_EALIGN: return "misaligned pointer or stride";
+    case VCE_EALIAS: return "buffer aliasing violates overwrite_input";
+    case VCE_EWORKSPACE: return "workspace too small";
+    case VCE_EHIP: return "HIP kernel launch failed";
+    case VCE_EUNSUPPORTED: return "size not supported by this build";
+    default: return "unknown status";
+  }
+}
+
+int ce_forward(const void* logits, int dtype, int64_t d0, int64_t d1, int64_t V, int64_t ls0,
+               int64_t ls1, const int64_t* targets, int64_t ts0, int64_t ts1,
+               float label_smoothing, int reduce_loss, int64_t ignore_idx, float* loss_tok,
+               float* loss_mean, float* stats, int32_t* n_valid, void* stream) {
+  CeShape sh;
+  int rc = check_ce_common(logits, dtype, d0, d1, V, ls0, ls1, targets, ts0, ts1,
+                           label_smoothing, reduce_loss, &sh);
+  if (rc != VCE_OK) return rc;
+  if (reduce_loss && (!loss_mean || !n_valid)) return VCE_EINVAL;
+  if (sh.N > 0 && (!loss_tok || !stats)) return VCE_EINVAL;
+  if (stats && !aligned(stats, 16)) return VCE_EALIGN;
+  if ((loss_tok && !aligned(loss_tok, 4)) || (loss_mean && !aligned(loss_mean, 4)) ||
+      (n_valid && !aligned(n_valid, 4)))
+    return VCE_EALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  vce::CeFwdParams p;
+  p.logits = logits;
+  p.d1 = d1 > 0 ? d1 : 1;
+  p.ls0 = ls0;
+  p.ls1 = ls1;
+  p.V = V;
+  p.targets = targets;
+  p.ts0 = ts0;
+  p.ts1 = ts1;
+  p.eps = label_smoothing;
+  p.ignore_idx = ignore_idx;
+  p.loss_tok = loss_tok;
+  p.stats = stats;
+  rc = launch_status(vce::launch_ce_forward(p, dtype, sh.N, s));
+  if (rc != VCE_OK) return rc;
+  if (reduce_loss || n_valid) {
+    vce::CeMeanParams mp;
+    mp.loss_tok = loss_tok;
+    mp.targets = targets;
+    mp.N = sh.N;
+    mp.d1 = d1 > 0 ? d1 : 1;
+    mp.ts0 = ts0;
+    mp.ts1 = ts1;
+    mp.ignore_idx = ignore_idx;
+    mp.loss_mean = reduce_loss ? loss_mean : nullptr;
+    mp.n_valid = n_valid;
+    rc = launch_status(vce::launch_ce_mean(mp, s));
+  }
+  return rc;
+}
+
+int ce_backward(const void* logits, void* grad, int dtype, int64_t d0, int64_t d1, int64_t V,
+                int64_t ls0, int64_t ls1, const int64_t* targets, int64_t ts0, int64_t ts1,
+                const float* stats, const int32_t* n_valid, const float* grad_output,
+                float label_smoothing, int reduce_loss, int64_t ignore_idx, int overwrite_input,
+                void* stream) {
+  CeShape sh;
+  int rc = check_ce_common(logits, dtype, d0, d1, V, ls0, ls1, targets, ts0, ts1,
+                           label_smoothing, reduce_loss, &sh);
+  if (rc != VCE_OK) return rc;
+  if (overwrite_input != 0 && overwrite_input != 1) return VCE_EINVAL;
+  if (sh.N == 0) return VCE_OK;
+  if (!grad || !stats || !grad_output || (reduce_loss && !n_valid)) return VCE_EINVAL;
+  if (!aligned(stats, 16) || !aligned(grad_output, 4) || (n_valid && !aligned(n_valid, 4)))
+    return VCE_EALIGN;
+  if (overwrite_input) {
+    if (grad != logits) return VCE_EALIAS;
+  } else {
+    uintptr_t a0, a1, b0, b1;
+    extent(logits, d0, d1, V, ls0, ls1, sh.es, &a0, &a1);
+    extent(grad, d0, d1, V, ls0, ls1, sh.es, &b0, &b1);
+    if (a0 < b1 && b0 < a1) return VCE_EALIAS;
+    // Both rows are split at the same 16-byte boundary.
+    if ((reinterpret_cast<uintptr_t>(logits) - reinterpret_cast<uintptr_t>(grad)) % 16 != 0)
+      return VCE_EALIGN;
+  }
+  vce::CeBwdParams p;
+  p.logits = logits;
+  p.grad = grad;
+  p.d1 = d1;
+  p.ls0 = ls0;
+  p.ls1 = ls1;
+  p.V = V;
+  p.targets = targets;
+  p.ts0 = ts0;
+  p.ts1 = ts1;
+  p.stats = stats;
+  p.n_valid = n_valid;
+  p.grad_output = grad_output;
+  p.eps = label_smoothing;
+  p.reduce_loss = reduce_loss;
+  p.ignore_idx = ignore_idx;
+  return launch_status(vce::launch_ce_backward(p, dtype, sh.N, static_cast<hipStream_t>(stream)));
+}
+
+size_t lce_workspace_size(int64_t M, int64_t H, int64_t V) {
+  vce::LcePlan plan;
+  if (!vce::lce_make_plan(M, H, V, &plan)) return 0;
+  return plan.total;
+}
+
+namespace {
+
+int check_lce_common(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
+                     const int64_t* targets, float eps, int reduce_loss, void* workspace,
+                     size_t workspace_bytes, vce::LcePlan* plan) {
+  if (M < 0 || H <= 0 || V <= 0) return VCE_EINVAL;
+  if (!(eps >= 0.0f && eps <= 1.0f)) return VCE_EINVAL;
+  if (reduce_loss != 0 && reduce_loss != 1) return VCE_EINVAL;
+  if (H % 8 != 0) return VCE_EUNSUPPORTED;
+  if (!vce::lce_make_plan(M, H, V, plan)) return VCE_EUNSUPPORTED;
+  if (M == 0) return VCE_OK;
+  if (!X || !W || !targets || !workspace) return VCE_EINVAL;
+  if (!aligned(X, 16) || !aligned(W, 16) || !aligned(targets, 8) || !aligned(workspace, 256))
+    return VCE_EALIGN;
+  if (workspace_bytes < plan->total) return VCE_EWORKSPACE;
+  return VCE_OK;
+}
+
+}  // namespace
+
+int lce_forward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
+                const int64_t* targets, float label_smoothing, int reduce_loss,
+                int64_t ignore_idx, float* loss_tok, float* loss_mean, float* stats,
+                int32_t* n_valid, void* workspace, size_t workspace_bytes, void* stream) {
+  vce::LcePlan plan;
+  int rc = check_lce_common(X, W, M, H, V, targets, label_smoothing, reduce_loss, workspace,
+                            workspace_bytes, &plan);
+  if (rc != VCE_OK) return rc;
+  if (reduce_loss && (!loss_mean || !n_valid)) return VCE_EINVAL;
+  if (M > 0 && (!loss_tok || !stats)) return VCE_EINVAL;
+  if (stats && !aligned(stats, 16)) return VCE_EALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M > 0) {
+    vce::LceFwdArgs a;
+    a.X = X;
+    a.W = W;
+    a.targets = targets;
+    a.eps = label_smoothing;
+    a.reduce_loss = reduce_loss;
+    a.ignore_idx = ignore_idx;
+    a.loss_tok = loss_tok;
+    a.loss_mean = loss_mean;
+    a.stats = stats;
+    a.n_valid = n_valid;
+    a.ws = static_cast<char*>(workspace);
+    rc = launch_status(vce::launch_lce_forward(plan, a, s));
+    if (rc != VCE_OK) return rc;
+  }
+  if (reduce_loss || n_valid) {
+    vce::CeMeanParams mp;
+    mp.loss_tok = loss_tok;
+    mp.targets = targets;
+    mp.N = M;
+    mp.d1 = M > 0 ? M : 1;
+    mp.ts0 = 0;
+    mp.ts1 = 1;
+    mp.ignore_idx = ignore_idx;
+    mp.loss_mean = reduce_loss ? loss_mean : nullptr;
+    mp.n_valid = n_valid;
+    rc = launch_status(vce::launch_ce_mean(mp, s));
+  }
+  return rc;
+}
+
+int lce_backward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
+                 const int64_t* targets, const float* stats, const int32_t* n_valid,
+                 const float* grad_output, float label_smoothing, int reduce_loss,
+                 int64_t ignore_idx, void* dX, void* dW, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  vce::LcePlan plan;
+  int rc = check_lce_common(X, W, M, H, V, targets, label_smoothing, reduce_loss, workspace,
+                            workspace_bytes, &plan);
+  if (rc != VCE_OK) return rc;
+  if (!dW) return VCE_EINVAL;
+  if (!aligned(dW, 16)) return VCE_EALIGN;
+  if (M > 0) {
+    if (!dX || !stats || !grad_output || (reduce_loss && !n_valid)) return VCE_EINVAL;
+    if (!aligned(dX, 16) || !aligned(stats, 16) || !aligned(grad_output, 4)) return VCE_EALIGN;
+  }
+  vce::LceBwdArgs a;
+  a.X = X;
+  a.W = W;
+  a.targets = targets;
+  a.stats = stats;
+  a.n_valid = n_valid;
+  a.grad_output = grad_output;
+  a.eps = label_smoothing;
+  a.reduce_loss = reduce_loss;
+  a.ignore_idx = ignore_idx;
+  a.dX = dX;
+  a.dW = dW;
+  a.ws = static_cast<char*>(workspace);
+  return launch_status(vce::launch_lce_backward(plan, a, static_cast<hipStream_t>(stream)));
+}
+
+int vce_gemm_bf16(const void* P, int p_kmajor, int64_t ldp, const void* Q, int q_kmajor,
+                  int64_t ldq, int64_t rows, int64_t cols, int64_t K, float* C, int64_t ldc,
+                  void* stream) {
+  if (rows < 0 || cols < 0 || K < 0 || (p_kmajor != 0 && p_kmajor != 1) ||
+      (q_kmajor != 0 && q_kmajor != 1))
+    return VCE_EINVAL;
+  if (rows == 0 || cols == 0) return VCE_OK;
+  if (!P || !Q || !C) return VCE_EINVAL;
+  if (K % 8 != 0 || ldp % 8 != 0 || ldq % 8 != 0) return VCE_EUNSUPPORTED;
+  if (ldc < cols || ldp < (p_kmajor ? K : rows) || ldq < (q_kmajor ? K : cols)) return VCE_EINVAL;
+  if (!aligned(P, 16) || !aligned(Q, 16) || !aligned(C, 16)) return VCE_EALIGN;
+  return launch_status(vce::launch_gemm_bf16(P, p_kmajor, ldp, Q, q_kmajor, ldq, rows, cols, K, C,
+                                             ldc, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

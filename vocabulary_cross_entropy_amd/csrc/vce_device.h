@@ -1,0 +1,79 @@
+// Device helpers shared by the gfx950 kernels of libvce.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vce {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// 2^x on the transcendental unit (v_exp_f32).  -inf gives 0.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+// log2(x) on the transcendental unit (v_log_f32).
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+// BF16 pair packed in one dword -> two floats (exact widening).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Sum of the two BF16 values of a dword, added to acc (v_dot2_f32_bf16 with ones).
+__device__ __forceinline__ float bf16_pair_sum(uint32_t w, float acc) {
+  bf16x2_t x = __builtin_bit_cast(bf16x2_t, w);
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(x, one, acc, false);
+}
+
+// Two floats -> BF16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float x) {
+  __bf16 b = (__bf16)x;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ float from_bf16(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Online log-sum-exp state: running max m, d = sum exp(z - m), s = sum z.
+struct LseState {
+  float m, d, s;
+};
+
+// Merge b into a.  Either side may be empty (m = -inf, d = 0).
+__device__ __forceinline__ void lse_merge(LseState& a, const LseState& b) {
+  float m = fmaxf(a.m, b.m);
+  float mref = (m == kNegInf) ? 0.0f : m;
+  float fa = exp2_hw((a.m - mref) * kLog2e);
+  float fb = exp2_hw((b.m - mref) * kLog2e);
+  a.d = a.d * fa + b.d * fb;
+  a.s = a.s + b.s;
+  a.m = m;
+}
+
+// Butterfly reduction of an LseState over the 64 lanes of a wavefront.
+__device__ __forceinline__ void lse_wave_reduce(LseState& st) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    LseState o;
+    o.m = __shfl_xor(st.m, off, 64);
+    o.d = __shfl_xor(st.d, off, 64);
+    o.s = __shfl_xor(st.s, off, 64);
+    lse_merge(st, o);
+  }
+}
+
+}  // namespace vce

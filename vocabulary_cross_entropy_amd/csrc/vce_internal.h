@@ -1,0 +1,97 @@
+// Kernel parameter blocks and launchers shared by the C-ABI layer and the
+// kernel translation units of libvce.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vce {
+
+struct CeFwdParams {
+  const void* logits;
+  int64_t d1, ls0, ls1, V;
+  const int64_t* targets;
+  int64_t ts0, ts1;
+  float eps;
+  int64_t ignore_idx;
+  float* loss_tok;
+  float* stats;
+};
+
+struct CeMeanParams {
+  const float* loss_tok;
+  const int64_t* targets;
+  int64_t N, d1, ts0, ts1, ignore_idx;
+  float* loss_mean;
+  int32_t* n_valid;
+};
+
+struct CeBwdParams {
+  const void* logits;
+  void* grad;
+  int64_t d1, ls0, ls1, V;
+  const int64_t* targets;
+  int64_t ts0, ts1;
+  const float* stats;
+  const int32_t* n_valid;
+  const float* grad_output;
+  float eps;
+  int reduce_loss;
+  int64_t ignore_idx;
+};
+
+hipError_t launch_ce_forward(const CeFwdParams& p, int dtype, int64_t N, hipStream_t stream);
+hipError_t launch_ce_mean(const CeMeanParams& p, hipStream_t stream);
+hipError_t launch_ce_backward(const CeBwdParams& p, int dtype, int64_t N, hipStream_t stream);
+
+// ---- fused linear cross-entropy ----------------------------------------------
+
+// Workspace plan of the linear form for an (M, H, V) problem.
+struct LcePlan {
+  int64_t M, H, V;
+  int64_t Mp;          // M rounded up to the token tile
+  int64_t n_vtiles;    // vocabulary tiles of the forward
+  int64_t chunk;       // vocabulary rows per backward chunk (multiple of the tile)
+  int64_t n_chunks;
+  int64_t ldz;         // row stride (elements) of the dZ chunk buffer
+  size_t off_part, off_dz, off_dx, total;
+};
+
+bool lce_make_plan(int64_t M, int64_t H, int64_t V, LcePlan* plan);
+
+struct LceFwdArgs {
+  const void* X;
+  const void* W;
+  const int64_t* targets;
+  float eps;
+  int reduce_loss;
+  int64_t ignore_idx;
+  float* loss_tok;
+  float* loss_mean;
+  float* stats;
+  int32_t* n_valid;
+  char* ws;
+};
+
+struct LceBwdArgs {
+  const void* X;
+  const void* W;
+  const int64_t* targets;
+  const float* stats;
+  const int32_t* n_valid;
+  const float* grad_output;
+  float eps;
+  int reduce_loss;
+  int64_t ignore_idx;
+  void* dX;
+  void* dW;
+  char* ws;
+};
+
+hipError_t launch_lce_forward(const LcePlan& plan, const LceFwdArgs& a, hipStream_t stream);
+hipError_t launch_lce_backward(const LcePlan& plan, const LceBwdArgs& a, hipStream_t stream);
+hipError_t launch_gemm_bf16(const void* P, int p_kmajor, int64_t ldp, const void* Q, int q_kmajor,
+                            int64_t ldq, int64_t rows, int64_t cols, int64_t K, float* C,
+                            int64_t ldc, hipStream_t stream);
+
+}  // namespace vce

@@ -36,7 +36,22 @@ DTYPE_BF16 = "bf16"
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round FP32 values to BF16 (nearest, ties to even); return uint16 bit patterns."""
+    """Round FP32 values to BF16 (nearest, ties to even); return uint16 bit patterns.
+
+    Large arrays go through torch's multithreaded CPU cast (also nearest-even;
+    the two agree bit for bit, which the CPU tests check)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.size >= (1 << 22):
+        try:
+            import torch
+            return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        except ImportError:
+            pass
+    return f32_to_bf16_bits_np(x)
+
+
+def f32_to_bf16_bits_np(x: np.ndarray) -> np.ndarray:
+    """NumPy statement of FP32 -> BF16 round to nearest even (bit patterns)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     bits = x.view(np.uint32)
     lsb = (bits >> np.uint32(16)) & np.uint32(1)
@@ -62,7 +77,7 @@ def _normal_f32(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
 
 
 def _ignore_rows(rng: np.random.Generator, n: int, frac: float | None, count: int | None) -> np.ndarray:
-    k = count if count is not None else int(round(frac * n))
+    k = count if count is not None else int(round((frac or 0.0) * n))
     k = max(0, min(n, k))
     if k == 0:
         return np.zeros(0, dtype=np.int64)
