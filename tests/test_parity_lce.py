@@ -1,0 +1,224 @@
+"""Parity of the HIP fused linear cross-entropy (lce_forward / lce_backward)
+and of its matrix-core GEMM building block with the FP64 oracle."""
+import hashlib
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import vocabulary_cross_entropy_amd as vce
+from oracle import linear
+from vocabulary_cross_entropy_amd import workloads as wl
+from vce_testutil import LINEAR_FROB_RTOL, LINEAR_LOSS_RTOL, rel_frobenius, to_device, to_host_bits
+
+pytestmark = pytest.mark.gpu
+IGN = wl.IGNORE_INDEX
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _say(msg):
+    print(f"[parity-lce] {msg}", flush=True)
+
+
+def _bf16(a):
+    return to_device(a, "bf16")
+
+
+# --- the GEMM building block -----------------------------------------------------
+
+@pytest.mark.parametrize("pk,qk", [(1, 1), (1, 0), (0, 1), (0, 0)])
+@pytest.mark.parametrize("rows,cols,K", [(300, 520, 200), (512, 768, 4096), (33, 7, 8)])
+def test_gemm_modes(pk, qk, rows, cols, K):
+    rng = np.random.default_rng(rows * 7 + cols + K + 10 * pk + qk)
+    Pm = wl.f32_to_bf16_bits(rng.standard_normal((rows, K)).astype(np.float32))
+    Qm = wl.f32_to_bf16_bits(rng.standard_normal((cols, K)).astype(np.float32))
+    # storage: K-major keeps (rows, K); dim-major stores the transpose, padded
+    # to a multiple of 8 columns as the library requires of its leading dim
+    def store(m, kmajor):
+        if kmajor:
+            return m
+        t = np.zeros((m.shape[1], (m.shape[0] + 7) // 8 * 8), np.uint16)
+        t[:, :m.shape[0]] = m.T
+        return t
+    Ps, Qs = store(Pm, pk), store(Qm, qk)
+    C = vce.gemm_bf16(_bf16(Ps), bool(pk), _bf16(Qs), bool(qk), rows, cols, K)
+    torch.cuda.synchronize()
+    Pf, Qf = oracle.bf16_to_f64(Pm), oracle.bf16_to_f64(Qm)
+    ref = Pf @ Qf.T
+    scale = np.abs(Pf) @ np.abs(Qf).T
+    err = np.abs(C.cpu().numpy().astype(np.float64) - ref)
+    # FP32 accumulation of exact BF16 products: error far below 2^-14 of the
+    # sum of |terms|; an indexing mistake gives errors of the order of the terms
+    assert np.all(err <= 2.0 ** -14 * scale + 1e-30), float((err / (scale + 1e-30)).max())
+
+
+# --- helpers -----------------------------------------------------------------------
+
+def run_lce(case, ws=None):
+    X, W = _bf16(case.X), _bf16(case.W)
+    t = torch.from_numpy(case.targets).cuda()
+    go = torch.from_numpy(case.grad_output).cuda()
+    loss, mean, stats, nv = vce.lce_forward(X, W, t, case.label_smoothing, case.reduce_loss,
+                                            case.ignore_idx, workspace=ws)
+    dX, dW = vce.lce_backward(X, W, t, stats, nv, go, case.label_smoothing, case.reduce_loss,
+                              case.ignore_idx, workspace=ws)
+    torch.cuda.synchronize()
+    out = dict(loss=loss.cpu().numpy().astype(np.float64), stats=stats.cpu().numpy(),
+               dX=oracle.bf16_to_f64(to_host_bits(dX)), dW_dev=dW)
+    if case.reduce_loss:
+        out["mean"] = float(mean.item())
+        out["n_valid"] = int(nv.item())
+    return out
+
+
+def check_loss(case, out, ref_loss, ref_stats=None):
+    valid = case.targets != case.ignore_idx
+    assert np.all(out["loss"][~valid] == 0.0)
+    rel = np.abs(out["loss"][valid] - ref_loss[valid]) / np.abs(ref_loss[valid])
+    worst = float(rel.max()) if rel.size else 0.0
+    assert worst <= LINEAR_LOSS_RTOL, worst
+    if case.reduce_loss:
+        rm = oracle.mean_loss(ref_loss, case.targets, case.ignore_idx)
+        assert abs(out["mean"] - rm) <= LINEAR_LOSS_RTOL * abs(rm)
+        assert out["n_valid"] == oracle.n_valid(case.targets, case.ignore_idx)
+    if ref_stats is not None:
+        st, rs = out["stats"][valid], ref_stats[valid]
+        np.testing.assert_allclose(st[:, 0], rs[:, 0], atol=1e-3)       # row max of FP32 logits
+        np.testing.assert_allclose(st[:, 1], rs[:, 1], rtol=2e-3)       # denominator
+        np.testing.assert_allclose(st[:, 2], rs[:, 2], atol=1e-3)       # target logit
+        np.testing.assert_allclose(st[:, 3], rs[:, 3], atol=1e-4)       # logit mean
+    return worst
+
+
+def full_check(case):
+    out = run_lce(case)
+    ref_loss, ref_stats, _ = linear.forward(case.X, case.W, case.targets, case.label_smoothing,
+                                            case.ignore_idx)
+    lw = check_loss(case, out, ref_loss, ref_stats)
+    g = oracle.row_scale(case.grad_output, case.targets, case.reduce_loss, case.ignore_idx)
+    rdX, rdW = linear.backward(case.X, case.W, case.targets, g, case.label_smoothing,
+                               case.ignore_idx)
+    dW = oracle.bf16_to_f64(to_host_bits(out["dW_dev"]))
+    fx, fw = rel_frobenius(out["dX"], rdX), rel_frobenius(dW, rdW)
+    _say(f"{case.name}: loss rel {lw:.2e}, dX frob {fx:.2e}, dW frob {fw:.2e}")
+    assert fx <= LINEAR_FROB_RTOL and fw <= LINEAR_FROB_RTOL
+    return out
+
+
+@pytest.mark.parametrize("eps", [0.0, 0.1])
+@pytest.mark.parametrize("reduce_loss", [True, False])
+def test_linear_small(eps, reduce_loss):
+    case = wl.make_linear(3001, 300, 264, 1000, ignore_count=7, label_smoothing=eps,
+                          reduce_loss=reduce_loss, grad_output="random",
+                          name=f"small_eps{eps}_red{int(reduce_loss)}")
+    full_check(case)
+
+
+def test_linear_multichunk_ragged_vocab():
+    # three backward chunks, the last ragged; V not a multiple of any tile
+    case = wl.make_linear(3002, 520, 136, 70001, ignore_frac=0.05, label_smoothing=0.1,
+                          reduce_loss=False, grad_output="random", name="m520_h136_v70001")
+    full_check(case)
+
+
+@pytest.mark.parametrize("M", [4097, 5000])
+def test_linear_token_wave_boundaries(M):
+    case = wl.make_linear(3003 + M, M, 128, 3001, ignore_frac=0.03, targets="zipf",
+                          label_smoothing=0.1, reduce_loss=True, name=f"m{M}_h128_v3001")
+    full_check(case)
+
+
+def test_linear_all_ignored():
+    case = wl.make_linear(3004, 64, 64, 500, ignore_count=64, reduce_loss=True)
+    out = run_lce(case)
+    assert out["mean"] == 0.0 and out["n_valid"] == 0
+    assert np.all(out["dX"] == 0.0)
+    assert torch.count_nonzero(out["dW_dev"].float()).item() == 0
+
+
+def test_linear_matches_logits_form():
+    # lce_forward(X, W) against ce_forward on Z = X W^T formed by the same GEMM core
+    case = wl.make_linear(3005, 256, 512, 4096, ignore_count=5, label_smoothing=0.1,
+                          reduce_loss=True)
+    X, W = _bf16(case.X), _bf16(case.W)
+    t = torch.from_numpy(case.targets).cuda()
+    loss, mean, stats, nv = vce.lce_forward(X, W, t, 0.1, True)
+    Z = vce.gemm_bf16(X, True, W, True, 256, 4096, 512)
+    loss2, mean2, stats2, nv2 = vce.ce_forward(Z, t, 0.1, True)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(loss.cpu().numpy(), loss2.cpu().numpy().reshape(-1), rtol=1e-5,
+                               atol=1e-5)
+    assert nv.item() == nv2.item()
+
+
+def test_linear_deterministic():
+    case = wl.make_linear(3006, 700, 192, 9000, ignore_frac=0.1, label_smoothing=0.1)
+    a, b = run_lce(case), run_lce(case)
+    np.testing.assert_array_equal(a["loss"], b["loss"])
+    np.testing.assert_array_equal(a["dX"], b["dX"])
+    assert torch.equal(a["dW_dev"], b["dW_dev"])
+
+
+# --- the full-size workloads: every token's loss against stored oracle values,
+# --- sampled rows of dX and dW computed by the oracle, and invariants ----------------
+
+def _digest(case):
+    h = hashlib.sha256()
+    for a in (case.X, case.W, case.targets):
+        h.update(np.ascontiguousarray(a).tobytes())
+    return h.hexdigest()
+
+
+def full_size(case):
+    gold = np.load(os.path.join(GOLDEN, case.name + ".npz"))
+    assert str(gold["digest"]) == _digest(case), "regenerated inputs differ from the golden's"
+    out = run_lce(case)
+    lw = check_loss(case, out, gold["loss"], gold["stats"])
+    g = oracle.row_scale(case.grad_output, case.targets, case.reduce_loss, case.ignore_idx)
+    rng = np.random.default_rng(7)
+    valid = np.nonzero(case.targets != case.ignore_idx)[0]
+    rows = np.unique(np.concatenate([rng.choice(valid, 24, replace=False), [0, case.M - 1]]))
+    rdx = linear.dx_rows(case.X, case.W, case.targets, g, rows, case.label_smoothing,
+                         case.ignore_idx)
+    fx = rel_frobenius(out["dX"][rows], rdx)
+    V = case.V
+    vrows = np.unique(np.concatenate([rng.choice(V, 24, replace=False),
+                                      [0, 1, 2, V - 1, V - 2, 32767, 32768],
+                                      np.unique(case.targets[valid])[:4]]))
+    vrows = vrows[vrows < V]
+    rdw = linear.dw_rows(case.X, case.W, case.targets, g, gold["lse"], vrows,
+                         case.label_smoothing, case.ignore_idx)
+    dW = out["dW_dev"]
+    dws = oracle.bf16_to_f64(to_host_bits(dW[torch.from_numpy(vrows).cuda()]))
+    fw = rel_frobenius(dws, rdw)
+    # Invariant at full size: every row of dZ sums to zero, so every column of
+    # dW sums to zero up to BF16 rounding.  Rounding model: dZ entries and dW
+    # entries carry relative errors below 2^-9; the dominant dZ entry of a row,
+    # g_r (p_t - 1), is close to the same value -g for most rows, so its
+    # rounding error is systematic (bounded by 2^-8 |sum_r g_r X_rh|); the rest
+    # are independent (at most 6 standard deviations of their sum).
+    colsum = dW.double().sum(dim=0).cpu().numpy()
+    D = (dW.double() ** 2).sum(dim=0).cpu().numpy()
+    Xf = oracle.bf16_to_f64(case.X)
+    gx = g[:, None] * Xf
+    S, Q = gx.sum(axis=0), (gx ** 2).sum(axis=0)
+    bound = 2.0 ** -8 * np.abs(S) + 6 * 2.0 ** -9 * np.sqrt((Q + D) / 3)
+    ratio = float(np.max(np.abs(colsum) / bound))
+    _say(f"{case.name}: loss rel {lw:.2e}, dX rows frob {fx:.2e}, dW rows frob {fw:.2e}, "
+         f"max |colsum dW| / bound {ratio:.2f}")
+    assert fx <= LINEAR_FROB_RTOL and fw <= LINEAR_FROB_RTOL
+    assert ratio <= 1.0
+
+
+def test_linear_m4096_h4096_v131072():
+    case = wl.linear_4k()
+    _say(case.name)
+    full_size(case)
+
+
+def test_linear_m16384_h2304_v256003():
+    case = wl.linear_16k()
+    _say(case.name)
+    full_size(case)
