@@ -36,7 +36,7 @@ def L():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("ce_forward", "ce_backward", "lce_forward", "lce_backward", "lce_workspace_size",
-              "vce_strerror", "vce_gemm_bf16"):
+              "vce_strerror", "vce_gemm_bf16", "vce_transpose_bf16"):
         assert n in names
     assert set(names) == set(binding.SIGNATURES), "binding and header disagree"
 
@@ -102,8 +102,8 @@ def test_lce_workspace_size(L):
     small = L.lce_workspace_size(4096, 4096, 131072)
     big = L.lce_workspace_size(16384, 2304, 256003)
     assert 0 < small < big
-    # the workspace holds no logit matrix: far below M * V * 2 bytes
-    assert big < 16384 * 256003 * 2 // 4
+    # the workspace holds no logit matrix: a third of one BF16 (M, V) matrix at most
+    assert big < 16384 * 256003 * 2 // 3
 
 
 def lfwd(L, X=A, W=A, M=64, H=64, V=1000, targets=A, eps=0.0, reduce_loss=1, ignore=-100,
@@ -147,8 +147,19 @@ def test_lce_backward_rejects(L):
 
 def test_gemm_rejects(L):
     g = L.vce_gemm_bf16
-    assert g(A, 1, 64, A, 1, 64, 10, 10, 12, A, 10, None) == 7   # K not a multiple of 8
-    assert g(A, 2, 64, A, 1, 64, 10, 10, 64, A, 10, None) == 1
-    assert g(A, 1, 64, A, 1, 64, 10, 10, 64, A, 5, None) == 1    # ldc < cols
-    assert g(A + 2, 1, 64, A, 1, 64, 10, 10, 64, A, 10, None) == 3
-    assert g(A, 1, 64, A, 1, 64, 0, 10, 64, A, 10, None) == 0    # empty: nothing to do
+    assert g(A, 64, A, 64, 10, 10, 12, A, 10, None) == 7      # K not a multiple of 8
+    assert g(A, 64, A, 64, 10, 10, 64, A, 5, None) == 1       # ldc < cols
+    assert g(A, 32, A, 64, 10, 10, 64, A, 10, None) == 1      # ldp < K
+    assert g(A + 2, 64, A, 64, 10, 10, 64, A, 10, None) == 3
+    assert g(A, 64, A, 1 << 23, 10, 10, 64, A, 10, None) == 7  # leading dim too large
+    assert g(A, 64, A, 64, 0, 10, 64, A, 10, None) == 0       # empty: nothing to do
+
+
+def test_transpose_rejects(L):
+    t = L.vce_transpose_bf16
+    assert t(A, 10, 20, 16, A + (1 << 20), 16, None) == 1     # ld_src < cols
+    assert t(A, 10, 20, 24, A + (1 << 20), 8, None) == 1      # ld_dst < rows
+    assert t(A, 10, 20, 20, A + (1 << 20), 16, None) == 3     # ld_src not a multiple of 8
+    assert t(A + 2, 10, 20, 24, A + (1 << 20), 16, None) == 3
+    assert t(A, 10, 20, 24, A + 64, 16, None) == 4            # overlapping buffers
+    assert t(A, 0, 20, 24, A + (1 << 20), 16, None) == 0

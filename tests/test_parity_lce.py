@@ -28,22 +28,13 @@ def _bf16(a):
 
 # --- the GEMM building block -----------------------------------------------------
 
-@pytest.mark.parametrize("pk,qk", [(1, 1), (1, 0), (0, 1), (0, 0)])
-@pytest.mark.parametrize("rows,cols,K", [(300, 520, 200), (512, 768, 4096), (33, 7, 8)])
-def test_gemm_modes(pk, qk, rows, cols, K):
-    rng = np.random.default_rng(rows * 7 + cols + K + 10 * pk + qk)
+@pytest.mark.parametrize("rows,cols,K", [(300, 520, 200), (512, 768, 4096), (33, 7, 8),
+                                         (773, 1000, 4104), (4096, 256, 64)])
+def test_gemm(rows, cols, K):
+    rng = np.random.default_rng(rows * 7 + cols + K)
     Pm = wl.f32_to_bf16_bits(rng.standard_normal((rows, K)).astype(np.float32))
     Qm = wl.f32_to_bf16_bits(rng.standard_normal((cols, K)).astype(np.float32))
-    # storage: K-major keeps (rows, K); dim-major stores the transpose, padded
-    # to a multiple of 8 columns as the library requires of its leading dim
-    def store(m, kmajor):
-        if kmajor:
-            return m
-        t = np.zeros((m.shape[1], (m.shape[0] + 7) // 8 * 8), np.uint16)
-        t[:, :m.shape[0]] = m.T
-        return t
-    Ps, Qs = store(Pm, pk), store(Qm, qk)
-    C = vce.gemm_bf16(_bf16(Ps), bool(pk), _bf16(Qs), bool(qk), rows, cols, K)
+    C = vce.gemm_bf16(_bf16(Pm), _bf16(Qm))
     torch.cuda.synchronize()
     Pf, Qf = oracle.bf16_to_f64(Pm), oracle.bf16_to_f64(Qm)
     ref = Pf @ Qf.T
@@ -52,6 +43,23 @@ def test_gemm_modes(pk, qk, rows, cols, K):
     # FP32 accumulation of exact BF16 products: error far below 2^-14 of the
     # sum of |terms|; an indexing mistake gives errors of the order of the terms
     assert np.all(err <= 2.0 ** -14 * scale + 1e-30), float((err / (scale + 1e-30)).max())
+
+
+@pytest.mark.parametrize("rows,cols", [(64, 64), (1001, 777), (5, 3000), (4096, 2304), (1, 8)])
+def test_transpose(rows, cols):
+    rng = np.random.default_rng(rows + 3 * cols)
+    a = rng.integers(0, 65536, size=(rows, cols), dtype=np.uint16)
+    ld = (cols + 7) // 8 * 8
+    src = np.zeros((rows, ld), np.uint16)
+    src[:, :cols] = a
+    t_src = _bf16(src)[:, :cols]
+    ldd = (rows + 7) // 8 * 8
+    out = torch.zeros((cols, ldd), dtype=torch.bfloat16, device="cuda")
+    vce.transpose_bf16(t_src, out=out[:, :rows])
+    torch.cuda.synchronize()
+    got = to_host_bits(out)
+    np.testing.assert_array_equal(got[:, :rows], a.T)
+    assert np.all(got[:, rows:] == 0)  # nothing written past the destination's columns
 
 
 # --- helpers -----------------------------------------------------------------------
@@ -145,7 +153,7 @@ def test_linear_matches_logits_form():
     X, W = _bf16(case.X), _bf16(case.W)
     t = torch.from_numpy(case.targets).cuda()
     loss, mean, stats, nv = vce.lce_forward(X, W, t, 0.1, True)
-    Z = vce.gemm_bf16(X, True, W, True, 256, 4096, 512)
+    Z = vce.gemm_bf16(X, W)
     loss2, mean2, stats2, nv2 = vce.ce_forward(Z, t, 0.1, True)
     torch.cuda.synchronize()
     np.testing.assert_allclose(loss.cpu().numpy(), loss2.cpu().numpy().reshape(-1), rtol=1e-5,

@@ -34,7 +34,8 @@ SIGNATURES = {
                            _VP, _SZ, _VP]),
     "lce_backward": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _F32, _I32, _I64, _VP,
                             _VP, _VP, _SZ, _VP]),
-    "vce_gemm_bf16": (_I32, [_VP, _I32, _I64, _VP, _I32, _I64, _I64, _I64, _I64, _VP, _I64, _VP]),
+    "vce_gemm_bf16": (_I32, [_VP, _I64, _VP, _I64, _I64, _I64, _I64, _VP, _I64, _VP]),
+    "vce_transpose_bf16": (_I32, [_VP, _I64, _I64, _I64, _VP, _I64, _VP]),
 }
 
 _lib = None
@@ -227,12 +228,27 @@ def lce_backward(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, stats:
     return dX, dW
 
 
-def gemm_bf16(P: torch.Tensor, p_kmajor: bool, Q: torch.Tensor, q_kmajor: bool, rows: int,
-              cols: int, K: int, *, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """C[i, j] = sum_k P(i, k) Q(j, k) with the library's matrix-core GEMM."""
+def gemm_bf16(P: torch.Tensor, Q: torch.Tensor, K: int | None = None, *,
+              out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """C[i, j] = sum_k P[i, k] Q[j, k] with the library's matrix-core GEMM
+    (P (rows, >=K) and Q (cols, >=K) BF16, K-contiguous)."""
     _need_cuda(P, Q)
+    rows, cols = P.shape[0], Q.shape[0]
+    K = P.shape[1] if K is None else K
     C = torch.empty((rows, cols), dtype=torch.float32, device=P.device) if out is None else out
-    rc = lib().vce_gemm_bf16(_ptr(P), int(p_kmajor), P.stride(0), _ptr(Q), int(q_kmajor),
-                             Q.stride(0), rows, cols, K, _ptr(C), C.stride(0), _stream(stream))
+    rc = lib().vce_gemm_bf16(_ptr(P), P.stride(0), _ptr(Q), Q.stride(0), rows, cols, K, _ptr(C),
+                             C.stride(0), _stream(stream))
     _check("vce_gemm_bf16", rc)
     return C
+
+
+def transpose_bf16(src: torch.Tensor, *, out: torch.Tensor | None = None,
+                   stream=None) -> torch.Tensor:
+    """out[c, r] = src[r, c] for a 2-D 16-bit tensor, with the library's kernel."""
+    _need_cuda(src)
+    rows, cols = src.shape
+    dst = torch.empty((cols, rows), dtype=src.dtype, device=src.device) if out is None else out
+    rc = lib().vce_transpose_bf16(_ptr(src), rows, cols, src.stride(0), _ptr(dst), dst.stride(0),
+                                  _stream(stream))
+    _check("vce_transpose_bf16", rc)
+    return dst

@@ -9,27 +9,31 @@
 // Performance methodology: four GEMMs for forward+backward).
 //
 // Design for CDNA4 (not the SM100 design of that PR):
-//  * One GEMM core: a 256 x 256 output tile per 256-thread workgroup, four
-//    wavefronts of 128 x 128, v_mfma_f32_32x32x16_bf16, K staged through LDS
-//    in 64-deep slices, double buffered (128 KB of the 160 KB LDS), one
-//    barrier per slice.  16-byte chunks are XOR-swizzled across rows so the
-//    fragment reads and the tile writes avoid bank conflicts.  An operand may
-//    be stored K-contiguous or dim-contiguous; the latter is transposed in
-//    registers (8 x 8 BF16 blocks) on its way into LDS, so every GEMM of the
-//    backward reads X, W and dZ in place.
+//  * One GEMM core, C[i][j] = sum_k P[i][k] Q[j][k] with both operands stored
+//    K-contiguous: a 256 x 256 output tile per 512-thread workgroup, eight
+//    wavefronts (two per SIMD, so one wave's waits overlap the other's
+//    matrix work) of 128 x 64 each, v_mfma_f32_32x32x16_bf16.  K advances in
+//    64-deep slices through two LDS stages (128 KB of the 160 KB); global
+//    data goes straight to LDS (buffer_load ... lds), one 1 KB load per wave
+//    per operand and k-step, so the next slice streams in under the current
+//    one's MFMAs.  16-byte chunks are XOR-swizzled across rows (the loads
+//    pick their source addresses so the linear LDS writes land swizzled) and
+//    the fragment reads are bank-conflict free.
+//  * Tile order: hardware workgroup ids go round-robin over the 8 XCDs, so
+//    each XCD is given a contiguous range of tiles, walked in bands of 8 row
+//    tiles so the 32 workgroups an XCD runs at once share both operands in
+//    its L2.
 //  * Forward: tiles are (vocabulary x tokens); each lane owns tokens, so the
 //    epilogue reduces the online LSE (max, sum of exp, sum of logits) over the
 //    vocabulary inside the lane, then across the two lane halves and the two
 //    wavefronts that share the tokens.  Per-tile partials are merged per
 //    token by a second kernel in a fixed order.
-//  * Backward: the vocabulary is processed in chunks.  Per chunk: recompute
-//    the logits and write dZ (BF16) to the workspace; dW rows of the chunk are
-//    finished by one GEMM over all tokens (written once, never accumulated);
-//    dX accumulates chunk by chunk in an FP32 buffer, the last chunk writes
-//    BF16.
-//  * Tile order is XCD-aware: consecutive workgroups go round-robin over the
-//    8 XCDs, so each XCD is given a contiguous range of tiles, in which
-//    neighbouring tiles share their vocabulary slice of W (L2 reuse).
+//  * Backward, per vocabulary chunk: recompute the logits and write dZ (BF16)
+//    token-major and vocabulary-major; dW rows of the chunk are finished by
+//    one GEMM over all tokens (written once, never accumulated); dX
+//    accumulates chunk by chunk in FP32, the last chunk writes BF16.  The
+//    K-contiguous copies this needs (X^T once per call, W_c^T per chunk) are
+//    made by an LDS-tiled transpose; they cost a few percent of the GEMM time.
 #include "vce_device.h"
 #include "vce_internal.h"
 
@@ -39,19 +43,24 @@ namespace {
 
 constexpr int BM = 256;   // output rows per tile (P side)
 constexpr int BN = 256;   // output cols per tile (Q side)
-constexpr int BK = 64;    // K slice
-constexpr int NT = 256;   // threads per workgroup
-constexpr int kLdsElems = 2 * (BM + BN) * BK;  // two stages of P and Q, BF16
-constexpr int64_t kChunk = 32768;              // backward vocabulary chunk
+constexpr int BK = 64;    // K slice per stage
+constexpr int NT = 512;   // threads per workgroup: 8 wavefronts
+constexpr int WN = 64;    // output cols per wavefront
+constexpr int NB = WN / 32;                        // 32-column blocks per wavefront
+constexpr int ROWS_PER_LD = 1024 / (BK * 2);       // rows one 1 KB LDS load covers (8)
+constexpr int LD_PER_WAVE = BM / 8 / ROWS_PER_LD;  // loads per wave per operand per slice (4)
+constexpr int GROUP_I = 8;                         // row tiles per band of the tile order
+constexpr int64_t kChunk = 32768;                  // backward vocabulary chunk
+constexpr uint32_t kOob = 0x80000000u;             // buffer offset that reads as 0
 
-static_assert(BM == BN, "the tile loaders assume square tiles");
+static_assert(BM == BN, "one loader shape serves both operands");
+static_assert(LD_PER_WAVE == BK / 16, "one load per operand per k-step");
 
-// An operand of C[i][j] = sum_k P(i, k) Q(j, k).
-//   K-contiguous:   element (d, k) at base[d * ld + k]
-//   dim-contiguous: element (d, k) at base[k * ld + d]
-// dim_limit: d >= dim_limit reads as 0.  k_limit: k >= k_limit reads as 0.
-// For K-contiguous operands k is tested per 8-element chunk (chunk start),
-// for dim-contiguous ones d is tested per 8-element chunk.
+#define LDS_AS __attribute__((address_space(3)))
+
+// Both operands: element (d, k) at base[d * ld + k].  d >= dim_limit reads as
+// 0; k is masked per 8-element chunk (chunk start >= k_limit reads as 0), so
+// a buffer must hold zeros from k_limit up to the next multiple of 8.
 struct Operand {
   const uint16_t* base;
   int64_t ld;
@@ -59,154 +68,146 @@ struct Operand {
   int64_t k_limit;
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return chunk ^ ((row ^ (row >> 3)) & 7);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const uint16_t* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), (short)0, 0x7fffffff,
+                                           0x00020000);
 }
 
-template <bool KC>
-struct TileLoader;
+// LDS rows are BK elements (128 B, 8 chunks); chunk c of row r lives at
+// c ^ swz(r).
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
-// K-contiguous: 256 rows x 8 chunks; thread t loads chunk (t & 7) of rows
-// (t >> 3) + 32 i: eight threads cover one row's 128 contiguous bytes.
-template <>
-struct TileLoader<true> {
-  u32x4_t r[8];
-  __device__ __forceinline__ void load(const Operand& op, int64_t d0, int64_t k0, int tid) {
-    const int c = tid & 7;
-    const int64_t k = k0 + c * 8;
-    const bool kok = k < op.k_limit;
+// Streams one operand's 256 x 64 slice into an LDS stage: wave w brings rows
+// 32 w .. 32 w + 31, as LD_PER_WAVE loads of 8 rows (1 KB); lane l of a load
+// writes LDS bytes 16 l .. 16 l + 15, i.e. row l / 8, physical chunk l % 8,
+// so it reads the logical chunk (l % 8) ^ swz(row) from global memory.
+struct SliceLoader {
+  const uint16_t* tbase;  // operand at the tile's first row, k = 0
+  int64_t k_limit;
+  uint32_t off[LD_PER_WAVE];  // byte offset of this lane's chunk, or kOob
+  int kc[LD_PER_WAVE];        // element offset of this lane's chunk within the slice
+  __device__ __forceinline__ void init(const Operand& op, int64_t d0, int wave, int lane) {
+    tbase = op.base + d0 * op.ld;
+    k_limit = op.k_limit;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t d = d0 + (tid >> 3) + 32 * i;
-      if (kok && d < op.dim_limit)
-        r[i] = *reinterpret_cast<const u32x4_t*>(op.base + d * op.ld + k);
-      else
-        r[i] = u32x4_t{0u, 0u, 0u, 0u};
+    for (int i = 0; i < LD_PER_WAVE; ++i) {
+      const int row = wave * (BM / 8) + i * ROWS_PER_LD + (lane >> 3);
+      const int c = (lane & 7) ^ swz(row);
+      kc[i] = c * 8;
+      off[i] = (d0 + row < op.dim_limit) ? (uint32_t)(row * op.ld * 2 + c * 16) : kOob;
     }
   }
-  __device__ __forceinline__ void store(uint16_t* s, int tid) const {
-    const int c = tid & 7;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = (tid >> 3) + 32 * i;
-      *reinterpret_cast<u32x4_t*>(s + row * BK + swz(row, c) * 8) = r[i];
-    }
+  // load i of the slice starting at k0; `tail`: the slice reaches past k_limit
+  __device__ __forceinline__ void issue(uint16_t LDS_AS* stage, int64_t k0, int wave, int i,
+                                        bool tail) {
+    const __amdgpu_buffer_rsrc_t rs = rsrc_at(tbase + k0);
+    uint32_t o = off[i];
+    if (tail) o = (k0 + kc[i] < k_limit) ? o : kOob;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (void LDS_AS*)(stage + (wave * (BM / 8) + i * ROWS_PER_LD) * BK), 16, o, 0, 0, 0);
   }
 };
 
-// dim-contiguous: 64 k-rows x 256 dims; thread t loads the 8 x 8 block of
-// k-rows 8 (t >> 5) .. +7 and dims 8 (t & 31) .. +7 (32 threads cover 512
-// contiguous bytes of one k-row), then transposes it so LDS holds dim-rows.
-template <>
-struct TileLoader<false> {
-  u32x4_t r[8];
-  __device__ __forceinline__ void load(const Operand& op, int64_t d0, int64_t k0, int tid) {
-    const int kb = tid >> 5, db = tid & 31;
-    const int64_t d = d0 + db * 8;
-    const bool dok = d < op.dim_limit;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int64_t k = k0 + kb * 8 + kk;
-      if (dok && k < op.k_limit)
-        r[kk] = *reinterpret_cast<const u32x4_t*>(op.base + k * op.ld + d);
-      else
-        r[kk] = u32x4_t{0u, 0u, 0u, 0u};
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* s, int tid) const {
-    const int kb = tid >> 5, db = tid & 31;
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      const int q = dd >> 1;
-      u32x4_t o;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t lo = r[2 * p][q], hi = r[2 * p + 1][q];
-        o[p] = (dd & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-      }
-      const int row = db * 8 + dd;
-      *reinterpret_cast<u32x4_t*>(s + row * BK + swz(row, kb) * 8) = o;
-    }
-  }
-};
-
-__device__ __forceinline__ bf16x8_t frag(const uint16_t* s, int row, int chunk) {
-  return __builtin_bit_cast(bf16x8_t,
-                            *reinterpret_cast<const u32x4_t*>(s + row * BK + swz(row, chunk) * 8));
+__device__ __forceinline__ bf16x8_t frag(const uint16_t LDS_AS* s, int row, int chunk) {
+  return __builtin_bit_cast(
+      bf16x8_t, *reinterpret_cast<const u32x4_t LDS_AS*>(s + row * BK + ((chunk ^ swz(row)) * 8)));
 }
 
-// Hardware workgroup id -> logical tile: the dispatcher deals workgroups to
-// the 8 XCDs round-robin; give XCD x the contiguous logical range
-// [x q + min(x, rem), ...) so neighbouring tiles run on the same L2.
-__device__ __forceinline__ int xcd_remap(int b, int n) {
+// Hardware workgroup id -> (row tile, col tile).
+__device__ __forceinline__ void tile_of(int b, int n_ti, int n_tj, int* ti, int* tj) {
+  const int n = n_ti * n_tj;
   const int q = n >> 3, rem = n & 7;
   const int x = b & 7, slot = b >> 3;
-  return x * q + (x < rem ? x : rem) + slot;
+  const int t = x * q + (x < rem ? x : rem) + slot;  // contiguous range per XCD
+  const int band = t / (GROUP_I * n_tj);
+  const int in_band = t - band * GROUP_I * n_tj;
+  const int left = n_ti - band * GROUP_I;
+  const int gi = left < GROUP_I ? left : GROUP_I;
+  *ti = band * GROUP_I + in_band % gi;
+  *tj = in_band / gi;
 }
 
-// Output element of accumulator register r of block (a, b) for this lane:
+// Accumulator register r of block (a, b) of a lane holds
 //   row i = i0 + 128 wr + 32 a + 8 (r / 4) + 4 (lane / 32) + r % 4
-//   col j = j0 + 128 wc + 32 b + lane % 32
-template <bool PKC, bool QKC, class Epi>
-__global__ __launch_bounds__(NT, 1) void gemm_kernel(Operand P, Operand Q, int64_t K, int n_tj,
-                                                   int n_tiles, typename Epi::Params ep) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[kLdsElems];
-  // stage s: P slice at smem + s * BM * BK, Q slice at smem + 2 * BM * BK + s * BN * BK
-  uint16_t* const sQbase = smem + 2 * BM * BK;
+//   col j = j0 + 64 wc + 32 b + lane % 32
+// for wavefront (wr, wc) = (wave / 4, wave % 4).
+template <class Epi>
+__global__ __launch_bounds__(NT) void gemm_kernel(Operand P, Operand Q, int64_t K, int n_ti,
+                                                  int n_tj, typename Epi::Params ep) {
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * (BM + BN) * BK];
+  uint16_t LDS_AS* const sp = (uint16_t LDS_AS*)smem;  // P stages: sp + s * BM * BK
+  uint16_t LDS_AS* const sq = sp + 2 * BM * BK;         // Q stages: sq + s * BN * BK
 
-  const int tile = xcd_remap(blockIdx.x, n_tiles);
-  const int ti = tile / n_tj, tj = tile - (tile / n_tj) * n_tj;
+  int ti, tj;
+  tile_of(blockIdx.x, n_ti, n_tj, &ti, &tj);
   const int64_t i0 = (int64_t)ti * BM, j0 = (int64_t)tj * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
+  const int wr = wave >> 2, wc = wave & 3;
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][NB];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-  TileLoader<PKC> lp;
-  TileLoader<QKC> lq;
+  SliceLoader lp, lq;
+  lp.init(P, i0, wave, lane);
+  lq.init(Q, j0, wave, lane);
   const int nk = (int)((K + BK - 1) / BK);
-  lp.load(P, i0, 0, tid);
-  lq.load(Q, j0, 0, tid);
-  lp.store(smem, tid);
-  lq.store(sQbase, tid);
-  __syncthreads();
-
-  const int prow = wr * 128 + (lane & 31), qrow = wc * 128 + (lane & 31);
+  {
+    const bool tail = BK > K;
+#pragma unroll
+    for (int i = 0; i < LD_PER_WAVE; ++i) {
+      lp.issue(sp, 0, wave, i, tail);
+      lq.issue(sq, 0, wave, i, tail);
+    }
+  }
+  const int prow = wr * 128 + (lane & 31), qrow = wc * WN + (lane & 31);
   const int khalf = lane >> 5;
   for (int kt = 0; kt < nk; ++kt) {
+    // this wave's loads of slice kt have landed; after the barrier everyone's
+    // have, and nobody still reads the stage slice kt + 1 goes into
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
     const int cur = kt & 1;
+    const uint16_t LDS_AS* cp = sp + cur * BM * BK;
+    const uint16_t LDS_AS* cq = sq + cur * BN * BK;
+    uint16_t LDS_AS* np = sp + (cur ^ 1) * BM * BK;
+    uint16_t LDS_AS* nq = sq + (cur ^ 1) * BN * BK;
     const bool more = kt + 1 < nk;
-    if (more) {
-      lp.load(P, i0, (int64_t)(kt + 1) * BK, tid);
-      lq.load(Q, j0, (int64_t)(kt + 1) * BK, tid);
-    }
-    const uint16_t* cp = smem + cur * (BM * BK);
-    const uint16_t* cq = sQbase + cur * (BN * BK);
+    const int64_t kn = (int64_t)(kt + 1) * BK;
+    const bool tail = kn + BK > K;
+    bf16x8_t fa[2][4], fb[2][NB];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) fa[0][a] = frag(cp, prow + 32 * a, khalf);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) fb[0][b] = frag(cq, qrow + 32 * b, khalf);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8_t fa[4], fb[4];
+      const int f = ks & 1;
+      if (ks + 1 < BK / 16) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a) fa[a] = frag(cp, prow + 32 * a, 2 * ks + khalf);
+        for (int a = 0; a < 4; ++a) fa[f ^ 1][a] = frag(cp, prow + 32 * a, 2 * (ks + 1) + khalf);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) fb[b] = frag(cq, qrow + 32 * b, 2 * ks + khalf);
+        for (int b = 0; b < NB; ++b) fb[f ^ 1][b] = frag(cq, qrow + 32 * b, 2 * (ks + 1) + khalf);
+      }
+      if (more) {
+        lp.issue(np, kn, wave, ks, tail);
+        lq.issue(nq, kn, wave, ks, tail);
+      }
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+        for (int b = 0; b < NB; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][a], fb[f][b], acc[a][b], 0, 0, 0);
+      // k-step regions: keep each step's reads and loads under its MFMAs
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) {
-      lp.store(smem + (cur ^ 1) * (BM * BK), tid);
-      lq.store(sQbase + (cur ^ 1) * (BN * BK), tid);
-    }
-    __syncthreads();
   }
+  __syncthreads();  // LDS is free for the epilogue
   Epi::apply(ep, acc, i0, j0, wr, wc, lane, smem);
 }
 
@@ -218,11 +219,11 @@ struct EpiF32 {
     float* C;
     int64_t ldc, rows, cols;
   };
-  __device__ static void apply(const Params& p, f32x16_t (&acc)[4][4], int64_t i0, int64_t j0,
+  __device__ static void apply(const Params& p, f32x16_t (&acc)[4][NB], int64_t i0, int64_t j0,
                                int wr, int wc, int lane, uint16_t*) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int64_t j = j0 + wc * 128 + b * 32 + (lane & 31);
+    for (int b = 0; b < NB; ++b) {
+      const int64_t j = j0 + wc * WN + b * 32 + (lane & 31);
       if (j >= p.cols) continue;
 #pragma unroll
       for (int a = 0; a < 4; ++a)
@@ -247,7 +248,7 @@ struct EpiLse {
     const int64_t* targets;
     int64_t M, V, Mp, ignore_idx;
   };
-  __device__ static void apply(const Params& p, f32x16_t (&acc)[4][4], int64_t i0, int64_t j0,
+  __device__ static void apply(const Params& p, f32x16_t (&acc)[4][NB], int64_t i0, int64_t j0,
                                int wr, int wc, int lane, uint16_t* smem) {
     float* sh = reinterpret_cast<float*>(smem);  // [wr][wc][b][lane 0..31][3]
     const int64_t vbase = i0 + wr * 128 + 4 * (lane >> 5);
@@ -255,8 +256,8 @@ struct EpiLse {
     const int64_t lim64 = p.V - vbase;
     const int lim = lim64 > 128 ? 128 : (lim64 < 0 ? 0 : (int)lim64);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int64_t j = j0 + wc * 128 + b * 32 + (lane & 31);
+    for (int b = 0; b < NB; ++b) {
+      const int64_t j = j0 + wc * WN + b * 32 + (lane & 31);
       float mx = kNegInf;
 #pragma unroll
       for (int a = 0; a < 4; ++a)
@@ -296,21 +297,21 @@ struct EpiLse {
         if (inr) p.zt[j] = zt;
       }
       if (lane < 32) {
-        float* e = sh + (((wr * 2 + wc) * 4 + b) * 32 + lane) * 3;
+        float* e = sh + (((wr * 4 + wc) * NB + b) * 32 + lane) * 3;
         e[0] = mx;
         e[1] = d;
         e[2] = s;
       }
     }
     __syncthreads();
-    // one wavefront per token column half merges the two vocabulary halves
+    // the wavefront of the first vocabulary half merges the second half's state
     if (wr == 0 && lane < 32) {
       const int64_t vt = i0 / BM;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int64_t j = j0 + wc * 128 + b * 32 + lane;
-        const float* e0 = sh + (((0 * 2 + wc) * 4 + b) * 32 + lane) * 3;
-        const float* e1 = sh + (((1 * 2 + wc) * 4 + b) * 32 + lane) * 3;
+      for (int b = 0; b < NB; ++b) {
+        const int64_t j = j0 + wc * WN + b * 32 + lane;
+        const float* e0 = sh + (((0 * 4 + wc) * NB + b) * 32 + lane) * 3;
+        const float* e1 = sh + (((1 * 4 + wc) * NB + b) * 32 + lane) * 3;
         LseState st{e0[0], e0[1], e0[2]};
         lse_merge(st, LseState{e1[0], e1[1], e1[2]});
         if (j < p.M) {
@@ -324,11 +325,14 @@ struct EpiLse {
 };
 
 // Backward dZ: rows = vocabulary of the chunk, cols = tokens.
-// dZ = g (exp(z - lse) - (1-eps)[v = t] - eps/V), stored BF16 token-major.
+// dZ = g (exp(z - lse) - (1-eps)[v = t] - eps/V), BF16, written token-major
+// (dz[m * ldz + v]) and vocabulary-major (dzt[v * ldt + m]).  Padding rows and
+// columns of both buffers receive zeros.
 struct EpiDz {
   struct Params {
     uint16_t* dz;
-    int64_t ldz, c0, vc_valid;
+    uint16_t* dzt;
+    int64_t ldz, ldt, c0, vc_valid;
     const float* stats;
     const int64_t* targets;
     const float* grad_output;
@@ -337,7 +341,7 @@ struct EpiDz {
     int reduce_loss;
     int64_t ignore_idx, M, V;
   };
-  __device__ static void apply(const Params& p, f32x16_t (&acc)[4][4], int64_t i0, int64_t j0,
+  __device__ static void apply(const Params& p, f32x16_t (&acc)[4][NB], int64_t i0, int64_t j0,
                                int wr, int wc, int lane, uint16_t*) {
     float gscale = 0.0f;
     if (p.reduce_loss) {
@@ -345,8 +349,8 @@ struct EpiDz {
       gscale = p.grad_output[0] / (float)(nv > 0 ? nv : 1);
     }
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int64_t j = j0 + wc * 128 + b * 32 + (lane & 31);
+    for (int b = 0; b < NB; ++b) {
+      const int64_t j = j0 + wc * WN + b * 32 + (lane & 31);
       int64_t t = -1;
       float g = 0.0f, lse2 = 0.0f;
       bool live = false, bad = false;
@@ -385,8 +389,14 @@ struct EpiDz {
             x = (off == trel) ? x - gt : x;
             val[e] = (live && off < lim) ? x : fill;
           }
-          u32x2_t w = {pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
-          *reinterpret_cast<u32x2_t*>(p.dz + j * p.ldz + vrow0 + a * 32 + 8 * q) = w;
+          const uint32_t w01 = pack_bf16x2(val[0], val[1]), w23 = pack_bf16x2(val[2], val[3]);
+          const int64_t v = vrow0 + a * 32 + 8 * q;
+          *reinterpret_cast<u32x2_t*>(p.dz + j * p.ldz + v) = u32x2_t{w01, w23};
+          uint16_t* col = p.dzt + v * p.ldt + j;
+          col[0] = (uint16_t)(w01 & 0xffffu);
+          col[p.ldt] = (uint16_t)(w01 >> 16);
+          col[2 * p.ldt] = (uint16_t)(w23 & 0xffffu);
+          col[3 * p.ldt] = (uint16_t)(w23 >> 16);
         }
     }
   }
@@ -398,11 +408,11 @@ struct EpiDw {
     uint16_t* dW;
     int64_t H, c0, vc_valid;
   };
-  __device__ static void apply(const Params& p, f32x16_t (&acc)[4][4], int64_t i0, int64_t j0,
+  __device__ static void apply(const Params& p, f32x16_t (&acc)[4][NB], int64_t i0, int64_t j0,
                                int wr, int wc, int lane, uint16_t*) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int64_t j = j0 + wc * 128 + b * 32 + (lane & 31);
+    for (int b = 0; b < NB; ++b) {
+      const int64_t j = j0 + wc * WN + b * 32 + (lane & 31);
       if (j >= p.vc_valid) continue;
       uint16_t* row = p.dW + (p.c0 + j) * p.H;
 #pragma unroll
@@ -429,11 +439,11 @@ struct EpiDx {
     int64_t H, M;
     int mode;
   };
-  __device__ static void apply(const Params& p, f32x16_t (&acc)[4][4], int64_t i0, int64_t j0,
+  __device__ static void apply(const Params& p, f32x16_t (&acc)[4][NB], int64_t i0, int64_t j0,
                                int wr, int wc, int lane, uint16_t*) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int64_t j = j0 + wc * 128 + b * 32 + (lane & 31);
+    for (int b = 0; b < NB; ++b) {
+      const int64_t j = j0 + wc * WN + b * 32 + (lane & 31);
       if (j >= p.M) continue;
 #pragma unroll
       for (int a = 0; a < 4; ++a)
@@ -455,6 +465,69 @@ struct EpiDx {
     }
   }
 };
+
+// ---- transpose -------------------------------------------------------------------
+
+// dst[c * ld_dst + r] = src[r * ld_src + c] for r < rows, c < cols, and 0 for
+// rows <= r < rows_pad.  64 x 64 tiles through LDS.
+struct TransposeParams {
+  const uint16_t* src;
+  uint16_t* dst;
+  int64_t rows, cols, ld_src, ld_dst, rows_pad;
+};
+
+constexpr int TT = 64;   // tile edge
+constexpr int TPAD = 2;  // LDS row padding (elements): column reads hit distinct banks
+
+__global__ __launch_bounds__(256) void transpose_kernel(TransposeParams p) {
+  __shared__ uint16_t tile[TT][TT + TPAD];
+  const int64_t r0 = (int64_t)blockIdx.y * TT, c0 = (int64_t)blockIdx.x * TT;
+  const int tid = threadIdx.x;
+  // load: 64 rows x 8 vectors of 8 elements; thread -> (row tid/8 + 32 h, vector tid%8)
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int rr = (tid >> 3) + 32 * h, vv = tid & 7;
+    const int64_t r = r0 + rr, c = c0 + vv * 8;
+    uint16_t e[8];
+    if (r < p.rows && c + 8 <= p.cols) {
+      const u32x4_t w = *reinterpret_cast<const u32x4_t*>(p.src + r * p.ld_src + c);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        e[2 * k] = (uint16_t)(w[k] & 0xffffu);
+        e[2 * k + 1] = (uint16_t)(w[k] >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        e[k] = (r < p.rows && c + k < p.cols) ? p.src[r * p.ld_src + c + k] : (uint16_t)0;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) tile[rr][vv * 8 + k] = e[k];
+  }
+  __syncthreads();
+  // store: dst rows c0 .. c0+63, 8 vectors of 8 along r
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int cc = (tid >> 3) + 32 * h, vv = tid & 7;
+    const int64_t c = c0 + cc, r = r0 + vv * 8;
+    if (c >= p.cols || r >= p.rows_pad) continue;
+    uint16_t e[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) e[k] = tile[vv * 8 + k][cc];
+    if (r + 8 <= p.rows_pad) {
+      u32x4_t w;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[k] = (uint32_t)e[2 * k] | ((uint32_t)e[2 * k + 1] << 16);
+      *reinterpret_cast<u32x4_t*>(p.dst + c * p.ld_dst + r) = w;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (r + k < p.rows_pad) p.dst[c * p.ld_dst + r + k] = e[k];
+    }
+  }
+}
+
+// ---- merge ------------------------------------------------------------------------
 
 // Per-token merge of the forward partials (fixed order), then loss and stats.
 struct MergeParams {
@@ -499,15 +572,27 @@ __global__ __launch_bounds__(256) void lce_merge_kernel(MergeParams p) {
   *reinterpret_cast<f32x4_t*>(p.stats + 4 * j) = f32x4_t{st.m, st.d, zt, mean};
 }
 
-template <bool PKC, bool QKC, class Epi>
+// ---- host side ------------------------------------------------------------------
+
+template <class Epi>
 hipError_t run_gemm(const Operand& P, const Operand& Q, int64_t rows, int64_t cols, int64_t K,
                     const typename Epi::Params& ep, hipStream_t stream) {
   const int64_t n_ti = (rows + BM - 1) / BM, n_tj = (cols + BN - 1) / BN;
   const int64_t n = n_ti * n_tj;
   if (n <= 0) return hipSuccess;
-  if (n > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_kernel<PKC, QKC, Epi>), dim3((unsigned)n), dim3(NT), 0, stream, P, Q,
-                     K, (int)n_tj, (int)n, ep);
+  if (n > INT32_MAX / 2) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_kernel<Epi>), dim3((unsigned)n), dim3(NT), 0, stream, P, Q, K,
+                     (int)n_ti, (int)n_tj, ep);
+  return hipGetLastError();
+}
+
+hipError_t run_transpose(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld_src,
+                         uint16_t* dst, int64_t ld_dst, int64_t rows_pad, hipStream_t stream) {
+  if (rows_pad <= 0 || cols <= 0) return hipSuccess;
+  const int64_t gx = (cols + TT - 1) / TT, gy = (rows_pad + TT - 1) / TT;
+  if (gx > INT32_MAX || gy > 65535) return hipErrorInvalidValue;
+  TransposeParams tp{src, dst, rows, cols, ld_src, ld_dst, rows_pad};
+  hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream, tp);
   return hipGetLastError();
 }
 
@@ -517,25 +602,35 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool lce_make_plan(int64_t M, int64_t H, int64_t V, LcePlan* plan) {
   if (M < 0 || H <= 0 || V <= 0 || H % 8 != 0) return false;
-  if (M > ((int64_t)1 << 31) || V > ((int64_t)1 << 31) || H > ((int64_t)1 << 20)) return false;
+  // Every buffer offset a GEMM load forms (256 rows x leading dimension x 2 B)
+  // stays below 2^31; transpose grids stay within range.
+  if (H > ((int64_t)1 << 20) || V > ((int64_t)1 << 31)) return false;
   LcePlan p;
   p.M = M;
   p.H = H;
   p.V = V;
   p.Mp = ((M > 0 ? M : 1) + BN - 1) / BN * BN;
+  if (p.Mp > ((int64_t)1 << 22) - BN) return false;
   p.n_vtiles = (V + BM - 1) / BM;
   const int64_t vr = (V + BM - 1) / BM * BM;
   p.chunk = vr < kChunk ? vr : kChunk;
   p.n_chunks = (V + p.chunk - 1) / p.chunk;
   p.ldz = p.chunk;
   const size_t part = align256((size_t)p.n_vtiles * p.Mp * 4);
-  p.off_part = 0;
   const size_t fwd = 3 * part + align256((size_t)p.Mp * 4);
-  const size_t dz = align256((size_t)p.Mp * p.ldz * 2);
+  // backward: X^T (H x Mp), W_c^T (H x chunk), dZ (Mp x chunk), dZ^T (chunk x Mp), dX acc
+  const size_t xt = align256((size_t)H * p.Mp * 2);
+  const size_t wt = align256((size_t)H * p.chunk * 2);
+  const size_t dz = align256((size_t)p.Mp * p.chunk * 2);
   const size_t dx = p.n_chunks > 1 ? align256((size_t)p.Mp * H * 4) : 0;
-  p.off_dz = 0;
-  p.off_dx = dz;
-  p.total = fwd > dz + dx ? fwd : dz + dx;
+  p.off_part = 0;
+  p.off_xt = 0;
+  p.off_wt = xt;
+  p.off_dz = xt + wt;
+  p.off_dzt = xt + wt + dz;
+  p.off_dx = xt + wt + 2 * dz;
+  const size_t bwd = p.off_dx + dx;
+  p.total = fwd > bwd ? fwd : bwd;
   *plan = p;
   return true;
 }
@@ -552,7 +647,7 @@ hipError_t launch_lce_forward(const LcePlan& plan, const LceFwdArgs& a, hipStrea
   Operand P{W, plan.H, plan.V, plan.H};
   Operand Q{X, plan.H, plan.M, plan.H};
   EpiLse::Params ep{pm, pd, ps, zt, a.targets, plan.M, plan.V, plan.Mp, a.ignore_idx};
-  hipError_t e = run_gemm<true, true, EpiLse>(P, Q, plan.V, plan.Mp, plan.H, ep, stream);
+  hipError_t e = run_gemm<EpiLse>(P, Q, plan.V, plan.Mp, plan.H, ep, stream);
   if (e != hipSuccess) return e;
   MergeParams mp{pm, pd, ps, zt, a.targets, plan.M, plan.Mp, plan.V, plan.n_vtiles,
                  a.ignore_idx, a.eps, a.loss_tok, a.stats};
@@ -563,54 +658,65 @@ hipError_t launch_lce_forward(const LcePlan& plan, const LceFwdArgs& a, hipStrea
 
 hipError_t launch_lce_backward(const LcePlan& plan, const LceBwdArgs& a, hipStream_t stream) {
   if (plan.M == 0) return hipSuccess;  // dW of an empty batch: nothing reads it
+  uint16_t* xt = reinterpret_cast<uint16_t*>(a.ws + plan.off_xt);
+  uint16_t* wt = reinterpret_cast<uint16_t*>(a.ws + plan.off_wt);
   uint16_t* dz = reinterpret_cast<uint16_t*>(a.ws + plan.off_dz);
+  uint16_t* dzt = reinterpret_cast<uint16_t*>(a.ws + plan.off_dzt);
   float* dxacc = reinterpret_cast<float*>(a.ws + plan.off_dx);
   const uint16_t* X = static_cast<const uint16_t*>(a.X);
   const uint16_t* W = static_cast<const uint16_t*>(a.W);
+  // X^T (H x Mp), tokens M..Mp-1 zero
+  hipError_t e = run_transpose(X, plan.M, plan.H, plan.H, xt, plan.Mp, plan.Mp, stream);
+  if (e != hipSuccess) return e;
   for (int64_t c = 0; c < plan.n_chunks; ++c) {
     const int64_t c0 = c * plan.chunk;
     const int64_t vc = (plan.V - c0) < plan.chunk ? (plan.V - c0) : plan.chunk;
     const uint16_t* Wc = W + c0 * plan.H;
-    // dZ of the chunk: (vocabulary x tokens), K = H
+    // dZ of the chunk (both layouts): (vocabulary x tokens), K = H
     {
       Operand P{Wc, plan.H, vc, plan.H};
       Operand Q{X, plan.H, plan.M, plan.H};
-      EpiDz::Params ep{dz, plan.ldz, c0, vc, a.stats, a.targets, a.grad_output, a.n_valid,
-                       a.eps, a.reduce_loss, a.ignore_idx, plan.M, plan.V};
-      hipError_t e = run_gemm<true, true, EpiDz>(P, Q, vc, plan.Mp, plan.H, ep, stream);
+      EpiDz::Params ep{dz, dzt, plan.ldz, plan.Mp, c0, vc, a.stats, a.targets, a.grad_output,
+                       a.n_valid, a.eps, a.reduce_loss, a.ignore_idx, plan.M, plan.V};
+      e = run_gemm<EpiDz>(P, Q, vc, plan.Mp, plan.H, ep, stream);
       if (e != hipSuccess) return e;
     }
     // dW rows of the chunk: (hidden x vocabulary), K = tokens
     {
-      Operand P{X, plan.H, plan.H, plan.M};
-      Operand Q{dz, plan.ldz, plan.ldz, plan.M};
+      Operand P{xt, plan.Mp, plan.H, plan.M};
+      Operand Q{dzt, plan.Mp, vc, plan.M};
       EpiDw::Params ep{static_cast<uint16_t*>(a.dW), plan.H, c0, vc};
-      hipError_t e = run_gemm<false, false, EpiDw>(P, Q, plan.H, vc, plan.M, ep, stream);
+      e = run_gemm<EpiDw>(P, Q, plan.H, vc, plan.M, ep, stream);
       if (e != hipSuccess) return e;
     }
+    // W_c^T (H x chunk), vocabulary rows vc .. next multiple of 64 zero; then
     // dX += dZ_c W_c: (hidden x tokens), K = vocabulary of the chunk
     {
-      Operand P{Wc, plan.H, plan.H, vc};
-      Operand Q{dz, plan.ldz, plan.M, (vc + 7) / 8 * 8};
+      e = run_transpose(Wc, vc, plan.H, plan.H, wt, plan.chunk, (vc + 63) / 64 * 64, stream);
+      if (e != hipSuccess) return e;
+      Operand P{wt, plan.chunk, plan.H, vc};
+      Operand Q{dz, plan.ldz, plan.M, vc};
       const int mode = (c > 0 ? 1 : 0) | (c + 1 == plan.n_chunks ? 2 : 0);
       EpiDx::Params ep{dxacc, static_cast<uint16_t*>(a.dX), plan.H, plan.M, mode};
-      hipError_t e = run_gemm<false, true, EpiDx>(P, Q, plan.H, plan.M, vc, ep, stream);
+      e = run_gemm<EpiDx>(P, Q, plan.H, plan.M, vc, ep, stream);
       if (e != hipSuccess) return e;
     }
   }
   return hipSuccess;
 }
 
-hipError_t launch_gemm_bf16(const void* P, int p_kmajor, int64_t ldp, const void* Q, int q_kmajor,
-                            int64_t ldq, int64_t rows, int64_t cols, int64_t K, float* C,
-                            int64_t ldc, hipStream_t stream) {
+hipError_t launch_gemm_bf16(const void* P, int64_t ldp, const void* Q, int64_t ldq, int64_t rows,
+                            int64_t cols, int64_t K, float* C, int64_t ldc, hipStream_t stream) {
   Operand op{static_cast<const uint16_t*>(P), ldp, rows, K};
   Operand oq{static_cast<const uint16_t*>(Q), ldq, cols, K};
   EpiF32::Params ep{C, ldc, rows, cols};
-  if (p_kmajor && q_kmajor) return run_gemm<true, true, EpiF32>(op, oq, rows, cols, K, ep, stream);
-  if (p_kmajor) return run_gemm<true, false, EpiF32>(op, oq, rows, cols, K, ep, stream);
-  if (q_kmajor) return run_gemm<false, true, EpiF32>(op, oq, rows, cols, K, ep, stream);
-  return run_gemm<false, false, EpiF32>(op, oq, rows, cols, K, ep, stream);
+  return run_gemm<EpiF32>(op, oq, rows, cols, K, ep, stream);
+}
+
+hipError_t launch_transpose_bf16(const void* src, int64_t rows, int64_t cols, int64_t ld_src,
+                                 void* dst, int64_t ld_dst, hipStream_t stream) {
+  return run_transpose(static_cast<const uint16_t*>(src), rows, cols, ld_src,
+                       static_cast<uint16_t*>(dst), ld_dst, rows, stream);
 }
 
 }  // namespace vce

@@ -54,7 +54,9 @@ struct LcePlan {
   int64_t chunk;       // vocabulary rows per backward chunk (multiple of the tile)
   int64_t n_chunks;
   int64_t ldz;         // row stride (elements) of the dZ chunk buffer
-  size_t off_part, off_dz, off_dx, total;
+  size_t off_part;     // forward: per-tile partials and target logits
+  size_t off_xt, off_wt, off_dz, off_dzt, off_dx;  // backward buffers
+  size_t total;
 };
 
 bool lce_make_plan(int64_t M, int64_t H, int64_t V, LcePlan* plan);
@@ -90,8 +92,9 @@ struct LceBwdArgs {
 
 hipError_t launch_lce_forward(const LcePlan& plan, const LceFwdArgs& a, hipStream_t stream);
 hipError_t launch_lce_backward(const LcePlan& plan, const LceBwdArgs& a, hipStream_t stream);
-hipError_t launch_gemm_bf16(const void* P, int p_kmajor, int64_t ldp, const void* Q, int q_kmajor,
-                            int64_t ldq, int64_t rows, int64_t cols, int64_t K, float* C,
-                            int64_t ldc, hipStream_t stream);
+hipError_t launch_gemm_bf16(const void* P, int64_t ldp, const void* Q, int64_t ldq, int64_t rows,
+                            int64_t cols, int64_t K, float* C, int64_t ldc, hipStream_t stream);
+hipError_t launch_transpose_bf16(const void* src, int64_t rows, int64_t cols, int64_t ld_src,
+                                 void* dst, int64_t ld_dst, hipStream_t stream);
 
 }  // namespace vce
