@@ -172,11 +172,34 @@ def bench_linear(case, steps: int, warmup: int):
         roofline={"bound": "mfma", "achieved": round(f_fwd / (avg_f * 1e-3) / 1e12, 2),
                   "peak": peak, "unit": "TFLOP/s",
                   "frac": round(f_fwd / (avg_f * 1e-3) / 1e12 / peak, 4),
-                  "traffic": None, "kernel": "lce_forward (GEMM + online-LSE epilogue, merge)"},
+                  "traffic": recorded_traffic("lce_forward"),
+                  "kernel": "lce_forward (GEMM + online-LSE epilogue, merge)"},
         bwd_tflops=f_bwd / (avg_b * 1e-3) / 1e12,
         fb_frac_of_peak=f_fb / (ms_step * 1e-3) / 1e12 / peak,
         workspace_MiB=ws.numel() / 2 ** 20,
     )
+
+
+def recorded_traffic(key: str):
+    """HBM bytes per launch of kernel `key`, from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary under profiles/ (copy-calibrated), or None when the kernel's
+    sources have changed since the counters were taken (sha256 of the listed files)."""
+    import glob
+    import hashlib
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "pmc_hbm_bytes_*.md"))):
+        with open(path) as f:
+            for line in f:
+                if not line.startswith("traffic-json:"):
+                    continue
+                rec = json.loads(line.split(":", 1)[1]).get(key)
+                if rec is None:
+                    continue
+                h = hashlib.sha256()
+                for src in rec["sources"]:
+                    with open(os.path.join(ROOT, src), "rb") as g:
+                        h.update(g.read())
+                return rec["bytes_per_launch"] if h.hexdigest() == rec["sha256"] else None
+    return None
 
 
 def cpu_baseline(case, budget_s: float = 10.0):
@@ -274,7 +297,7 @@ def main():
                    "label_smoothing": case.label_smoothing, "reduce_loss": case.reduce_loss,
                    "ignored_rows": case.meta["n_ignored"], "grad": "separate buffer"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": peak, "unit": "GB/s",
-                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "frac": round(achieved / peak, 4), "traffic": recorded_traffic("ce_bwd"),
                      "kernel": "ce_bwd (ce_backward row sweep)",
                      "bytes_per_launch": res["bytes_bwd"]},
         "cpu_baseline": cpu,
