@@ -91,7 +91,7 @@ const char* vce_strerror(int status);
  *  stats    (N, 4) FP32 saved statistics (see above), always written.
  *  n_valid  1 int32: count of non-ignored rows; required iff reduce_loss
  *           (the backward of the averaged loss reads it), else may be NULL.
- *  Kernels: one row sweep (one 256-thread workgroup per row), plus one
+ *  Kernels: one row sweep (one 1024-thread workgroup per row), plus one
  *  single-workgroup deterministic mean when reduce_loss or n_valid is given.
  */
 int ce_forward(const void* logits, int dtype, int64_t d0, int64_t d1, int64_t V,
