@@ -173,14 +173,29 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Operand P, Operand Q, int64_t 
   // Phases end at workgroup barriers; the second group starts one phase late.
   //   group 0: phase 4k = M(k,0), 4k+1 = C(k,0), 4k+2 = M(k,1), 4k+3 = C(k,1)
   //   group 1: one phase later.
-  // Slice k+1 goes into the stage slice k-1 used; its last reader (group 1,
-  // M(k-1,1), phase 4k-1) is done before phase 4k.  Both groups issue their
-  // loads of slice k+1 in M(k,0) and wait for them before the barrier that
-  // ends phase 4k+3, so slice k+1 is complete when group 0 reads it in 4k+4.
+  // Wave w loads rows 32w..32w+31 of both operands, so the P rows a group
+  // loads are read by that group only; Q rows are read by both.
+  //  * Q rows of slice k+1 go into the stage slice k-1 used, in M(k,0), after
+  //    its last readers (group 0 in 4k-2, group 1 in 4k-1).
+  //  * P rows of slice k+2 go into the stage of slice k, in M(k,1), right
+  //    after the group's own last reads of them (lgkmcnt(0) first): two
+  //    phases earlier than M(k+1,0), which gives those loads more time.
+  // Group 0 reads slice k+1 from phase 4k+4: at the end of 4k+3 each wave
+  // waits until only its four P loads of slice k+2 are in flight
+  // (vmcnt(4)), which covers its Q loads of slice k+1 and the P loads of
+  // slice k+1 issued before them.
   // Every wave passes the same number of barriers (group 0 adds one at the
   // end), so no barrier waits on a wave that has left the loop.
   const bool g1 = wave >= 4;
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (nk > 1) {  // P rows of slice 1 (its Q rows follow in M(0,0))
+#pragma unroll
+    for (int i = 0; i < LD_PER_WAVE; ++i) lp.issue(sp + BM * BK, BK, wave, i, 2 * BK > K);
+  }
+  // slice 0 complete (only the P loads of slice 1 may be in flight)
+  if (nk > 1)
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
@@ -195,6 +210,10 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Operand P, Operand Q, int64_t 
     const bool more = kt + 1 < nk;
     const int64_t kn = (int64_t)(kt + 1) * BK;
     const bool tail = kn + BK > K;
+    const bool more2 = kt + 2 < nk;
+    const int64_t kn2 = (int64_t)(kt + 2) * BK;
+    const bool tail2 = kn2 + BK > K;
+    uint16_t LDS_AS* cpw = sp + cur * BM * BK;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       // memory phase: fragments of k-steps 2h and 2h+1; the next slice's loads
@@ -209,14 +228,23 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Operand P, Operand Q, int64_t 
       }
       if (h == 0 && more) {
 #pragma unroll
-        for (int i = 0; i < LD_PER_WAVE; ++i) {
-          lp.issue(np, kn, wave, i, tail);
-          lq.issue(nq, kn, wave, i, tail);
+        for (int i = 0; i < LD_PER_WAVE; ++i) lq.issue(nq, kn, wave, i, tail);
+      }
+      // reads complete: the stage may be refilled (now by this wave, after
+      // the barrier by the others)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (h == 1) {
+        if (more2) {
+#pragma unroll
+          for (int i = 0; i < LD_PER_WAVE; ++i) lp.issue(cpw, kn2, wave, i, tail2);
+        }
+        if (g1) {
+          if (more2)
+            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+          else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
       }
-      if (h == 1 && g1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      // reads complete before the barrier: the stage may be refilled after it
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
@@ -228,7 +256,13 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Operand P, Operand Q, int64_t 
 #pragma unroll
           for (int b = 0; b < NB; ++b)
             acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s2][a], fb[s2][b], acc[a][b], 0, 0, 0);
-      if (h == 1 && !g1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);  // the wait stays behind the MFMAs
+      if (h == 1 && !g1) {
+        if (more2)
+          asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
