@@ -162,21 +162,17 @@ int lce_backward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
 /*
  * vce_gemm_bf16: the matrix-core building block of the linear form, exported
  * so it can be checked and timed on its own.  C (rows, cols) FP32 row-major
- * with leading dimension ldc:  C[i][j] = sum_k P[i*ldp + k] Q[j*ldq + k]
- * (both operands K-contiguous, BF16; FP32 accumulation).  K, ldp and ldq
- * multiples of 8; ldp, ldq <= 2^22; P and Q 16-byte aligned.
+ * with leading dimension ldc:  C[i][j] = sum_k P(i, k) Q(j, k), BF16 operands,
+ * FP32 accumulation.  Each operand is stored
+ *   K-contiguous   (p_dim / q_dim = 0): P(i, k) = P[i * ldp + k]
+ *   dim-contiguous (p_dim / q_dim = 1): P(i, k) = P[k * ldp + i]
+ * (likewise Q with j, ldq).  The contiguous axis must be a multiple of 8 long
+ * (K for a K-contiguous operand, rows / cols for a dim-contiguous one); ldp,
+ * ldq multiples of 8 and at most 2^22; P and Q 16-byte aligned.  The backward
+ * of the linear form uses all three layout pairs it needs through this core.
  */
-int vce_gemm_bf16(const void* P, int64_t ldp, const void* Q, int64_t ldq, int64_t rows,
-                  int64_t cols, int64_t K, float* C, int64_t ldc, void* stream);
-
-/*
- * vce_transpose_bf16: dst[c*ld_dst + r] = src[r*ld_src + c] for r < rows,
- * c < cols (16-bit elements).  The backward of the linear form uses it to
- * give every GEMM K-contiguous operands.  ld_src >= cols, ld_dst >= rows,
- * both multiples of 8; 16-byte aligned, non-overlapping buffers.
- */
-int vce_transpose_bf16(const void* src, int64_t rows, int64_t cols, int64_t ld_src, void* dst,
-                       int64_t ld_dst, void* stream);
+int vce_gemm_bf16(const void* P, int64_t ldp, int p_dim, const void* Q, int64_t ldq, int q_dim,
+                  int64_t rows, int64_t cols, int64_t K, float* C, int64_t ldc, void* stream);
 
 #ifdef __cplusplus
 }

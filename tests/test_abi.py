@@ -36,7 +36,7 @@ def L():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("ce_forward", "ce_backward", "lce_forward", "lce_backward", "lce_workspace_size",
-              "vce_strerror", "vce_gemm_bf16", "vce_transpose_bf16"):
+              "vce_strerror", "vce_gemm_bf16"):
         assert n in names
     assert set(names) == set(binding.SIGNATURES), "binding and header disagree"
 
@@ -147,19 +147,20 @@ def test_lce_backward_rejects(L):
 
 def test_gemm_rejects(L):
     g = L.vce_gemm_bf16
-    assert g(A, 64, A, 64, 10, 10, 12, A, 10, None) == 7      # K not a multiple of 8
-    assert g(A, 64, A, 64, 10, 10, 64, A, 5, None) == 1       # ldc < cols
-    assert g(A, 32, A, 64, 10, 10, 64, A, 10, None) == 1      # ldp < K
-    assert g(A + 2, 64, A, 64, 10, 10, 64, A, 10, None) == 3
-    assert g(A, 64, A, 1 << 23, 10, 10, 64, A, 10, None) == 7  # leading dim too large
-    assert g(A, 64, A, 64, 0, 10, 64, A, 10, None) == 0       # empty: nothing to do
 
+    def call(P=A, ldp=64, p_dim=0, Q=A, ldq=64, q_dim=0, rows=10, cols=10, K=64, C=A, ldc=10):
+        return g(P, ldp, p_dim, Q, ldq, q_dim, rows, cols, K, C, ldc, None)
 
-def test_transpose_rejects(L):
-    t = L.vce_transpose_bf16
-    assert t(A, 10, 20, 16, A + (1 << 20), 16, None) == 1     # ld_src < cols
-    assert t(A, 10, 20, 24, A + (1 << 20), 8, None) == 1      # ld_dst < rows
-    assert t(A, 10, 20, 20, A + (1 << 20), 16, None) == 3     # ld_src not a multiple of 8
-    assert t(A + 2, 10, 20, 24, A + (1 << 20), 16, None) == 3
-    assert t(A, 10, 20, 24, A + 64, 16, None) == 4            # overlapping buffers
-    assert t(A, 0, 20, 24, A + (1 << 20), 16, None) == 0
+    assert call(K=12) == 7                          # K-contiguous operand, K not a multiple of 8
+    # K need not be a multiple of 8 when both operands are dim-contiguous: the
+    # call gets as far as the (last) alignment check
+    assert call(P=A + 2, p_dim=1, q_dim=1, K=12, rows=16, cols=16, ldc=16) == 3
+    assert call(p_dim=1) == 7                       # dim-contiguous P needs rows % 8 == 0
+    assert call(q_dim=1, rows=16, ldc=16) == 7      # dim-contiguous Q needs cols % 8 == 0
+    assert call(p_dim=2) == 1
+    assert call(ldc=5) == 1                         # ldc < cols
+    assert call(ldp=32) == 1                        # ldp < K
+    assert call(p_dim=1, rows=16, ldp=8) == 1       # ldp < rows for a dim-contiguous P
+    assert call(P=A + 2) == 3
+    assert call(ldq=1 << 23) == 7                   # leading dimension too large
+    assert call(rows=0) == 0                        # empty: nothing to do

@@ -28,13 +28,24 @@ def _bf16(a):
 
 # --- the GEMM building block -----------------------------------------------------
 
-@pytest.mark.parametrize("rows,cols,K", [(300, 520, 200), (512, 768, 4096), (33, 7, 8),
-                                         (773, 1000, 4104), (4096, 256, 64)])
-def test_gemm(rows, cols, K):
+@pytest.mark.parametrize("p_dim,q_dim", [(False, False), (False, True), (True, False), (True, True)])
+@pytest.mark.parametrize("rows,cols,K", [(300, 520, 200), (512, 768, 4096), (40, 8, 8),
+                                         (776, 1000, 4104), (4096, 256, 64), (264, 256, 333)])
+def test_gemm(rows, cols, K, p_dim, q_dim):
+    """The GEMM core in each operand layout against an FP64 product of the same
+    BF16 values.  Ragged rows, columns and K cover the masked loads; a
+    dim-contiguous operand needs its dim to be a multiple of 8 and a
+    K-contiguous one its K."""
+    if (not p_dim or not q_dim) and K % 8:
+        pytest.skip("a K-contiguous operand needs K % 8 == 0")
+    if (p_dim and rows % 8) or (q_dim and cols % 8):
+        pytest.skip("a dim-contiguous operand needs its dim % 8 == 0")
     rng = np.random.default_rng(rows * 7 + cols + K)
     Pm = wl.f32_to_bf16_bits(rng.standard_normal((rows, K)).astype(np.float32))
     Qm = wl.f32_to_bf16_bits(rng.standard_normal((cols, K)).astype(np.float32))
-    C = vce.gemm_bf16(_bf16(Pm), _bf16(Qm))
+    Pd = _bf16(np.ascontiguousarray(Pm.T) if p_dim else Pm)
+    Qd = _bf16(np.ascontiguousarray(Qm.T) if q_dim else Qm)
+    C = vce.gemm_bf16(Pd, Qd, K, p_dim=p_dim, q_dim=q_dim)
     torch.cuda.synchronize()
     Pf, Qf = oracle.bf16_to_f64(Pm), oracle.bf16_to_f64(Qm)
     ref = Pf @ Qf.T
@@ -43,23 +54,6 @@ def test_gemm(rows, cols, K):
     # FP32 accumulation of exact BF16 products: error far below 2^-14 of the
     # sum of |terms|; an indexing mistake gives errors of the order of the terms
     assert np.all(err <= 2.0 ** -14 * scale + 1e-30), float((err / (scale + 1e-30)).max())
-
-
-@pytest.mark.parametrize("rows,cols", [(64, 64), (1001, 777), (5, 3000), (4096, 2304), (1, 8)])
-def test_transpose(rows, cols):
-    rng = np.random.default_rng(rows + 3 * cols)
-    a = rng.integers(0, 65536, size=(rows, cols), dtype=np.uint16)
-    ld = (cols + 7) // 8 * 8
-    src = np.zeros((rows, ld), np.uint16)
-    src[:, :cols] = a
-    t_src = _bf16(src)[:, :cols]
-    ldd = (rows + 7) // 8 * 8
-    out = torch.zeros((cols, ldd), dtype=torch.bfloat16, device="cuda")
-    vce.transpose_bf16(t_src, out=out[:, :rows])
-    torch.cuda.synchronize()
-    got = to_host_bits(out)
-    np.testing.assert_array_equal(got[:, :rows], a.T)
-    assert np.all(got[:, rows:] == 0)  # nothing written past the destination's columns
 
 
 # --- helpers -----------------------------------------------------------------------

@@ -34,8 +34,7 @@ SIGNATURES = {
                            _VP, _SZ, _VP]),
     "lce_backward": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _F32, _I32, _I64, _VP,
                             _VP, _VP, _SZ, _VP]),
-    "vce_gemm_bf16": (_I32, [_VP, _I64, _VP, _I64, _I64, _I64, _I64, _VP, _I64, _VP]),
-    "vce_transpose_bf16": (_I32, [_VP, _I64, _I64, _I64, _VP, _I64, _VP]),
+    "vce_gemm_bf16": (_I32, [_VP, _I64, _I32, _VP, _I64, _I32, _I64, _I64, _I64, _VP, _I64, _VP]),
 }
 
 _lib = None
@@ -228,27 +227,20 @@ def lce_backward(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, stats:
     return dX, dW
 
 
-def gemm_bf16(P: torch.Tensor, Q: torch.Tensor, K: int | None = None, *,
-              out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """C[i, j] = sum_k P[i, k] Q[j, k] with the library's matrix-core GEMM
-    (P (rows, >=K) and Q (cols, >=K) BF16, K-contiguous)."""
+def gemm_bf16(P: torch.Tensor, Q: torch.Tensor, K: int | None = None, *, p_dim: bool = False,
+              q_dim: bool = False, out: torch.Tensor | None = None,
+              stream=None) -> torch.Tensor:
+    """C[i, j] = sum_k P(i, k) Q(j, k) with the library's matrix-core GEMM.
+
+    P is (rows, K) K-contiguous, or with ``p_dim`` (K, rows) holding P(i, k) at
+    [k, i]; likewise Q with ``q_dim``.  BF16, row-major, unit inner stride."""
     _need_cuda(P, Q)
-    rows, cols = P.shape[0], Q.shape[0]
-    K = P.shape[1] if K is None else K
+    rows = P.shape[1] if p_dim else P.shape[0]
+    cols = Q.shape[1] if q_dim else Q.shape[0]
+    if K is None:
+        K = P.shape[0] if p_dim else P.shape[1]
     C = torch.empty((rows, cols), dtype=torch.float32, device=P.device) if out is None else out
-    rc = lib().vce_gemm_bf16(_ptr(P), P.stride(0), _ptr(Q), Q.stride(0), rows, cols, K, _ptr(C),
-                             C.stride(0), _stream(stream))
+    rc = lib().vce_gemm_bf16(_ptr(P), P.stride(0), int(p_dim), _ptr(Q), Q.stride(0), int(q_dim),
+                             rows, cols, K, _ptr(C), C.stride(0), _stream(stream))
     _check("vce_gemm_bf16", rc)
     return C
-
-
-def transpose_bf16(src: torch.Tensor, *, out: torch.Tensor | None = None,
-                   stream=None) -> torch.Tensor:
-    """out[c, r] = src[r, c] for a 2-D 16-bit tensor, with the library's kernel."""
-    _need_cuda(src)
-    rows, cols = src.shape
-    dst = torch.empty((cols, rows), dtype=src.dtype, device=src.device) if out is None else out
-    rc = lib().vce_transpose_bf16(_ptr(src), rows, cols, src.stride(0), _ptr(dst), dst.stride(0),
-                                  _stream(stream))
-    _check("vce_transpose_bf16", rc)
-    return dst

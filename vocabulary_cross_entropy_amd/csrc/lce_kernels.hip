@@ -58,9 +58,12 @@ static_assert(BM == BN, "one loader shape serves both operands");
 
 #define LDS_AS __attribute__((address_space(3)))
 
-// Both operands: element (d, k) at base[d * ld + k].  d >= dim_limit reads as
-// 0; k is masked per 8-element chunk (chunk start >= k_limit reads as 0), so
-// a buffer must hold zeros from k_limit up to the next multiple of 8.
+// An operand of C[i][j] = sum_k P(i, k) Q(j, k), BF16:
+//   K-contiguous   (DIM = false): element (d, k) at base[d * ld + k]
+//   dim-contiguous (DIM = true):  element (d, k) at base[k * ld + d]
+// Reads with d >= dim_limit or k >= k_limit return 0.  Along the contiguous
+// axis the test is per 8-element chunk (its first element), so a buffer must
+// hold zeros from its limit on that axis up to the next multiple of 8.
 struct Operand {
   const uint16_t* base;
   int64_t ld;
@@ -73,44 +76,96 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const uint16_t* p) {
                                            0x00020000);
 }
 
-// LDS rows are BK elements (128 B, 8 chunks); chunk c of row r lives at
-// c ^ swz(r).
+// LDS stage of one operand (256 x 64 elements, 32 KB):
+//  * K-contiguous: 256 rows (d) of 64 k (128 B, eight 16-byte chunks);
+//    logical chunk c of row d sits at c ^ swz(d).
+//  * dim-contiguous: two halves (d < 128, d >= 128) of 64 rows (k) of 128 d
+//    (256 B, sixteen chunks); logical chunk c of row k sits at c ^ 4 (k & 3).
+// Both make the fragment reads below bank-conflict free (measured: a
+// transposed read serves 32 lanes, 4 rows x 64 B, per 256-byte bank cycle,
+// so the four rows must fall in different 64-byte quarters).
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
-// Streams one operand's 256 x 64 slice into an LDS stage: wave w brings rows
-// 32 w .. 32 w + 31, as LD_PER_WAVE loads of 8 rows (1 KB); lane l of a load
-// writes LDS bytes 16 l .. 16 l + 15, i.e. row l / 8, physical chunk l % 8,
-// so it reads the logical chunk (l % 8) ^ swz(row) from global memory.
+// Streams one operand's 256 x 64 slice into an LDS stage.  Load i of wave w
+// writes 1 KB at element 2048 w + 512 i of the stage, lane l the 16 bytes at
+// 16 l, and each lane reads the logical chunk that lands there:
+//  * K-contiguous: rows 32 w + 8 i .. + 7 (lane: row l / 8, chunk l % 8);
+//  * dim-contiguous: half w / 4, k rows 16 (w % 4) + 4 i .. + 3 (lane: row
+//    l / 16, chunk l % 16).
+// So wave w brings rows 32 w .. 32 w + 31 of the tile (K-contiguous) or the
+// half w / 4 (dim-contiguous): either way waves 0-3 bring exactly the rows
+// 0..127 of P and waves 4-7 the rows 128..255.
+template <bool DIM>
 struct SliceLoader {
-  const uint16_t* tbase;  // operand at the tile's first row, k = 0
+  const uint16_t* tbase;  // operand at the tile's first element, k = 0
+  int64_t kstep;          // elements per unit of k
   int64_t k_limit;
-  uint32_t off[LD_PER_WAVE];  // byte offset of this lane's chunk, or kOob
-  int kc[LD_PER_WAVE];        // element offset of this lane's chunk within the slice
+  uint32_t off[LD_PER_WAVE];  // byte offset of this lane's 16 bytes, or kOob
+  int kc[LD_PER_WAVE];        // k offset (within the slice) this lane's data starts at
   __device__ __forceinline__ void init(const Operand& op, int64_t d0, int wave, int lane) {
-    tbase = op.base + d0 * op.ld;
     k_limit = op.k_limit;
+    if (!DIM) {
+      tbase = op.base + d0 * op.ld;
+      kstep = 1;
 #pragma unroll
-    for (int i = 0; i < LD_PER_WAVE; ++i) {
-      const int row = wave * (BM / 8) + i * ROWS_PER_LD + (lane >> 3);
-      const int c = (lane & 7) ^ swz(row);
-      kc[i] = c * 8;
-      off[i] = (d0 + row < op.dim_limit) ? (uint32_t)(row * op.ld * 2 + c * 16) : kOob;
+      for (int i = 0; i < LD_PER_WAVE; ++i) {
+        const int row = wave * (BM / 8) + i * ROWS_PER_LD + (lane >> 3);
+        const int c = (lane & 7) ^ swz(row);
+        kc[i] = c * 8;
+        off[i] = (d0 + row < op.dim_limit) ? (uint32_t)(row * op.ld * 2 + c * 16) : kOob;
+      }
+    } else {
+      tbase = op.base + d0;
+      kstep = op.ld;
+      const int half = wave >> 2;
+#pragma unroll
+      for (int i = 0; i < LD_PER_WAVE; ++i) {
+        const int krow = 16 * (wave & 3) + 4 * i + (lane >> 4);
+        const int c = (lane & 15) ^ (4 * (krow & 3));
+        const int d = 128 * half + 8 * c;
+        kc[i] = krow;
+        off[i] = (d0 + d < op.dim_limit) ? (uint32_t)(krow * op.ld * 2 + d * 2) : kOob;
+      }
     }
   }
   // load i of the slice starting at k0; `tail`: the slice reaches past k_limit
   __device__ __forceinline__ void issue(uint16_t LDS_AS* stage, int64_t k0, int wave, int i,
                                         bool tail) {
-    const __amdgpu_buffer_rsrc_t rs = rsrc_at(tbase + k0);
+    const __amdgpu_buffer_rsrc_t rs = rsrc_at(tbase + k0 * kstep);
     uint32_t o = off[i];
     if (tail) o = (k0 + kc[i] < k_limit) ? o : kOob;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (void LDS_AS*)(stage + (wave * (BM / 8) + i * ROWS_PER_LD) * BK), 16, o, 0, 0, 0);
+        rs, (void LDS_AS*)(stage + 2048 * wave + 512 * i), 16, o, 0, 0, 0);
   }
 };
 
-__device__ __forceinline__ bf16x8_t frag(const uint16_t LDS_AS* s, int row, int chunk) {
-  return __builtin_bit_cast(
-      bf16x8_t, *reinterpret_cast<const u32x4_t LDS_AS*>(s + row * BK + ((chunk ^ swz(row)) * 8)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// MFMA operand of the 32 tile rows d0 .. d0 + 31 (d0 a multiple of 32) for
+// k-step ks (k = 16 ks .. 16 ks + 15): lane l gets row d0 + l % 32 and the 8 k
+// values from 16 ks + 8 (l / 32).
+template <bool DIM>
+__device__ __forceinline__ bf16x8_t frag(const uint16_t LDS_AS* s, int d0, int ks, int lane) {
+  if (!DIM) {
+    const int row = d0 + (lane & 31), chunk = 2 * ks + (lane >> 5);
+    return __builtin_bit_cast(
+        bf16x8_t,
+        *reinterpret_cast<const u32x4_t LDS_AS*>(s + row * BK + ((chunk ^ swz(row)) * 8)));
+  } else {
+    // ds_read_tr16_b64: in each 16-lane group, lane 4 j + q gives the address
+    // of 4 elements (q-th quarter) of source row j; lane i receives element i
+    // of rows 0..3.  Rows are k here, so lane i gets 4 consecutive k of
+    // column d = base + i; two reads give the 8 k values.
+    const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
+    const int d = d0 + 16 * (g & 1) + 4 * q;
+    const int k = 16 * ks + 8 * (g >> 1) + j;
+    const uint16_t LDS_AS* p =
+        s + (d >> 7) * 8192 + k * 128 + ((((d & 127) >> 3) ^ (4 * j)) * 8) + (d & 7);
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4i16_t LDS_AS*)p);
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4i16_t LDS_AS*)(p + 4 * 128));
+    const u32x2_t a = __builtin_bit_cast(u32x2_t, lo), b = __builtin_bit_cast(u32x2_t, hi);
+    return __builtin_bit_cast(bf16x8_t, u32x4_t{a[0], a[1], b[0], b[1]});
+  }
 }
 
 // Hardware workgroup id -> (row tile, col tile).
@@ -131,7 +186,7 @@ __device__ __forceinline__ void tile_of(int b, int n_ti, int n_tj, int* ti, int*
 //   row i = i0 + 128 wr + 32 a + 8 (r / 4) + 4 (lane / 32) + r % 4
 //   col j = j0 + 64 wc + 32 b + lane % 32
 // for wavefront (wr, wc) = (wave / 4, wave % 4).
-template <class Epi>
+template <class Epi, bool PD, bool QD>
 __global__ __launch_bounds__(NT) void gemm_kernel(Operand P, Operand Q, int64_t K, int n_ti,
                                                   int n_tj, typename Epi::Params ep) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * (BM + BN) * BK];
@@ -152,7 +207,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Operand P, Operand Q, int64_t 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-  SliceLoader lp, lq;
+  SliceLoader<PD> lp;
+  SliceLoader<QD> lq;
   lp.init(P, i0, wave, lane);
   lq.init(Q, j0, wave, lane);
   const int nk = (int)((K + BK - 1) / BK);
@@ -164,8 +220,6 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Operand P, Operand Q, int64_t 
       lq.issue(sq, 0, wave, i, tail);
     }
   }
-  const int prow = wr * 128 + (lane & 31), qrow = wc * WN + (lane & 31);
-  const int khalf = lane >> 5;
   // Ping-pong: the two wavefronts of a SIMD (waves w and w + 4) alternate
   // between a memory phase (fragment reads of a half slice, plus the next
   // slice's loads) and a compute phase (16 MFMAs back to back), so one issues
@@ -222,9 +276,9 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Operand P, Operand Q, int64_t 
       for (int s2 = 0; s2 < 2; ++s2) {
         const int ks = 2 * h + s2;
 #pragma unroll
-        for (int a = 0; a < 4; ++a) fa[s2][a] = frag(cp, prow + 32 * a, 2 * ks + khalf);
+        for (int a = 0; a < 4; ++a) fa[s2][a] = frag<PD>(cp, wr * 128 + 32 * a, ks, lane);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) fb[s2][b] = frag(cq, qrow + 32 * b, 2 * ks + khalf);
+        for (int b = 0; b < NB; ++b) fb[s2][b] = frag<QD>(cq, wc * WN + 32 * b, ks, lane);
       }
       if (h == 0 && more) {
 #pragma unroll
@@ -389,13 +443,12 @@ struct EpiLse {
 
 // Backward dZ: rows = vocabulary of the chunk, cols = tokens.
 // dZ = g (exp(z - lse) - (1-eps)[v = t] - eps/V), BF16, written token-major
-// (dz[m * ldz + v]) and vocabulary-major (dzt[v * ldt + m]).  Padding rows and
-// columns of both buffers receive zeros.
+// (dz[m * ldz + v]); padding rows and columns receive zeros.  The dW GEMM
+// reads it dim-contiguous, the dX GEMM K-contiguous.
 struct EpiDz {
   struct Params {
     uint16_t* dz;
-    uint16_t* dzt;
-    int64_t ldz, ldt, c0, vc_valid;
+    int64_t ldz, c0, vc_valid;
     const float* stats;
     const int64_t* targets;
     const float* grad_output;
@@ -455,11 +508,6 @@ struct EpiDz {
           const uint32_t w01 = pack_bf16x2(val[0], val[1]), w23 = pack_bf16x2(val[2], val[3]);
           const int64_t v = vrow0 + a * 32 + 8 * q;
           *reinterpret_cast<u32x2_t*>(p.dz + j * p.ldz + v) = u32x2_t{w01, w23};
-          uint16_t* col = p.dzt + v * p.ldt + j;
-          col[0] = (uint16_t)(w01 & 0xffffu);
-          col[p.ldt] = (uint16_t)(w01 >> 16);
-          col[2 * p.ldt] = (uint16_t)(w23 & 0xffffu);
-          col[3 * p.ldt] = (uint16_t)(w23 >> 16);
         }
     }
   }
@@ -529,67 +577,6 @@ struct EpiDx {
   }
 };
 
-// ---- transpose -------------------------------------------------------------------
-
-// dst[c * ld_dst + r] = src[r * ld_src + c] for r < rows, c < cols, and 0 for
-// rows <= r < rows_pad.  64 x 64 tiles through LDS.
-struct TransposeParams {
-  const uint16_t* src;
-  uint16_t* dst;
-  int64_t rows, cols, ld_src, ld_dst, rows_pad;
-};
-
-constexpr int TT = 64;   // tile edge
-constexpr int TPAD = 2;  // LDS row padding (elements): column reads hit distinct banks
-
-__global__ __launch_bounds__(256) void transpose_kernel(TransposeParams p) {
-  __shared__ uint16_t tile[TT][TT + TPAD];
-  const int64_t r0 = (int64_t)blockIdx.y * TT, c0 = (int64_t)blockIdx.x * TT;
-  const int tid = threadIdx.x;
-  // load: 64 rows x 8 vectors of 8 elements; thread -> (row tid/8 + 32 h, vector tid%8)
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int rr = (tid >> 3) + 32 * h, vv = tid & 7;
-    const int64_t r = r0 + rr, c = c0 + vv * 8;
-    uint16_t e[8];
-    if (r < p.rows && c + 8 <= p.cols) {
-      const u32x4_t w = *reinterpret_cast<const u32x4_t*>(p.src + r * p.ld_src + c);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        e[2 * k] = (uint16_t)(w[k] & 0xffffu);
-        e[2 * k + 1] = (uint16_t)(w[k] >> 16);
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        e[k] = (r < p.rows && c + k < p.cols) ? p.src[r * p.ld_src + c + k] : (uint16_t)0;
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) tile[rr][vv * 8 + k] = e[k];
-  }
-  __syncthreads();
-  // store: dst rows c0 .. c0+63, 8 vectors of 8 along r
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int cc = (tid >> 3) + 32 * h, vv = tid & 7;
-    const int64_t c = c0 + cc, r = r0 + vv * 8;
-    if (c >= p.cols || r >= p.rows_pad) continue;
-    uint16_t e[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) e[k] = tile[vv * 8 + k][cc];
-    if (r + 8 <= p.rows_pad) {
-      u32x4_t w;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) w[k] = (uint32_t)e[2 * k] | ((uint32_t)e[2 * k + 1] << 16);
-      *reinterpret_cast<u32x4_t*>(p.dst + c * p.ld_dst + r) = w;
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (r + k < p.rows_pad) p.dst[c * p.ld_dst + r + k] = e[k];
-    }
-  }
-}
-
 // ---- merge ------------------------------------------------------------------------
 
 // Per-token merge of the forward partials (fixed order), then loss and stats.
@@ -637,25 +624,15 @@ __global__ __launch_bounds__(256) void lce_merge_kernel(MergeParams p) {
 
 // ---- host side ------------------------------------------------------------------
 
-template <class Epi>
+template <class Epi, bool PD, bool QD>
 hipError_t run_gemm(const Operand& P, const Operand& Q, int64_t rows, int64_t cols, int64_t K,
                     const typename Epi::Params& ep, hipStream_t stream) {
   const int64_t n_ti = (rows + BM - 1) / BM, n_tj = (cols + BN - 1) / BN;
   const int64_t n = n_ti * n_tj;
   if (n <= 0) return hipSuccess;
   if (n > INT32_MAX / 2) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_kernel<Epi>), dim3((unsigned)n), dim3(NT), 0, stream, P, Q, K,
+  hipLaunchKernelGGL((gemm_kernel<Epi, PD, QD>), dim3((unsigned)n), dim3(NT), 0, stream, P, Q, K,
                      (int)n_ti, (int)n_tj, ep);
-  return hipGetLastError();
-}
-
-hipError_t run_transpose(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld_src,
-                         uint16_t* dst, int64_t ld_dst, int64_t rows_pad, hipStream_t stream) {
-  if (rows_pad <= 0 || cols <= 0) return hipSuccess;
-  const int64_t gx = (cols + TT - 1) / TT, gy = (rows_pad + TT - 1) / TT;
-  if (gx > INT32_MAX || gy > 65535) return hipErrorInvalidValue;
-  TransposeParams tp{src, dst, rows, cols, ld_src, ld_dst, rows_pad};
-  hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream, tp);
   return hipGetLastError();
 }
 
@@ -666,7 +643,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 bool lce_make_plan(int64_t M, int64_t H, int64_t V, LcePlan* plan) {
   if (M < 0 || H <= 0 || V <= 0 || H % 8 != 0) return false;
   // Every buffer offset a GEMM load forms (256 rows x leading dimension x 2 B)
-  // stays below 2^31; transpose grids stay within range.
+  // stays below 2^31.
   if (H > ((int64_t)1 << 20) || V > ((int64_t)1 << 31)) return false;
   LcePlan p;
   p.M = M;
@@ -681,17 +658,12 @@ bool lce_make_plan(int64_t M, int64_t H, int64_t V, LcePlan* plan) {
   p.ldz = p.chunk;
   const size_t part = align256((size_t)p.n_vtiles * p.Mp * 4);
   const size_t fwd = 3 * part + align256((size_t)p.Mp * 4);
-  // backward: X^T (H x Mp), W_c^T (H x chunk), dZ (Mp x chunk), dZ^T (chunk x Mp), dX acc
-  const size_t xt = align256((size_t)H * p.Mp * 2);
-  const size_t wt = align256((size_t)H * p.chunk * 2);
+  // backward: dZ of one chunk (Mp x chunk, token-major) and the dX accumulator
   const size_t dz = align256((size_t)p.Mp * p.chunk * 2);
   const size_t dx = p.n_chunks > 1 ? align256((size_t)p.Mp * H * 4) : 0;
   p.off_part = 0;
-  p.off_xt = 0;
-  p.off_wt = xt;
-  p.off_dz = xt + wt;
-  p.off_dzt = xt + wt + dz;
-  p.off_dx = xt + wt + 2 * dz;
+  p.off_dz = 0;
+  p.off_dx = dz;
   const size_t bwd = p.off_dx + dx;
   p.total = fwd > bwd ? fwd : bwd;
   *plan = p;
@@ -710,7 +682,7 @@ hipError_t launch_lce_forward(const LcePlan& plan, const LceFwdArgs& a, hipStrea
   Operand P{W, plan.H, plan.V, plan.H};
   Operand Q{X, plan.H, plan.M, plan.H};
   EpiLse::Params ep{pm, pd, ps, zt, a.targets, plan.M, plan.V, plan.Mp, a.ignore_idx};
-  hipError_t e = run_gemm<EpiLse>(P, Q, plan.V, plan.Mp, plan.H, ep, stream);
+  hipError_t e = run_gemm<EpiLse, false, false>(P, Q, plan.V, plan.Mp, plan.H, ep, stream);
   if (e != hipSuccess) return e;
   MergeParams mp{pm, pd, ps, zt, a.targets, plan.M, plan.Mp, plan.V, plan.n_vtiles,
                  a.ignore_idx, a.eps, a.loss_tok, a.stats};
@@ -721,65 +693,56 @@ hipError_t launch_lce_forward(const LcePlan& plan, const LceFwdArgs& a, hipStrea
 
 hipError_t launch_lce_backward(const LcePlan& plan, const LceBwdArgs& a, hipStream_t stream) {
   if (plan.M == 0) return hipSuccess;  // dW of an empty batch: nothing reads it
-  uint16_t* xt = reinterpret_cast<uint16_t*>(a.ws + plan.off_xt);
-  uint16_t* wt = reinterpret_cast<uint16_t*>(a.ws + plan.off_wt);
   uint16_t* dz = reinterpret_cast<uint16_t*>(a.ws + plan.off_dz);
-  uint16_t* dzt = reinterpret_cast<uint16_t*>(a.ws + plan.off_dzt);
   float* dxacc = reinterpret_cast<float*>(a.ws + plan.off_dx);
   const uint16_t* X = static_cast<const uint16_t*>(a.X);
   const uint16_t* W = static_cast<const uint16_t*>(a.W);
-  // X^T (H x Mp), tokens M..Mp-1 zero
-  hipError_t e = run_transpose(X, plan.M, plan.H, plan.H, xt, plan.Mp, plan.Mp, stream);
-  if (e != hipSuccess) return e;
   for (int64_t c = 0; c < plan.n_chunks; ++c) {
     const int64_t c0 = c * plan.chunk;
     const int64_t vc = (plan.V - c0) < plan.chunk ? (plan.V - c0) : plan.chunk;
     const uint16_t* Wc = W + c0 * plan.H;
-    // dZ of the chunk (both layouts): (vocabulary x tokens), K = H
+    // dZ of the chunk: (vocabulary x tokens), K = H, both operands K-contiguous
     {
       Operand P{Wc, plan.H, vc, plan.H};
       Operand Q{X, plan.H, plan.M, plan.H};
-      EpiDz::Params ep{dz, dzt, plan.ldz, plan.Mp, c0, vc, a.stats, a.targets, a.grad_output,
-                       a.n_valid, a.eps, a.reduce_loss, a.ignore_idx, plan.M, plan.V};
-      e = run_gemm<EpiDz>(P, Q, vc, plan.Mp, plan.H, ep, stream);
+      EpiDz::Params ep{dz, plan.ldz, c0, vc, a.stats, a.targets, a.grad_output, a.n_valid,
+                       a.eps, a.reduce_loss, a.ignore_idx, plan.M, plan.V};
+      hipError_t e = run_gemm<EpiDz, false, false>(P, Q, vc, plan.Mp, plan.H, ep, stream);
       if (e != hipSuccess) return e;
     }
-    // dW rows of the chunk: (hidden x vocabulary), K = tokens
+    // dW rows of the chunk: (hidden x vocabulary), K = tokens; X (h contiguous
+    // per token) and dZ (v contiguous per token) are both read dim-contiguous
     {
-      Operand P{xt, plan.Mp, plan.H, plan.M};
-      Operand Q{dzt, plan.Mp, vc, plan.M};
+      Operand P{X, plan.H, plan.H, plan.M};
+      Operand Q{dz, plan.ldz, vc, plan.M};
       EpiDw::Params ep{static_cast<uint16_t*>(a.dW), plan.H, c0, vc};
-      e = run_gemm<EpiDw>(P, Q, plan.H, vc, plan.M, ep, stream);
+      hipError_t e = run_gemm<EpiDw, true, true>(P, Q, plan.H, vc, plan.M, ep, stream);
       if (e != hipSuccess) return e;
     }
-    // W_c^T (H x chunk), vocabulary rows vc .. next multiple of 64 zero; then
-    // dX += dZ_c W_c: (hidden x tokens), K = vocabulary of the chunk
+    // dX += dZ_c W_c: (hidden x tokens), K = vocabulary of the chunk; W_c is
+    // read dim-contiguous (h contiguous per vocabulary row), dZ K-contiguous
     {
-      e = run_transpose(Wc, vc, plan.H, plan.H, wt, plan.chunk, (vc + 63) / 64 * 64, stream);
-      if (e != hipSuccess) return e;
-      Operand P{wt, plan.chunk, plan.H, vc};
+      Operand P{Wc, plan.H, plan.H, vc};
       Operand Q{dz, plan.ldz, plan.M, vc};
       const int mode = (c > 0 ? 1 : 0) | (c + 1 == plan.n_chunks ? 2 : 0);
       EpiDx::Params ep{dxacc, static_cast<uint16_t*>(a.dX), plan.H, plan.M, mode};
-      e = run_gemm<EpiDx>(P, Q, plan.H, plan.M, vc, ep, stream);
+      hipError_t e = run_gemm<EpiDx, true, false>(P, Q, plan.H, plan.M, vc, ep, stream);
       if (e != hipSuccess) return e;
     }
   }
   return hipSuccess;
 }
 
-hipError_t launch_gemm_bf16(const void* P, int64_t ldp, const void* Q, int64_t ldq, int64_t rows,
-                            int64_t cols, int64_t K, float* C, int64_t ldc, hipStream_t stream) {
+hipError_t launch_gemm_bf16(const void* P, int64_t ldp, int p_dim, const void* Q, int64_t ldq,
+                            int q_dim, int64_t rows, int64_t cols, int64_t K, float* C,
+                            int64_t ldc, hipStream_t stream) {
   Operand op{static_cast<const uint16_t*>(P), ldp, rows, K};
   Operand oq{static_cast<const uint16_t*>(Q), ldq, cols, K};
   EpiF32::Params ep{C, ldc, rows, cols};
-  return run_gemm<EpiF32>(op, oq, rows, cols, K, ep, stream);
-}
-
-hipError_t launch_transpose_bf16(const void* src, int64_t rows, int64_t cols, int64_t ld_src,
-                                 void* dst, int64_t ld_dst, hipStream_t stream) {
-  return run_transpose(static_cast<const uint16_t*>(src), rows, cols, ld_src,
-                       static_cast<uint16_t*>(dst), ld_dst, rows, stream);
+  if (!p_dim && !q_dim) return run_gemm<EpiF32, false, false>(op, oq, rows, cols, K, ep, stream);
+  if (!p_dim && q_dim) return run_gemm<EpiF32, false, true>(op, oq, rows, cols, K, ep, stream);
+  if (p_dim && !q_dim) return run_gemm<EpiF32, true, false>(op, oq, rows, cols, K, ep, stream);
+  return run_gemm<EpiF32, true, true>(op, oq, rows, cols, K, ep, stream);
 }
 
 }  // namespace vce

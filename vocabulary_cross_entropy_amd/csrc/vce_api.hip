@@ -272,36 +272,25 @@ int lce_backward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
   return launch_status(vce::launch_lce_backward(plan, a, static_cast<hipStream_t>(stream)));
 }
 
-int vce_gemm_bf16(const void* P, int64_t ldp, const void* Q, int64_t ldq, int64_t rows,
-                  int64_t cols, int64_t K, float* C, int64_t ldc, void* stream) {
+int vce_gemm_bf16(const void* P, int64_t ldp, int p_dim, const void* Q, int64_t ldq, int q_dim,
+                  int64_t rows, int64_t cols, int64_t K, float* C, int64_t ldc, void* stream) {
   if (rows < 0 || cols < 0 || K < 0) return VCE_EINVAL;
+  if ((p_dim != 0 && p_dim != 1) || (q_dim != 0 && q_dim != 1)) return VCE_EINVAL;
   if (rows == 0 || cols == 0) return VCE_OK;
   if (!P || !Q || !C) return VCE_EINVAL;
-  if (K % 8 != 0 || ldp % 8 != 0 || ldq % 8 != 0) return VCE_EUNSUPPORTED;
-  if (ldc < cols || ldp < K || ldq < K) return VCE_EINVAL;
+  // the contiguous axis is masked per 8-element chunk
+  if (!p_dim && K % 8 != 0) return VCE_EUNSUPPORTED;
+  if (!q_dim && K % 8 != 0) return VCE_EUNSUPPORTED;
+  if (p_dim && rows % 8 != 0) return VCE_EUNSUPPORTED;
+  if (q_dim && cols % 8 != 0) return VCE_EUNSUPPORTED;
+  if (ldp % 8 != 0 || ldq % 8 != 0) return VCE_EUNSUPPORTED;
+  if (ldc < cols || ldp < (p_dim ? rows : K) || ldq < (q_dim ? cols : K)) return VCE_EINVAL;
   // 256 rows x leading dimension x 2 bytes must stay below 2^31 (buffer offsets)
   if (ldp > ((int64_t)1 << 22) || ldq > ((int64_t)1 << 22)) return VCE_EUNSUPPORTED;
   if (rows > ((int64_t)1 << 31) || cols > ((int64_t)1 << 31)) return VCE_EUNSUPPORTED;
   if (!aligned(P, 16) || !aligned(Q, 16) || !aligned(C, 4)) return VCE_EALIGN;
-  return launch_status(vce::launch_gemm_bf16(P, ldp, Q, ldq, rows, cols, K, C, ldc,
+  return launch_status(vce::launch_gemm_bf16(P, ldp, p_dim, Q, ldq, q_dim, rows, cols, K, C, ldc,
                                              static_cast<hipStream_t>(stream)));
-}
-
-int vce_transpose_bf16(const void* src, int64_t rows, int64_t cols, int64_t ld_src, void* dst,
-                       int64_t ld_dst, void* stream) {
-  if (rows < 0 || cols < 0) return VCE_EINVAL;
-  if (rows == 0 || cols == 0) return VCE_OK;
-  if (!src || !dst) return VCE_EINVAL;
-  if (ld_src < cols || ld_dst < rows) return VCE_EINVAL;
-  if (ld_src % 8 != 0 || ld_dst % 8 != 0) return VCE_EALIGN;
-  if (!aligned(src, 16) || !aligned(dst, 16)) return VCE_EALIGN;
-  if ((rows + 63) / 64 > 65535) return VCE_EUNSUPPORTED;
-  uintptr_t a0, a1, b0, b1;
-  extent(src, 1, rows, cols, 0, ld_src, 2, &a0, &a1);
-  extent(dst, 1, cols, rows, 0, ld_dst, 2, &b0, &b1);
-  if (a0 < b1 && b0 < a1) return VCE_EALIAS;
-  return launch_status(vce::launch_transpose_bf16(src, rows, cols, ld_src, dst, ld_dst,
-                                                  static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -55,7 +55,7 @@ struct LcePlan {
   int64_t n_chunks;
   int64_t ldz;         // row stride (elements) of the dZ chunk buffer
   size_t off_part;     // forward: per-tile partials and target logits
-  size_t off_xt, off_wt, off_dz, off_dzt, off_dx;  // backward buffers
+  size_t off_dz, off_dx;  // backward: dZ of one chunk, FP32 dX accumulator
   size_t total;
 };
 
@@ -92,9 +92,8 @@ struct LceBwdArgs {
 
 hipError_t launch_lce_forward(const LcePlan& plan, const LceFwdArgs& a, hipStream_t stream);
 hipError_t launch_lce_backward(const LcePlan& plan, const LceBwdArgs& a, hipStream_t stream);
-hipError_t launch_gemm_bf16(const void* P, int64_t ldp, const void* Q, int64_t ldq, int64_t rows,
-                            int64_t cols, int64_t K, float* C, int64_t ldc, hipStream_t stream);
-hipError_t launch_transpose_bf16(const void* src, int64_t rows, int64_t cols, int64_t ld_src,
-                                 void* dst, int64_t ld_dst, hipStream_t stream);
+hipError_t launch_gemm_bf16(const void* P, int64_t ldp, int p_dim, const void* Q, int64_t ldq,
+                            int q_dim, int64_t rows, int64_t cols, int64_t K, float* C,
+                            int64_t ldc, hipStream_t stream);
 
 }  // namespace vce
