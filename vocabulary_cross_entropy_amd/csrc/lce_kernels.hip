@@ -53,6 +53,8 @@ constexpr int LD_PER_WAVE = BM / 8 / ROWS_PER_LD;  // loads per wave per operand
 constexpr int GROUP_I = 8;                         // row tiles per band of the tile order
 constexpr int64_t kChunk = 32768;                  // backward vocabulary chunk
 constexpr uint32_t kOob = 0x80000000u;             // buffer offset that reads as 0
+constexpr int kDzLd = BM + 4;   // LDS row (elements) of the staged dZ tile: 520 B, conflict-free
+constexpr int kSmemElems = (2 * (BM + BN) * BK > BN * kDzLd) ? 2 * (BM + BN) * BK : BN * kDzLd;
 
 static_assert(BM == BN, "one loader shape serves both operands");
 
@@ -189,7 +191,7 @@ __device__ __forceinline__ void tile_of(int b, int n_ti, int n_tj, int* ti, int*
 template <class Epi, bool PD, bool QD>
 __global__ __launch_bounds__(NT) void gemm_kernel(Operand P, Operand Q, int64_t K, int n_ti,
                                                   int n_tj, typename Epi::Params ep) {
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * (BM + BN) * BK];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[kSmemElems];
   uint16_t LDS_AS* const sp = (uint16_t LDS_AS*)smem;  // P stages: sp + s * BM * BK
   uint16_t LDS_AS* const sq = sp + 2 * BM * BK;         // Q stages: sq + s * BN * BK
 
@@ -444,7 +446,11 @@ struct EpiLse {
 // Backward dZ: rows = vocabulary of the chunk, cols = tokens.
 // dZ = g (exp(z - lse) - (1-eps)[v = t] - eps/V), BF16, written token-major
 // (dz[m * ldz + v]); padding rows and columns receive zeros.  The dW GEMM
-// reads it dim-contiguous, the dX GEMM K-contiguous.
+// reads it dim-contiguous, the dX GEMM K-contiguous.  The tile is staged in
+// LDS as [token][vocabulary] (rows padded to 520 B: the 8-byte writes of 32
+// consecutive tokens hit distinct banks) and leaves as whole 512-byte token
+// rows, 16 bytes per lane (direct 8-byte stores from the MFMA layout left
+// partial lines: 1.6x the bytes written, measured).
 struct EpiDz {
   struct Params {
     uint16_t* dz;
@@ -458,7 +464,8 @@ struct EpiDz {
     int64_t ignore_idx, M, V;
   };
   __device__ static void apply(const Params& p, f32x16_t (&acc)[4][NB], int64_t i0, int64_t j0,
-                               int wr, int wc, int lane, uint16_t*) {
+                               int wr, int wc, int lane, uint16_t* smem) {
+    uint16_t LDS_AS* const st = (uint16_t LDS_AS*)smem;  // [256 tokens][kDzLd]
     float gscale = 0.0f;
     if (p.reduce_loss) {
       const int32_t nv = p.n_valid[0];
@@ -506,9 +513,20 @@ struct EpiDz {
             val[e] = (live && off < lim) ? x : fill;
           }
           const uint32_t w01 = pack_bf16x2(val[0], val[1]), w23 = pack_bf16x2(val[2], val[3]);
-          const int64_t v = vrow0 + a * 32 + 8 * q;
-          *reinterpret_cast<u32x2_t*>(p.dz + j * p.ldz + v) = u32x2_t{w01, w23};
+          const int jl = wc * WN + b * 32 + (lane & 31);
+          const int vl = wr * 128 + 4 * (lane >> 5) + a * 32 + 8 * q;
+          *reinterpret_cast<u32x2_t LDS_AS*>(st + jl * kDzLd + vl) = u32x2_t{w01, w23};
         }
+    }
+    __syncthreads();
+    // 256 token rows x 32 chunks of 16 B; 512 threads, consecutive threads
+    // take consecutive chunks of a row
+    const int tid = threadIdx.x;
+#pragma unroll 4
+    for (int u = 0; u < (BN * BM / 8) / NT; ++u) {
+      const int idx = u * NT + tid, jl = idx >> 5, ch = idx & 31;
+      const u32x4_t w = *reinterpret_cast<const u32x4_t LDS_AS*>(st + jl * kDzLd + ch * 8);
+      *reinterpret_cast<u32x4_t*>(p.dz + (j0 + jl) * p.ldz + i0 + ch * 8) = w;
     }
   }
 };
