@@ -59,6 +59,12 @@ def _load():
         lib.vce_oracle_backward.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, i64, vp, i64, i64,
                                             dbl, i64, vp, vp, i64, vp]
         lib.vce_oracle_backward.restype = ctypes.c_int
+        lib.vce_oracle_entropy.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, i64, vp, i64, i64,
+                                           i64, vp, i64, vp]
+        lib.vce_oracle_entropy.restype = ctypes.c_int
+        lib.vce_oracle_entropy_grad.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, i64, vp, i64,
+                                                i64, i64, vp, vp, i64, vp]
+        lib.vce_oracle_entropy_grad.restype = ctypes.c_int
         lib.vce_oracle_round_bf16.argtypes = [vp, i64, vp]
         lib.vce_oracle_round_bf16.restype = None
         lib.vce_oracle_threads.argtypes = []
@@ -172,6 +178,47 @@ def ce_backward(logits: np.ndarray, targets: np.ndarray, g: np.ndarray,
         _ptr(gsel), _ptr(rr), n, _ptr(grad))
     if rc != 0:
         raise ValueError("oracle backward rejected its arguments")
+    return grad
+
+
+def entropy(logits: np.ndarray, targets: np.ndarray, ignore_idx: int = -100,
+            rows: np.ndarray | None = None) -> np.ndarray:
+    """Per-row entropy -sum_v p_v ln p_v of softmax(z) in FP64 (0 for ignored
+    rows), the optional entropy output of the Liger-Kernel PR (Summary)."""
+    lg, tg = _as_3d(logits, targets)
+    d0, d1, V = lg.shape
+    it = lg.itemsize
+    rr = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    n = d0 * d1 if rr is None else rr.size
+    ent = np.empty(n, np.float64)
+    rc = _load().vce_oracle_entropy(
+        _ptr(lg), _dtype_code(lg), d0, d1, V, lg.strides[0] // it, lg.strides[1] // it,
+        _ptr(tg), tg.strides[0] // 8, tg.strides[1] // 8, int(ignore_idx), _ptr(rr), n, _ptr(ent))
+    if rc != 0:
+        raise ValueError("oracle entropy rejected its arguments")
+    return ent
+
+
+def add_entropy_grad(grad: np.ndarray, logits: np.ndarray, targets: np.ndarray,
+                     grad_entropy: np.ndarray, ignore_idx: int = -100,
+                     rows: np.ndarray | None = None) -> np.ndarray:
+    """grad[i] += gH_r dH/dz for the selected rows, dH/dz_v = -p_v (ln p_v + H),
+    in place (FP64, shape (n, V)); ``grad_entropy`` holds gH for every row."""
+    lg, tg = _as_3d(logits, targets)
+    d0, d1, V = lg.shape
+    it = lg.itemsize
+    rr = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    n = d0 * d1 if rr is None else rr.size
+    gh = np.asarray(grad_entropy, np.float64).reshape(-1)
+    gsel = np.ascontiguousarray(gh[rr] if rr is not None else gh)
+    if grad.shape != (n, V) or grad.dtype != np.float64 or not grad.flags.c_contiguous:
+        raise ValueError("grad must be a C-contiguous float64 (n, V) array")
+    rc = _load().vce_oracle_entropy_grad(
+        _ptr(lg), _dtype_code(lg), d0, d1, V, lg.strides[0] // it, lg.strides[1] // it,
+        _ptr(tg), tg.strides[0] // 8, tg.strides[1] // 8, int(ignore_idx), _ptr(gsel), _ptr(rr), n,
+        _ptr(grad))
+    if rc != 0:
+        raise ValueError("oracle entropy gradient rejected its arguments")
     return grad
 
 

@@ -25,6 +25,17 @@
  * Saved statistics per row (same PR, Sequence Diagram "max/denominator
  * stats"): m, d = sum_v exp(z_v - m), z_t and mean_v z_v.
  *
+ * Entropy of the predicted distribution (the optional entropy output of the
+ * Liger-Kernel fused cross-entropy PR, Summary), also by definition:
+ *
+ *   H     = - sum_v p_v ln p_v                 (terms with p_v = 0 skipped)
+ *   dH/dz_v = - p_v (ln p_v + H)               (differentiating the sum term
+ *           by term through dp_u/dz_v = p_u ([u = v] - p_v))
+ *
+ * and a row's gradient gains gH * dH/dz when an upstream gradient gH of the
+ * entropy is given.  Ignored rows have entropy 0 and no entropy gradient;
+ * the entropy does not depend on the target otherwise.
+ *
  * Logits are addressed as (d0, d1, V) with element strides ls0, ls1 for the
  * leading dimensions and 1 for V, which covers the (B,SQ,V) and (SQ,B,V)
  * layouts of the API page.  dtype: 0 = FP32, 1 = BF16 bit patterns (uint16),
@@ -178,6 +189,76 @@ int vce_oracle_backward(const void *logits, int dtype, int64_t d0, int64_t d1, i
             double p = exp(load_value(logits, dtype, base + v) - lse);
             double q = qoff + (v == t ? 1.0 - eps : 0.0);
             out[v] = g[i] * (p - q);
+        }
+    }
+    return 0;
+}
+
+/* Entropy H = -sum_v p_v ln p_v of each row (0 for ignored rows). */
+int vce_oracle_entropy(const void *logits, int dtype, int64_t d0, int64_t d1, int64_t V,
+                       int64_t ls0, int64_t ls1, const int64_t *targets, int64_t ts0,
+                       int64_t ts1, int64_t ignore_idx, const int64_t *rows, int64_t nrows,
+                       double *ent)
+{
+    if (!logits || !targets || !ent || V <= 0 || d0 < 0 || d1 <= 0)
+        return 1;
+    int64_t n = rows ? nrows : d0 * d1;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t r = rows ? rows[i] : i;
+        int64_t base = row_offset(r, d1, ls0, ls1);
+        int64_t t = targets[row_offset(r, d1, ts0, ts1)];
+        if (t == ignore_idx) {
+            ent[i] = 0.0;
+            continue;
+        }
+        double m, d, lse;
+        row_lse(logits, dtype, base, V, &m, &d, &lse);
+        double h = 0.0;
+        for (int64_t v = 0; v < V; ++v) {
+            double lp = load_value(logits, dtype, base + v) - lse; /* ln p_v */
+            double p = exp(lp);
+            if (p == 0.0)
+                continue;
+            h -= p * lp;
+        }
+        ent[i] = h;
+    }
+    return 0;
+}
+
+/* grad[i, v] += gH[i] * dH/dz_v with dH/dz_v = -p_v (ln p_v + H) (ignored
+ * rows unchanged). */
+int vce_oracle_entropy_grad(const void *logits, int dtype, int64_t d0, int64_t d1, int64_t V,
+                            int64_t ls0, int64_t ls1, const int64_t *targets, int64_t ts0,
+                            int64_t ts1, int64_t ignore_idx, const double *gH,
+                            const int64_t *rows, int64_t nrows, double *grad)
+{
+    if (!logits || !targets || !gH || !grad || V <= 0 || d0 < 0 || d1 <= 0)
+        return 1;
+    int64_t n = rows ? nrows : d0 * d1;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t r = rows ? rows[i] : i;
+        int64_t base = row_offset(r, d1, ls0, ls1);
+        int64_t t = targets[row_offset(r, d1, ts0, ts1)];
+        if (t == ignore_idx)
+            continue;
+        double m, d, lse;
+        row_lse(logits, dtype, base, V, &m, &d, &lse);
+        double h = 0.0;
+        for (int64_t v = 0; v < V; ++v) {
+            double lp = load_value(logits, dtype, base + v) - lse;
+            double p = exp(lp);
+            if (p != 0.0)
+                h -= p * lp;
+        }
+        double *out = grad + i * V;
+        for (int64_t v = 0; v < V; ++v) {
+            double lp = load_value(logits, dtype, base + v) - lse;
+            double p = exp(lp);
+            if (p != 0.0)
+                out[v] += gH[i] * (-p * (lp + h));
         }
     }
     return 0;

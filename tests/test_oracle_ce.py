@@ -300,3 +300,81 @@ def test_layouts_and_strides():
     l_sub, _, _ = oracle.ce_forward(z, t, 0.1, rows=rows)
     np.testing.assert_array_equal(l_sub, loss_sb[rows])
     np.testing.assert_array_equal(oracle.ce_backward(z, t, g, 0.1, rows=rows), gr_sb[rows])
+
+
+# --- entropy (the optional output of the Liger-Kernel PR, Summary) -------------
+
+@pytest.mark.parametrize("V", [1, 2, 7, 1000, 128256])
+def test_entropy_uniform_is_ln_V(V):
+    # p = 1/V: -sum p ln p = ln V
+    z = np.full((1, 2, V), 0.75)
+    t = np.zeros((1, 2), np.int64)
+    h = oracle.entropy(z, t)
+    # a V-term FP64 sum: rounding grows with V
+    np.testing.assert_allclose(h, math.log(V), rtol=1e-13 + V * 2.0 ** -52, atol=1e-15)
+
+
+@pytest.mark.parametrize("a,b", [(0.0, 0.0), (1.5, -0.5), (-3.0, 7.0), (30.0, 0.0)])
+def test_entropy_two_classes_is_binary_entropy(a, b):
+    # textbook binary entropy of p = sigmoid(a - b), q = 1 - p = sigmoid(b - a),
+    # with ln p and ln q in their cancellation-free forms
+    x = a - b
+    lp = -math.log1p(math.exp(-x)) if x >= 0 else x - math.log1p(math.exp(x))
+    lq = -math.log1p(math.exp(x)) if x <= 0 else -x - math.log1p(math.exp(-x))
+    ref = -(math.exp(lp) * lp + math.exp(lq) * lq)
+    h = oracle.entropy(np.array([[[a, b]]]), np.zeros((1, 1), np.int64))
+    # ln p = z - lse carries an absolute FP64 rounding of about ulp(lse)
+    # (3.6e-15 at lse = 30), which dominates when H itself is ~1e-12
+    np.testing.assert_allclose(h, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_entropy_point_mass_is_zero_and_ignored_rows_are_zero():
+    z = np.full((1, 3, 9), -np.inf)
+    z[0, :, 4] = 2.0  # all mass on one class
+    t = np.array([[1, IGN, 4]], np.int64)
+    h = oracle.entropy(z, t)
+    assert h[0] == 0.0 and h[1] == 0.0 and h[2] == 0.0
+
+
+def test_entropy_shift_invariance_and_target_independence():
+    z = _rand_logits(51, 6, 300, sigma=3.0)
+    t1, t2 = _rand_targets(51, 6, 300), _rand_targets(52, 6, 300)
+    h1 = oracle.entropy(z, t1)
+    np.testing.assert_allclose(oracle.entropy(z + 11.0, t1), h1, rtol=1e-12)
+    np.testing.assert_array_equal(oracle.entropy(z, t2), h1)
+
+
+def test_entropy_against_torch_float64():
+    z = _rand_logits(53, 40, 3001, sigma=2.5)
+    t = _rand_targets(53, 40, 3001, n_ign=3)
+    ref = torch.distributions.Categorical(logits=torch.from_numpy(z)).entropy().numpy()
+    ref[t == IGN] = 0.0
+    np.testing.assert_allclose(oracle.entropy(z, t), ref, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("V", [2, 3, 5, 17])
+def test_entropy_gradient_matches_central_differences(V):
+    rng = np.random.default_rng(60 + V)
+    z = rng.standard_normal((3, V)) * 1.5
+    t = np.zeros(3, np.int64)
+    gH = np.array([1.0, -0.7, 2.5])
+    grad = np.zeros((3, V))
+    oracle.add_entropy_grad(grad, z, t, gH)
+    h = 1e-6
+    for r in range(3):
+        for v in range(V):
+            zp, zm = z.copy(), z.copy()
+            zp[r, v] += h
+            zm[r, v] -= h
+            fd = (oracle.entropy(zp, t)[r] - oracle.entropy(zm, t)[r]) / (2 * h)
+            assert abs(grad[r, v] - gH[r] * fd) <= 1e-7, (r, v)
+
+
+def test_entropy_gradient_rows_sum_to_zero_and_ignored_rows_untouched():
+    # sum_v dH/dz_v = -sum p (ln p + H) = H - H = 0
+    z = _rand_logits(61, 8, 500, sigma=2.0)
+    t = _rand_targets(61, 8, 500, n_ign=2)
+    grad = np.full((8, 500), 0.25)
+    oracle.add_entropy_grad(grad, z, t, np.linspace(-1, 1, 8))
+    np.testing.assert_allclose((grad - 0.25).sum(axis=1), 0.0, atol=1e-12)
+    assert np.all(grad[t == IGN] == 0.25)

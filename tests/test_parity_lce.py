@@ -155,6 +155,50 @@ def test_linear_matches_logits_form():
     assert nv.item() == nv2.item()
 
 
+def test_linear_graph_capture_replay():
+    # lce_forward and lce_backward only enqueue kernels on the given stream
+    # (no allocation, no memset, no synchronisation), so both can be captured
+    # into one graph and replayed; every replay must equal the eager result
+    # bit for bit (the kernels are deterministic).  Two vocabulary chunks make
+    # the dX accumulator path part of the graph.
+    case = wl.make_linear(3007, 600, 256, 40000, ignore_frac=0.05, label_smoothing=0.1,
+                          reduce_loss=True)
+    X, W = _bf16(case.X), _bf16(case.W)
+    t = torch.from_numpy(case.targets).cuda()
+    go = torch.ones(1, device="cuda")
+    M, H, V = case.X.shape[0], case.X.shape[1], case.W.shape[0]
+    ws = vce.lce_workspace(M, H, V)
+    loss = torch.empty(M, device="cuda")
+    mean = torch.empty((), device="cuda")
+    stats = torch.empty((M, 4), device="cuda")
+    nv = torch.empty((), dtype=torch.int32, device="cuda")
+    dX, dW = torch.empty_like(X), torch.empty_like(W)
+    out = (loss, mean, stats, nv)
+    vce.lce_forward(X, W, t, 0.1, True, workspace=ws, out=out)
+    vce.lce_backward(X, W, t, stats, nv, go, 0.1, True, workspace=ws, dX=dX, dW=dW)
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (loss, mean, stats, dX, dW)]
+    s = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            vce.lce_forward(X, W, t, 0.1, True, workspace=ws, out=out, stream=s)
+            vce.lce_backward(X, W, t, stats, nv, go, 0.1, True, workspace=ws, dX=dX, dW=dW,
+                             stream=s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for x in (loss, mean, stats, dX, dW):
+            x.zero_()
+        ws.fill_(0xAB)  # eager work between replays; the graph must not depend on it
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("loss", "mean", "stats", "dX", "dW"), (loss, mean, stats, dX, dW),
+                              ref):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs"
+    _say("graph capture + 3 replays of lce_forward + lce_backward: bit-identical")
+
+
 def test_linear_deterministic():
     case = wl.make_linear(3006, 700, 192, 9000, ignore_frac=0.1, label_smoothing=0.1)
     a, b = run_lce(case), run_lce(case)
