@@ -37,6 +37,13 @@
  * Saved statistics: stats is (N, 4) FP32 per row = (m, d, z_t, mean_v z_v),
  * 16 bytes per row.  Rows that are ignored hold zeros there.
  *
+ * Entropy (optional, the "optional entropy" output of the Liger-Kernel PR,
+ * Summary): H_r = -sum_v p_v ln p_v of p = softmax(z_r), FP32 per row, 0 for
+ * ignored rows (it does not depend on the target otherwise).  Given an
+ * upstream gradient gH of the entropy, the backward adds
+ *     gH_r dH/dz_v = gH_r p_v (E_p[z] - z_v),   E_p[z] = lse_r - H_r,
+ * to the loss gradient; it reads H_r from the forward's entropy output.
+ *
  * Conventions for every entry point:
  *  - All pointers are DEVICE pointers on the current HIP device, owned by
  *    the caller.  The library never allocates, frees or synchronises and
@@ -93,12 +100,14 @@ const char* vce_strerror(int status);
  *           (the backward of the averaged loss reads it), else may be NULL.
  *  Kernels: one row sweep (one 1024-thread workgroup per row), plus one
  *  single-workgroup deterministic mean when reduce_loss or n_valid is given.
+ *  entropy  (N) FP32, or NULL: written iff non-NULL (costs one more FMA per
+ *           logit; the path without it is unchanged).
  */
 int ce_forward(const void* logits, int dtype, int64_t d0, int64_t d1, int64_t V,
                int64_t ls0, int64_t ls1, const int64_t* targets, int64_t ts0, int64_t ts1,
                float label_smoothing, int reduce_loss, int64_t ignore_idx,
                float* loss_tok, float* loss_mean, float* stats, int32_t* n_valid,
-               void* stream);
+               float* entropy, void* stream);
 
 /*
  * ce_backward: rebuild the logits gradient from the saved statistics.
@@ -115,12 +124,15 @@ int ce_forward(const void* logits, int dtype, int64_t d0, int64_t d1, int64_t V,
  *  overwrite_input  nonzero: grad must equal logits, and the logits are
  *           replaced by the gradient (no extra buffer).  Zero: grad and
  *           logits must not overlap (VCE_EALIAS otherwise).
+ *  entropy, grad_entropy  (N) FP32 each, or NULL: with grad_entropy the
+ *           gradient also gets grad_entropy[r] dH/dz (see above), entropy being
+ *           the forward's entropy output (required then).
  */
 int ce_backward(const void* logits, void* grad, int dtype, int64_t d0, int64_t d1, int64_t V,
                 int64_t ls0, int64_t ls1, const int64_t* targets, int64_t ts0, int64_t ts1,
                 const float* stats, const int32_t* n_valid, const float* grad_output,
-                float label_smoothing, int reduce_loss, int64_t ignore_idx, int overwrite_input,
-                void* stream);
+                const float* entropy, const float* grad_entropy, float label_smoothing,
+                int reduce_loss, int64_t ignore_idx, int overwrite_input, void* stream);
 
 /*
  * lce_workspace_size: bytes of device workspace lce_forward and lce_backward
@@ -138,12 +150,14 @@ size_t lce_workspace_size(int64_t M, int64_t H, int64_t V);
  *  accumulation on the matrix cores.
  *  targets (M) int64 contiguous.   Outputs as ce_forward with N = M:
  *  loss_tok (M), loss_mean (iff reduce_loss), stats (M, 4), n_valid.
+ *  entropy (M) FP32 or NULL, as in ce_forward.
  *  workspace: at least lce_workspace_size(M, H, V) bytes, 256-byte aligned.
  */
 int lce_forward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
                 const int64_t* targets, float label_smoothing, int reduce_loss,
                 int64_t ignore_idx, float* loss_tok, float* loss_mean, float* stats,
-                int32_t* n_valid, void* workspace, size_t workspace_bytes, void* stream);
+                int32_t* n_valid, float* entropy, void* workspace, size_t workspace_bytes,
+                void* stream);
 
 /*
  * lce_backward: dX (M, H) and dW (V, H), BF16, overwritten (not accumulated).
@@ -152,12 +166,13 @@ int lce_forward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
  *  to lce_forward.  stats, n_valid: from lce_forward.  grad_output: FP32, 1
  *  element if reduce_loss else (M).  The logits are recomputed chunk by chunk
  *  over the vocabulary; the gradient of each chunk is held in the workspace.
+ *  entropy, grad_entropy: as in ce_backward.
  */
 int lce_backward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
                  const int64_t* targets, const float* stats, const int32_t* n_valid,
-                 const float* grad_output, float label_smoothing, int reduce_loss,
-                 int64_t ignore_idx, void* dX, void* dW, void* workspace,
-                 size_t workspace_bytes, void* stream);
+                 const float* grad_output, const float* entropy, const float* grad_entropy,
+                 float label_smoothing, int reduce_loss, int64_t ignore_idx, void* dX, void* dW,
+                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * vce_gemm_bf16: the matrix-core building block of the linear form, exported

@@ -12,6 +12,7 @@ logits, then dX = dZ W and dW = dZ^T X):
     Z  = X W^T                    (FP64 product of the exact BF16 values)
     loss, stats = logits cross-entropy of Z   (the C core of this package)
     dZ = g_r (softmax(Z_r) - q_r)             (the C core of this package)
+         [+ gH_r dH/dZ_r when an entropy gradient is given]
     dX = dZ W,   dW = dZ^T X                  (FP64 matrix products)
 
 Rows (tokens) are independent, so large problems are processed in token
@@ -22,7 +23,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import bf16_to_f64, ce_backward, ce_forward
+from . import add_entropy_grad, bf16_to_f64, ce_backward, ce_forward, entropy as _entropy
 
 
 def _rows(a: np.ndarray, rows):
@@ -68,9 +69,23 @@ def forward(X_bits, W_bits, targets, label_smoothing=0.0, ignore_idx=-100, rows=
     return loss, stats, lse
 
 
+def entropy(X_bits, W_bits, targets, ignore_idx=-100, token_chunk: int | None = None):
+    """Per-token entropy of softmax(X W^T) in FP64 (0 for ignored tokens)."""
+    t_all = np.asarray(targets, np.int64).reshape(-1)
+    W = _dec(W_bits)
+    M = t_all.size
+    chunk = token_chunk or max(1, M)
+    out = np.empty(M)
+    for s in range(0, M, chunk):
+        Z = _dec(X_bits[s:s + chunk]) @ W.T
+        out[s:s + chunk] = _entropy(Z, t_all[s:s + chunk], ignore_idx)
+    return out
+
+
 def backward(X_bits, W_bits, targets, g, label_smoothing=0.0, ignore_idx=-100,
-             token_chunk: int | None = None):
-    """Full dX (M, H) and dW (V, H) in FP64.  ``g`` is g_r for every token."""
+             token_chunk: int | None = None, grad_entropy=None):
+    """Full dX (M, H) and dW (V, H) in FP64.  ``g`` is g_r for every token;
+    ``grad_entropy`` (per token, optional) adds the entropy's gradient."""
     t_all = np.asarray(targets, np.int64).reshape(-1)
     g_all = np.asarray(g, np.float64).reshape(-1)
     M = t_all.size
@@ -82,6 +97,9 @@ def backward(X_bits, W_bits, targets, g, label_smoothing=0.0, ignore_idx=-100,
         Xc = _dec(X_bits[s:s + chunk])
         Z = Xc @ W.T
         dZ = ce_backward(Z, t_all[s:s + chunk], g_all[s:s + chunk], label_smoothing, ignore_idx)
+        if grad_entropy is not None:
+            gh = np.asarray(grad_entropy, np.float64).reshape(-1)[s:s + chunk]
+            add_entropy_grad(dZ, Z, t_all[s:s + chunk], gh, ignore_idx)
         dX[s:s + chunk] = dZ @ W
         dW += dZ.T @ Xc
     return dX, dW

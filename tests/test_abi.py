@@ -54,15 +54,17 @@ def test_strerror(L):
 
 
 def fwd(L, logits=A, dtype=1, d0=2, d1=3, V=1000, ls0=3000, ls1=1000, targets=A, ts0=3, ts1=1,
-        eps=0.0, reduce_loss=0, ignore=-100, loss_tok=A, loss_mean=A, stats=A, n_valid=A):
+        eps=0.0, reduce_loss=0, ignore=-100, loss_tok=A, loss_mean=A, stats=A, n_valid=A,
+        entropy=None):
     return L.ce_forward(logits, dtype, d0, d1, V, ls0, ls1, targets, ts0, ts1, eps, reduce_loss,
-                        ignore, loss_tok, loss_mean, stats, n_valid, None)
+                        ignore, loss_tok, loss_mean, stats, n_valid, entropy, None)
 
 
 def bwd(L, logits=A, grad=A + (1 << 30), dtype=1, d0=2, d1=3, V=1000, ls0=3000, ls1=1000, targets=A,
-        ts0=3, ts1=1, stats=A, n_valid=A, go=A, eps=0.0, reduce_loss=0, ignore=-100, overwrite=0):
+        ts0=3, ts1=1, stats=A, n_valid=A, go=A, eps=0.0, reduce_loss=0, ignore=-100, overwrite=0,
+        entropy=None, grad_entropy=None):
     return L.ce_backward(logits, grad, dtype, d0, d1, V, ls0, ls1, targets, ts0, ts1, stats, n_valid,
-                         go, eps, reduce_loss, ignore, overwrite, None)
+                         go, entropy, grad_entropy, eps, reduce_loss, ignore, overwrite, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -73,7 +75,7 @@ def bwd(L, logits=A, grad=A + (1 << 30), dtype=1, d0=2, d1=3, V=1000, ls0=3000, 
     (dict(logits=None), 1), (dict(targets=None), 1), (dict(loss_tok=None), 1), (dict(stats=None), 1),
     (dict(reduce_loss=1, loss_mean=None), 1), (dict(reduce_loss=1, n_valid=None), 1),
     (dict(logits=A + 1), 3), (dict(dtype=0, logits=A + 2), 3), (dict(targets=A + 4), 3),
-    (dict(stats=A + 4), 3),
+    (dict(stats=A + 4), 3), (dict(entropy=A + 2), 3),
     (dict(d0=1 << 32, d1=1 << 32), 1),
     (dict(d0=1 << 20, d1=1 << 12), 1),  # N above INT32_MAX rows
 ])
@@ -89,6 +91,8 @@ def test_ce_forward_rejects(L, kw, code):
     (dict(grad=A + 4096), 4),                   # separate buffers that overlap
     (dict(grad=A + (1 << 30) + 2), 3),          # rows would split at different 16-byte boundaries
     (dict(stats=A + 8), 3),
+    (dict(grad_entropy=A), 1),                  # entropy gradient without the entropy
+    (dict(entropy=A, grad_entropy=A + 2), 3),
 ])
 def test_ce_backward_rejects(L, kw, code):
     assert bwd(L, **kw) == code
@@ -107,11 +111,11 @@ def test_lce_workspace_size(L):
 
 
 def lfwd(L, X=A, W=A, M=64, H=64, V=1000, targets=A, eps=0.0, reduce_loss=1, ignore=-100,
-         loss_tok=A, loss_mean=A, stats=A, n_valid=A, ws=A, ws_bytes=None):
+         loss_tok=A, loss_mean=A, stats=A, n_valid=A, entropy=None, ws=A, ws_bytes=None):
     if ws_bytes is None:
         ws_bytes = L.lce_workspace_size(max(M, 0), H, V)
     return L.lce_forward(X, W, M, H, V, targets, eps, reduce_loss, ignore, loss_tok, loss_mean,
-                         stats, n_valid, ws, ws_bytes, None)
+                         stats, n_valid, entropy, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -120,7 +124,7 @@ def lfwd(L, X=A, W=A, M=64, H=64, V=1000, targets=A, eps=0.0, reduce_loss=1, ign
     (dict(X=None), 1), (dict(W=None), 1), (dict(targets=None), 1), (dict(ws=None), 1),
     (dict(X=A + 8), 3), (dict(W=A + 2), 3), (dict(ws=A + 16), 3),
     (dict(ws_bytes=1), 5),
-    (dict(reduce_loss=1, loss_mean=None), 1), (dict(stats=A + 4), 3),
+    (dict(reduce_loss=1, loss_mean=None), 1), (dict(stats=A + 4), 3), (dict(entropy=A + 1), 3),
 ])
 def test_lce_forward_rejects(L, kw, code):
     assert lfwd(L, **kw) == code
@@ -130,12 +134,13 @@ def test_lce_backward_rejects(L):
     ws = L.lce_workspace_size(64, 64, 1000)
 
     def call(**kw):
-        a = dict(X=A, W=A, M=64, H=64, V=1000, targets=A, stats=A, n_valid=A, go=A, eps=0.0,
-                 reduce_loss=1, ignore=-100, dX=A, dW=A, ws=A, ws_bytes=ws)
+        a = dict(X=A, W=A, M=64, H=64, V=1000, targets=A, stats=A, n_valid=A, go=A, ent=None,
+                 gent=None, eps=0.0, reduce_loss=1, ignore=-100, dX=A, dW=A, ws=A, ws_bytes=ws)
         a.update(kw)
         return L.lce_backward(a["X"], a["W"], a["M"], a["H"], a["V"], a["targets"], a["stats"],
-                              a["n_valid"], a["go"], a["eps"], a["reduce_loss"], a["ignore"],
-                              a["dX"], a["dW"], a["ws"], a["ws_bytes"], None)
+                              a["n_valid"], a["go"], a["ent"], a["gent"], a["eps"],
+                              a["reduce_loss"], a["ignore"], a["dX"], a["dW"], a["ws"],
+                              a["ws_bytes"], None)
 
     assert call(dW=None) == 1
     assert call(dX=None) == 1
@@ -143,6 +148,8 @@ def test_lce_backward_rejects(L):
     assert call(ws_bytes=ws - 1) == 5
     assert call(reduce_loss=1, n_valid=None) == 1
     assert call(H=20) == 7
+    assert call(gent=A) == 1            # entropy gradient without the entropy
+    assert call(ent=A, gent=A + 2) == 3
 
 
 def test_gemm_rejects(L):

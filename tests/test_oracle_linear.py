@@ -70,6 +70,32 @@ def test_finite_differences_tiny():
             assert abs((total(X, Wp) - total(X, Wm)) / (2 * h) - dW[v, j]) < 1e-7
 
 
+def test_finite_differences_with_entropy_tiny():
+    # J = sum_r g_r loss_r + gH_r H_r: its gradient is dX, dW from backward()
+    # with grad_entropy (M=3, H=4, V=7, central differences)
+    X, W, t = _case(4, 3, 4, 7)
+    eps = 0.1
+    g = np.array([1.0, 0.5, -0.25])
+    gH = np.array([0.8, -1.2, 0.3])
+    dX, dW = linear.backward(X, W, t, g, eps, grad_entropy=gH)
+    h = 1e-6
+
+    def total(Xa, Wa):
+        loss, _, _ = linear.forward(Xa, Wa, t, eps)
+        return float(np.dot(g, loss) + np.dot(gH, linear.entropy(Xa, Wa, t)))
+
+    for i in range(3):
+        for j in range(4):
+            Xp = X.copy(); Xp[i, j] += h
+            Xm = X.copy(); Xm[i, j] -= h
+            assert abs((total(Xp, W) - total(Xm, W)) / (2 * h) - dX[i, j]) < 1e-7
+    for v in range(7):
+        for j in range(4):
+            Wp = W.copy(); Wp[v, j] += h
+            Wm = W.copy(); Wm[v, j] -= h
+            assert abs((total(X, Wp) - total(X, Wm)) / (2 * h) - dW[v, j]) < 1e-7
+
+
 def test_pure_python_tiny():
     X, W, t = _case(3, 2, 3, 5)
     Z = tiny.matmul_nt(X.tolist(), W.tolist())

@@ -26,14 +26,14 @@ _I64, _I32, _F32, _VP, _SZ = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctype
 SIGNATURES = {
     "vce_strerror": (ctypes.c_char_p, [_I32]),
     "ce_forward": (_I32, [_VP, _I32, _I64, _I64, _I64, _I64, _I64, _VP, _I64, _I64, _F32, _I32, _I64,
-                          _VP, _VP, _VP, _VP, _VP]),
+                          _VP, _VP, _VP, _VP, _VP, _VP]),
     "ce_backward": (_I32, [_VP, _VP, _I32, _I64, _I64, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _VP,
-                           _VP, _F32, _I32, _I64, _I32, _VP]),
+                           _VP, _VP, _VP, _F32, _I32, _I64, _I32, _VP]),
     "lce_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "lce_forward": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _F32, _I32, _I64, _VP, _VP, _VP, _VP,
-                           _VP, _SZ, _VP]),
-    "lce_backward": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _F32, _I32, _I64, _VP,
-                            _VP, _VP, _SZ, _VP]),
+                           _VP, _VP, _SZ, _VP]),
+    "lce_backward": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _F32, _I32,
+                            _I64, _VP, _VP, _VP, _SZ, _VP]),
     "vce_gemm_bf16": (_I32, [_VP, _I64, _I32, _VP, _I64, _I32, _I64, _I64, _I64, _VP, _I64, _VP]),
 }
 
@@ -108,9 +108,11 @@ def _logits3d(logits: torch.Tensor, targets: torch.Tensor):
 
 
 def ce_forward(logits: torch.Tensor, targets: torch.Tensor, label_smoothing: float = 0.0,
-               reduce_loss: bool = False, ignore_idx: int = -100, *, stream=None, out=None):
-    """Forward of logits cross-entropy.  Returns (loss_tok, loss_mean, stats, n_valid);
-    loss_mean and n_valid are None unless reduce_loss."""
+               reduce_loss: bool = False, ignore_idx: int = -100, *, stream=None, out=None,
+               with_entropy: bool = False):
+    """Forward of logits cross-entropy.  Returns (loss_tok, loss_mean, stats, n_valid),
+    plus the per-row entropy with ``with_entropy``; loss_mean and n_valid are None
+    unless reduce_loss.  ``out`` gives the output tensors in the same order."""
     logits, targets = _logits3d(logits, targets)
     _need_cuda(logits, targets)
     d0, d1, V = logits.shape
@@ -120,23 +122,30 @@ def ce_forward(logits: torch.Tensor, targets: torch.Tensor, label_smoothing: flo
         stats = torch.empty((d0, d1, 4), dtype=torch.float32, device=dev)
         loss_mean = torch.empty((), dtype=torch.float32, device=dev) if reduce_loss else None
         n_valid = torch.empty((), dtype=torch.int32, device=dev) if reduce_loss else None
+        ent = torch.empty((d0, d1), dtype=torch.float32, device=dev) if with_entropy else None
     else:
-        loss_tok, loss_mean, stats, n_valid = out
+        loss_tok, loss_mean, stats, n_valid = out[:4]
+        ent = out[4] if with_entropy else None
     rc = lib().ce_forward(_ptr(logits), _dtype_code(logits), d0, d1, V, logits.stride(0),
                           logits.stride(1), _ptr(targets), targets.stride(0), targets.stride(1),
                           float(label_smoothing), int(bool(reduce_loss)), int(ignore_idx),
-                          _ptr(loss_tok), _ptr(loss_mean), _ptr(stats), _ptr(n_valid),
+                          _ptr(loss_tok), _ptr(loss_mean), _ptr(stats), _ptr(n_valid), _ptr(ent),
                           _stream(stream))
     _check("ce_forward", rc)
+    if with_entropy:
+        return loss_tok, loss_mean, stats, n_valid, ent
     return loss_tok, loss_mean, stats, n_valid
 
 
 def ce_backward(logits: torch.Tensor, targets: torch.Tensor, stats: torch.Tensor,
                 n_valid: torch.Tensor | None, grad_output: torch.Tensor,
                 label_smoothing: float = 0.0, reduce_loss: bool = False, ignore_idx: int = -100,
-                overwrite_input: bool = False, *, grad: torch.Tensor | None = None, stream=None):
+                overwrite_input: bool = False, *, grad: torch.Tensor | None = None, stream=None,
+                entropy: torch.Tensor | None = None, grad_entropy: torch.Tensor | None = None):
     """Gradient of logits cross-entropy rebuilt from ``stats``.  With
-    ``overwrite_input`` the logits tensor itself receives the gradient."""
+    ``overwrite_input`` the logits tensor itself receives the gradient.  With
+    ``grad_entropy`` (per row) the entropy's gradient is added; ``entropy`` is
+    then the forward's entropy output."""
     logits, targets = _logits3d(logits, targets)
     _need_cuda(logits, targets, stats, grad_output)
     d0, d1, V = logits.shape
@@ -152,8 +161,9 @@ def ce_backward(logits: torch.Tensor, targets: torch.Tensor, stats: torch.Tensor
     rc = lib().ce_backward(_ptr(logits), _ptr(grad), _dtype_code(logits), d0, d1, V,
                            logits.stride(0), logits.stride(1), _ptr(targets), targets.stride(0),
                            targets.stride(1), _ptr(stats), _ptr(n_valid), _ptr(grad_output),
-                           float(label_smoothing), int(bool(reduce_loss)), int(ignore_idx),
-                           int(bool(overwrite_input)), _stream(stream))
+                           _ptr(entropy), _ptr(grad_entropy), float(label_smoothing),
+                           int(bool(reduce_loss)), int(ignore_idx), int(bool(overwrite_input)),
+                           _stream(stream))
     _check("ce_backward", rc)
     return grad
 
@@ -183,8 +193,10 @@ def _check_linear(X, W, targets):
 
 def lce_forward(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
                 label_smoothing: float = 0.0, reduce_loss: bool = True, ignore_idx: int = -100,
-                *, workspace: torch.Tensor | None = None, stream=None, out=None):
-    """Fused linear cross-entropy forward.  Returns (loss_tok, loss_mean, stats, n_valid)."""
+                *, workspace: torch.Tensor | None = None, stream=None, out=None,
+                with_entropy: bool = False):
+    """Fused linear cross-entropy forward.  Returns (loss_tok, loss_mean, stats, n_valid),
+    plus the per-token entropy with ``with_entropy``."""
     _check_linear(X, W, targets)
     M, H = X.shape
     V = W.shape[0]
@@ -196,13 +208,17 @@ def lce_forward(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
         stats = torch.empty((M, 4), dtype=torch.float32, device=dev)
         loss_mean = torch.empty((), dtype=torch.float32, device=dev) if reduce_loss else None
         n_valid = torch.empty((), dtype=torch.int32, device=dev) if reduce_loss else None
+        ent = torch.empty(M, dtype=torch.float32, device=dev) if with_entropy else None
     else:
-        loss_tok, loss_mean, stats, n_valid = out
+        loss_tok, loss_mean, stats, n_valid = out[:4]
+        ent = out[4] if with_entropy else None
     rc = lib().lce_forward(_ptr(X), _ptr(W), M, H, V, _ptr(targets), float(label_smoothing),
                            int(bool(reduce_loss)), int(ignore_idx), _ptr(loss_tok),
-                           _ptr(loss_mean), _ptr(stats), _ptr(n_valid), _ptr(workspace),
-                           workspace.numel(), _stream(stream))
+                           _ptr(loss_mean), _ptr(stats), _ptr(n_valid), _ptr(ent),
+                           _ptr(workspace), workspace.numel(), _stream(stream))
     _check("lce_forward", rc)
+    if with_entropy:
+        return loss_tok, loss_mean, stats, n_valid, ent
     return loss_tok, loss_mean, stats, n_valid
 
 
@@ -210,8 +226,11 @@ def lce_backward(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, stats:
                  n_valid: torch.Tensor | None, grad_output: torch.Tensor,
                  label_smoothing: float = 0.0, reduce_loss: bool = True, ignore_idx: int = -100,
                  *, workspace: torch.Tensor | None = None, dX: torch.Tensor | None = None,
-                 dW: torch.Tensor | None = None, stream=None):
-    """Fused linear cross-entropy backward.  Returns (dX, dW), BF16."""
+                 dW: torch.Tensor | None = None, stream=None, entropy: torch.Tensor | None = None,
+                 grad_entropy: torch.Tensor | None = None):
+    """Fused linear cross-entropy backward.  Returns (dX, dW), BF16.  With
+    ``grad_entropy`` the entropy's gradient is added (``entropy``: the
+    forward's entropy output)."""
     _check_linear(X, W, targets)
     M, H = X.shape
     V = W.shape[0]
@@ -220,9 +239,10 @@ def lce_backward(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, stats:
     dX = torch.empty_like(X) if dX is None else dX
     dW = torch.empty_like(W) if dW is None else dW
     rc = lib().lce_backward(_ptr(X), _ptr(W), M, H, V, _ptr(targets), _ptr(stats), _ptr(n_valid),
-                            _ptr(grad_output), float(label_smoothing), int(bool(reduce_loss)),
-                            int(ignore_idx), _ptr(dX), _ptr(dW), _ptr(workspace),
-                            workspace.numel(), _stream(stream))
+                            _ptr(grad_output), _ptr(entropy), _ptr(grad_entropy),
+                            float(label_smoothing), int(bool(reduce_loss)), int(ignore_idx),
+                            _ptr(dX), _ptr(dW), _ptr(workspace), workspace.numel(),
+                            _stream(stream))
     _check("lce_backward", rc)
     return dX, dW
 

@@ -92,10 +92,12 @@ __device__ __forceinline__ float vec_sum<1>(const u32x4_t& w, const float*, floa
 }
 
 // Fold n vectors (already loaded) into the running state; only the first
-// `nvalid` take part (the others may hold anything).
-template <int DT, int N>
-__device__ __forceinline__ void fold(LseState& st, const u32x4_t* w, int nvalid = N) {
+// `nvalid` take part (the others may hold anything).  S = LseEntState also
+// accumulates w = sum exp(z - m) (z - m) log2(e) for the entropy.
+template <int DT, int N, class S>
+__device__ __forceinline__ void fold(S& st, const u32x4_t* w, int nvalid = N) {
   constexpr int vec = Elem<DT>::kVec;
+  constexpr bool kEnt = __is_same(S, LseEntState);
   float z[N][vec];
 #pragma unroll
   for (int u = 0; u < N; ++u) {
@@ -113,39 +115,67 @@ __device__ __forceinline__ void fold(LseState& st, const u32x4_t* w, int nvalid 
   const float m_new = fmaxf(st.m, cm);
   const float mref = (m_new == kNegInf) ? 0.0f : m_new;
   const float mL = mref * kLog2e;
-  float dpart[N];
+  float dpart[N], wpart[N];
 #pragma unroll
   for (int u = 0; u < N; ++u) {
-    float acc = 0.0f;
+    float acc = 0.0f, accw = 0.0f;
 #pragma unroll
-    for (int i = 0; i < vec; ++i) acc += exp2_hw(__builtin_fmaf(z[u][i], kLog2e, -mL));
+    for (int i = 0; i < vec; ++i) {
+      const float t = __builtin_fmaf(z[u][i], kLog2e, -mL);  // (z - m) log2(e)
+      const float e = exp2_hw(t);
+      acc += e;
+      // -inf logits: e = 0 and t = -inf; the clamp keeps 0 * t finite
+      if constexpr (kEnt) accw = __builtin_fmaf(e, fmaxf(t, -200.0f), accw);
+    }
     dpart[u] = acc;
+    wpart[u] = accw;
   }
   float dsum = dpart[0];
 #pragma unroll
   for (int u = 1; u < N; ++u) dsum += dpart[u];
-  st.d = st.d * exp2_hw((st.m - mref) * kLog2e) + dsum;
+  const float f = exp2_hw((st.m - mref) * kLog2e);
+  if constexpr (kEnt) {
+    float wsum = wpart[0];
+#pragma unroll
+    for (int u = 1; u < N; ++u) wsum += wpart[u];
+    // move the old w from the old max to the new one (nothing when empty)
+    const float wold = st.d > 0.0f ? f * (st.w - (mref - st.m) * kLog2e * st.d) : 0.0f;
+    st.w = wold + wsum;
+  }
+  st.d = st.d * f + dsum;
 #pragma unroll
   for (int u = 0; u < N; ++u)
     if (u < nvalid) st.s = vec_sum<DT>(w[u], z[u], st.s);
   st.m = m_new;
 }
 
-__device__ __forceinline__ LseState block_reduce(LseState st, LseState* sh) {
+template <class S>
+__device__ __forceinline__ S block_reduce(S st, S* sh) {
   lse_wave_reduce(st);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) sh[wave] = st;
   __syncthreads();
-  LseState r = sh[0];
+  S r = sh[0];
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) lse_merge(r, sh[w]);
   return r;
 }
 
-template <int DT>
+template <bool ENT>
+struct StateOf {
+  using T = LseState;
+};
+template <>
+struct StateOf<true> {
+  using T = LseEntState;
+};
+
+// ENT: also the entropy of softmax(z) per row (0 for ignored rows).
+template <int DT, bool ENT>
 __global__ __launch_bounds__(kThreads) void ce_fwd_kernel(CeFwdParams p) {
   using T = typename Elem<DT>::T;
-  __shared__ LseState sh[kWaves];
+  using S = typename StateOf<ENT>::T;
+  __shared__ S sh[kWaves];
   const int64_t r = blockIdx.x;
   const int64_t i0 = r / p.d1, i1 = r - i0 * p.d1;
   const int64_t t = p.targets[i0 * p.ts0 + i1 * p.ts1];
@@ -154,6 +184,7 @@ __global__ __launch_bounds__(kThreads) void ce_fwd_kernel(CeFwdParams p) {
     if (tid == 0) {
       p.loss_tok[r] = 0.0f;
       *reinterpret_cast<f32x4_t*>(p.stats + 4 * r) = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      if (ENT) p.entropy[r] = 0.0f;
     }
     return;
   }
@@ -164,7 +195,11 @@ __global__ __launch_bounds__(kThreads) void ce_fwd_kernel(CeFwdParams p) {
   if (tid == 0 && t_ok) zt = Elem<DT>::load(row + t);
 
   const RowSplit rs = split_row<DT>(row, V);
-  LseState st = {kNegInf, 0.0f, 0.0f};
+  S st;
+  st.m = kNegInf;
+  st.d = 0.0f;
+  st.s = 0.0f;
+  if constexpr (ENT) st.w = 0.0f;  // one element: z - m = 0
   {
     const int64_t nscal = rs.head + (V - rs.tail0);
     if (tid < nscal) {
@@ -191,8 +226,9 @@ __global__ __launch_bounds__(kThreads) void ce_fwd_kernel(CeFwdParams p) {
       w[u] = u < nvalid ? __builtin_nontemporal_load(vrow + j + u * kThreads) : u32x4_t{0, 0, 0, 0};
     fold<DT, kUnroll>(st, w, nvalid);
   }
-  const LseState tot = block_reduce(st, sh);
+  const S tot = block_reduce(st, sh);
   if (tid == 0) {
+    if constexpr (ENT) p.entropy[r] = entropy_of(tot.d, tot.w);
     const float eps = p.eps;
     const float lse_shift = log2_hw(tot.d) * kLn2;  // lse - m
     const float mean = tot.s / (float)V;
@@ -256,7 +292,9 @@ __device__ __forceinline__ void store_one<0>(float* dst, float g) { *dst = g; }
 template <>
 __device__ __forceinline__ void store_one<1>(uint16_t* dst, float g) { *dst = to_bf16(g); }
 
-template <int DT>
+// ENT: adds grad_entropy[r] dH/dz_v = grad_entropy[r] p_v (E_p[z] - z_v), with
+// E_p[z] = lse - H from the forward's entropy.
+template <int DT, bool ENT>
 __global__ __launch_bounds__(kThreads) void ce_bwd_kernel(CeBwdParams p) {
   using T = typename Elem<DT>::T;
   constexpr int vec = Elem<DT>::kVec;
@@ -300,13 +338,27 @@ __global__ __launch_bounds__(kThreads) void ce_bwd_kernel(CeBwdParams p) {
   const float gs = g / d;
   const float goff = g * (p.eps / (float)V);
   const float gt = g * (1.0f - p.eps);
+  float gHd = 0.0f, ez = 0.0f;
+  if constexpr (ENT) {
+    gHd = p.grad_entropy[r] / d;
+    ez = mref + kLn2 * log2_hw(d) - p.entropy[r];  // E_p[z] = lse - H
+  }
+  // gradient of one logit, before the target correction; -inf logits (p = 0)
+  // are clamped so that p (E_p[z] - z) stays 0
+  auto gval = [&](float z) -> float {
+    const float e = exp2_hw(__builtin_fmaf(z, kLog2e, -mL));
+    if constexpr (ENT)
+      return e * __builtin_fmaf(gHd, ez - fmaxf(z, -1e30f), gs) - goff;
+    else
+      return e * gs - goff;
+  };
 
   {
     const int64_t nscal = rs.head + (V - rs.tail0);
     if (tid < nscal) {
       const int64_t idx = tid < rs.head ? tid : rs.tail0 + (tid - rs.head);
       const float z = Elem<DT>::load(row + idx);
-      float gv = exp2_hw(__builtin_fmaf(z, kLog2e, -mL)) * gs - goff;
+      float gv = gval(z);
       if (idx == t) gv -= gt;
       store_one<DT>(grow + idx, gv);
     }
@@ -327,7 +379,7 @@ __global__ __launch_bounds__(kThreads) void ce_bwd_kernel(CeBwdParams p) {
       unpack<DT>(w[u], z);
       float gv[vec];
 #pragma unroll
-      for (int i = 0; i < vec; ++i) gv[i] = exp2_hw(__builtin_fmaf(z[i], kLog2e, -mL)) * gs - goff;
+      for (int i = 0; i < vec; ++i) gv[i] = gval(z[i]);
       const int64_t base = (j + u * kThreads) * vec;
       if (tv >= base && tv < base + vec) {
 #pragma unroll
@@ -350,7 +402,7 @@ __global__ __launch_bounds__(kThreads) void ce_bwd_kernel(CeBwdParams p) {
       unpack<DT>(w[u], z);
       float gv[vec];
 #pragma unroll
-      for (int i = 0; i < vec; ++i) gv[i] = exp2_hw(__builtin_fmaf(z[i], kLog2e, -mL)) * gs - goff;
+      for (int i = 0; i < vec; ++i) gv[i] = gval(z[i]);
       const int64_t base = (j + u * kThreads) * vec;
       if (tv >= base && tv < base + vec) {
 #pragma unroll
@@ -366,10 +418,15 @@ __global__ __launch_bounds__(kThreads) void ce_bwd_kernel(CeBwdParams p) {
 
 hipError_t launch_ce_forward(const CeFwdParams& p, int dtype, int64_t N, hipStream_t stream) {
   if (N <= 0) return hipSuccess;
-  if (dtype == 0)
-    hipLaunchKernelGGL(ce_fwd_kernel<0>, dim3((unsigned)N), dim3(kThreads), 0, stream, p);
+  const bool ent = p.entropy != nullptr;
+  if (dtype == 0 && !ent)
+    hipLaunchKernelGGL((ce_fwd_kernel<0, false>), dim3((unsigned)N), dim3(kThreads), 0, stream, p);
+  else if (dtype == 0)
+    hipLaunchKernelGGL((ce_fwd_kernel<0, true>), dim3((unsigned)N), dim3(kThreads), 0, stream, p);
+  else if (!ent)
+    hipLaunchKernelGGL((ce_fwd_kernel<1, false>), dim3((unsigned)N), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(ce_fwd_kernel<1>, dim3((unsigned)N), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((ce_fwd_kernel<1, true>), dim3((unsigned)N), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -380,10 +437,15 @@ hipError_t launch_ce_mean(const CeMeanParams& p, hipStream_t stream) {
 
 hipError_t launch_ce_backward(const CeBwdParams& p, int dtype, int64_t N, hipStream_t stream) {
   if (N <= 0) return hipSuccess;
-  if (dtype == 0)
-    hipLaunchKernelGGL(ce_bwd_kernel<0>, dim3((unsigned)N), dim3(kThreads), 0, stream, p);
+  const bool ent = p.grad_entropy != nullptr;
+  if (dtype == 0 && !ent)
+    hipLaunchKernelGGL((ce_bwd_kernel<0, false>), dim3((unsigned)N), dim3(kThreads), 0, stream, p);
+  else if (dtype == 0)
+    hipLaunchKernelGGL((ce_bwd_kernel<0, true>), dim3((unsigned)N), dim3(kThreads), 0, stream, p);
+  else if (!ent)
+    hipLaunchKernelGGL((ce_bwd_kernel<1, false>), dim3((unsigned)N), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(ce_bwd_kernel<1>, dim3((unsigned)N), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((ce_bwd_kernel<1, true>), dim3((unsigned)N), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -356,20 +356,22 @@ struct EpiF32 {
 };
 
 // Forward: rows = vocabulary, cols = tokens.  Per token and vocabulary tile:
-// (max, sum exp(z - max), sum z) into the partial arrays, plus the target
-// logit written by the one lane that holds it.
+// (max, sum exp(z - max), sum z, sum exp(z - max) (z - max) log2(e)) into the
+// partial arrays (the last one gives the entropy), plus the target logit
+// written by the one lane that holds it.
 struct EpiLse {
   struct Params {
     float* pm;
     float* pd;
     float* ps;
+    float* pw;
     float* zt;
     const int64_t* targets;
     int64_t M, V, Mp, ignore_idx;
   };
   __device__ static void apply(const Params& p, f32x16_t (&acc)[4][NB], int64_t i0, int64_t j0,
                                int wr, int wc, int lane, uint16_t* smem) {
-    float* sh = reinterpret_cast<float*>(smem);  // [wr][wc][b][lane 0..31][3]
+    float* sh = reinterpret_cast<float*>(smem);  // [wr][wc][b][lane 0..31][4]
     const int64_t vbase = i0 + wr * 128 + 4 * (lane >> 5);
     // rows at offsets >= lim from vbase lie beyond the vocabulary
     const int64_t lim64 = p.V - vbase;
@@ -386,17 +388,21 @@ struct EpiLse {
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float mref = (mx == kNegInf) ? 0.0f : mx;
       const float mL = mref * kLog2e;
-      float d = 0.0f, s = 0.0f;
+      float d = 0.0f, s = 0.0f, w = 0.0f;
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (a * 32 + 8 * (r >> 2) + (r & 3) < lim) {
-            d += exp2_hw(__builtin_fmaf(acc[a][b][r], kLog2e, -mL));
+            const float t = __builtin_fmaf(acc[a][b][r], kLog2e, -mL);
+            const float e = exp2_hw(t);
+            d += e;
+            w = __builtin_fmaf(e, t, w);
             s += acc[a][b][r];
           }
       d += __shfl_xor(d, 32, 64);
       s += __shfl_xor(s, 32, 64);
+      w += __shfl_xor(w, 32, 64);
       // Target logit: the lane holding row t picks it with a two-level select
       // (row block a, then register r), no dynamic register index.
       if (j < p.M) {
@@ -416,10 +422,11 @@ struct EpiLse {
         if (inr) p.zt[j] = zt;
       }
       if (lane < 32) {
-        float* e = sh + (((wr * 4 + wc) * NB + b) * 32 + lane) * 3;
+        float* e = sh + (((wr * 4 + wc) * NB + b) * 32 + lane) * 4;
         e[0] = mx;
         e[1] = d;
         e[2] = s;
+        e[3] = w;
       }
     }
     __syncthreads();
@@ -429,14 +436,15 @@ struct EpiLse {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int64_t j = j0 + wc * WN + b * 32 + lane;
-        const float* e0 = sh + (((0 * 4 + wc) * NB + b) * 32 + lane) * 3;
-        const float* e1 = sh + (((1 * 4 + wc) * NB + b) * 32 + lane) * 3;
-        LseState st{e0[0], e0[1], e0[2]};
-        lse_merge(st, LseState{e1[0], e1[1], e1[2]});
+        const float* e0 = sh + (((0 * 4 + wc) * NB + b) * 32 + lane) * 4;
+        const float* e1 = sh + (((1 * 4 + wc) * NB + b) * 32 + lane) * 4;
+        LseEntState st{e0[0], e0[1], e0[2], e0[3]};
+        lse_merge(st, LseEntState{e1[0], e1[1], e1[2], e1[3]});
         if (j < p.M) {
           p.pm[vt * p.Mp + j] = st.m;
           p.pd[vt * p.Mp + j] = st.d;
           p.ps[vt * p.Mp + j] = st.s;
+          p.pw[vt * p.Mp + j] = st.w;
         }
       }
     }
@@ -459,6 +467,8 @@ struct EpiDz {
     const int64_t* targets;
     const float* grad_output;
     const int32_t* n_valid;
+    const float* entropy;       // with grad_entropy: the forward's entropy
+    const float* grad_entropy;  // optional: adds grad_entropy[m] dH/dz
     float eps;
     int reduce_loss;
     int64_t ignore_idx, M, V;
@@ -477,6 +487,7 @@ struct EpiDz {
       int64_t t = -1;
       float g = 0.0f, lse2 = 0.0f;
       bool live = false, bad = false;
+      float gH = 0.0f, ez = 0.0f;
       if (j < p.M) {
         t = p.targets[j];
         if (t != p.ignore_idx) {
@@ -485,6 +496,10 @@ struct EpiDz {
             g = p.reduce_loss ? gscale : p.grad_output[j];
             const f32x4_t sv = *reinterpret_cast<const f32x4_t*>(p.stats + 4 * j);
             lse2 = sv[0] * kLog2e + log2_hw(sv[1]);
+            if (p.grad_entropy) {  // dH/dz_v = p_v (E_p[z] - z_v), E_p[z] = lse - H
+              gH = p.grad_entropy[j];
+              ez = lse2 * kLn2 - p.entropy[j];
+            }
           } else {
             bad = true;
           }
@@ -508,7 +523,8 @@ struct EpiDz {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int off = a * 32 + 8 * q + e;
-            float x = g * exp2_hw(__builtin_fmaf(acc[a][b][4 * q + e], kLog2e, -lse2)) - goff;
+            const float z = acc[a][b][4 * q + e];
+            float x = exp2_hw(__builtin_fmaf(z, kLog2e, -lse2)) * __builtin_fmaf(gH, ez - z, g) - goff;
             x = (off == trel) ? x - gt : x;
             val[e] = (live && off < lim) ? x : fill;
           }
@@ -602,23 +618,25 @@ struct MergeParams {
   const float* pm;
   const float* pd;
   const float* ps;
+  const float* pw;
   const float* zt;
   const int64_t* targets;
   int64_t M, Mp, V, n_vt, ignore_idx;
   float eps;
   float* loss_tok;
   float* stats;
+  float* entropy;  // optional
 };
 
 __global__ __launch_bounds__(256) void lce_merge_kernel(MergeParams p) {
-  __shared__ LseState sh[8][32];
+  __shared__ LseEntState sh[8][32];
   const int tl = threadIdx.x & 31, grp = threadIdx.x >> 5;
   const int64_t j = (int64_t)blockIdx.x * 32 + tl;
-  LseState st = {kNegInf, 0.0f, 0.0f};
+  LseEntState st = {kNegInf, 0.0f, 0.0f, 0.0f};
   if (j < p.M) {
     for (int64_t vt = grp; vt < p.n_vt; vt += 8) {
       const int64_t o = vt * p.Mp + j;
-      lse_merge(st, LseState{p.pm[o], p.pd[o], p.ps[o]});
+      lse_merge(st, LseEntState{p.pm[o], p.pd[o], p.ps[o], p.pw[o]});
     }
   }
   sh[grp][tl] = st;
@@ -629,8 +647,10 @@ __global__ __launch_bounds__(256) void lce_merge_kernel(MergeParams p) {
   if (t == p.ignore_idx) {
     p.loss_tok[j] = 0.0f;
     *reinterpret_cast<f32x4_t*>(p.stats + 4 * j) = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    if (p.entropy) p.entropy[j] = 0.0f;
     return;
   }
+  if (p.entropy) p.entropy[j] = entropy_of(st.d, st.w);
   const bool t_ok = t >= 0 && t < p.V;
   const float zt = t_ok ? p.zt[j] : __builtin_nanf("");
   const float mean = st.s / (float)p.V;
@@ -675,7 +695,7 @@ bool lce_make_plan(int64_t M, int64_t H, int64_t V, LcePlan* plan) {
   p.n_chunks = (V + p.chunk - 1) / p.chunk;
   p.ldz = p.chunk;
   const size_t part = align256((size_t)p.n_vtiles * p.Mp * 4);
-  const size_t fwd = 3 * part + align256((size_t)p.Mp * 4);
+  const size_t fwd = 4 * part + align256((size_t)p.Mp * 4);
   // backward: dZ of one chunk (Mp x chunk, token-major) and the dX accumulator
   const size_t dz = align256((size_t)p.Mp * p.chunk * 2);
   const size_t dx = p.n_chunks > 1 ? align256((size_t)p.Mp * H * 4) : 0;
@@ -693,17 +713,18 @@ hipError_t launch_lce_forward(const LcePlan& plan, const LceFwdArgs& a, hipStrea
   float* pm = reinterpret_cast<float*>(a.ws + plan.off_part);
   float* pd = reinterpret_cast<float*>(a.ws + plan.off_part + part);
   float* ps = reinterpret_cast<float*>(a.ws + plan.off_part + 2 * part);
-  float* zt = reinterpret_cast<float*>(a.ws + plan.off_part + 3 * part);
+  float* pw = reinterpret_cast<float*>(a.ws + plan.off_part + 3 * part);
+  float* zt = reinterpret_cast<float*>(a.ws + plan.off_part + 4 * part);
   const uint16_t* X = static_cast<const uint16_t*>(a.X);
   const uint16_t* W = static_cast<const uint16_t*>(a.W);
 
   Operand P{W, plan.H, plan.V, plan.H};
   Operand Q{X, plan.H, plan.M, plan.H};
-  EpiLse::Params ep{pm, pd, ps, zt, a.targets, plan.M, plan.V, plan.Mp, a.ignore_idx};
+  EpiLse::Params ep{pm, pd, ps, pw, zt, a.targets, plan.M, plan.V, plan.Mp, a.ignore_idx};
   hipError_t e = run_gemm<EpiLse, false, false>(P, Q, plan.V, plan.Mp, plan.H, ep, stream);
   if (e != hipSuccess) return e;
-  MergeParams mp{pm, pd, ps, zt, a.targets, plan.M, plan.Mp, plan.V, plan.n_vtiles,
-                 a.ignore_idx, a.eps, a.loss_tok, a.stats};
+  MergeParams mp{pm, pd, ps, pw, zt, a.targets, plan.M, plan.Mp, plan.V, plan.n_vtiles,
+                 a.ignore_idx, a.eps, a.loss_tok, a.stats, a.entropy};
   hipLaunchKernelGGL(lce_merge_kernel, dim3((unsigned)((plan.M + 31) / 32)), dim3(256), 0, stream,
                      mp);
   return hipGetLastError();
@@ -724,7 +745,8 @@ hipError_t launch_lce_backward(const LcePlan& plan, const LceBwdArgs& a, hipStre
       Operand P{Wc, plan.H, vc, plan.H};
       Operand Q{X, plan.H, plan.M, plan.H};
       EpiDz::Params ep{dz, plan.ldz, c0, vc, a.stats, a.targets, a.grad_output, a.n_valid,
-                       a.eps, a.reduce_loss, a.ignore_idx, plan.M, plan.V};
+                       a.entropy, a.grad_entropy, a.eps, a.reduce_loss, a.ignore_idx, plan.M,
+                       plan.V};
       hipError_t e = run_gemm<EpiDz, false, false>(P, Q, vc, plan.Mp, plan.H, ep, stream);
       if (e != hipSuccess) return e;
     }

@@ -83,7 +83,7 @@ const char* vce_strerror(int status) {
 int ce_forward(const void* logits, int dtype, int64_t d0, int64_t d1, int64_t V, int64_t ls0,
                int64_t ls1, const int64_t* targets, int64_t ts0, int64_t ts1,
                float label_smoothing, int reduce_loss, int64_t ignore_idx, float* loss_tok,
-               float* loss_mean, float* stats, int32_t* n_valid, void* stream) {
+               float* loss_mean, float* stats, int32_t* n_valid, float* entropy, void* stream) {
   CeShape sh;
   int rc = check_ce_common(logits, dtype, d0, d1, V, ls0, ls1, targets, ts0, ts1,
                            label_smoothing, reduce_loss, &sh);
@@ -92,7 +92,7 @@ int ce_forward(const void* logits, int dtype, int64_t d0, int64_t d1, int64_t V,
   if (sh.N > 0 && (!loss_tok || !stats)) return VCE_EINVAL;
   if (stats && !aligned(stats, 16)) return VCE_EALIGN;
   if ((loss_tok && !aligned(loss_tok, 4)) || (loss_mean && !aligned(loss_mean, 4)) ||
-      (n_valid && !aligned(n_valid, 4)))
+      (n_valid && !aligned(n_valid, 4)) || (entropy && !aligned(entropy, 4)))
     return VCE_EALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
@@ -109,6 +109,7 @@ int ce_forward(const void* logits, int dtype, int64_t d0, int64_t d1, int64_t V,
   p.ignore_idx = ignore_idx;
   p.loss_tok = loss_tok;
   p.stats = stats;
+  p.entropy = entropy;
   rc = launch_status(vce::launch_ce_forward(p, dtype, sh.N, s));
   if (rc != VCE_OK) return rc;
   if (reduce_loss || n_valid) {
@@ -130,8 +131,8 @@ int ce_forward(const void* logits, int dtype, int64_t d0, int64_t d1, int64_t V,
 int ce_backward(const void* logits, void* grad, int dtype, int64_t d0, int64_t d1, int64_t V,
                 int64_t ls0, int64_t ls1, const int64_t* targets, int64_t ts0, int64_t ts1,
                 const float* stats, const int32_t* n_valid, const float* grad_output,
-                float label_smoothing, int reduce_loss, int64_t ignore_idx, int overwrite_input,
-                void* stream) {
+                const float* entropy, const float* grad_entropy, float label_smoothing,
+                int reduce_loss, int64_t ignore_idx, int overwrite_input, void* stream) {
   CeShape sh;
   int rc = check_ce_common(logits, dtype, d0, d1, V, ls0, ls1, targets, ts0, ts1,
                            label_smoothing, reduce_loss, &sh);
@@ -139,7 +140,9 @@ int ce_backward(const void* logits, void* grad, int dtype, int64_t d0, int64_t d
   if (overwrite_input != 0 && overwrite_input != 1) return VCE_EINVAL;
   if (sh.N == 0) return VCE_OK;
   if (!grad || !stats || !grad_output || (reduce_loss && !n_valid)) return VCE_EINVAL;
-  if (!aligned(stats, 16) || !aligned(grad_output, 4) || (n_valid && !aligned(n_valid, 4)))
+  if (grad_entropy && !entropy) return VCE_EINVAL;
+  if (!aligned(stats, 16) || !aligned(grad_output, 4) || (n_valid && !aligned(n_valid, 4)) ||
+      (entropy && !aligned(entropy, 4)) || (grad_entropy && !aligned(grad_entropy, 4)))
     return VCE_EALIGN;
   if (overwrite_input) {
     if (grad != logits) return VCE_EALIAS;
@@ -165,6 +168,8 @@ int ce_backward(const void* logits, void* grad, int dtype, int64_t d0, int64_t d
   p.stats = stats;
   p.n_valid = n_valid;
   p.grad_output = grad_output;
+  p.entropy = entropy;
+  p.grad_entropy = grad_entropy;
   p.eps = label_smoothing;
   p.reduce_loss = reduce_loss;
   p.ignore_idx = ignore_idx;
@@ -200,7 +205,8 @@ int check_lce_common(const void* X, const void* W, int64_t M, int64_t H, int64_t
 int lce_forward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
                 const int64_t* targets, float label_smoothing, int reduce_loss,
                 int64_t ignore_idx, float* loss_tok, float* loss_mean, float* stats,
-                int32_t* n_valid, void* workspace, size_t workspace_bytes, void* stream) {
+                int32_t* n_valid, float* entropy, void* workspace, size_t workspace_bytes,
+                void* stream) {
   vce::LcePlan plan;
   int rc = check_lce_common(X, W, M, H, V, targets, label_smoothing, reduce_loss, workspace,
                             workspace_bytes, &plan);
@@ -208,6 +214,9 @@ int lce_forward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
   if (reduce_loss && (!loss_mean || !n_valid)) return VCE_EINVAL;
   if (M > 0 && (!loss_tok || !stats)) return VCE_EINVAL;
   if (stats && !aligned(stats, 16)) return VCE_EALIGN;
+  if ((loss_tok && !aligned(loss_tok, 4)) || (loss_mean && !aligned(loss_mean, 4)) ||
+      (n_valid && !aligned(n_valid, 4)) || (entropy && !aligned(entropy, 4)))
+    return VCE_EALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (M > 0) {
     vce::LceFwdArgs a;
@@ -221,6 +230,7 @@ int lce_forward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
     a.loss_mean = loss_mean;
     a.stats = stats;
     a.n_valid = n_valid;
+    a.entropy = entropy;
     a.ws = static_cast<char*>(workspace);
     rc = launch_status(vce::launch_lce_forward(plan, a, s));
     if (rc != VCE_OK) return rc;
@@ -243,9 +253,9 @@ int lce_forward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
 
 int lce_backward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
                  const int64_t* targets, const float* stats, const int32_t* n_valid,
-                 const float* grad_output, float label_smoothing, int reduce_loss,
-                 int64_t ignore_idx, void* dX, void* dW, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+                 const float* grad_output, const float* entropy, const float* grad_entropy,
+                 float label_smoothing, int reduce_loss, int64_t ignore_idx, void* dX, void* dW,
+                 void* workspace, size_t workspace_bytes, void* stream) {
   vce::LcePlan plan;
   int rc = check_lce_common(X, W, M, H, V, targets, label_smoothing, reduce_loss, workspace,
                             workspace_bytes, &plan);
@@ -254,7 +264,10 @@ int lce_backward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
   if (!aligned(dW, 16)) return VCE_EALIGN;
   if (M > 0) {
     if (!dX || !stats || !grad_output || (reduce_loss && !n_valid)) return VCE_EINVAL;
-    if (!aligned(dX, 16) || !aligned(stats, 16) || !aligned(grad_output, 4)) return VCE_EALIGN;
+    if (grad_entropy && !entropy) return VCE_EINVAL;
+    if (!aligned(dX, 16) || !aligned(stats, 16) || !aligned(grad_output, 4) ||
+        (entropy && !aligned(entropy, 4)) || (grad_entropy && !aligned(grad_entropy, 4)))
+      return VCE_EALIGN;
   }
   vce::LceBwdArgs a;
   a.X = X;
@@ -263,6 +276,8 @@ int lce_backward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
   a.stats = stats;
   a.n_valid = n_valid;
   a.grad_output = grad_output;
+  a.entropy = grad_entropy ? entropy : nullptr;
+  a.grad_entropy = grad_entropy;
   a.eps = label_smoothing;
   a.reduce_loss = reduce_loss;
   a.ignore_idx = ignore_idx;

@@ -76,4 +76,46 @@ __device__ __forceinline__ void lse_wave_reduce(LseState& st) {
   }
 }
 
+// Online state with the entropy accumulator as well:
+//   w = sum exp(z - m) (z - m) log2(e),
+// so that the entropy of softmax(z) is H = ln(2) (log2(d) - w / d)
+// (H = lse - E_p[z] = ln d - sum p (z - m)).  Terms stay bounded
+// (exp(x) x >= -1/e for x <= 0), so no large sum cancels.
+struct LseEntState {
+  float m, d, s, w;
+};
+
+// Merge b into a: each side's w is moved from its own max to the common one,
+// sum exp(z - m*) (z - m*) = f (w - (m* - m) log2(e) d) with f = exp(m - m*).
+// An empty side (d = 0) contributes nothing.
+__device__ __forceinline__ void lse_merge(LseEntState& a, const LseEntState& b) {
+  const float m = fmaxf(a.m, b.m);
+  const float mref = (m == kNegInf) ? 0.0f : m;
+  const float fa = exp2_hw((a.m - mref) * kLog2e);
+  const float fb = exp2_hw((b.m - mref) * kLog2e);
+  const float wa = a.d > 0.0f ? fa * (a.w - (mref - a.m) * kLog2e * a.d) : 0.0f;
+  const float wb = b.d > 0.0f ? fb * (b.w - (mref - b.m) * kLog2e * b.d) : 0.0f;
+  a.d = a.d * fa + b.d * fb;
+  a.s = a.s + b.s;
+  a.w = wa + wb;
+  a.m = m;
+}
+
+__device__ __forceinline__ void lse_wave_reduce(LseEntState& st) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    LseEntState o;
+    o.m = __shfl_xor(st.m, off, 64);
+    o.d = __shfl_xor(st.d, off, 64);
+    o.s = __shfl_xor(st.s, off, 64);
+    o.w = __shfl_xor(st.w, off, 64);
+    lse_merge(st, o);
+  }
+}
+
+// Entropy from a final state (NaN when d = 0: no finite logit).
+__device__ __forceinline__ float entropy_of(float d, float w) {
+  return kLn2 * (log2_hw(d) - w / d);
+}
+
 }  // namespace vce

@@ -16,6 +16,7 @@ struct CeFwdParams {
   int64_t ignore_idx;
   float* loss_tok;
   float* stats;
+  float* entropy;  // optional (N)
 };
 
 struct CeMeanParams {
@@ -35,6 +36,8 @@ struct CeBwdParams {
   const float* stats;
   const int32_t* n_valid;
   const float* grad_output;
+  const float* entropy;       // with grad_entropy: the forward's entropy (N)
+  const float* grad_entropy;  // optional (N): adds grad_entropy[r] dH/dz
   float eps;
   int reduce_loss;
   int64_t ignore_idx;
@@ -72,6 +75,7 @@ struct LceFwdArgs {
   float* loss_mean;
   float* stats;
   int32_t* n_valid;
+  float* entropy;  // optional (M)
   char* ws;
 };
 
@@ -82,6 +86,8 @@ struct LceBwdArgs {
   const float* stats;
   const int32_t* n_valid;
   const float* grad_output;
+  const float* entropy;       // with grad_entropy: the forward's entropy (M)
+  const float* grad_entropy;  // optional (M)
   float eps;
   int reduce_loss;
   int64_t ignore_idx;
