@@ -15,6 +15,8 @@ Contents
     rows and the per-row upstream factor g_r.
   * ``round_bf16``: FP64 -> BF16 round-to-nearest-even (C core).
   * ``linear``: fused linear cross-entropy in NumPy FP64 (``linear.py``).
+  * ``shard``: vocabulary-sharded local statistics, their merge and the
+    per-shard gradient in NumPy FP64 (``shard.py``).
   * ``tiny``: a pure-Python ``math`` version for tiny cases (``tiny.py``).
 
 Every function here is pinned by the ``-m "not gpu"`` tests in

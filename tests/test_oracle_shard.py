@@ -1,0 +1,150 @@
+"""Pins for the vocabulary-sharded oracle (CPU only).
+
+The sharded flow must give back the loss, the statistics and the gradient of
+the unsharded logits whatever the column split: merging the local statistics
+of any partition of the vocabulary is the log-sum-exp of the whole row.  The
+unsharded side is the C core of the oracle (pinned on its own), so these
+tie the NumPy shard module to an independent statement, and also to torch's
+float64 cross-entropy and to the pure-Python version on tiny rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import shard, tiny
+
+IGN = -100
+
+
+def _case(seed, N, V, n_ign=0, sigma=3.0):
+    rng = np.random.default_rng(seed)
+    z = rng.standard_normal((N, V)) * sigma
+    t = rng.integers(0, V, size=N).astype(np.int64)
+    if n_ign:
+        t[rng.choice(N, n_ign, replace=False)] = IGN
+    return z, t
+
+
+def _split(V, k, seed):
+    """k contiguous, uneven, non-empty column ranges covering [0, V)."""
+    rng = np.random.default_rng(seed)
+    cuts = np.sort(rng.choice(np.arange(1, V), k - 1, replace=False)) if k > 1 else []
+    b = [0, *[int(c) for c in cuts], V]
+    return list(zip(b[:-1], b[1:]))
+
+
+def _sharded_forward(z, t, bounds, eps=0.0, order=None):
+    parts = [shard.shard_partials(z[:, a:b], t, a, IGN) for a, b in bounds]
+    if order is not None:
+        parts = [parts[i] for i in order]
+    return shard.merge_shards(parts, t, z.shape[1], eps, IGN)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 8])
+@pytest.mark.parametrize("eps", [0.0, 0.1, 1.0])
+def test_merge_of_any_split_equals_unsharded(k, eps):
+    z, t = _case(k * 10 + int(eps * 10), 40, 997, n_ign=5)
+    loss, st = _sharded_forward(z, t, _split(997, k, k), eps)
+    rl, rst, _ = oracle.ce_forward(z, t, eps, IGN)
+    np.testing.assert_allclose(loss, rl, rtol=1e-12, atol=1e-12)
+    ok = t != IGN            # the C core leaves ignored rows' statistics undefined (NaN)
+    assert np.all(st[~ok] == 0.0)
+    st, rst = st[ok], rst[ok]
+    np.testing.assert_array_equal(st[:, 0], rst[:, 0])              # max is exact
+    np.testing.assert_allclose(st[:, 1], rst[:, 1], rtol=1e-12)
+    np.testing.assert_array_equal(st[:, 2], rst[:, 2])              # z_t is copied
+    np.testing.assert_allclose(st[:, 3], rst[:, 3], rtol=1e-12, atol=1e-12)
+
+
+def test_shard_order_does_not_change_the_result():
+    z, t = _case(3, 30, 500)
+    b = _split(500, 5, 1)
+    l0, s0 = _sharded_forward(z, t, b)
+    l1, s1 = _sharded_forward(z, t, b, order=[4, 2, 0, 3, 1])
+    np.testing.assert_allclose(l1, l0, rtol=1e-13)
+    np.testing.assert_allclose(s1, s0, rtol=1e-13)
+
+
+def test_local_statistics_of_one_shard():
+    # brute force on a tiny shard, element by element
+    z = np.array([[1.0, -2.0, 0.5], [3.0, 3.0, 3.0], [0.0, 1.0, 2.0]])
+    t = np.array([11, 4, IGN])              # 11 lies in this shard (start 10), 4 does not
+    p = shard.shard_partials(z, t, 10, IGN)
+    e0 = np.exp(np.array([1.0, -2.0, 0.5]) - 1.0).sum()
+    np.testing.assert_allclose(p[0], [1.0, e0, -0.5, -2.0], rtol=1e-15)
+    np.testing.assert_allclose(p[1], [3.0, 3.0, 9.0, 0.0], rtol=1e-15)
+    np.testing.assert_array_equal(p[2], 0.0)
+
+
+def test_smoothing_uses_the_full_vocabulary():
+    # eps = 1 with equal logits: loss is ln V of the FULL vocabulary, and each
+    # shard's gradient is g (1/V - 1/V) = 0
+    V = 120
+    z = np.full((4, V), 0.25)
+    t = np.array([0, 60, 119, 5])
+    b = _split(V, 4, 2)
+    loss, st = _sharded_forward(z, t, b, eps=1.0)
+    np.testing.assert_allclose(loss, np.log(V), rtol=1e-13)
+    for a, e in b:
+        gk = shard.shard_backward(z[:, a:e], t, a, V, st, np.ones(4), 1.0, IGN)
+        np.testing.assert_allclose(gk, 0.0, atol=1e-15)
+
+
+def test_against_torch_float64():
+    z, t = _case(5, 25, 300, n_ign=3)
+    loss, _ = _sharded_forward(z, t, _split(300, 6, 3), eps=0.2)
+    ref = torch.nn.functional.cross_entropy(torch.from_numpy(z), torch.from_numpy(t),
+                                            ignore_index=IGN, reduction="none",
+                                            label_smoothing=0.2).numpy()
+    np.testing.assert_allclose(loss, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_against_pure_python():
+    z, t = _case(6, 6, 9)
+    b = _split(9, 3, 4)
+    loss, st = _sharded_forward(z, t, b, eps=0.3)
+    g = np.array([1.0, -0.5, 2.0, 0.25, 1.5, 3.0])
+    grads = np.concatenate([shard.shard_backward(z[:, a:e], t, a, 9, st, g, 0.3, IGN)
+                            for a, e in b], axis=1)
+    for r in range(6):
+        assert loss[r] == pytest.approx(tiny.loss_row(list(z[r]), int(t[r]), 0.3), rel=1e-13)
+        np.testing.assert_allclose(grads[r], tiny.grad_row(list(z[r]), int(t[r]), g[r], 0.3),
+                                   rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("eps", [0.0, 0.1])
+def test_concatenated_shard_gradients_equal_unsharded(eps):
+    z, t = _case(7, 30, 777, n_ign=4)
+    b = _split(777, 8, 5)
+    _, st = _sharded_forward(z, t, b, eps)
+    g = np.random.default_rng(1).standard_normal(30)
+    grads = np.concatenate([shard.shard_backward(z[:, a:e], t, a, 777, st, g, eps, IGN)
+                            for a, e in b], axis=1)
+    ref = oracle.ce_backward(z, t, g, eps, IGN)
+    np.testing.assert_allclose(grads, ref, rtol=1e-11, atol=1e-15)
+
+
+def test_target_outside_the_vocabulary_and_ignored_rows():
+    z, t = _case(8, 4, 50)
+    t[:] = [IGN, 50, -1, 3]
+    b = _split(50, 3, 6)
+    loss, st = _sharded_forward(z, t, b)
+    assert loss[0] == 0.0 and np.all(st[0] == 0.0)
+    assert np.isnan(loss[1]) and np.isnan(loss[2]) and np.isfinite(loss[3])
+    for a, e in b:
+        gk = shard.shard_backward(z[:, a:e], t, a, 50, st, np.ones(4), 0.0, IGN)
+        assert np.all(gk[0] == 0.0) and np.all(np.isnan(gk[1:3])) and np.all(np.isfinite(gk[3]))
+
+
+def test_shard_of_negative_infinity_columns():
+    # a shard holding only -inf (padded vocabulary) contributes nothing
+    z, t = _case(9, 5, 64)
+    z[:, 48:] = -np.inf
+    t[:] = np.minimum(t, 47)
+    loss, st = _sharded_forward(z, t, [(0, 20), (20, 48), (48, 64)])
+    rl, rst, _ = oracle.ce_forward(z, t, 0.0, IGN)
+    np.testing.assert_allclose(loss, rl, rtol=1e-12)
+    np.testing.assert_allclose(st[:, :3], rst[:, :3], rtol=1e-12)
+    p = shard.shard_partials(z[:, 48:], t, 48, IGN)
+    assert np.all(p[:, 0] == -np.inf) and np.all(p[:, 1] == 0.0) and np.all(p[:, 3] == 0.0)
