@@ -116,3 +116,36 @@ def shard_backward(logits_shard: np.ndarray, targets: np.ndarray, vocab_start: i
         q = eps / V + (1.0 - eps) * (cols == t[r])
         out[r] = gg[r] * (np.exp(z[r] - lse) - q)
     return out
+
+
+# --- vocabulary-sharded linear cross-entropy ----------------------------------
+#
+# The tensor-parallel form of the Liger-Kernel fused linear cross-entropy PR
+# (Summary): the classifier W is split by vocabulary rows, shard k holding
+# W_k = W[a_k:b_k].  Its logits are Z_k = X W_k^T, the columns a_k..b_k of
+# Z = X W^T, so the forward is the logits flow above on Z_k; the backward
+# gives dW_k = dZ_k^T X (rows a_k..b_k of dW) and dX_k = dZ_k W_k, whose sum
+# over the shards is dX = dZ W.
+
+def _dec_bf16(a: np.ndarray) -> np.ndarray:
+    a = np.asarray(a)
+    return bf16_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def linear_shard_partials(X_bits: np.ndarray, W_shard_bits: np.ndarray, targets: np.ndarray,
+                          vocab_start: int, ignore_idx: int = -100) -> np.ndarray:
+    """Local statistics (M, 4) of Z_k = X W_k^T (see ``shard_partials``)."""
+    Zk = _dec_bf16(X_bits) @ _dec_bf16(W_shard_bits).T
+    return shard_partials(Zk, targets, vocab_start, ignore_idx)
+
+
+def linear_shard_backward(X_bits: np.ndarray, W_shard_bits: np.ndarray, targets: np.ndarray,
+                          vocab_start: int, V: int, stats: np.ndarray, g: np.ndarray,
+                          label_smoothing: float = 0.0, ignore_idx: int = -100):
+    """(dX_k, dW_k) of one shard from the global statistics: dZ_k from
+    ``shard_backward`` on Z_k, then dX_k = dZ_k W_k and dW_k = dZ_k^T X."""
+    X = _dec_bf16(X_bits)
+    Wk = _dec_bf16(W_shard_bits)
+    dZk = shard_backward(X @ Wk.T, targets, vocab_start, V, stats, g, label_smoothing,
+                         ignore_idx)
+    return dZk @ Wk, dZk.T @ X

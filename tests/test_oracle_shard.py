@@ -148,3 +148,54 @@ def test_shard_of_negative_infinity_columns():
     np.testing.assert_allclose(st[:, :3], rst[:, :3], rtol=1e-12)
     p = shard.shard_partials(z[:, 48:], t, 48, IGN)
     assert np.all(p[:, 0] == -np.inf) and np.all(p[:, 1] == 0.0) and np.all(p[:, 3] == 0.0)
+
+
+# --- linear form ---------------------------------------------------------------
+
+def _linear_case(seed, M, H, V, n_ign=0):
+    from vocabulary_cross_entropy_amd import workloads as wl
+    rng = np.random.default_rng(seed)
+    X = wl.f32_to_bf16_bits((rng.standard_normal((M, H)) * 0.5).astype(np.float32))
+    W = wl.f32_to_bf16_bits((rng.standard_normal((V, H)) * 0.5).astype(np.float32))
+    t = rng.integers(0, V, size=M).astype(np.int64)
+    if n_ign:
+        t[rng.choice(M, n_ign, replace=False)] = IGN
+    return X, W, t
+
+
+@pytest.mark.parametrize("eps", [0.0, 0.1])
+def test_linear_shards_sum_to_the_unsharded_gradients(eps):
+    from oracle import linear
+    X, W, t = _linear_case(21, 24, 16, 300, n_ign=3)
+    b = _split(300, 4, 7)
+    parts = [shard.linear_shard_partials(X, W[a:e], t, a, IGN) for a, e in b]
+    loss, st = shard.merge_shards(parts, t, 300, eps, IGN)
+    rl, rst, _ = linear.forward(X, W, t, eps, IGN)
+    np.testing.assert_allclose(loss, rl, rtol=1e-12, atol=1e-12)
+    g = np.random.default_rng(2).standard_normal(24)
+    outs = [shard.linear_shard_backward(X, W[a:e], t, a, 300, st, g, eps, IGN) for a, e in b]
+    rdX, rdW = linear.backward(X, W, t, g, eps, IGN)
+    np.testing.assert_allclose(sum(o[0] for o in outs), rdX, rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(np.concatenate([o[1] for o in outs]), rdW, rtol=1e-10, atol=1e-13)
+
+
+def test_linear_shard_against_pure_python():
+    # tiny: dX_k and dW_k from the pure-Python gradient rows and products
+    X, W, t = _linear_case(22, 3, 4, 7)
+    Xf, Wf = oracle.bf16_to_f64(X), oracle.bf16_to_f64(W)
+    Z = tiny.matmul_nt(Xf.tolist(), Wf.tolist())
+    b = [(0, 2), (2, 7)]
+    parts = [shard.linear_shard_partials(X, W[a:e], t, a, IGN) for a, e in b]
+    _, st = shard.merge_shards(parts, t, 7, 0.0, IGN)
+    g = np.ones(3)
+    dZ = np.array([tiny.grad_row(Z[r], int(t[r]), 1.0, 0.0) for r in range(3)])
+    for a, e in b:
+        dXk, dWk = shard.linear_shard_backward(X, W[a:e], t, a, 7, st, g, 0.0, IGN)
+        for r in range(3):
+            for h in range(4):
+                ref = sum(dZ[r][v] * Wf[v][h] for v in range(a, e))
+                assert dXk[r, h] == pytest.approx(ref, rel=1e-12, abs=1e-14)
+        for v in range(a, e):
+            for h in range(4):
+                ref = sum(dZ[r][v] * Xf[r][h] for r in range(3))
+                assert dWk[v - a, h] == pytest.approx(ref, rel=1e-12, abs=1e-14)
