@@ -135,6 +135,54 @@ int ce_backward(const void* logits, void* grad, int dtype, int64_t d0, int64_t d
                 int reduce_loss, int64_t ignore_idx, int overwrite_input, void* stream);
 
 /*
+ * Vocabulary-sharded logits cross-entropy.  The per-shard half of the
+ * tensor-parallel flow of the TransformerEngine PR "Minimize the memory usage
+ * of the fused cross entropy kernel" (Changes: the multi-GPU path with two
+ * kernels; Sequence Diagram: local statistics, all-gather, global statistics).
+ * Shard k holds vocabulary columns [vocab_start_k, vocab_start_k + V_local_k)
+ * of a V-column vocabulary.  The exchange between shards is the caller's:
+ * one process per shard gathers the partials of every shard (e.g. an
+ * all-gather of N x 16 bytes each) and calls ce_merge_shards, which runs the
+ * same on every shard.  The backward is then local to each shard.
+ *
+ *  ce_forward_shard: partial (N, 4) FP32 per row = (m_k, d_k, sum_v z_v,
+ *    z_t if vocab_start <= t < vocab_start + V_local else 0) over the shard's
+ *    columns; ignored rows hold zeros.  logits, dtype, d0, d1, ls0, ls1,
+ *    targets, ts0, ts1, ignore_idx as in ce_forward with V = V_local; targets
+ *    are indices into the full vocabulary.  partial: 16-byte aligned.
+ */
+int ce_forward_shard(const void* logits, int dtype, int64_t d0, int64_t d1, int64_t V_local,
+                     int64_t ls0, int64_t ls1, const int64_t* targets, int64_t ts0, int64_t ts1,
+                     int64_t vocab_start, int64_t ignore_idx, float* partial, void* stream);
+
+/*
+ *  ce_merge_shards: partials (n_shards, N, 4), the shards' partial outputs
+ *    stacked in a fixed order (the result is bitwise the same on every
+ *    process given the same order).  Merges m = max_k m_k, d = sum_k d_k
+ *    exp(m_k - m), sum z and z_t, and writes loss_tok, loss_mean, stats and
+ *    n_valid exactly as ce_forward would for the whole (N, V) logits, the
+ *    label smoothing eps / V and the mean logit taken over the full V.  A
+ *    target neither ignore_idx nor in [0, V) gives NaN, as in ce_forward.
+ */
+int ce_merge_shards(const float* partials, int64_t n_shards, int64_t d0, int64_t d1,
+                    const int64_t* targets, int64_t ts0, int64_t ts1, int64_t V,
+                    float label_smoothing, int reduce_loss, int64_t ignore_idx, float* loss_tok,
+                    float* loss_mean, float* stats, int32_t* n_valid, void* stream);
+
+/*
+ *  ce_backward_shard: ce_backward for the shard's columns of the gradient,
+ *    from the merged stats and n_valid of ce_merge_shards: V is the full
+ *    vocabulary (vocab_start + V_local <= V), and only the shard holding the
+ *    target subtracts (1 - eps) g there.  Other arguments as in ce_backward.
+ */
+int ce_backward_shard(const void* logits, void* grad, int dtype, int64_t d0, int64_t d1,
+                      int64_t V_local, int64_t ls0, int64_t ls1, const int64_t* targets,
+                      int64_t ts0, int64_t ts1, int64_t vocab_start, int64_t V,
+                      const float* stats, const int32_t* n_valid, const float* grad_output,
+                      float label_smoothing, int reduce_loss, int64_t ignore_idx,
+                      int overwrite_input, void* stream);
+
+/*
  * lce_workspace_size: bytes of device workspace lce_forward and lce_backward
  * need for an (M, H, V) problem (one buffer serves both; its contents need
  * not survive between calls).  Analogue of the workspace query API of the
@@ -166,13 +214,44 @@ int lce_forward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
  *  to lce_forward.  stats, n_valid: from lce_forward.  grad_output: FP32, 1
  *  element if reduce_loss else (M).  The logits are recomputed chunk by chunk
  *  over the vocabulary; the gradient of each chunk is held in the workspace.
- *  entropy, grad_entropy: as in ce_backward.
+ *  entropy, grad_entropy: as in ce_backward.  With M = 0, dW is set to zero
+ *  (X, targets and the workspace are not read).
  */
 int lce_backward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
                  const int64_t* targets, const float* stats, const int32_t* n_valid,
                  const float* grad_output, const float* entropy, const float* grad_entropy,
                  float label_smoothing, int reduce_loss, int64_t ignore_idx, void* dX, void* dW,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Vocabulary-sharded linear cross-entropy: the per-shard half of the
+ * tensor-parallel forward of the Liger-Kernel PR (Summary: tensor-parallel
+ * fused linear cross-entropy; the classifier W sharded by vocabulary rows),
+ * with the same partial statistics as ce_forward_shard, so ce_merge_shards
+ * merges them.  W_local (V_local, H) holds vocabulary rows
+ * [vocab_start, vocab_start + V_local) of the full classifier.  The
+ * workspace is sized by lce_workspace_size(M, H, V_local).
+ *
+ *  lce_forward_shard: partial (M, 4) FP32 as in ce_forward_shard, for the
+ *    logits X W_local^T, which are never stored.  Other arguments as in
+ *    lce_forward.
+ */
+int lce_forward_shard(const void* X, const void* W, int64_t M, int64_t H, int64_t V_local,
+                      const int64_t* targets, int64_t vocab_start, int64_t ignore_idx,
+                      float* partial, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ *  lce_backward_shard: from the merged stats and n_valid (ce_merge_shards
+ *    over every shard, V the full vocabulary), dW_local (V_local, H) of this
+ *    shard and this shard's share of dX, dZ_k W_local (M, H): the full dX is
+ *    the sum of the shards' shares (the caller's reduction across shards).
+ *    BF16 outputs, overwritten.  Other arguments as in lce_backward.
+ */
+int lce_backward_shard(const void* X, const void* W, int64_t M, int64_t H, int64_t V_local,
+                       const int64_t* targets, int64_t vocab_start, int64_t V,
+                       const float* stats, const int32_t* n_valid, const float* grad_output,
+                       float label_smoothing, int reduce_loss, int64_t ignore_idx, void* dX,
+                       void* dW, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * vce_gemm_bf16: the matrix-core building block of the linear form, exported

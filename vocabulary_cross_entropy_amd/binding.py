@@ -29,11 +29,21 @@ SIGNATURES = {
                           _VP, _VP, _VP, _VP, _VP, _VP]),
     "ce_backward": (_I32, [_VP, _VP, _I32, _I64, _I64, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _VP,
                            _VP, _VP, _VP, _F32, _I32, _I64, _I32, _VP]),
+    "ce_forward_shard": (_I32, [_VP, _I32, _I64, _I64, _I64, _I64, _I64, _VP, _I64, _I64, _I64,
+                                _I64, _VP, _VP]),
+    "ce_merge_shards": (_I32, [_VP, _I64, _I64, _I64, _VP, _I64, _I64, _I64, _F32, _I32, _I64,
+                               _VP, _VP, _VP, _VP, _VP]),
+    "ce_backward_shard": (_I32, [_VP, _VP, _I32, _I64, _I64, _I64, _I64, _I64, _VP, _I64, _I64,
+                                 _I64, _I64, _VP, _VP, _VP, _F32, _I32, _I64, _I32, _VP]),
     "lce_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "lce_forward": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _F32, _I32, _I64, _VP, _VP, _VP, _VP,
                            _VP, _VP, _SZ, _VP]),
     "lce_backward": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _F32, _I32,
                             _I64, _VP, _VP, _VP, _SZ, _VP]),
+    "lce_forward_shard": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _VP, _SZ,
+                                 _VP]),
+    "lce_backward_shard": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _VP, _VP,
+                                  _F32, _I32, _I64, _VP, _VP, _VP, _SZ, _VP]),
     "vce_gemm_bf16": (_I32, [_VP, _I64, _I32, _VP, _I64, _I32, _I64, _I64, _I64, _VP, _I64, _VP]),
 }
 
@@ -107,6 +117,17 @@ def _logits3d(logits: torch.Tensor, targets: torch.Tensor):
     return logits, targets
 
 
+def _grad_like(logits: torch.Tensor) -> torch.Tensor:
+    """An uninitialised tensor with the dtype and strides of ``logits`` whose
+    rows start at the same offset within 16 bytes (the backward splits the
+    logits row and the gradient row at the same element)."""
+    es = logits.element_size()
+    pad = (logits.data_ptr() % 16) // es
+    span = 1 + sum((n - 1) * st for n, st in zip(logits.shape, logits.stride()))
+    buf = torch.empty(pad + span, dtype=logits.dtype, device=logits.device)
+    return buf.as_strided(logits.shape, logits.stride(), pad)
+
+
 def ce_forward(logits: torch.Tensor, targets: torch.Tensor, label_smoothing: float = 0.0,
                reduce_loss: bool = False, ignore_idx: int = -100, *, stream=None, out=None,
                with_entropy: bool = False):
@@ -152,8 +173,7 @@ def ce_backward(logits: torch.Tensor, targets: torch.Tensor, stats: torch.Tensor
     if overwrite_input:
         grad = logits
     elif grad is None:
-        grad = torch.empty_strided(logits.shape, logits.stride(), dtype=logits.dtype,
-                                   device=logits.device)
+        grad = _grad_like(logits)
     elif grad.dim() == 2:
         grad = grad.unsqueeze(0)
     if tuple(grad.stride()) != tuple(logits.stride()) or grad.dtype != logits.dtype:
@@ -165,6 +185,83 @@ def ce_backward(logits: torch.Tensor, targets: torch.Tensor, stats: torch.Tensor
                            int(bool(reduce_loss)), int(ignore_idx), int(bool(overwrite_input)),
                            _stream(stream))
     _check("ce_backward", rc)
+    return grad
+
+
+def ce_forward_shard(logits: torch.Tensor, targets: torch.Tensor, vocab_start: int,
+                     ignore_idx: int = -100, *, stream=None, out=None) -> torch.Tensor:
+    """Partial statistics (d0, d1, 4) of one vocabulary shard: ``logits`` holds
+    columns vocab_start .. vocab_start + V_local - 1 of the full vocabulary."""
+    logits, targets = _logits3d(logits, targets)
+    _need_cuda(logits, targets)
+    d0, d1, V = logits.shape
+    part = torch.empty((d0, d1, 4), dtype=torch.float32, device=logits.device) if out is None \
+        else out
+    rc = lib().ce_forward_shard(_ptr(logits), _dtype_code(logits), d0, d1, V, logits.stride(0),
+                                logits.stride(1), _ptr(targets), targets.stride(0),
+                                targets.stride(1), int(vocab_start), int(ignore_idx), _ptr(part),
+                                _stream(stream))
+    _check("ce_forward_shard", rc)
+    return part
+
+
+def ce_merge_shards(partials: torch.Tensor, targets: torch.Tensor, V: int,
+                    label_smoothing: float = 0.0, reduce_loss: bool = False,
+                    ignore_idx: int = -100, *, stream=None, out=None):
+    """Merge stacked shard partials (n_shards, d0, d1, 4) (or (n_shards, N, 4)
+    with targets (N)) into (loss_tok, loss_mean, stats, n_valid) over the full
+    vocabulary of V columns, as ce_forward returns them."""
+    if targets.dim() == 1:
+        targets = targets.unsqueeze(0)
+    if targets.dtype != torch.int64:
+        raise TypeError("targets must be int64")
+    d0, d1 = targets.shape
+    if not partials.is_contiguous() or partials.dtype != torch.float32 or \
+            partials.numel() != partials.shape[0] * d0 * d1 * 4:
+        raise ValueError("partials must be contiguous float32 (n_shards, d0, d1, 4)")
+    _need_cuda(partials, targets)
+    dev = partials.device
+    if out is None:
+        loss_tok = torch.empty((d0, d1), dtype=torch.float32, device=dev)
+        stats = torch.empty((d0, d1, 4), dtype=torch.float32, device=dev)
+        loss_mean = torch.empty((), dtype=torch.float32, device=dev) if reduce_loss else None
+        n_valid = torch.empty((), dtype=torch.int32, device=dev) if reduce_loss else None
+    else:
+        loss_tok, loss_mean, stats, n_valid = out
+    rc = lib().ce_merge_shards(_ptr(partials), partials.shape[0], d0, d1, _ptr(targets),
+                               targets.stride(0), targets.stride(1), int(V),
+                               float(label_smoothing), int(bool(reduce_loss)), int(ignore_idx),
+                               _ptr(loss_tok), _ptr(loss_mean), _ptr(stats), _ptr(n_valid),
+                               _stream(stream))
+    _check("ce_merge_shards", rc)
+    return loss_tok, loss_mean, stats, n_valid
+
+
+def ce_backward_shard(logits: torch.Tensor, targets: torch.Tensor, vocab_start: int, V: int,
+                      stats: torch.Tensor, n_valid: torch.Tensor | None,
+                      grad_output: torch.Tensor, label_smoothing: float = 0.0,
+                      reduce_loss: bool = False, ignore_idx: int = -100,
+                      overwrite_input: bool = False, *, grad: torch.Tensor | None = None,
+                      stream=None):
+    """Gradient of one vocabulary shard's logits from the merged ``stats``."""
+    logits, targets = _logits3d(logits, targets)
+    _need_cuda(logits, targets, stats, grad_output)
+    d0, d1, VL = logits.shape
+    if overwrite_input:
+        grad = logits
+    elif grad is None:
+        grad = _grad_like(logits)
+    elif grad.dim() == 2:
+        grad = grad.unsqueeze(0)
+    if tuple(grad.stride()) != tuple(logits.stride()) or grad.dtype != logits.dtype:
+        raise ValueError("grad must have the dtype and strides of logits")
+    rc = lib().ce_backward_shard(_ptr(logits), _ptr(grad), _dtype_code(logits), d0, d1, VL,
+                                 logits.stride(0), logits.stride(1), _ptr(targets),
+                                 targets.stride(0), targets.stride(1), int(vocab_start), int(V),
+                                 _ptr(stats), _ptr(n_valid), _ptr(grad_output),
+                                 float(label_smoothing), int(bool(reduce_loss)), int(ignore_idx),
+                                 int(bool(overwrite_input)), _stream(stream))
+    _check("ce_backward_shard", rc)
     return grad
 
 
@@ -244,6 +341,48 @@ def lce_backward(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, stats:
                             _ptr(dX), _ptr(dW), _ptr(workspace), workspace.numel(),
                             _stream(stream))
     _check("lce_backward", rc)
+    return dX, dW
+
+
+def lce_forward_shard(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, vocab_start: int,
+                      ignore_idx: int = -100, *, workspace: torch.Tensor | None = None,
+                      stream=None, out=None) -> torch.Tensor:
+    """Partial statistics (M, 4) of the vocabulary shard W (V_local, H) holding
+    rows vocab_start .. vocab_start + V_local - 1 of the full classifier."""
+    _check_linear(X, W, targets)
+    M, H = X.shape
+    V = W.shape[0]
+    if workspace is None:
+        workspace = lce_workspace(M, H, V, X.device)
+    part = torch.empty((M, 4), dtype=torch.float32, device=X.device) if out is None else out
+    rc = lib().lce_forward_shard(_ptr(X), _ptr(W), M, H, V, _ptr(targets), int(vocab_start),
+                                 int(ignore_idx), _ptr(part), _ptr(workspace), workspace.numel(),
+                                 _stream(stream))
+    _check("lce_forward_shard", rc)
+    return part
+
+
+def lce_backward_shard(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, vocab_start: int,
+                       V: int, stats: torch.Tensor, n_valid: torch.Tensor | None,
+                       grad_output: torch.Tensor, label_smoothing: float = 0.0,
+                       reduce_loss: bool = True, ignore_idx: int = -100, *,
+                       workspace: torch.Tensor | None = None, dX: torch.Tensor | None = None,
+                       dW: torch.Tensor | None = None, stream=None):
+    """(dX share, dW) of one vocabulary shard from the merged ``stats``; the
+    shards' dX shares sum to the full dX."""
+    _check_linear(X, W, targets)
+    M, H = X.shape
+    VL = W.shape[0]
+    if workspace is None:
+        workspace = lce_workspace(M, H, VL, X.device)
+    dX = torch.empty_like(X) if dX is None else dX
+    dW = torch.empty_like(W) if dW is None else dW
+    rc = lib().lce_backward_shard(_ptr(X), _ptr(W), M, H, VL, _ptr(targets), int(vocab_start),
+                                  int(V), _ptr(stats), _ptr(n_valid), _ptr(grad_output),
+                                  float(label_smoothing), int(bool(reduce_loss)),
+                                  int(ignore_idx), _ptr(dX), _ptr(dW), _ptr(workspace),
+                                  workspace.numel(), _stream(stream))
+    _check("lce_backward_shard", rc)
     return dX, dW
 
 

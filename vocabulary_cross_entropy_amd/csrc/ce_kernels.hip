@@ -139,10 +139,10 @@ __device__ __forceinline__ void fold(S& st, const u32x4_t* w, int nvalid = N) {
 #pragma unroll
     for (int u = 1; u < N; ++u) wsum += wpart[u];
     // move the old w from the old max to the new one (nothing when empty)
-    const float wold = st.d > 0.0f ? f * (st.w - (mref - st.m) * kLog2e * st.d) : 0.0f;
+    const float wold = st.d > 0.0f ? f * __builtin_fmaf((st.m - mref) * kLog2e, st.d, st.w) : 0.0f;
     st.w = wold + wsum;
   }
-  st.d = st.d * f + dsum;
+  st.d = __builtin_fmaf(st.d, f, dsum);
 #pragma unroll
   for (int u = 0; u < N; ++u)
     if (u < nvalid) st.s = vec_sum<DT>(w[u], z[u], st.s);
@@ -171,7 +171,10 @@ struct StateOf<true> {
 };
 
 // ENT: also the entropy of softmax(z) per row (0 for ignored rows).
-template <int DT, bool ENT>
+// SHARD: the row holds vocabulary columns v0 .. v0 + V - 1 of a larger
+// vocabulary; instead of the loss, write the shard's partial statistics
+// (m, d, sum z, z_t if this shard holds the target else 0) for a later merge.
+template <int DT, bool ENT, bool SHARD>
 __global__ __launch_bounds__(kThreads) void ce_fwd_kernel(CeFwdParams p) {
   using T = typename Elem<DT>::T;
   using S = typename StateOf<ENT>::T;
@@ -182,17 +185,22 @@ __global__ __launch_bounds__(kThreads) void ce_fwd_kernel(CeFwdParams p) {
   const int tid = threadIdx.x;
   if (t == p.ignore_idx) {
     if (tid == 0) {
-      p.loss_tok[r] = 0.0f;
-      *reinterpret_cast<f32x4_t*>(p.stats + 4 * r) = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-      if (ENT) p.entropy[r] = 0.0f;
+      if (SHARD) {
+        *reinterpret_cast<f32x4_t*>(p.partial + 4 * r) = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      } else {
+        p.loss_tok[r] = 0.0f;
+        *reinterpret_cast<f32x4_t*>(p.stats + 4 * r) = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        if (ENT) p.entropy[r] = 0.0f;
+      }
     }
     return;
   }
   const int64_t V = p.V;
   const T* row = static_cast<const T*>(p.logits) + i0 * p.ls0 + i1 * p.ls1;
-  const bool t_ok = (t >= 0 && t < V);
-  float zt = __builtin_nanf("");
-  if (tid == 0 && t_ok) zt = Elem<DT>::load(row + t);
+  const int64_t tl = t - p.v0;  // target column within this row
+  const bool t_ok = (tl >= 0 && tl < V);
+  float zt = SHARD ? 0.0f : __builtin_nanf("");
+  if (tid == 0 && t_ok) zt = Elem<DT>::load(row + tl);
 
   const RowSplit rs = split_row<DT>(row, V);
   S st;
@@ -227,13 +235,15 @@ __global__ __launch_bounds__(kThreads) void ce_fwd_kernel(CeFwdParams p) {
     fold<DT, kUnroll>(st, w, nvalid);
   }
   const S tot = block_reduce(st, sh);
+  if (SHARD) {
+    if (tid == 0)
+      *reinterpret_cast<f32x4_t*>(p.partial + 4 * r) = f32x4_t{tot.m, tot.d, tot.s, zt};
+    return;
+  }
   if (tid == 0) {
     if constexpr (ENT) p.entropy[r] = entropy_of(tot.d, tot.w);
-    const float eps = p.eps;
-    const float lse_shift = log2_hw(tot.d) * kLn2;  // lse - m
     const float mean = tot.s / (float)V;
-    float loss = lse_shift - (1.0f - eps) * (zt - tot.m);
-    if (eps != 0.0f) loss -= eps * (mean - tot.m);
+    const float loss = ce_row_loss(tot.m, tot.d, zt, mean, p.eps);
     p.loss_tok[r] = t_ok ? loss : __builtin_nanf("");
     *reinterpret_cast<f32x4_t*>(p.stats + 4 * r) = f32x4_t{tot.m, tot.d, zt, mean};
   }
@@ -309,7 +319,9 @@ __global__ __launch_bounds__(kThreads) void ce_bwd_kernel(CeBwdParams p) {
   const RowSplit rs = split_row<DT>(grow, V);
   u32x4_t* gvec = reinterpret_cast<u32x4_t*>(grow + rs.head);
 
-  if (t == p.ignore_idx || !(t >= 0 && t < V)) {
+  // targets index the full vocabulary of Vg columns; this row holds columns
+  // v0 .. v0 + V - 1 of it (v0 = 0, Vg = V unless sharded)
+  if (t == p.ignore_idx || !(t >= 0 && t < p.Vg)) {
     // Ignored row: zero gradient.  Target out of range: NaN gradient.
     const float fill = (t == p.ignore_idx) ? 0.0f : __builtin_nanf("");
     float f[vec];
@@ -336,7 +348,8 @@ __global__ __launch_bounds__(kThreads) void ce_bwd_kernel(CeBwdParams p) {
   const float mref = (m == kNegInf) ? 0.0f : m;
   const float mL = mref * kLog2e;
   const float gs = g / d;
-  const float goff = g * (p.eps / (float)V);
+  const float goff = g * (p.eps / (float)p.Vg);
+  const int64_t tl = t - p.v0;  // target column within this row (may lie outside)
   const float gt = g * (1.0f - p.eps);
   float gHd = 0.0f, ez = 0.0f;
   if constexpr (ENT) {
@@ -359,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void ce_bwd_kernel(CeBwdParams p) {
       const int64_t idx = tid < rs.head ? tid : rs.tail0 + (tid - rs.head);
       const float z = Elem<DT>::load(row + idx);
       float gv = gval(z);
-      if (idx == t) gv -= gt;
+      if (idx == tl) gv -= gt;
       store_one<DT>(grow + idx, gv);
     }
   }
@@ -367,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void ce_bwd_kernel(CeBwdParams p) {
   // only if their base offsets agree; the host guarantees it (same strides and
   // equal base alignment), so the same split serves both.
   const u32x4_t* vrow = reinterpret_cast<const u32x4_t*>(row + rs.head);
-  const int64_t tv = t - rs.head;  // target position inside the vector body
+  const int64_t tv = tl - rs.head;  // target position inside the vector body
   int64_t j = tid;
   for (; j + (kUnroll - 1) * kThreads < rs.nvec; j += kUnroll * kThreads) {
     u32x4_t w[kUnroll];
@@ -416,17 +429,62 @@ __global__ __launch_bounds__(kThreads) void ce_bwd_kernel(CeBwdParams p) {
 
 }  // namespace
 
+// Per-row merge of vocabulary-shard statistics, shards in fixed order
+// (bitwise reproducible): m = max m_k, d = sum d_k exp(m_k - m), sum z, and
+// z_t from the shard holding the target (the others contribute 0); then the
+// loss and the saved statistics as ce_fwd_kernel writes them, with the mean
+// logit and eps / V over the full vocabulary.
+__global__ __launch_bounds__(256) void ce_merge_shards_kernel(CeMergeParams p) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= p.N) return;
+  const int64_t i0 = r / p.d1, i1 = r - i0 * p.d1;
+  const int64_t t = p.targets[i0 * p.ts0 + i1 * p.ts1];
+  if (t == p.ignore_idx) {
+    p.loss_tok[r] = 0.0f;
+    *reinterpret_cast<f32x4_t*>(p.stats + 4 * r) = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    return;
+  }
+  LseState st = {kNegInf, 0.0f, 0.0f};
+  float zt = 0.0f;
+  for (int64_t k = 0; k < p.n_shards; ++k) {
+    const f32x4_t q = *reinterpret_cast<const f32x4_t*>(p.partials + (k * p.N + r) * 4);
+    lse_merge(st, LseState{q[0], q[1], q[2]});
+    zt += q[3];
+  }
+  const bool t_ok = t >= 0 && t < p.V;
+  if (!t_ok) zt = __builtin_nanf("");
+  const float mean = st.s / (float)p.V;
+  const float loss = ce_row_loss(st.m, st.d, zt, mean, p.eps);
+  p.loss_tok[r] = t_ok ? loss : __builtin_nanf("");
+  *reinterpret_cast<f32x4_t*>(p.stats + 4 * r) = f32x4_t{st.m, st.d, zt, mean};
+}
+
 hipError_t launch_ce_forward(const CeFwdParams& p, int dtype, int64_t N, hipStream_t stream) {
   if (N <= 0) return hipSuccess;
+  const dim3 g((unsigned)N), b(kThreads);
+  if (p.partial) {
+    if (dtype == 0)
+      hipLaunchKernelGGL((ce_fwd_kernel<0, false, true>), g, b, 0, stream, p);
+    else
+      hipLaunchKernelGGL((ce_fwd_kernel<1, false, true>), g, b, 0, stream, p);
+    return hipGetLastError();
+  }
   const bool ent = p.entropy != nullptr;
   if (dtype == 0 && !ent)
-    hipLaunchKernelGGL((ce_fwd_kernel<0, false>), dim3((unsigned)N), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((ce_fwd_kernel<0, false, false>), g, b, 0, stream, p);
   else if (dtype == 0)
-    hipLaunchKernelGGL((ce_fwd_kernel<0, true>), dim3((unsigned)N), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((ce_fwd_kernel<0, true, false>), g, b, 0, stream, p);
   else if (!ent)
-    hipLaunchKernelGGL((ce_fwd_kernel<1, false>), dim3((unsigned)N), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((ce_fwd_kernel<1, false, false>), g, b, 0, stream, p);
   else
-    hipLaunchKernelGGL((ce_fwd_kernel<1, true>), dim3((unsigned)N), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((ce_fwd_kernel<1, true, false>), g, b, 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_merge_shards(const CeMergeParams& p, hipStream_t stream) {
+  if (p.N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(ce_merge_shards_kernel, dim3((unsigned)((p.N + 255) / 256)), dim3(256), 0,
+                     stream, p);
   return hipGetLastError();
 }
 

@@ -368,6 +368,7 @@ struct EpiLse {
     float* zt;
     const int64_t* targets;
     int64_t M, V, Mp, ignore_idx;
+    int64_t v0;  // vocabulary index of W's first row (0 unless sharded)
   };
   __device__ static void apply(const Params& p, f32x16_t (&acc)[4][NB], int64_t i0, int64_t j0,
                                int wr, int wc, int lane, uint16_t* smem) {
@@ -407,7 +408,7 @@ struct EpiLse {
       // (row block a, then register r), no dynamic register index.
       if (j < p.M) {
         const int64_t t = p.targets[j];
-        const int64_t tl64 = t - vbase;
+        const int64_t tl64 = t - p.v0 - vbase;
         const bool inr = t != p.ignore_idx && tl64 >= 0 && tl64 < 128 && ((tl64 >> 2) & 1) == 0;
         const int tl = inr ? (int)tl64 : 0;
         const int ra = tl >> 5, rr = ((tl >> 3) & 3) * 4 + (tl & 3);
@@ -472,6 +473,7 @@ struct EpiDz {
     float eps;
     int reduce_loss;
     int64_t ignore_idx, M, V;
+    int64_t v0, Vg;  // W holds vocabulary rows v0 .. v0 + V - 1 of Vg (0, V unless sharded)
   };
   __device__ static void apply(const Params& p, f32x16_t (&acc)[4][NB], int64_t i0, int64_t j0,
                                int wr, int wc, int lane, uint16_t* smem) {
@@ -491,7 +493,7 @@ struct EpiDz {
       if (j < p.M) {
         t = p.targets[j];
         if (t != p.ignore_idx) {
-          if (t >= 0 && t < p.V) {
+          if (t >= 0 && t < p.Vg) {
             live = true;
             g = p.reduce_loss ? gscale : p.grad_output[j];
             const f32x4_t sv = *reinterpret_cast<const f32x4_t*>(p.stats + 4 * j);
@@ -505,12 +507,12 @@ struct EpiDz {
           }
         }
       }
-      const float goff = g * (p.eps / (float)p.V);
+      const float goff = g * (p.eps / (float)p.Vg);
       const float gt = g * (1.0f - p.eps);
       // Offsets relative to this lane's first row keep the per-element tests
       // in 32-bit compares against constants.
       const int64_t vrow0 = i0 + wr * 128 + 4 * (lane >> 5);  // chunk-local row of r = 0
-      const int64_t tr64 = t - p.c0 - vrow0;
+      const int64_t tr64 = t - p.v0 - p.c0 - vrow0;
       const int trel = (live && tr64 >= 0 && tr64 < 128) ? (int)tr64 : -1;
       const int64_t lim64 = p.vc_valid - vrow0;
       const int lim = lim64 > 128 ? 128 : (lim64 < 0 ? 0 : (int)lim64);
@@ -626,6 +628,8 @@ struct MergeParams {
   float* loss_tok;
   float* stats;
   float* entropy;  // optional
+  int64_t v0;      // vocabulary index of W's first row (0 unless sharded)
+  float* partial;  // shard mode: (M, 4) = (m, d, sum z, z_t or 0) instead of loss/stats
 };
 
 __global__ __launch_bounds__(256) void lce_merge_kernel(MergeParams p) {
@@ -644,6 +648,15 @@ __global__ __launch_bounds__(256) void lce_merge_kernel(MergeParams p) {
   if (grp != 0 || j >= p.M) return;
   for (int g = 1; g < 8; ++g) lse_merge(st, sh[g][tl]);
   const int64_t t = p.targets[j];
+  if (p.partial) {  // one vocabulary shard: local statistics for a later merge
+    f32x4_t q = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (t != p.ignore_idx) {
+      const int64_t c = t - p.v0;
+      q = f32x4_t{st.m, st.d, st.s, (c >= 0 && c < p.V) ? p.zt[j] : 0.0f};
+    }
+    *reinterpret_cast<f32x4_t*>(p.partial + 4 * j) = q;
+    return;
+  }
   if (t == p.ignore_idx) {
     p.loss_tok[j] = 0.0f;
     *reinterpret_cast<f32x4_t*>(p.stats + 4 * j) = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -654,8 +667,7 @@ __global__ __launch_bounds__(256) void lce_merge_kernel(MergeParams p) {
   const bool t_ok = t >= 0 && t < p.V;
   const float zt = t_ok ? p.zt[j] : __builtin_nanf("");
   const float mean = st.s / (float)p.V;
-  float loss = log2_hw(st.d) * kLn2 - (1.0f - p.eps) * (zt - st.m);
-  if (p.eps != 0.0f) loss -= p.eps * (mean - st.m);
+  const float loss = ce_row_loss(st.m, st.d, zt, mean, p.eps);
   p.loss_tok[j] = t_ok ? loss : __builtin_nanf("");
   *reinterpret_cast<f32x4_t*>(p.stats + 4 * j) = f32x4_t{st.m, st.d, zt, mean};
 }
@@ -720,18 +732,30 @@ hipError_t launch_lce_forward(const LcePlan& plan, const LceFwdArgs& a, hipStrea
 
   Operand P{W, plan.H, plan.V, plan.H};
   Operand Q{X, plan.H, plan.M, plan.H};
-  EpiLse::Params ep{pm, pd, ps, pw, zt, a.targets, plan.M, plan.V, plan.Mp, a.ignore_idx};
+  EpiLse::Params ep{pm, pd, ps, pw, zt, a.targets, plan.M, plan.V, plan.Mp, a.ignore_idx, a.v0};
   hipError_t e = run_gemm<EpiLse, false, false>(P, Q, plan.V, plan.Mp, plan.H, ep, stream);
   if (e != hipSuccess) return e;
   MergeParams mp{pm, pd, ps, pw, zt, a.targets, plan.M, plan.Mp, plan.V, plan.n_vtiles,
-                 a.ignore_idx, a.eps, a.loss_tok, a.stats, a.entropy};
+                 a.ignore_idx, a.eps, a.loss_tok, a.stats, a.entropy, a.v0, a.partial};
   hipLaunchKernelGGL(lce_merge_kernel, dim3((unsigned)((plan.M + 31) / 32)), dim3(256), 0, stream,
                      mp);
   return hipGetLastError();
 }
 
+// Zero n 16-byte words (dW of an empty batch).
+__global__ __launch_bounds__(256) void lce_zero_kernel(u32x4_t* out, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    out[i] = u32x4_t{0u, 0u, 0u, 0u};
+}
+
 hipError_t launch_lce_backward(const LcePlan& plan, const LceBwdArgs& a, hipStream_t stream) {
-  if (plan.M == 0) return hipSuccess;  // dW of an empty batch: nothing reads it
+  if (plan.M == 0) {  // no token: dW = 0 (H is a multiple of 8, dW 16-byte aligned)
+    const int64_t n = plan.V * plan.H / 8;
+    const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+    hipLaunchKernelGGL(lce_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<u32x4_t*>(a.dW), n);
+    return hipGetLastError();
+  }
   uint16_t* dz = reinterpret_cast<uint16_t*>(a.ws + plan.off_dz);
   float* dxacc = reinterpret_cast<float*>(a.ws + plan.off_dx);
   const uint16_t* X = static_cast<const uint16_t*>(a.X);
@@ -746,7 +770,7 @@ hipError_t launch_lce_backward(const LcePlan& plan, const LceBwdArgs& a, hipStre
       Operand Q{X, plan.H, plan.M, plan.H};
       EpiDz::Params ep{dz, plan.ldz, c0, vc, a.stats, a.targets, a.grad_output, a.n_valid,
                        a.entropy, a.grad_entropy, a.eps, a.reduce_loss, a.ignore_idx, plan.M,
-                       plan.V};
+                       plan.V, a.v0, a.Vg};
       hipError_t e = run_gemm<EpiDz, false, false>(P, Q, vc, plan.Mp, plan.H, ep, stream);
       if (e != hipSuccess) return e;
     }

@@ -110,6 +110,8 @@ int ce_forward(const void* logits, int dtype, int64_t d0, int64_t d1, int64_t V,
   p.loss_tok = loss_tok;
   p.stats = stats;
   p.entropy = entropy;
+  p.v0 = 0;
+  p.partial = nullptr;
   rc = launch_status(vce::launch_ce_forward(p, dtype, sh.N, s));
   if (rc != VCE_OK) return rc;
   if (reduce_loss || n_valid) {
@@ -173,6 +175,138 @@ int ce_backward(const void* logits, void* grad, int dtype, int64_t d0, int64_t d
   p.eps = label_smoothing;
   p.reduce_loss = reduce_loss;
   p.ignore_idx = ignore_idx;
+  p.v0 = 0;
+  p.Vg = V;
+  return launch_status(vce::launch_ce_backward(p, dtype, sh.N, static_cast<hipStream_t>(stream)));
+}
+
+int ce_forward_shard(const void* logits, int dtype, int64_t d0, int64_t d1, int64_t V_local,
+                     int64_t ls0, int64_t ls1, const int64_t* targets, int64_t ts0, int64_t ts1,
+                     int64_t vocab_start, int64_t ignore_idx, float* partial, void* stream) {
+  CeShape sh;
+  int rc = check_ce_common(logits, dtype, d0, d1, V_local, ls0, ls1, targets, ts0, ts1, 0.0f, 0,
+                           &sh);
+  if (rc != VCE_OK) return rc;
+  if (vocab_start < 0 || vocab_start > INT64_MAX - V_local) return VCE_EINVAL;
+  if (sh.N == 0) return VCE_OK;
+  if (!partial) return VCE_EINVAL;
+  if (!aligned(partial, 16)) return VCE_EALIGN;
+  vce::CeFwdParams p;
+  p.logits = logits;
+  p.d1 = d1;
+  p.ls0 = ls0;
+  p.ls1 = ls1;
+  p.V = V_local;
+  p.targets = targets;
+  p.ts0 = ts0;
+  p.ts1 = ts1;
+  p.eps = 0.0f;
+  p.ignore_idx = ignore_idx;
+  p.loss_tok = nullptr;
+  p.stats = nullptr;
+  p.entropy = nullptr;
+  p.v0 = vocab_start;
+  p.partial = partial;
+  return launch_status(vce::launch_ce_forward(p, dtype, sh.N, static_cast<hipStream_t>(stream)));
+}
+
+int ce_merge_shards(const float* partials, int64_t n_shards, int64_t d0, int64_t d1,
+                    const int64_t* targets, int64_t ts0, int64_t ts1, int64_t V,
+                    float label_smoothing, int reduce_loss, int64_t ignore_idx, float* loss_tok,
+                    float* loss_mean, float* stats, int32_t* n_valid, void* stream) {
+  if (n_shards <= 0 || d0 < 0 || d1 < 0 || V <= 0 || ts0 < 0 || ts1 < 0) return VCE_EINVAL;
+  if (!(label_smoothing >= 0.0f && label_smoothing <= 1.0f)) return VCE_EINVAL;
+  if (reduce_loss != 0 && reduce_loss != 1) return VCE_EINVAL;
+  int64_t N, tot;
+  if (!mul_ok(d0, d1, &N) || N > (int64_t)INT32_MAX) return VCE_EINVAL;
+  if (!mul_ok(n_shards, N, &tot) || tot > INT64_MAX / 16) return VCE_EINVAL;
+  if (reduce_loss && (!loss_mean || !n_valid)) return VCE_EINVAL;
+  if (N > 0 && (!partials || !targets || !loss_tok || !stats)) return VCE_EINVAL;
+  if ((partials && !aligned(partials, 16)) || (stats && !aligned(stats, 16)) ||
+      (targets && !aligned(targets, 8)) || (loss_tok && !aligned(loss_tok, 4)) ||
+      (loss_mean && !aligned(loss_mean, 4)) || (n_valid && !aligned(n_valid, 4)))
+    return VCE_EALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int rc = VCE_OK;
+  if (N > 0) {
+    vce::CeMergeParams mp;
+    mp.partials = partials;
+    mp.n_shards = n_shards;
+    mp.N = N;
+    mp.d1 = d1;
+    mp.targets = targets;
+    mp.ts0 = ts0;
+    mp.ts1 = ts1;
+    mp.V = V;
+    mp.ignore_idx = ignore_idx;
+    mp.eps = label_smoothing;
+    mp.loss_tok = loss_tok;
+    mp.stats = stats;
+    rc = launch_status(vce::launch_ce_merge_shards(mp, s));
+    if (rc != VCE_OK) return rc;
+  }
+  if (reduce_loss || n_valid) {
+    vce::CeMeanParams mp;
+    mp.loss_tok = loss_tok;
+    mp.targets = targets;
+    mp.N = N;
+    mp.d1 = d1 > 0 ? d1 : 1;
+    mp.ts0 = ts0;
+    mp.ts1 = ts1;
+    mp.ignore_idx = ignore_idx;
+    mp.loss_mean = reduce_loss ? loss_mean : nullptr;
+    mp.n_valid = n_valid;
+    rc = launch_status(vce::launch_ce_mean(mp, s));
+  }
+  return rc;
+}
+
+int ce_backward_shard(const void* logits, void* grad, int dtype, int64_t d0, int64_t d1,
+                      int64_t V_local, int64_t ls0, int64_t ls1, const int64_t* targets,
+                      int64_t ts0, int64_t ts1, int64_t vocab_start, int64_t V,
+                      const float* stats, const int32_t* n_valid, const float* grad_output,
+                      float label_smoothing, int reduce_loss, int64_t ignore_idx,
+                      int overwrite_input, void* stream) {
+  CeShape sh;
+  int rc = check_ce_common(logits, dtype, d0, d1, V_local, ls0, ls1, targets, ts0, ts1,
+                           label_smoothing, reduce_loss, &sh);
+  if (rc != VCE_OK) return rc;
+  if (overwrite_input != 0 && overwrite_input != 1) return VCE_EINVAL;
+  if (vocab_start < 0 || V < V_local || vocab_start > V - V_local) return VCE_EINVAL;
+  if (sh.N == 0) return VCE_OK;
+  if (!grad || !stats || !grad_output || (reduce_loss && !n_valid)) return VCE_EINVAL;
+  if (!aligned(stats, 16) || !aligned(grad_output, 4) || (n_valid && !aligned(n_valid, 4)))
+    return VCE_EALIGN;
+  if (overwrite_input) {
+    if (grad != logits) return VCE_EALIAS;
+  } else {
+    uintptr_t a0, a1, b0, b1;
+    extent(logits, d0, d1, V_local, ls0, ls1, sh.es, &a0, &a1);
+    extent(grad, d0, d1, V_local, ls0, ls1, sh.es, &b0, &b1);
+    if (a0 < b1 && b0 < a1) return VCE_EALIAS;
+    if ((reinterpret_cast<uintptr_t>(logits) - reinterpret_cast<uintptr_t>(grad)) % 16 != 0)
+      return VCE_EALIGN;
+  }
+  vce::CeBwdParams p;
+  p.logits = logits;
+  p.grad = grad;
+  p.d1 = d1;
+  p.ls0 = ls0;
+  p.ls1 = ls1;
+  p.V = V_local;
+  p.targets = targets;
+  p.ts0 = ts0;
+  p.ts1 = ts1;
+  p.stats = stats;
+  p.n_valid = n_valid;
+  p.grad_output = grad_output;
+  p.entropy = nullptr;
+  p.grad_entropy = nullptr;
+  p.eps = label_smoothing;
+  p.reduce_loss = reduce_loss;
+  p.ignore_idx = ignore_idx;
+  p.v0 = vocab_start;
+  p.Vg = V;
   return launch_status(vce::launch_ce_backward(p, dtype, sh.N, static_cast<hipStream_t>(stream)));
 }
 
@@ -232,6 +366,8 @@ int lce_forward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
     a.n_valid = n_valid;
     a.entropy = entropy;
     a.ws = static_cast<char*>(workspace);
+    a.v0 = 0;
+    a.partial = nullptr;
     rc = launch_status(vce::launch_lce_forward(plan, a, s));
     if (rc != VCE_OK) return rc;
   }
@@ -266,7 +402,8 @@ int lce_backward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
     if (!dX || !stats || !grad_output || (reduce_loss && !n_valid)) return VCE_EINVAL;
     if (grad_entropy && !entropy) return VCE_EINVAL;
     if (!aligned(dX, 16) || !aligned(stats, 16) || !aligned(grad_output, 4) ||
-        (entropy && !aligned(entropy, 4)) || (grad_entropy && !aligned(grad_entropy, 4)))
+        (n_valid && !aligned(n_valid, 4)) || (entropy && !aligned(entropy, 4)) ||
+        (grad_entropy && !aligned(grad_entropy, 4)))
       return VCE_EALIGN;
   }
   vce::LceBwdArgs a;
@@ -284,6 +421,75 @@ int lce_backward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
   a.dX = dX;
   a.dW = dW;
   a.ws = static_cast<char*>(workspace);
+  a.v0 = 0;
+  a.Vg = V;
+  return launch_status(vce::launch_lce_backward(plan, a, static_cast<hipStream_t>(stream)));
+}
+
+int lce_forward_shard(const void* X, const void* W, int64_t M, int64_t H, int64_t V_local,
+                      const int64_t* targets, int64_t vocab_start, int64_t ignore_idx,
+                      float* partial, void* workspace, size_t workspace_bytes, void* stream) {
+  vce::LcePlan plan;
+  int rc = check_lce_common(X, W, M, H, V_local, targets, 0.0f, 0, workspace, workspace_bytes,
+                            &plan);
+  if (rc != VCE_OK) return rc;
+  if (vocab_start < 0 || vocab_start > INT64_MAX - V_local) return VCE_EINVAL;
+  if (M == 0) return VCE_OK;
+  if (!partial) return VCE_EINVAL;
+  if (!aligned(partial, 16)) return VCE_EALIGN;
+  vce::LceFwdArgs a;
+  a.X = X;
+  a.W = W;
+  a.targets = targets;
+  a.eps = 0.0f;
+  a.reduce_loss = 0;
+  a.ignore_idx = ignore_idx;
+  a.loss_tok = nullptr;
+  a.loss_mean = nullptr;
+  a.stats = nullptr;
+  a.n_valid = nullptr;
+  a.entropy = nullptr;
+  a.ws = static_cast<char*>(workspace);
+  a.v0 = vocab_start;
+  a.partial = partial;
+  return launch_status(vce::launch_lce_forward(plan, a, static_cast<hipStream_t>(stream)));
+}
+
+int lce_backward_shard(const void* X, const void* W, int64_t M, int64_t H, int64_t V_local,
+                       const int64_t* targets, int64_t vocab_start, int64_t V,
+                       const float* stats, const int32_t* n_valid, const float* grad_output,
+                       float label_smoothing, int reduce_loss, int64_t ignore_idx, void* dX,
+                       void* dW, void* workspace, size_t workspace_bytes, void* stream) {
+  vce::LcePlan plan;
+  int rc = check_lce_common(X, W, M, H, V_local, targets, label_smoothing, reduce_loss, workspace,
+                            workspace_bytes, &plan);
+  if (rc != VCE_OK) return rc;
+  if (vocab_start < 0 || V < V_local || vocab_start > V - V_local) return VCE_EINVAL;
+  if (!dW) return VCE_EINVAL;
+  if (!aligned(dW, 16)) return VCE_EALIGN;
+  if (M > 0) {
+    if (!dX || !stats || !grad_output || (reduce_loss && !n_valid)) return VCE_EINVAL;
+    if (!aligned(dX, 16) || !aligned(stats, 16) || !aligned(grad_output, 4) ||
+        (n_valid && !aligned(n_valid, 4)))
+      return VCE_EALIGN;
+  }
+  vce::LceBwdArgs a;
+  a.X = X;
+  a.W = W;
+  a.targets = targets;
+  a.stats = stats;
+  a.n_valid = n_valid;
+  a.grad_output = grad_output;
+  a.entropy = nullptr;
+  a.grad_entropy = nullptr;
+  a.eps = label_smoothing;
+  a.reduce_loss = reduce_loss;
+  a.ignore_idx = ignore_idx;
+  a.dX = dX;
+  a.dW = dW;
+  a.ws = static_cast<char*>(workspace);
+  a.v0 = vocab_start;
+  a.Vg = V;
   return launch_status(vce::launch_lce_backward(plan, a, static_cast<hipStream_t>(stream)));
 }
 

@@ -53,13 +53,15 @@ struct LseState {
   float m, d, s;
 };
 
-// Merge b into a.  Either side may be empty (m = -inf, d = 0).
+// Merge b into a.  Either side may be empty (m = -inf, d = 0).  The sums of
+// products are written as explicit FMAs so that every kernel rounds them the
+// same way (the compiler would otherwise pick which product to fuse).
 __device__ __forceinline__ void lse_merge(LseState& a, const LseState& b) {
   float m = fmaxf(a.m, b.m);
   float mref = (m == kNegInf) ? 0.0f : m;
   float fa = exp2_hw((a.m - mref) * kLog2e);
   float fb = exp2_hw((b.m - mref) * kLog2e);
-  a.d = a.d * fa + b.d * fb;
+  a.d = __builtin_fmaf(a.d, fa, b.d * fb);
   a.s = a.s + b.s;
   a.m = m;
 }
@@ -93,9 +95,9 @@ __device__ __forceinline__ void lse_merge(LseEntState& a, const LseEntState& b) 
   const float mref = (m == kNegInf) ? 0.0f : m;
   const float fa = exp2_hw((a.m - mref) * kLog2e);
   const float fb = exp2_hw((b.m - mref) * kLog2e);
-  const float wa = a.d > 0.0f ? fa * (a.w - (mref - a.m) * kLog2e * a.d) : 0.0f;
-  const float wb = b.d > 0.0f ? fb * (b.w - (mref - b.m) * kLog2e * b.d) : 0.0f;
-  a.d = a.d * fa + b.d * fb;
+  const float wa = a.d > 0.0f ? fa * __builtin_fmaf((a.m - mref) * kLog2e, a.d, a.w) : 0.0f;
+  const float wb = b.d > 0.0f ? fb * __builtin_fmaf((b.m - mref) * kLog2e, b.d, b.w) : 0.0f;
+  a.d = __builtin_fmaf(a.d, fa, b.d * fb);
   a.s = a.s + b.s;
   a.w = wa + wb;
   a.m = m;
@@ -111,6 +113,17 @@ __device__ __forceinline__ void lse_wave_reduce(LseEntState& st) {
     o.w = __shfl_xor(st.w, off, 64);
     lse_merge(st, o);
   }
+}
+
+// Per-row loss from the row statistics, written with explicit FMAs so that
+// every kernel that forms it rounds the same way:
+//   (lse - m) - (1 - eps)(z_t - m) - eps (mean z - m),  lse - m = ln d.
+// The smoothing term is skipped for eps = 0 (a -inf logit would give 0 * inf).
+__device__ __forceinline__ float ce_row_loss(float m, float d, float zt, float mean, float eps) {
+  const float lse_shift = log2_hw(d) * kLn2;
+  float loss = __builtin_fmaf(eps - 1.0f, zt - m, lse_shift);
+  if (eps != 0.0f) loss = __builtin_fmaf(-eps, mean - m, loss);
+  return loss;
 }
 
 // Entropy from a final state (NaN when d = 0: no finite logit).

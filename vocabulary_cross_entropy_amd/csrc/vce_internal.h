@@ -17,6 +17,18 @@ struct CeFwdParams {
   float* loss_tok;
   float* stats;
   float* entropy;  // optional (N)
+  int64_t v0;      // first vocabulary column of the row (0 unless sharded)
+  float* partial;  // shard mode: (N, 4) partial statistics instead of loss/stats
+};
+
+struct CeMergeParams {
+  const float* partials;  // (n_shards, N, 4)
+  int64_t n_shards, N, d1;
+  const int64_t* targets;
+  int64_t ts0, ts1, V, ignore_idx;  // V: the full vocabulary
+  float eps;
+  float* loss_tok;
+  float* stats;
 };
 
 struct CeMeanParams {
@@ -41,10 +53,12 @@ struct CeBwdParams {
   float eps;
   int reduce_loss;
   int64_t ignore_idx;
+  int64_t v0, Vg;  // the row holds columns v0 .. v0 + V - 1 of Vg (0, V unless sharded)
 };
 
 hipError_t launch_ce_forward(const CeFwdParams& p, int dtype, int64_t N, hipStream_t stream);
 hipError_t launch_ce_mean(const CeMeanParams& p, hipStream_t stream);
+hipError_t launch_ce_merge_shards(const CeMergeParams& p, hipStream_t stream);
 hipError_t launch_ce_backward(const CeBwdParams& p, int dtype, int64_t N, hipStream_t stream);
 
 // ---- fused linear cross-entropy ----------------------------------------------
@@ -77,6 +91,8 @@ struct LceFwdArgs {
   int32_t* n_valid;
   float* entropy;  // optional (M)
   char* ws;
+  int64_t v0;      // vocabulary index of W's first row (0 unless sharded)
+  float* partial;  // shard mode: (M, 4) local statistics instead of loss/stats
 };
 
 struct LceBwdArgs {
@@ -94,6 +110,7 @@ struct LceBwdArgs {
   void* dX;
   void* dW;
   char* ws;
+  int64_t v0, Vg;  // W holds vocabulary rows v0 .. v0 + V - 1 of Vg (0, V unless sharded)
 };
 
 hipError_t launch_lce_forward(const LcePlan& plan, const LceFwdArgs& a, hipStream_t stream);
