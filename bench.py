@@ -180,6 +180,106 @@ def bench_linear(case, steps: int, warmup: int):
     )
 
 
+def _time_steps(step, steps: int, warmup: int):
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    whole = _event_pairs(1)[0]
+    whole[0].record()
+    for _ in range(steps):
+        step()
+    whole[1].record()
+    torch.cuda.synchronize()
+    return whole[0].elapsed_time(whole[1]) / steps
+
+
+def bench_sharded_logits(case, n_shards: int, steps: int, warmup: int):
+    """One vocabulary shard of the logits workload, as one of n_shards
+    processes would run it: local statistics of its V/n_shards columns, the
+    merge of all shards' statistics (the other shards' partials computed
+    beforehand, standing in for the gather), and its backward."""
+    import torch
+    import vocabulary_cross_entropy_amd as vce
+    from vocabulary_cross_entropy_amd import accounting
+
+    dev = torch.device("cuda:0")
+    z = _bf16_dev(case.logits, dev)
+    t = torch.from_numpy(case.targets).to(dev)
+    go = torch.from_numpy(case.grad_output).to(dev)
+    N, V = case.N, case.V
+    vl = V // n_shards
+    shards = [z[:, :, k * vl:(k + 1) * vl].contiguous() for k in range(n_shards)]
+    del z
+    parts = torch.empty((n_shards, case.d0, case.d1, 4), device=dev)
+    for k in range(n_shards):
+        vce.ce_forward_shard(shards[k], t, k * vl, out=parts[k])
+    zk = shards[0]
+    del shards
+    loss = torch.empty((case.d0, case.d1), device=dev)
+    stats = torch.empty((case.d0, case.d1, 4), device=dev)
+    grad = torch.empty_like(zk)
+    eps = case.label_smoothing
+
+    def fwd():
+        vce.ce_forward_shard(zk, t, 0, out=parts[0])
+        vce.ce_merge_shards(parts, t, V, eps, False, out=(loss, None, stats, None))
+
+    def bwd():
+        vce.ce_backward_shard(zk, t, 0, V, stats, None, go, eps, False, grad=grad)
+
+    def step():
+        fwd()
+        bwd()
+
+    ms = _time_steps(step, steps, warmup)
+    ms_b = _time_steps(bwd, steps, warmup)
+    b_bwd = accounting.ce_bytes(N, vl, 2, int(case.meta["n_ignored"]), "bwd")
+    return dict(workload=f"logits_ce_shard_sqbv_2048x2_v{vl}_of_{V}", n_shards=n_shards,
+                V_local=vl, ms_per_step=round(ms, 4), tokens_per_s=round(N / (ms * 1e-3), 1),
+                bwd_ms=round(ms_b, 4),
+                bwd_hbm_frac=round(b_bwd / (ms_b * 1e-3) / 1e9 / accounting.HBM_PEAK_GBS, 4))
+
+
+def bench_sharded_linear(case, n_shards: int, steps: int, warmup: int):
+    """One vocabulary shard of the linear workload (W split by rows into
+    n_shards), forward statistics + merge + backward (dW rows and the dX
+    share), as one of n_shards processes would run it."""
+    import torch
+    import vocabulary_cross_entropy_amd as vce
+    from vocabulary_cross_entropy_amd import accounting
+
+    dev = torch.device("cuda:0")
+    M, H, V = case.M, case.H, case.V
+    vl = V // n_shards
+    X = _bf16_dev(case.X, dev)
+    t = torch.from_numpy(case.targets).to(dev)
+    go = torch.ones(1, device=dev)
+    ws = vce.lce_workspace(M, H, vl, dev)
+    parts = torch.empty((n_shards, M, 4), device=dev)
+    for k in range(n_shards):
+        Wk = _bf16_dev(case.W[k * vl:(k + 1) * vl], dev)
+        vce.lce_forward_shard(X, Wk, t, k * vl, workspace=ws, out=parts[k])
+    Wk = _bf16_dev(case.W[:vl], dev)
+    loss, mean = torch.empty(M, device=dev), torch.empty((), device=dev)
+    stats, nv = torch.empty((M, 4), device=dev), torch.empty((), dtype=torch.int32, device=dev)
+    dX, dW = torch.empty_like(X), torch.empty_like(Wk)
+    eps = case.label_smoothing
+
+    def step():
+        vce.lce_forward_shard(X, Wk, t, 0, workspace=ws, out=parts[0])
+        vce.ce_merge_shards(parts, t, V, eps, True, out=(loss, mean, stats, nv))
+        vce.lce_backward_shard(X, Wk, t, 0, V, stats, nv, go, eps, True, workspace=ws, dX=dX,
+                               dW=dW)
+
+    ms = _time_steps(step, steps, warmup)
+    f = accounting.linear_flops(M, H, vl, "fb")
+    return dict(workload=f"linear_ce_shard_m{M}_h{H}_v{vl}_of_{V}", n_shards=n_shards,
+                V_local=vl, ms_per_step=round(ms, 4), tflops=round(f / (ms * 1e-3) / 1e12, 1),
+                frac_of_mfma_peak=round(f / (ms * 1e-3) / 1e12 / accounting.BF16_MFMA_PEAK_TFLOPS,
+                                        4))
+
+
 def recorded_traffic(key: str):
     """HBM bytes per launch of kernel `key`, from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE summary under profiles/ (copy-calibrated), or None when the kernel's
@@ -235,6 +335,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-linear", action="store_true", help="skip the fused linear form")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-shard", action="store_true",
+                    help="skip the one-shard-of-eight vocabulary-sharded runs")
     ap.add_argument("--only", choices=["logits", "linear"], default=None,
                     help="run one form only (for profiling)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -266,6 +368,11 @@ def main():
     if args.only in (None, "logits"):
         res = bench_logits(case, args.steps, args.warmup)
         print(f"[bench] logits CE: {res['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
+    sharded = {}
+    if res is not None and not args.no_shard:
+        sharded["logits"] = bench_sharded_logits(case, 8, args.steps, min(args.warmup, 5))
+        print(f"[bench] logits CE, one shard of 8: {sharded['logits']['ms_per_step']:.3f} ms/step",
+              file=sys.stderr, flush=True)
     lin = None
     if not args.no_linear and args.only in (None, "linear"):
         print("[bench] generating the linear workload M=4096 H=4096 V=131072", file=sys.stderr,
@@ -273,6 +380,11 @@ def main():
         lcase = wl.linear_4k()
         lin = bench_linear(lcase, max(3, min(args.steps, 10)), min(args.warmup, 3))
         print(f"[bench] linear CE: {lin['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
+        if not args.no_shard:
+            sharded["linear"] = bench_sharded_linear(lcase, 8, max(3, min(args.steps, 10)),
+                                                     min(args.warmup, 3))
+            print(f"[bench] linear CE, one shard of 8: "
+                  f"{sharded['linear']['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
     if res is None:
         print(json.dumps({"linear_ce": lin}))
         return
@@ -308,6 +420,7 @@ def main():
                    "fb_GBs": round(res["fb_GBs"], 1),
                    "fb_frac_of_hbm_peak": round(res["fb_GBs"] / peak, 4)},
         "linear_ce": lin,
+        "vocab_sharded_one_of_8": sharded or None,
     }
     print(json.dumps(line))
 
