@@ -17,6 +17,7 @@ Contents
   * ``linear``: fused linear cross-entropy in NumPy FP64 (``linear.py``).
   * ``shard``: vocabulary-sharded local statistics, their merge and the
     per-shard gradient in NumPy FP64 (``shard.py``).
+  * ``shift``: the causal label shift (``shift.py``).
   * ``tiny``: a pure-Python ``math`` version for tiny cases (``tiny.py``).
 
 Every function here is pinned by the ``-m "not gpu"`` tests in
