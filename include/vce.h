@@ -183,6 +183,27 @@ int ce_backward_shard(const void* logits, void* grad, int dtype, int64_t d0, int
                       int overwrite_input, void* stream);
 
 /*
+ * vce_shift_targets: causal label shift, the optional token shifting of the
+ * cut-cross-entropy package description (what_it_does: shifting for causal
+ * language modelling): position s of a sequence is scored against the label
+ * of position s + 1, and the last position of every sequence has no label.
+ *
+ *  targets  int64 (d0, d1), element (i0, i1) at i0*ts0 + i1*ts1 (as given to
+ *           the other entry points).
+ *  seq_axis 0: the sequence runs along d0 ((SQ,B) storage); 1: along d1
+ *           ((B,SQ) storage, or (1, M) for the flattened tokens of one
+ *           sequence).
+ *  shifted  int64 (d0, d1) contiguous, flattened row order r = i0*d1 + i1,
+ *           8-byte aligned, must not overlap targets: shifted(i0, i1) =
+ *           targets(i0 + 1, i1) (seq_axis 0) or targets(i0, i1 + 1) (seq_axis 1),
+ *           and ignore_idx at the last position.  Pass it (strides d1, 1) as the
+ *           targets of any other entry point: the last positions are then
+ *           ignored rows (loss 0, excluded from the mean, zero gradient).
+ */
+int vce_shift_targets(const int64_t* targets, int64_t d0, int64_t d1, int64_t ts0, int64_t ts1,
+                      int seq_axis, int64_t ignore_idx, int64_t* shifted, void* stream);
+
+/*
  * lce_workspace_size: bytes of device workspace lce_forward and lce_backward
  * need for an (M, H, V) problem (one buffer serves both; its contents need
  * not survive between calls).  Analogue of the workspace query API of the

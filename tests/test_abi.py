@@ -265,3 +265,19 @@ def test_lce_shard_rejects(L):
     assert bwd_(n_valid=A + 2) == 3
     assert bwd_(ws_bytes=ws - 1) == 5
     assert bwd_(eps=2.0) == 1
+
+
+def test_shift_targets_rejects(L):
+    s = L.vce_shift_targets
+
+    def call(targets=A, d0=2, d1=8, ts0=8, ts1=1, axis=1, ignore=-100, out=A + (1 << 20)):
+        return s(targets, d0, d1, ts0, ts1, axis, ignore, out, None)
+
+    assert call(axis=2) == 1
+    assert call(d0=-1) == 1
+    assert call(ts1=-1) == 1
+    assert call(targets=None) == 1
+    assert call(out=None) == 1
+    assert call(targets=A + 4) == 3
+    assert call(out=A + 8) == 4           # overlaps the targets it reads
+    assert call(d0=0, targets=None, out=None) == 0

@@ -6,4 +6,4 @@ in ``include/vce.h``); ``binding`` marshals torch tensors into it.
 from .binding import (ce_backward, ce_backward_shard, ce_forward, ce_forward_shard,  # noqa: F401
                       ce_merge_shards, gemm_bf16, lce_backward, lce_backward_shard,
                       lce_forward, lce_forward_shard, lce_workspace, lce_workspace_size, lib,
-                      strerror, VceError)
+                      shift_targets, strerror, VceError)

@@ -35,6 +35,7 @@ SIGNATURES = {
                                _VP, _VP, _VP, _VP, _VP]),
     "ce_backward_shard": (_I32, [_VP, _VP, _I32, _I64, _I64, _I64, _I64, _I64, _VP, _I64, _I64,
                                  _I64, _I64, _VP, _VP, _VP, _F32, _I32, _I64, _I32, _VP]),
+    "vce_shift_targets": (_I32, [_VP, _I64, _I64, _I64, _I64, _I32, _I64, _VP, _VP]),
     "lce_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "lce_forward": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _F32, _I32, _I64, _VP, _VP, _VP, _VP,
                            _VP, _VP, _SZ, _VP]),
@@ -263,6 +264,29 @@ def ce_backward_shard(logits: torch.Tensor, targets: torch.Tensor, vocab_start: 
                                  int(bool(overwrite_input)), _stream(stream))
     _check("ce_backward_shard", rc)
     return grad
+
+
+def shift_targets(targets: torch.Tensor, seq_axis: int, ignore_idx: int = -100, *,
+                  stream=None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Causal label shift of (d0, d1) (or (M,) as one sequence) int64 targets
+    along ``seq_axis``: each position takes the next position's label, the
+    last one ``ignore_idx``.  Returns a contiguous tensor of the same shape."""
+    _need_cuda(targets)
+    if targets.dtype != torch.int64:
+        raise TypeError("targets must be int64")
+    t2 = targets.unsqueeze(0) if targets.dim() == 1 else targets
+    if t2.dim() != 2:
+        raise ValueError("targets must be (d0, d1) or (M,)")
+    if targets.dim() == 1 and seq_axis == 0:
+        raise ValueError("a 1-D target vector is one sequence: use seq_axis 1 (or -1)")
+    seq_axis = 1 if seq_axis == -1 else seq_axis
+    d0, d1 = t2.shape
+    res = torch.empty(targets.shape, dtype=torch.int64, device=targets.device) if out is None \
+        else out
+    rc = lib().vce_shift_targets(_ptr(t2), d0, d1, t2.stride(0), t2.stride(1), int(seq_axis),
+                                 int(ignore_idx), _ptr(res), _stream(stream))
+    _check("vce_shift_targets", rc)
+    return res
 
 
 def lce_workspace_size(M: int, H: int, V: int) -> int:

@@ -459,6 +459,26 @@ __global__ __launch_bounds__(256) void ce_merge_shards_kernel(CeMergeParams p) {
   *reinterpret_cast<f32x4_t*>(p.stats + 4 * r) = f32x4_t{st.m, st.d, zt, mean};
 }
 
+// Causal label shift: out[r] = the target one position later along the
+// sequence axis (axis 0 or 1 of the (d0, d1) grid), ignore_idx at the last
+// position.  out is (d0, d1) contiguous in flattened row order.
+__global__ __launch_bounds__(256) void shift_targets_kernel(ShiftParams p) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= p.N) return;
+  const int64_t i0 = r / p.d1, i1 = r - i0 * p.d1;
+  const int64_t j0 = p.seq_axis == 0 ? i0 + 1 : i0;
+  const int64_t j1 = p.seq_axis == 1 ? i1 + 1 : i1;
+  const bool last = (p.seq_axis == 0) ? (j0 >= p.d0) : (j1 >= p.d1);
+  p.out[r] = last ? p.ignore_idx : p.targets[j0 * p.ts0 + j1 * p.ts1];
+}
+
+hipError_t launch_shift_targets(const ShiftParams& p, hipStream_t stream) {
+  if (p.N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(shift_targets_kernel, dim3((unsigned)((p.N + 255) / 256)), dim3(256), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_ce_forward(const CeFwdParams& p, int dtype, int64_t N, hipStream_t stream) {
   if (N <= 0) return hipSuccess;
   const dim3 g((unsigned)N), b(kThreads);

@@ -310,6 +310,37 @@ int ce_backward_shard(const void* logits, void* grad, int dtype, int64_t d0, int
   return launch_status(vce::launch_ce_backward(p, dtype, sh.N, static_cast<hipStream_t>(stream)));
 }
 
+int vce_shift_targets(const int64_t* targets, int64_t d0, int64_t d1, int64_t ts0, int64_t ts1,
+                      int seq_axis, int64_t ignore_idx, int64_t* shifted, void* stream) {
+  if (d0 < 0 || d1 < 0 || ts0 < 0 || ts1 < 0) return VCE_EINVAL;
+  if (seq_axis != 0 && seq_axis != 1) return VCE_EINVAL;
+  int64_t N;
+  if (!mul_ok(d0, d1, &N)) return VCE_EINVAL;
+  if (N == 0) return VCE_OK;
+  int64_t span0, span1;
+  if (!mul_ok(d0 - 1, ts0, &span0) || !mul_ok(d1 - 1, ts1, &span1) ||
+      span0 > INT64_MAX / 8 - span1 - 1)
+    return VCE_EINVAL;
+  if (!targets || !shifted) return VCE_EINVAL;
+  if (!aligned(targets, 8) || !aligned(shifted, 8)) return VCE_EALIGN;
+  // the output must not overlap the targets it reads
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(targets);
+  const uintptr_t a1 = a0 + (uintptr_t)(span0 + span1 + 1) * 8;
+  const uintptr_t b0 = reinterpret_cast<uintptr_t>(shifted), b1 = b0 + (uintptr_t)N * 8;
+  if (a0 < b1 && b0 < a1) return VCE_EALIAS;
+  vce::ShiftParams p;
+  p.targets = targets;
+  p.d0 = d0;
+  p.d1 = d1;
+  p.ts0 = ts0;
+  p.ts1 = ts1;
+  p.N = N;
+  p.ignore_idx = ignore_idx;
+  p.seq_axis = seq_axis;
+  p.out = shifted;
+  return launch_status(vce::launch_shift_targets(p, static_cast<hipStream_t>(stream)));
+}
+
 size_t lce_workspace_size(int64_t M, int64_t H, int64_t V) {
   vce::LcePlan plan;
   if (!vce::lce_make_plan(M, H, V, &plan)) return 0;

@@ -59,6 +59,14 @@ struct CeBwdParams {
 hipError_t launch_ce_forward(const CeFwdParams& p, int dtype, int64_t N, hipStream_t stream);
 hipError_t launch_ce_mean(const CeMeanParams& p, hipStream_t stream);
 hipError_t launch_ce_merge_shards(const CeMergeParams& p, hipStream_t stream);
+
+struct ShiftParams {
+  const int64_t* targets;
+  int64_t d0, d1, ts0, ts1, N, ignore_idx;
+  int seq_axis;
+  int64_t* out;
+};
+hipError_t launch_shift_targets(const ShiftParams& p, hipStream_t stream);
 hipError_t launch_ce_backward(const CeBwdParams& p, int dtype, int64_t N, hipStream_t stream);
 
 // ---- fused linear cross-entropy ----------------------------------------------
