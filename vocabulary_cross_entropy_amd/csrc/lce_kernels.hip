@@ -9,17 +9,25 @@
 // Performance methodology: four GEMMs for forward+backward).
 //
 // Design for CDNA4 (not the SM100 design of that PR):
-//  * One GEMM core, C[i][j] = sum_k P[i][k] Q[j][k] with both operands stored
-//    K-contiguous: a 256 x 256 output tile per 512-thread workgroup, eight
-//    wavefronts (two per SIMD, so one wave's waits overlap the other's
-//    matrix work) of 128 x 64 each, v_mfma_f32_32x32x16_bf16.  K advances in
-//    64-deep slices through two LDS stages (128 KB of the 160 KB); global
-//    data goes straight to LDS (buffer_load ... lds).  The two wavefronts of
-//    each SIMD run ping-pong: while one issues its fragment reads and loads,
-//    the other runs 16 MFMAs back to back (measured on MI355X: 13% fewer
-//    cycles per slice than interleaving both kinds in every wave).  16-byte chunks are XOR-swizzled across rows (the loads
-//    pick their source addresses so the linear LDS writes land swizzled) and
-//    the fragment reads are bank-conflict free.
+//  * One GEMM core, C[i][j] = sum_k P(i, k) Q(j, k), each operand stored
+//    K-contiguous or dim-contiguous (a template flag), so the backward reads
+//    X, W and dZ where they lie.  A 256 x 256 output tile per 256-thread
+//    workgroup: four wavefronts, one per SIMD, of 128 x 128 each
+//    (v_mfma_f32_32x32x16_bf16, 16 accumulator blocks = all 256 AGPRs).  A
+//    wave tile this size reads a third fewer LDS bytes per flop than two
+//    waves of 128 x 64 per SIMD.
+//  * K advances in 64-deep slices through two LDS stages (128 KB of 160 KB).
+//    Operands travel global -> VGPRs -> LDS: every wave keeps two slices in
+//    flight in two register buffers (64 VGPRs each), so each 16-byte load is
+//    issued two slices before its data is written to LDS.  The 16 loads and
+//    16 LDS writes of a wave per slice are spread evenly, one pair every
+//    three MFMAs (loads issued in one burst after each barrier, as with
+//    direct-to-LDS loads into two stages, left the MFMAs waiting: measured
+//    1150-1200 TFLOP/s against 1470-1600 with the loads taken out).
+//  * One barrier per slice, before its last k-step: it publishes the next
+//    slice's LDS writes and frees the stage just read.  The fragment reads of
+//    the next k-step go out right after the second MFMA of each k-step, in
+//    the order the MFMAs consume them.
 //  * Tile order: hardware workgroup ids go round-robin over the 8 XCDs, so
 //    each XCD is given a contiguous range of tiles, walked in bands of 8 row
 //    tiles so the 32 workgroups an XCD runs at once share both operands in
@@ -29,12 +37,10 @@
 //    vocabulary inside the lane, then across the two lane halves and the two
 //    wavefronts that share the tokens.  Per-tile partials are merged per
 //    token by a second kernel in a fixed order.
-//  * Backward, per vocabulary chunk: recompute the logits and write dZ (BF16)
-//    token-major and vocabulary-major; dW rows of the chunk are finished by
-//    one GEMM over all tokens (written once, never accumulated); dX
-//    accumulates chunk by chunk in FP32, the last chunk writes BF16.  The
-//    K-contiguous copies this needs (X^T once per call, W_c^T per chunk) are
-//    made by an LDS-tiled transpose; they cost a few percent of the GEMM time.
+//  * Backward, per vocabulary chunk: recompute the logits and write dZ (BF16,
+//    token-major); dW rows of the chunk are finished by one GEMM over all
+//    tokens (written once, never accumulated); dX accumulates chunk by chunk
+//    in FP32, the last chunk writes BF16.
 #include "vce_device.h"
 #include "vce_internal.h"
 
@@ -45,11 +51,14 @@ namespace {
 constexpr int BM = 256;   // output rows per tile (P side)
 constexpr int BN = 256;   // output cols per tile (Q side)
 constexpr int BK = 64;    // K slice per stage
-constexpr int NT = 512;   // threads per workgroup: 8 wavefronts
-constexpr int WN = 64;    // output cols per wavefront
-constexpr int NB = WN / 32;                        // 32-column blocks per wavefront
-constexpr int ROWS_PER_LD = 1024 / (BK * 2);       // rows one 1 KB LDS load covers (8)
-constexpr int LD_PER_WAVE = BM / 8 / ROWS_PER_LD;  // loads per wave per operand per slice (4)
+constexpr int NT = 256;   // threads per workgroup: 4 wavefronts, one per SIMD
+constexpr int WM = 128;   // output rows per wavefront
+constexpr int WN = 128;   // output cols per wavefront
+constexpr int NA = WM / 32;                        // 32-row blocks per wavefront (4)
+constexpr int NB = WN / 32;                        // 32-column blocks per wavefront (4)
+constexpr int NWC = BN / WN;                       // wavefronts across the columns (2)
+constexpr int UNITS = BM * BK * 2 / 1024;          // 1 KB units per operand per slice (32)
+constexpr int UPW = UNITS / (NT / 64);             // units per wave per operand (8)
 constexpr int GROUP_I = 8;                         // row tiles per band of the tile order
 constexpr int64_t kChunk = 32768;                  // backward vocabulary chunk
 constexpr uint32_t kOob = 0x80000000u;             // buffer offset that reads as 0
@@ -57,6 +66,7 @@ constexpr int kDzLd = BM + 4;   // LDS row (elements) of the staged dZ tile: 520
 constexpr int kSmemElems = (2 * (BM + BN) * BK > BN * kDzLd) ? 2 * (BM + BN) * BK : BN * kDzLd;
 
 static_assert(BM == BN, "one loader shape serves both operands");
+static_assert(NA == 4 && NB == 4 && UPW == 8, "the schedule below assumes these");
 
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -73,12 +83,7 @@ struct Operand {
   int64_t k_limit;
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const uint16_t* p) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), (short)0, 0x7fffffff,
-                                           0x00020000);
-}
-
-// LDS stage of one operand (256 x 64 elements, 32 KB):
+// LDS stage of one operand (256 x 64 elements, 32 KB, 32 units of 1 KB):
 //  * K-contiguous: 256 rows (d) of 64 k (128 B, eight 16-byte chunks);
 //    logical chunk c of row d sits at c ^ swz(d).
 //  * dim-contiguous: two halves (d < 128, d >= 128) of 64 rows (k) of 128 d
@@ -88,56 +93,116 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const uint16_t* p) {
 // so the four rows must fall in different 64-byte quarters).
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
-// Streams one operand's 256 x 64 slice into an LDS stage.  Load i of wave w
-// writes 1 KB at element 2048 w + 512 i of the stage, lane l the 16 bytes at
-// 16 l, and each lane reads the logical chunk that lands there:
-//  * K-contiguous: rows 32 w + 8 i .. + 7 (lane: row l / 8, chunk l % 8);
-//  * dim-contiguous: half w / 4, k rows 16 (w % 4) + 4 i .. + 3 (lane: row
-//    l / 16, chunk l % 16).
-// So wave w brings rows 32 w .. 32 w + 31 of the tile (K-contiguous) or the
-// half w / 4 (dim-contiguous): either way waves 0-3 bring exactly the rows
-// 0..127 of P and waves 4-7 the rows 128..255.
+// Moves one operand's 256 x 64 slices in 1 KB units, 8 per wave: unit q =
+// 8 w + i of wave w, lane l, 16 bytes each.  All that varies with i is a
+// scalar offset of the global read and an immediate (or one XOR) of the LDS
+// write, so a loader holds two VGPRs:
+//  * K-contiguous: rows 8 q .. 8 q + 7, lane l reads logical chunk l % 8 of
+//    row 8 q + l / 8 and writes it at physical chunk (l % 8) ^ swz(row) =
+//    (l % 8) ^ (l / 8) ^ i.  Rows past dim_limit are cut off by the buffer
+//    size; with MASK, chunks at or past k_limit by an out-of-range offset.
+//  * dim-contiguous: half q / 16 (= w / 2), k rows 4 (q % 16) + l / 16, lane
+//    chunk l % 16 read from logical chunk (l % 16) ^ 4 (l / 16 % 4) of that
+//    row and written at 16 l of the unit.  Columns past dim_limit get an
+//    out-of-range offset; k rows past k_limit are cut off by the buffer size.
+// at(k0) gives the slice's buffer (scalar, once per slice); get() loads a
+// unit into registers, put() writes registers to the stage; direct() loads a
+// unit of the first slice straight into LDS (the prologue).
+struct SliceRef {
+  __amdgpu_buffer_rsrc_t rs;
+  int nv;  // K-contiguous with MASK: chunks (of 8 k) of the slice below k_limit, 0..8
+};
+
 template <bool DIM>
 struct SliceLoader {
   const uint16_t* tbase;  // operand at the tile's first element, k = 0
-  int64_t kstep;          // elements per unit of k
+  int64_t ld;
   int64_t k_limit;
-  uint32_t off[LD_PER_WAVE];  // byte offset of this lane's 16 bytes, or kOob
-  int kc[LD_PER_WAVE];        // k offset (within the slice) this lane's data starts at
+  int64_t rows_bytes;  // K-contiguous: bytes of the tile's rows below dim_limit
+  uint32_t voff;       // this lane's byte offset in unit 0, or kOob
+  uint32_t ustep;      // bytes between the sources of consecutive units
+  int lds;             // element offset of this lane's 16 bytes of unit 0 in a stage
+  int kch;             // K-contiguous: the logical chunk this lane reads (l % 8)
   __device__ __forceinline__ void init(const Operand& op, int64_t d0, int wave, int lane) {
     k_limit = op.k_limit;
+    ld = op.ld;
     if (!DIM) {
       tbase = op.base + d0 * op.ld;
-      kstep = 1;
-#pragma unroll
-      for (int i = 0; i < LD_PER_WAVE; ++i) {
-        const int row = wave * (BM / 8) + i * ROWS_PER_LD + (lane >> 3);
-        const int c = (lane & 7) ^ swz(row);
-        kc[i] = c * 8;
-        off[i] = (d0 + row < op.dim_limit) ? (uint32_t)(row * op.ld * 2 + c * 16) : kOob;
-      }
+      const int64_t rl = op.dim_limit - d0;
+      rows_bytes = rl <= 0 ? 0 : rl * op.ld * 2;
+      const int row = 8 * UPW * wave + (lane >> 3);
+      voff = (uint32_t)(row * op.ld * 2 + (lane & 7) * 16);
+      ustep = (uint32_t)__builtin_amdgcn_readfirstlane((int)(8 * op.ld * 2));
+      kch = lane & 7;
+      const int c0 = ((lane & 7) ^ (lane >> 3)) & 7;  // physical chunk in unit 0
+      lds = row * BK + c0 * 8;                        // unit i: (lds ^ 8 i) + 512 i
     } else {
       tbase = op.base + d0;
-      kstep = op.ld;
-      const int half = wave >> 2;
-#pragma unroll
-      for (int i = 0; i < LD_PER_WAVE; ++i) {
-        const int krow = 16 * (wave & 3) + 4 * i + (lane >> 4);
-        const int c = (lane & 15) ^ (4 * (krow & 3));
-        const int d = 128 * half + 8 * c;
-        kc[i] = krow;
-        off[i] = (d0 + d < op.dim_limit) ? (uint32_t)(krow * op.ld * 2 + d * 2) : kOob;
-      }
+      rows_bytes = 0;
+      const int krow = 32 * (wave & 1) + (lane >> 4);
+      const int c = (lane & 15) ^ (4 * ((lane >> 4) & 3));
+      const int d = 128 * (wave >> 1) + 8 * c;
+      voff = (d0 + d < op.dim_limit) ? (uint32_t)(krow * op.ld * 2 + d * 2) : kOob;
+      ustep = (uint32_t)__builtin_amdgcn_readfirstlane((int)(4 * op.ld * 2));
+      kch = 0;
+      lds = 512 * UPW * wave + 8 * lane;  // unit i: + 512 i
     }
   }
-  // load i of the slice starting at k0; `tail`: the slice reaches past k_limit
-  __device__ __forceinline__ void issue(uint16_t LDS_AS* stage, int64_t k0, int wave, int i,
-                                        bool tail) {
-    const __amdgpu_buffer_rsrc_t rs = rsrc_at(tbase + k0 * kstep);
-    uint32_t o = off[i];
-    if (tail) o = (k0 + kc[i] < k_limit) ? o : kOob;
+  // the slice starting at k0 (a multiple of BK, possibly past K).  MASK:
+  // reads at or past k_limit give 0.  Without it K is a multiple of 2 BK and
+  // the caller clamps slices past the end (prefetched, never used) to the
+  // last one.
+  template <bool MASK>
+  __device__ __forceinline__ SliceRef at(int64_t k0) const {
+    SliceRef r;
+    r.nv = 8;
+    const int64_t kb = k0;
+    if (!DIM) {
+      r.rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(tbase + kb), (short)0,
+          rows_bytes > 0x7fffffff ? 0x7fffffff : (int)rows_bytes, 0x00020000);
+      if (MASK) {
+        const int64_t left = k_limit - k0;
+        r.nv = left <= 0 ? 0 : (left >= BK ? 8 : (int)((left + 7) >> 3));
+      }
+    } else {
+      int64_t bytes = 0x7fffffff;
+      if (MASK) {
+        const int64_t left = k_limit - k0;
+        bytes = left <= 0 ? 0 : left * ld * 2;
+        if (bytes > 0x7fffffff) bytes = 0x7fffffff;
+      }
+      r.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(tbase + kb * ld), (short)0,
+                                               (int)bytes, 0x00020000);
+    }
+    return r;
+  }
+  template <bool MASK>
+  __device__ __forceinline__ u32x4_t get(const SliceRef& r, int i) const {
+    // K-contiguous: this lane reads logical chunk l % 8, which lies below
+    // k_limit iff (l % 8) < nv
+    const uint32_t o = (!MASK || DIM || kch < r.nv) ? voff : kOob;
+    return __builtin_bit_cast(
+        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r.rs, o, (int)(i * ustep), 0));
+  }
+  __device__ __forceinline__ void put(uint16_t LDS_AS* stage, int i, const u32x4_t& v) const {
+    const int e = DIM ? lds + 512 * i : (lds ^ (8 * i)) + 512 * i;
+    *reinterpret_cast<u32x4_t LDS_AS*>(stage + e) = v;
+  }
+  // Unit i straight into LDS: lane l fills the 16 bytes at 16 l of the unit,
+  // so a K-contiguous lane reads the logical chunk that sits there,
+  // (l % 8) ^ (l / 8) ^ i, instead of l % 8.
+  template <bool MASK>
+  __device__ __forceinline__ void direct(uint16_t LDS_AS* stage, const SliceRef& r, int wave,
+                                         int lane, int i) const {
+    uint32_t o = voff;
+    if (!DIM) {
+      const int c = ((lane & 7) ^ (lane >> 3) ^ i) & 7;
+      o = voff - (uint32_t)((lane & 7) * 16) + (uint32_t)(c * 16);
+      if (MASK && c >= r.nv) o = kOob;
+    }
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (void LDS_AS*)(stage + 2048 * wave + 512 * i), 16, o, 0, 0, 0);
+        r.rs, (void LDS_AS*)(stage + 512 * (UPW * wave + i)), 16, o, (int)(i * ustep), 0, 0);
   }
 };
 
@@ -184,13 +249,88 @@ __device__ __forceinline__ void tile_of(int b, int n_ti, int n_tj, int* ti, int*
   *tj = in_band / gi;
 }
 
+// Per-wave state of the main loop.
+struct LoopState {
+  f32x16_t acc[NA][NB];
+  bf16x8_t FA[NA];          // P fragments (refilled for the next k-step as they die)
+  bf16x8_t FB[2][NB];       // Q fragments of the current and the next k-step
+  u32x4_t R[2][2 * UPW];    // register buffers: units 0..7 of P, 8..15 of Q
+};
+
+// Slice k of the main loop (its data in stage k & 1, its first k-step's
+// fragments in FA and FB[0]).  During k-steps 0..2 the wave writes slice
+// k + 1 from register buffer B1 = (k + 1) & 1 to the other stage and refills
+// the buffer with slice k + 3.  The barrier before k-step 3 publishes slice
+// k + 1 (every wave waited for its own writes) and tells that stage k is no
+// longer read (every wave's fragments of k-step 3 are in registers), so the
+// next round of writes may go there.  MFMAs run a-major: P fragment a dies
+// after MFMA 4 a + 3 and is refilled with the next k-step's right then; the
+// next Q fragments go to the other buffer after MFMA 1.  Waits: the compiler
+// places s_waitcnt vmcnt before each LDS write (its load was issued 32 loads
+// earlier) and lgkmcnt before the MFMAs that use fresh fragments.
+template <int B1, bool PD, bool QD, bool MASK>
+__device__ __forceinline__ void loop_slice(LoopState& S, const SliceLoader<PD>& lp,
+                                           const SliceLoader<QD>& lq, uint16_t LDS_AS* sp,
+                                           uint16_t LDS_AS* sq, int k, int klast, int wr,
+                                           int wc, int lane) {
+  constexpr int cur = B1 ^ 1;  // k & 1: the loop runs slices in pairs
+  const uint16_t LDS_AS* cp = sp + cur * BM * BK;
+  const uint16_t LDS_AS* cq = sq + cur * BN * BK;
+  uint16_t LDS_AS* np = sp + (cur ^ 1) * BM * BK;
+  uint16_t LDS_AS* nq = sq + (cur ^ 1) * BN * BK;
+  const int k3 = MASK || k + 3 < klast ? k + 3 : klast;
+  const SliceRef rp = lp.template at<MASK>((int64_t)k3 * BK);
+  const SliceRef rq = lq.template at<MASK>((int64_t)k3 * BK);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int f = ks & 1;
+    if (ks == 3) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        S.acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(S.FA[a], S.FB[f][b], S.acc[a][b],
+                                                              0, 0, 0);
+        const int m = a * NB + b;
+        if (m == 1) {
+#pragma unroll
+          for (int r = 0; r < NB; ++r)
+            S.FB[f ^ 1][r] = ks < 3 ? frag<QD>(cq, wc * WN + 32 * r, ks + 1, lane)
+                                    : frag<QD>(nq, wc * WN + 32 * r, 0, lane);
+        }
+        if (b == NB - 1)
+          S.FA[a] = ks < 3 ? frag<PD>(cp, wr * WM + 32 * a, ks + 1, lane)
+                           : frag<PD>(np, wr * WM + 32 * a, 0, lane);
+        const int pos = ks * 16 + m;
+        if (ks < 3 && pos % 3 == 2) {
+          const int u = pos / 3;  // 0..15
+          if (u < UPW) {
+            lp.put(np, u, S.R[B1][u]);
+            S.R[B1][u] = lp.template get<MASK>(rp, u);
+          } else {
+            lq.put(nq, u - UPW, S.R[B1][u]);
+            S.R[B1][u] = lq.template get<MASK>(rq, u - UPW);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+}
+
 // Accumulator register r of block (a, b) of a lane holds
 //   row i = i0 + 128 wr + 32 a + 8 (r / 4) + 4 (lane / 32) + r % 4
-//   col j = j0 + 64 wc + 32 b + lane % 32
-// for wavefront (wr, wc) = (wave / 4, wave % 4).
-template <class Epi, bool PD, bool QD>
-__global__ __launch_bounds__(NT) void gemm_kernel(Operand P, Operand Q, int64_t K, int n_ti,
-                                                  int n_tj, typename Epi::Params ep) {
+//   col j = j0 + 128 wc + 32 b + lane % 32
+// for wavefront (wr, wc) = (wave / 2, wave % 2).
+// MASK: K is not a multiple of 2 BK (or is 0): k is masked on every read.
+template <class Epi, bool PD, bool QD, bool MASK>
+__global__ __launch_bounds__(NT, 1) void gemm_kernel(Operand P, Operand Q, int64_t K, int n_ti,
+                                                     int n_tj, typename Epi::Params ep) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[kSmemElems];
   uint16_t LDS_AS* const sp = (uint16_t LDS_AS*)smem;  // P stages: sp + s * BM * BK
   uint16_t LDS_AS* const sq = sp + 2 * BM * BK;         // Q stages: sq + s * BN * BK
@@ -199,135 +339,65 @@ __global__ __launch_bounds__(NT) void gemm_kernel(Operand P, Operand Q, int64_t 
   tile_of(blockIdx.x, n_ti, n_tj, &ti, &tj);
   const int64_t i0 = (int64_t)ti * BM, j0 = (int64_t)tj * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wr = wave >> 2, wc = wave & 3;
+  const int wr = wave / NWC, wc = wave % NWC;
 
-  f32x16_t acc[4][NB];
+  LoopState S;
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < NA; ++a)
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+      for (int r = 0; r < 16; ++r) S.acc[a][b][r] = 0.0f;
 
   SliceLoader<PD> lp;
   SliceLoader<QD> lq;
   lp.init(P, i0, wave, lane);
   lq.init(Q, j0, wave, lane);
-  const int nk = (int)((K + BK - 1) / BK);
+  // An even number of slices (the loop body runs two); slices at or past K
+  // read as zeros and add nothing.
+  const int nk = (int)((K + 2 * BK - 1) / (2 * BK)) * 2;
+  // last real slice (without MASK, prefetches past it re-read it)
+  const int klast = (int)((K + BK - 1) / BK) - 1;
+  // slice 0 straight to stage 0, slices 1 and 2 into register buffers 1 and
+  // 0 right behind it; then wait for slice 0 only (its 16 loads went first)
   {
-    const bool tail = BK > K;
+    const SliceRef p0 = lp.template at<MASK>(0), q0 = lq.template at<MASK>(0);
 #pragma unroll
-    for (int i = 0; i < LD_PER_WAVE; ++i) {
-      lp.issue(sp, 0, wave, i, tail);
-      lq.issue(sq, 0, wave, i, tail);
-    }
-  }
-  // Ping-pong: the two wavefronts of a SIMD (waves w and w + 4) alternate
-  // between a memory phase (fragment reads of a half slice, plus the next
-  // slice's loads) and a compute phase (16 MFMAs back to back), so one issues
-  // LDS and load instructions while the other keeps the matrix core busy.
-  // Phases end at workgroup barriers; the second group starts one phase late.
-  //   group 0: phase 4k = M(k,0), 4k+1 = C(k,0), 4k+2 = M(k,1), 4k+3 = C(k,1)
-  //   group 1: one phase later.
-  // Wave w loads rows 32w..32w+31 of both operands, so the P rows a group
-  // loads are read by that group only; Q rows are read by both.
-  //  * Q rows of slice k+1 go into the stage slice k-1 used, in M(k,0), after
-  //    its last readers (group 0 in 4k-2, group 1 in 4k-1).
-  //  * P rows of slice k+2 go into the stage of slice k, in M(k,1), right
-  //    after the group's own last reads of them (lgkmcnt(0) first): two
-  //    phases earlier than M(k+1,0), which gives those loads more time.
-  // Group 0 reads slice k+1 from phase 4k+4: at the end of 4k+3 each wave
-  // waits until only its four P loads of slice k+2 are in flight
-  // (vmcnt(4)), which covers its Q loads of slice k+1 and the P loads of
-  // slice k+1 issued before them.
-  // Every wave passes the same number of barriers (group 0 adds one at the
-  // end), so no barrier waits on a wave that has left the loop.
-  const bool g1 = wave >= 4;
-  if (nk > 1) {  // P rows of slice 1 (its Q rows follow in M(0,0))
+    for (int i = 0; i < UPW; ++i) lp.template direct<MASK>(sp, p0, wave, lane, i);
 #pragma unroll
-    for (int i = 0; i < LD_PER_WAVE; ++i) lp.issue(sp + BM * BK, BK, wave, i, 2 * BK > K);
+    for (int i = 0; i < UPW; ++i) lq.template direct<MASK>(sq, q0, wave, lane, i);
+    const int k1 = MASK || klast >= 1 ? 1 : klast, k2 = MASK || klast >= 2 ? 2 : klast;
+    const SliceRef p1 = lp.template at<MASK>((int64_t)k1 * BK);
+    const SliceRef q1 = lq.template at<MASK>((int64_t)k1 * BK);
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) S.R[1][i] = lp.template get<MASK>(p1, i);
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) S.R[1][UPW + i] = lq.template get<MASK>(q1, i);
+    const SliceRef p2 = lp.template at<MASK>((int64_t)k2 * BK);
+    const SliceRef q2 = lq.template at<MASK>((int64_t)k2 * BK);
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) S.R[0][i] = lp.template get<MASK>(p2, i);
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) S.R[0][UPW + i] = lq.template get<MASK>(q2, i);
   }
-  // slice 0 complete (only the P loads of slice 1 may be in flight)
-  if (nk > 1)
-    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  if (g1) __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const uint16_t LDS_AS* cp = sp + cur * BM * BK;
-    const uint16_t LDS_AS* cq = sq + cur * BN * BK;
-    uint16_t LDS_AS* np = sp + (cur ^ 1) * BM * BK;
-    uint16_t LDS_AS* nq = sq + (cur ^ 1) * BN * BK;
-    const bool more = kt + 1 < nk;
-    const int64_t kn = (int64_t)(kt + 1) * BK;
-    const bool tail = kn + BK > K;
-    const bool more2 = kt + 2 < nk;
-    const int64_t kn2 = (int64_t)(kt + 2) * BK;
-    const bool tail2 = kn2 + BK > K;
-    uint16_t LDS_AS* cpw = sp + cur * BM * BK;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      // memory phase: fragments of k-steps 2h and 2h+1; the next slice's loads
-      bf16x8_t fa[2][4], fb[2][NB];
+  for (int a = 0; a < NA; ++a) S.FA[a] = frag<PD>(sp, wr * WM + 32 * a, 0, lane);
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int ks = 2 * h + s2;
-#pragma unroll
-        for (int a = 0; a < 4; ++a) fa[s2][a] = frag<PD>(cp, wr * 128 + 32 * a, ks, lane);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) fb[s2][b] = frag<QD>(cq, wc * WN + 32 * b, ks, lane);
-      }
-      if (h == 0 && more) {
-#pragma unroll
-        for (int i = 0; i < LD_PER_WAVE; ++i) lq.issue(nq, kn, wave, i, tail);
-      }
-      // reads complete: the stage may be refilled (now by this wave, after
-      // the barrier by the others)
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      if (h == 1) {
-        if (more2) {
-#pragma unroll
-          for (int i = 0; i < LD_PER_WAVE; ++i) lp.issue(cpw, kn2, wave, i, tail2);
-        }
-        if (g1) {
-          if (more2)
-            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-          else
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      // compute phase
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-          for (int b = 0; b < NB; ++b)
-            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s2][a], fb[s2][b], acc[a][b], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);  // the wait stays behind the MFMAs
-      if (h == 1 && !g1) {
-        if (more2)
-          asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  for (int b = 0; b < NB; ++b) S.FB[0][b] = frag<QD>(sq, wc * WN + 32 * b, 0, lane);
+  for (int k = 0; k < nk; k += 2) {
+    loop_slice<1, PD, QD, MASK>(S, lp, lq, sp, sq, k, klast, wr, wc, lane);
+    loop_slice<0, PD, QD, MASK>(S, lp, lq, sp, sq, k + 1, klast, wr, wc, lane);
   }
-  if (!g1) __builtin_amdgcn_s_barrier();
+  // drain the loads of the slices past the end (zeros, never used) and let
+  // every wave finish with LDS before the epilogue reuses it
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
-  __syncthreads();  // LDS is free for the epilogue
-  Epi::apply(ep, acc, i0, j0, wr, wc, lane, smem);
+  __syncthreads();
+  Epi::apply(ep, S.acc, i0, j0, wr, wc, lane, smem);
 }
 
 // ---- epilogues ------------------------------------------------------------------
@@ -338,7 +408,7 @@ struct EpiF32 {
     float* C;
     int64_t ldc, rows, cols;
   };
-  __device__ static void apply(const Params& p, f32x16_t (&acc)[4][NB], int64_t i0, int64_t j0,
+  __device__ static void apply(const Params& p, f32x16_t (&acc)[NA][NB], int64_t i0, int64_t j0,
                                int wr, int wc, int lane, uint16_t*) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -370,7 +440,7 @@ struct EpiLse {
     int64_t M, V, Mp, ignore_idx;
     int64_t v0;  // vocabulary index of W's first row (0 unless sharded)
   };
-  __device__ static void apply(const Params& p, f32x16_t (&acc)[4][NB], int64_t i0, int64_t j0,
+  __device__ static void apply(const Params& p, f32x16_t (&acc)[NA][NB], int64_t i0, int64_t j0,
                                int wr, int wc, int lane, uint16_t* smem) {
     float* sh = reinterpret_cast<float*>(smem);  // [wr][wc][b][lane 0..31][4]
     const int64_t vbase = i0 + wr * 128 + 4 * (lane >> 5);
@@ -423,7 +493,7 @@ struct EpiLse {
         if (inr) p.zt[j] = zt;
       }
       if (lane < 32) {
-        float* e = sh + (((wr * 4 + wc) * NB + b) * 32 + lane) * 4;
+        float* e = sh + (((wr * NWC + wc) * NB + b) * 32 + lane) * 4;
         e[0] = mx;
         e[1] = d;
         e[2] = s;
@@ -437,8 +507,8 @@ struct EpiLse {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int64_t j = j0 + wc * WN + b * 32 + lane;
-        const float* e0 = sh + (((0 * 4 + wc) * NB + b) * 32 + lane) * 4;
-        const float* e1 = sh + (((1 * 4 + wc) * NB + b) * 32 + lane) * 4;
+        const float* e0 = sh + (((0 * NWC + wc) * NB + b) * 32 + lane) * 4;
+        const float* e1 = sh + (((1 * NWC + wc) * NB + b) * 32 + lane) * 4;
         LseEntState st{e0[0], e0[1], e0[2], e0[3]};
         lse_merge(st, LseEntState{e1[0], e1[1], e1[2], e1[3]});
         if (j < p.M) {
@@ -475,7 +545,7 @@ struct EpiDz {
     int64_t ignore_idx, M, V;
     int64_t v0, Vg;  // W holds vocabulary rows v0 .. v0 + V - 1 of Vg (0, V unless sharded)
   };
-  __device__ static void apply(const Params& p, f32x16_t (&acc)[4][NB], int64_t i0, int64_t j0,
+  __device__ static void apply(const Params& p, f32x16_t (&acc)[NA][NB], int64_t i0, int64_t j0,
                                int wr, int wc, int lane, uint16_t* smem) {
     uint16_t LDS_AS* const st = (uint16_t LDS_AS*)smem;  // [256 tokens][kDzLd]
     float gscale = 0.0f;
@@ -555,7 +625,7 @@ struct EpiDw {
     uint16_t* dW;
     int64_t H, c0, vc_valid;
   };
-  __device__ static void apply(const Params& p, f32x16_t (&acc)[4][NB], int64_t i0, int64_t j0,
+  __device__ static void apply(const Params& p, f32x16_t (&acc)[NA][NB], int64_t i0, int64_t j0,
                                int wr, int wc, int lane, uint16_t*) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -586,7 +656,7 @@ struct EpiDx {
     int64_t H, M;
     int mode;
   };
-  __device__ static void apply(const Params& p, f32x16_t (&acc)[4][NB], int64_t i0, int64_t j0,
+  __device__ static void apply(const Params& p, f32x16_t (&acc)[NA][NB], int64_t i0, int64_t j0,
                                int wr, int wc, int lane, uint16_t*) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -681,8 +751,13 @@ hipError_t run_gemm(const Operand& P, const Operand& Q, int64_t rows, int64_t co
   const int64_t n = n_ti * n_tj;
   if (n <= 0) return hipSuccess;
   if (n > INT32_MAX / 2) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_kernel<Epi, PD, QD>), dim3((unsigned)n), dim3(NT), 0, stream, P, Q, K,
-                     (int)n_ti, (int)n_tj, ep);
+  // both operands have k_limit = K
+  if (K % (2 * BK) != 0 || K == 0)
+    hipLaunchKernelGGL((gemm_kernel<Epi, PD, QD, true>), dim3((unsigned)n), dim3(NT), 0, stream,
+                       P, Q, K, (int)n_ti, (int)n_tj, ep);
+  else
+    hipLaunchKernelGGL((gemm_kernel<Epi, PD, QD, false>), dim3((unsigned)n), dim3(NT), 0, stream,
+                       P, Q, K, (int)n_ti, (int)n_tj, ep);
   return hipGetLastError();
 }
 
