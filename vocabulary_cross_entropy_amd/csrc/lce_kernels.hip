@@ -41,6 +41,8 @@
 //    token-major); dW rows of the chunk are finished by one GEMM over all
 //    tokens (written once, never accumulated); dX accumulates chunk by chunk
 //    in FP32, the last chunk writes BF16.
+#include <type_traits>
+
 #include "vce_device.h"
 #include "vce_internal.h"
 
@@ -429,7 +431,19 @@ struct EpiF32 {
 // (max, sum exp(z - max), sum z, sum exp(z - max) (z - max) log2(e)) into the
 // partial arrays (the last one gives the entropy), plus the target logit
 // written by the one lane that holds it.
-struct EpiLse {
+// Tree reductions of one accumulator block (16 values): short dependency
+// chains, since one wavefront per SIMD has no other wave to fill the gaps.
+__device__ __forceinline__ float max16(const f32x16_t& v) {
+  float m[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m[i] = fmaxf(v[i], v[i + 8]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m[i] = fmaxf(m[i], m[i + 4]);
+  return fmaxf(fmaxf(m[0], m[2]), fmaxf(m[1], m[3]));
+}
+
+template <bool ENT>
+struct EpiLseT {
   struct Params {
     float* pm;
     float* pd;
@@ -440,64 +454,114 @@ struct EpiLse {
     int64_t M, V, Mp, ignore_idx;
     int64_t v0;  // vocabulary index of W's first row (0 unless sharded)
   };
+  // Sum over the block's values of exp(z - m) (as d), z (as s) and, with ENT,
+  // exp(z - m) (z - m) log2(e) (as w), each as a tree; rows at offsets >= lim
+  // left out when MASKED.
+  template <bool MASKED>
+  __device__ static void sums(const f32x16_t& v, int a, float mL, int lim, float& d, float& s,
+                              float& w) {
+    float e[16], t[16], z[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const bool in = !MASKED || a * 32 + 8 * (r >> 2) + (r & 3) < lim;
+      t[r] = __builtin_fmaf(v[r], kLog2e, -mL);
+      e[r] = in ? exp2_hw(t[r]) : 0.0f;
+      z[r] = in ? v[r] : 0.0f;
+      if (ENT) t[r] = in ? e[r] * t[r] : 0.0f;
+    }
+#pragma unroll
+    for (int h = 8; h >= 1; h >>= 1)
+#pragma unroll
+      for (int r = 0; r < h; ++r) {
+        e[r] += e[r + h];
+        z[r] += z[r + h];
+        if (ENT) t[r] += t[r + h];
+      }
+    d += e[0];
+    s += z[0];
+    if (ENT) w += t[0];
+  }
   __device__ static void apply(const Params& p, f32x16_t (&acc)[NA][NB], int64_t i0, int64_t j0,
                                int wr, int wc, int lane, uint16_t* smem) {
     float* sh = reinterpret_cast<float*>(smem);  // [wr][wc][b][lane 0..31][4]
-    const int64_t vbase = i0 + wr * 128 + 4 * (lane >> 5);
-    // rows at offsets >= lim from vbase lie beyond the vocabulary
-    const int64_t lim64 = p.V - vbase;
-    const int lim = lim64 > 128 ? 128 : (lim64 < 0 ? 0 : (int)lim64);
+    // the lane's four targets first: one memory round trip under the math
+    int64_t tg[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int64_t j = j0 + wc * WN + b * 32 + (lane & 31);
-      float mx = kNegInf;
+      tg[b] = j < p.M ? p.targets[j] : p.ignore_idx;
+    }
+    const int64_t vbase = i0 + wr * 128 + 4 * (lane >> 5);
+    // rows at offsets >= lim from vbase lie beyond the vocabulary; a wave
+    // whose 128 rows are all inside skips every per-element test
+    const bool full = p.V - (i0 + wr * 128) >= 128;
+    const int64_t lim64 = p.V - vbase;
+    const int lim = lim64 > 128 ? 128 : (lim64 < 0 ? 0 : (int)lim64);
+    float mx[NB], d[NB], s[NB], w[NB];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+    for (int b = 0; b < NB; ++b) {
+      if (full) {
+        mx[b] = fmaxf(fmaxf(max16(acc[0][b]), max16(acc[1][b])),
+                      fmaxf(max16(acc[2][b]), max16(acc[3][b])));
+      } else {
+        float m = kNegInf;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (a * 32 + 8 * (r >> 2) + (r & 3) < lim) mx = fmaxf(mx, acc[a][b][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mref = (mx == kNegInf) ? 0.0f : mx;
-      const float mL = mref * kLog2e;
-      float d = 0.0f, s = 0.0f, w = 0.0f;
+        for (int a = 0; a < NA; ++a)
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+          for (int r = 0; r < 16; ++r)
+            if (a * 32 + 8 * (r >> 2) + (r & 3) < lim) m = fmaxf(m, acc[a][b][r]);
+        mx[b] = m;
+      }
+    }
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (a * 32 + 8 * (r >> 2) + (r & 3) < lim) {
-            const float t = __builtin_fmaf(acc[a][b][r], kLog2e, -mL);
-            const float e = exp2_hw(t);
-            d += e;
-            w = __builtin_fmaf(e, t, w);
-            s += acc[a][b][r];
-          }
-      d += __shfl_xor(d, 32, 64);
-      s += __shfl_xor(s, 32, 64);
-      w += __shfl_xor(w, 32, 64);
-      // Target logit: the lane holding row t picks it with a two-level select
-      // (row block a, then register r), no dynamic register index.
-      if (j < p.M) {
-        const int64_t t = p.targets[j];
+    for (int b = 0; b < NB; ++b) mx[b] = fmaxf(mx[b], __shfl_xor(mx[b], 32, 64));
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float mL = ((mx[b] == kNegInf) ? 0.0f : mx[b]) * kLog2e;
+      d[b] = 0.0f;
+      s[b] = 0.0f;
+      w[b] = 0.0f;
+#pragma unroll
+      for (int a = 0; a < NA; ++a) {
+        if (full)
+          sums<false>(acc[a][b], a, mL, lim, d[b], s[b], w[b]);
+        else
+          sums<true>(acc[a][b], a, mL, lim, d[b], s[b], w[b]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      d[b] += __shfl_xor(d[b], 32, 64);
+      s[b] += __shfl_xor(s[b], 32, 64);
+      if (ENT) w[b] += __shfl_xor(w[b], 32, 64);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      // Target logit: only a lane whose token's target lies in this wave's
+      // rows (rarely any) picks it, with a two-level select (row block a,
+      // then register r): no dynamic register index.
+      const int64_t j = j0 + wc * WN + b * 32 + (lane & 31);
+      {
+        const int64_t t = tg[b];
         const int64_t tl64 = t - p.v0 - vbase;
         const bool inr = t != p.ignore_idx && tl64 >= 0 && tl64 < 128 && ((tl64 >> 2) & 1) == 0;
-        const int tl = inr ? (int)tl64 : 0;
-        const int ra = tl >> 5, rr = ((tl >> 3) & 3) * 4 + (tl & 3);
-        float zt = 0.0f;
+        if (inr) {
+          const int tl = (int)tl64;
+          const int ra = tl >> 5, rr = ((tl >> 3) & 3) * 4 + (tl & 3);
+          float zt = 0.0f;
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          float x = acc[a][b][0];
+          for (int a = 0; a < NA; ++a) {
+            float x = acc[a][b][0];
 #pragma unroll
-          for (int r = 1; r < 16; ++r) x = (rr == r) ? acc[a][b][r] : x;
-          zt = (ra == a) ? x : zt;
+            for (int r = 1; r < 16; ++r) x = (rr == r) ? acc[a][b][r] : x;
+            zt = (ra == a) ? x : zt;
+          }
+          p.zt[j] = zt;
         }
-        if (inr) p.zt[j] = zt;
       }
       if (lane < 32) {
         float* e = sh + (((wr * NWC + wc) * NB + b) * 32 + lane) * 4;
-        e[0] = mx;
-        e[1] = d;
-        e[2] = s;
-        e[3] = w;
+        *reinterpret_cast<f32x4_t*>(e) = f32x4_t{mx[b], d[b], s[b], w[b]};
       }
     }
     __syncthreads();
@@ -507,15 +571,22 @@ struct EpiLse {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int64_t j = j0 + wc * WN + b * 32 + lane;
-        const float* e0 = sh + (((0 * NWC + wc) * NB + b) * 32 + lane) * 4;
-        const float* e1 = sh + (((1 * NWC + wc) * NB + b) * 32 + lane) * 4;
-        LseEntState st{e0[0], e0[1], e0[2], e0[3]};
-        lse_merge(st, LseEntState{e1[0], e1[1], e1[2], e1[3]});
-        if (j < p.M) {
+        const f32x4_t e0 = *reinterpret_cast<const f32x4_t*>(sh + (((0 * NWC + wc) * NB + b) * 32 + lane) * 4);
+        const f32x4_t e1 = *reinterpret_cast<const f32x4_t*>(sh + (((1 * NWC + wc) * NB + b) * 32 + lane) * 4);
+        if (j >= p.M) continue;
+        if (ENT) {
+          LseEntState st{e0[0], e0[1], e0[2], e0[3]};
+          lse_merge(st, LseEntState{e1[0], e1[1], e1[2], e1[3]});
           p.pm[vt * p.Mp + j] = st.m;
           p.pd[vt * p.Mp + j] = st.d;
           p.ps[vt * p.Mp + j] = st.s;
           p.pw[vt * p.Mp + j] = st.w;
+        } else {
+          LseState st{e0[0], e0[1], e0[2]};
+          lse_merge(st, LseState{e1[0], e1[1], e1[2]});
+          p.pm[vt * p.Mp + j] = st.m;
+          p.pd[vt * p.Mp + j] = st.d;
+          p.ps[vt * p.Mp + j] = st.s;
         }
       }
     }
@@ -530,7 +601,8 @@ struct EpiLse {
 // consecutive tokens hit distinct banks) and leaves as whole 512-byte token
 // rows, 16 bytes per lane (direct 8-byte stores from the MFMA layout left
 // partial lines: 1.6x the bytes written, measured).
-struct EpiDz {
+template <bool ENT>
+struct EpiDzT {
   struct Params {
     uint16_t* dz;
     int64_t ldz, c0, vc_valid;
@@ -538,8 +610,8 @@ struct EpiDz {
     const int64_t* targets;
     const float* grad_output;
     const int32_t* n_valid;
-    const float* entropy;       // with grad_entropy: the forward's entropy
-    const float* grad_entropy;  // optional: adds grad_entropy[m] dH/dz
+    const float* entropy;       // ENT: the forward's entropy
+    const float* grad_entropy;  // ENT: adds grad_entropy[m] dH/dz
     float eps;
     int reduce_loss;
     int64_t ignore_idx, M, V;
@@ -548,63 +620,96 @@ struct EpiDz {
   __device__ static void apply(const Params& p, f32x16_t (&acc)[NA][NB], int64_t i0, int64_t j0,
                                int wr, int wc, int lane, uint16_t* smem) {
     uint16_t LDS_AS* const st = (uint16_t LDS_AS*)smem;  // [256 tokens][kDzLd]
+    // every per-token input of the lane's four tokens first, so that they
+    // share one memory round trip
+    int64_t tg[NB];
+    f32x4_t sv[NB];
+    float go[NB], gh[NB], hv[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int64_t j = j0 + wc * WN + b * 32 + (lane & 31);
+      const bool in = j < p.M;
+      tg[b] = in ? p.targets[j] : p.ignore_idx;
+      sv[b] = in ? *reinterpret_cast<const f32x4_t*>(p.stats + 4 * j) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      go[b] = (in && !p.reduce_loss) ? p.grad_output[j] : 0.0f;
+      gh[b] = (ENT && in) ? p.grad_entropy[j] : 0.0f;
+      hv[b] = (ENT && in) ? p.entropy[j] : 0.0f;
+    }
     float gscale = 0.0f;
     if (p.reduce_loss) {
       const int32_t nv = p.n_valid[0];
       gscale = p.grad_output[0] / (float)(nv > 0 ? nv : 1);
     }
+    const int64_t vrow0 = i0 + wr * 128 + 4 * (lane >> 5);  // chunk-local row of r = 0
+    // a wave whose 128 rows all lie in the chunk skips the per-element test
+    const bool full = p.vc_valid - (i0 + wr * 128) >= 128;
+    const int64_t lim64 = p.vc_valid - vrow0;
+    const int lim = lim64 > 128 ? 128 : (lim64 < 0 ? 0 : (int)lim64);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int64_t j = j0 + wc * WN + b * 32 + (lane & 31);
+      // Rows that give zero (ignored token, padding column) or NaN (target
+      // out of range) are folded into the arithmetic: g = 0 or NaN, and an
+      // exponent pushed to -inf so that exp() is 0 for every finite logit.
       int64_t t = -1;
-      float g = 0.0f, lse2 = 0.0f;
-      bool live = false, bad = false;
+      float g = 0.0f, lse2 = 1e30f;
+      bool live = false;
       float gH = 0.0f, ez = 0.0f;
       if (j < p.M) {
-        t = p.targets[j];
+        t = tg[b];
         if (t != p.ignore_idx) {
           if (t >= 0 && t < p.Vg) {
             live = true;
-            g = p.reduce_loss ? gscale : p.grad_output[j];
-            const f32x4_t sv = *reinterpret_cast<const f32x4_t*>(p.stats + 4 * j);
-            lse2 = sv[0] * kLog2e + log2_hw(sv[1]);
-            if (p.grad_entropy) {  // dH/dz_v = p_v (E_p[z] - z_v), E_p[z] = lse - H
-              gH = p.grad_entropy[j];
-              ez = lse2 * kLn2 - p.entropy[j];
+            g = p.reduce_loss ? gscale : go[b];
+            lse2 = sv[b][0] * kLog2e + log2_hw(sv[b][1]);
+            if (ENT) {  // dH/dz_v = p_v (E_p[z] - z_v), E_p[z] = lse - H
+              gH = gh[b];
+              ez = lse2 * kLn2 - hv[b];
             }
           } else {
-            bad = true;
+            g = __builtin_nanf("");
           }
         }
       }
       const float goff = g * (p.eps / (float)p.Vg);
-      const float gt = g * (1.0f - p.eps);
-      // Offsets relative to this lane's first row keep the per-element tests
-      // in 32-bit compares against constants.
-      const int64_t vrow0 = i0 + wr * 128 + 4 * (lane >> 5);  // chunk-local row of r = 0
-      const int64_t tr64 = t - p.v0 - p.c0 - vrow0;
-      const int trel = (live && tr64 >= 0 && tr64 < 128) ? (int)tr64 : -1;
-      const int64_t lim64 = p.vc_valid - vrow0;
-      const int lim = lim64 > 128 ? 128 : (lim64 < 0 ? 0 : (int)lim64);
-      const float fill = bad ? __builtin_nanf("") : 0.0f;
+      const int jl = wc * WN + b * 32 + (lane & 31);
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < NA; ++a)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float val[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int off = a * 32 + 8 * q + e;
             const float z = acc[a][b][4 * q + e];
-            float x = exp2_hw(__builtin_fmaf(z, kLog2e, -lse2)) * __builtin_fmaf(gH, ez - z, g) - goff;
-            x = (off == trel) ? x - gt : x;
-            val[e] = (live && off < lim) ? x : fill;
+            const float ex = exp2_hw(__builtin_fmaf(z, kLog2e, -lse2));
+            float x = ENT ? ex * __builtin_fmaf(gH, ez - z, g) - goff : ex * g - goff;
+            if (!full) x = (a * 32 + 8 * q + e < lim) ? x : 0.0f;
+            val[e] = x;
           }
           const uint32_t w01 = pack_bf16x2(val[0], val[1]), w23 = pack_bf16x2(val[2], val[3]);
-          const int jl = wc * WN + b * 32 + (lane & 31);
           const int vl = wr * 128 + 4 * (lane >> 5) + a * 32 + 8 * q;
           *reinterpret_cast<u32x2_t LDS_AS*>(st + jl * kDzLd + vl) = u32x2_t{w01, w23};
         }
+      // The target's element also gets -(1 - eps) g: only a lane whose target
+      // lies in this wave's rows (rarely any) recomputes that one value and
+      // overwrites it (its own earlier LDS write, so program order suffices).
+      const int64_t tr64 = t - p.v0 - p.c0 - vrow0;
+      if (live && tr64 >= 0 && tr64 < 128 && ((tr64 >> 2) & 1) == 0 && tr64 < lim) {
+        const int tl = (int)tr64;
+        const int ra = tl >> 5, rr = ((tl >> 3) & 3) * 4 + (tl & 3);
+        float z = 0.0f;
+#pragma unroll
+        for (int a = 0; a < NA; ++a) {
+          float x = acc[a][b][0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) x = (rr == r) ? acc[a][b][r] : x;
+          z = (ra == a) ? x : z;
+        }
+        const float ex = exp2_hw(__builtin_fmaf(z, kLog2e, -lse2));
+        const float x = (ENT ? ex * __builtin_fmaf(gH, ez - z, g) - goff : ex * g - goff) -
+                        g * (1.0f - p.eps);
+        st[jl * kDzLd + wr * 128 + 4 * (lane >> 5) + tl] = to_bf16(x);
+      }
     }
     __syncthreads();
     // 256 token rows x 32 chunks of 16 B; 512 threads, consecutive threads
@@ -702,15 +807,30 @@ struct MergeParams {
   float* partial;  // shard mode: (M, 4) = (m, d, sum z, z_t or 0) instead of loss/stats
 };
 
+// ENT: the partials carry the entropy accumulator too (and the entropy is written).
+template <bool ENT>
 __global__ __launch_bounds__(256) void lce_merge_kernel(MergeParams p) {
-  __shared__ LseEntState sh[8][32];
+  using S = typename std::conditional<ENT, LseEntState, LseState>::type;
+  __shared__ S sh[8][32];
   const int tl = threadIdx.x & 31, grp = threadIdx.x >> 5;
   const int64_t j = (int64_t)blockIdx.x * 32 + tl;
-  LseEntState st = {kNegInf, 0.0f, 0.0f, 0.0f};
+  S st;
+  st.m = kNegInf;
+  st.d = 0.0f;
+  st.s = 0.0f;
+  if constexpr (ENT) st.w = 0.0f;
   if (j < p.M) {
+    // tiles in a fixed order (group grp takes every 8th); unrolled so that
+    // the loads of several tiles are in flight at once
+#pragma unroll 8
     for (int64_t vt = grp; vt < p.n_vt; vt += 8) {
       const int64_t o = vt * p.Mp + j;
-      lse_merge(st, LseEntState{p.pm[o], p.pd[o], p.ps[o], p.pw[o]});
+      S q;
+      q.m = p.pm[o];
+      q.d = p.pd[o];
+      q.s = p.ps[o];
+      if constexpr (ENT) q.w = p.pw[o];
+      lse_merge(st, q);
     }
   }
   sh[grp][tl] = st;
@@ -733,7 +853,7 @@ __global__ __launch_bounds__(256) void lce_merge_kernel(MergeParams p) {
     if (p.entropy) p.entropy[j] = 0.0f;
     return;
   }
-  if (p.entropy) p.entropy[j] = entropy_of(st.d, st.w);
+  if constexpr (ENT) p.entropy[j] = entropy_of(st.d, st.w);
   const bool t_ok = t >= 0 && t < p.V;
   const float zt = t_ok ? p.zt[j] : __builtin_nanf("");
   const float mean = st.s / (float)p.V;
@@ -807,13 +927,25 @@ hipError_t launch_lce_forward(const LcePlan& plan, const LceFwdArgs& a, hipStrea
 
   Operand P{W, plan.H, plan.V, plan.H};
   Operand Q{X, plan.H, plan.M, plan.H};
-  EpiLse::Params ep{pm, pd, ps, pw, zt, a.targets, plan.M, plan.V, plan.Mp, a.ignore_idx, a.v0};
-  hipError_t e = run_gemm<EpiLse, false, false>(P, Q, plan.V, plan.Mp, plan.H, ep, stream);
+  hipError_t e;
+  if (a.entropy) {
+    EpiLseT<true>::Params ep{pm, pd, ps, pw, zt, a.targets, plan.M, plan.V, plan.Mp,
+                             a.ignore_idx, a.v0};
+    e = run_gemm<EpiLseT<true>, false, false>(P, Q, plan.V, plan.Mp, plan.H, ep, stream);
+  } else {
+    EpiLseT<false>::Params ep{pm, pd, ps, pw, zt, a.targets, plan.M, plan.V, plan.Mp,
+                              a.ignore_idx, a.v0};
+    e = run_gemm<EpiLseT<false>, false, false>(P, Q, plan.V, plan.Mp, plan.H, ep, stream);
+  }
   if (e != hipSuccess) return e;
   MergeParams mp{pm, pd, ps, pw, zt, a.targets, plan.M, plan.Mp, plan.V, plan.n_vtiles,
                  a.ignore_idx, a.eps, a.loss_tok, a.stats, a.entropy, a.v0, a.partial};
-  hipLaunchKernelGGL(lce_merge_kernel, dim3((unsigned)((plan.M + 31) / 32)), dim3(256), 0, stream,
-                     mp);
+  if (a.entropy)
+    hipLaunchKernelGGL(lce_merge_kernel<true>, dim3((unsigned)((plan.M + 31) / 32)), dim3(256), 0,
+                       stream, mp);
+  else
+    hipLaunchKernelGGL(lce_merge_kernel<false>, dim3((unsigned)((plan.M + 31) / 32)), dim3(256), 0,
+                       stream, mp);
   return hipGetLastError();
 }
 
@@ -843,10 +975,18 @@ hipError_t launch_lce_backward(const LcePlan& plan, const LceBwdArgs& a, hipStre
     {
       Operand P{Wc, plan.H, vc, plan.H};
       Operand Q{X, plan.H, plan.M, plan.H};
-      EpiDz::Params ep{dz, plan.ldz, c0, vc, a.stats, a.targets, a.grad_output, a.n_valid,
-                       a.entropy, a.grad_entropy, a.eps, a.reduce_loss, a.ignore_idx, plan.M,
-                       plan.V, a.v0, a.Vg};
-      hipError_t e = run_gemm<EpiDz, false, false>(P, Q, vc, plan.Mp, plan.H, ep, stream);
+      hipError_t e;
+      if (a.grad_entropy) {
+        EpiDzT<true>::Params ep{dz, plan.ldz, c0, vc, a.stats, a.targets, a.grad_output,
+                                a.n_valid, a.entropy, a.grad_entropy, a.eps, a.reduce_loss,
+                                a.ignore_idx, plan.M, plan.V, a.v0, a.Vg};
+        e = run_gemm<EpiDzT<true>, false, false>(P, Q, vc, plan.Mp, plan.H, ep, stream);
+      } else {
+        EpiDzT<false>::Params ep{dz, plan.ldz, c0, vc, a.stats, a.targets, a.grad_output,
+                                 a.n_valid, nullptr, nullptr, a.eps, a.reduce_loss,
+                                 a.ignore_idx, plan.M, plan.V, a.v0, a.Vg};
+        e = run_gemm<EpiDzT<false>, false, false>(P, Q, vc, plan.Mp, plan.H, ep, stream);
+      }
       if (e != hipSuccess) return e;
     }
     // dW rows of the chunk: (hidden x vocabulary), K = tokens; X (h contiguous
