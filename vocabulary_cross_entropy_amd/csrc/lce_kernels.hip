@@ -442,6 +442,23 @@ __device__ __forceinline__ float max16(const f32x16_t& v) {
   return fmaxf(fmaxf(m[0], m[2]), fmaxf(m[1], m[3]));
 }
 
+// Register (a, r) = (tl / 32, 4 ((tl / 8) % 4) + tl % 4) of a lane's column
+// b, for a row offset tl of that lane (bit 2 clear), without a dynamic
+// register index: a running select that reads one accumulator at a time
+// (used only by the rare lanes that hold a target, so it is kept out of the
+// register budget of the common path).
+__device__ __forceinline__ float pick(const f32x16_t (&acc)[NA][NB], int b, int tl) {
+  const int want = (tl >> 5) * 16 + ((tl >> 3) & 3) * 4 + (tl & 3);
+  float z = 0.0f;
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) z = (want == a * 16 + r) ? acc[a][b][r] : z;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return z;
+}
+
 template <bool ENT>
 struct EpiLseT {
   struct Params {
@@ -497,72 +514,50 @@ struct EpiLseT {
     const bool full = p.V - (i0 + wr * 128) >= 128;
     const int64_t lim64 = p.V - vbase;
     const int lim = lim64 > 128 ? 128 : (lim64 < 0 ? 0 : (int)lim64);
-    float mx[NB], d[NB], s[NB], w[NB];
+    // one token column at a time (the scheduling barriers keep the columns
+    // apart, so the accumulator copies of one column are live at once)
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
+      float mx;
       if (full) {
-        mx[b] = fmaxf(fmaxf(max16(acc[0][b]), max16(acc[1][b])),
-                      fmaxf(max16(acc[2][b]), max16(acc[3][b])));
+        mx = fmaxf(fmaxf(max16(acc[0][b]), max16(acc[1][b])),
+                   fmaxf(max16(acc[2][b]), max16(acc[3][b])));
       } else {
-        float m = kNegInf;
+        mx = kNegInf;
 #pragma unroll
         for (int a = 0; a < NA; ++a)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (a * 32 + 8 * (r >> 2) + (r & 3) < lim) m = fmaxf(m, acc[a][b][r]);
-        mx[b] = m;
+            if (a * 32 + 8 * (r >> 2) + (r & 3) < lim) mx = fmaxf(mx, acc[a][b][r]);
       }
-    }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) mx[b] = fmaxf(mx[b], __shfl_xor(mx[b], 32, 64));
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const float mL = ((mx[b] == kNegInf) ? 0.0f : mx[b]) * kLog2e;
-      d[b] = 0.0f;
-      s[b] = 0.0f;
-      w[b] = 0.0f;
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mL = ((mx == kNegInf) ? 0.0f : mx) * kLog2e;
+      float d = 0.0f, sz = 0.0f, w = 0.0f;
 #pragma unroll
       for (int a = 0; a < NA; ++a) {
         if (full)
-          sums<false>(acc[a][b], a, mL, lim, d[b], s[b], w[b]);
+          sums<false>(acc[a][b], a, mL, lim, d, sz, w);
         else
-          sums<true>(acc[a][b], a, mL, lim, d[b], s[b], w[b]);
+          sums<true>(acc[a][b], a, mL, lim, d, sz, w);
+        __builtin_amdgcn_sched_barrier(0);  // one block's temporaries at a time
       }
-    }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      d[b] += __shfl_xor(d[b], 32, 64);
-      s[b] += __shfl_xor(s[b], 32, 64);
-      if (ENT) w[b] += __shfl_xor(w[b], 32, 64);
-    }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
+      d += __shfl_xor(d, 32, 64);
+      sz += __shfl_xor(sz, 32, 64);
+      if (ENT) w += __shfl_xor(w, 32, 64);
       // Target logit: only a lane whose token's target lies in this wave's
-      // rows (rarely any) picks it, with a two-level select (row block a,
-      // then register r): no dynamic register index.
+      // rows (rarely any) picks it.
       const int64_t j = j0 + wc * WN + b * 32 + (lane & 31);
       {
         const int64_t t = tg[b];
         const int64_t tl64 = t - p.v0 - vbase;
         const bool inr = t != p.ignore_idx && tl64 >= 0 && tl64 < 128 && ((tl64 >> 2) & 1) == 0;
-        if (inr) {
-          const int tl = (int)tl64;
-          const int ra = tl >> 5, rr = ((tl >> 3) & 3) * 4 + (tl & 3);
-          float zt = 0.0f;
-#pragma unroll
-          for (int a = 0; a < NA; ++a) {
-            float x = acc[a][b][0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) x = (rr == r) ? acc[a][b][r] : x;
-            zt = (ra == a) ? x : zt;
-          }
-          p.zt[j] = zt;
-        }
+        if (inr) p.zt[j] = pick(acc, b, (int)tl64);
       }
       if (lane < 32) {
         float* e = sh + (((wr * NWC + wc) * NB + b) * 32 + lane) * 4;
-        *reinterpret_cast<f32x4_t*>(e) = f32x4_t{mx[b], d[b], s[b], w[b]};
+        *reinterpret_cast<f32x4_t*>(e) = f32x4_t{mx, d, sz, w};
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
     // the wavefront of the first vocabulary half merges the second half's state
@@ -696,15 +691,7 @@ struct EpiDzT {
       const int64_t tr64 = t - p.v0 - p.c0 - vrow0;
       if (live && tr64 >= 0 && tr64 < 128 && ((tr64 >> 2) & 1) == 0 && tr64 < lim) {
         const int tl = (int)tr64;
-        const int ra = tl >> 5, rr = ((tl >> 3) & 3) * 4 + (tl & 3);
-        float z = 0.0f;
-#pragma unroll
-        for (int a = 0; a < NA; ++a) {
-          float x = acc[a][b][0];
-#pragma unroll
-          for (int r = 1; r < 16; ++r) x = (rr == r) ? acc[a][b][r] : x;
-          z = (ra == a) ? x : z;
-        }
+        const float z = pick(acc, b, tl);
         const float ex = exp2_hw(__builtin_fmaf(z, kLog2e, -lse2));
         const float x = (ENT ? ex * __builtin_fmaf(gH, ez - z, g) - goff : ex * g - goff) -
                         g * (1.0f - p.eps);
