@@ -329,16 +329,17 @@ __device__ __forceinline__ void loop_slice(LoopState& S, const SliceLoader<PD>& 
 //   row i = i0 + 128 wr + 32 a + 8 (r / 4) + 4 (lane / 32) + r % 4
 //   col j = j0 + 128 wc + 32 b + lane % 32
 // for wavefront (wr, wc) = (wave / 2, wave % 2).
+// One output tile: tile number b of the problem (P, Q, K), then the epilogue.
 // MASK: K is not a multiple of 2 BK (or is 0): k is masked on every read.
 template <class Epi, bool PD, bool QD, bool MASK>
-__global__ __launch_bounds__(NT, 1) void gemm_kernel(Operand P, Operand Q, int64_t K, int n_ti,
-                                                     int n_tj, typename Epi::Params ep) {
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[kSmemElems];
+__device__ __forceinline__ void gemm_tile(const Operand& P, const Operand& Q, int64_t K, int bid,
+                                          int n_ti, int n_tj, const typename Epi::Params& ep,
+                                          uint16_t* smem) {
   uint16_t LDS_AS* const sp = (uint16_t LDS_AS*)smem;  // P stages: sp + s * BM * BK
   uint16_t LDS_AS* const sq = sp + 2 * BM * BK;         // Q stages: sq + s * BN * BK
 
   int ti, tj;
-  tile_of(blockIdx.x, n_ti, n_tj, &ti, &tj);
+  tile_of(bid, n_ti, n_tj, &ti, &tj);
   const int64_t i0 = (int64_t)ti * BM, j0 = (int64_t)tj * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave / NWC, wc = wave % NWC;
@@ -400,6 +401,33 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(Operand P, Operand Q, int64
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
   Epi::apply(ep, S.acc, i0, j0, wr, wc, lane, smem);
+}
+
+template <class Epi, bool PD, bool QD, bool MASK>
+__global__ __launch_bounds__(NT, 1) void gemm_kernel(Operand P, Operand Q, int64_t K, int n_ti,
+                                                     int n_tj, typename Epi::Params ep) {
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[kSmemElems];
+  gemm_tile<Epi, PD, QD, MASK>(P, Q, K, blockIdx.x, n_ti, n_tj, ep, smem);
+}
+
+// Two independent problems in one grid, the first one's tiles first: the
+// backward's dX and dW GEMMs of a chunk (both read only that chunk's dZ), so
+// that the short grid of one fills the last wave of the other.
+struct GemmProblem {
+  Operand P, Q;
+  int64_t K;
+  int n_ti, n_tj;
+};
+
+template <class EA, bool PA, bool QA, bool MA, class EB, bool PB, bool QB, bool MB>
+__global__ __launch_bounds__(NT, 1) void gemm2_kernel(GemmProblem A, typename EA::Params ea,
+                                                      GemmProblem B, typename EB::Params eb) {
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[kSmemElems];
+  const int na = A.n_ti * A.n_tj;
+  if ((int)blockIdx.x < na)
+    gemm_tile<EA, PA, QA, MA>(A.P, A.Q, A.K, blockIdx.x, A.n_ti, A.n_tj, ea, smem);
+  else
+    gemm_tile<EB, PB, QB, MB>(B.P, B.Q, B.K, blockIdx.x - na, B.n_ti, B.n_tj, eb, smem);
 }
 
 // ---- epilogues ------------------------------------------------------------------
@@ -868,6 +896,34 @@ hipError_t run_gemm(const Operand& P, const Operand& Q, int64_t rows, int64_t co
   return hipGetLastError();
 }
 
+inline bool needs_mask(int64_t K) { return K % (2 * BK) != 0 || K == 0; }
+
+template <class EA, bool PA, bool QA, bool MA, class EB, bool PB, bool QB, bool MB>
+hipError_t launch2(const GemmProblem& A, const typename EA::Params& ea, const GemmProblem& B,
+                   const typename EB::Params& eb, int64_t n, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm2_kernel<EA, PA, QA, MA, EB, PB, QB, MB>), dim3((unsigned)n), dim3(NT),
+                     0, stream, A, ea, B, eb);
+  return hipGetLastError();
+}
+
+// Problem A (rows x cols, K) and problem B in one launch, A's tiles first.
+template <class EA, bool PA, bool QA, class EB, bool PB, bool QB>
+hipError_t run_gemm2(const Operand& PAo, const Operand& QAo, int64_t rowsA, int64_t colsA,
+                     int64_t KA, const typename EA::Params& ea, const Operand& PBo,
+                     const Operand& QBo, int64_t rowsB, int64_t colsB, int64_t KB,
+                     const typename EB::Params& eb, hipStream_t stream) {
+  GemmProblem A{PAo, QAo, KA, (int)((rowsA + BM - 1) / BM), (int)((colsA + BN - 1) / BN)};
+  GemmProblem B{PBo, QBo, KB, (int)((rowsB + BM - 1) / BM), (int)((colsB + BN - 1) / BN)};
+  const int64_t n = (int64_t)A.n_ti * A.n_tj + (int64_t)B.n_ti * B.n_tj;
+  if (n <= 0) return hipSuccess;
+  if (n > INT32_MAX / 2) return hipErrorInvalidValue;
+  const bool ma = needs_mask(KA), mb = needs_mask(KB);
+  if (!ma && !mb) return launch2<EA, PA, QA, false, EB, PB, QB, false>(A, ea, B, eb, n, stream);
+  if (!ma && mb) return launch2<EA, PA, QA, false, EB, PB, QB, true>(A, ea, B, eb, n, stream);
+  if (ma && !mb) return launch2<EA, PA, QA, true, EB, PB, QB, false>(A, ea, B, eb, n, stream);
+  return launch2<EA, PA, QA, true, EB, PB, QB, true>(A, ea, B, eb, n, stream);
+}
+
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
@@ -976,23 +1032,21 @@ hipError_t launch_lce_backward(const LcePlan& plan, const LceBwdArgs& a, hipStre
       }
       if (e != hipSuccess) return e;
     }
-    // dW rows of the chunk: (hidden x vocabulary), K = tokens; X (h contiguous
-    // per token) and dZ (v contiguous per token) are both read dim-contiguous
-    {
-      Operand P{X, plan.H, plan.H, plan.M};
-      Operand Q{dz, plan.ldz, vc, plan.M};
-      EpiDw::Params ep{static_cast<uint16_t*>(a.dW), plan.H, c0, vc};
-      hipError_t e = run_gemm<EpiDw, true, true>(P, Q, plan.H, vc, plan.M, ep, stream);
-      if (e != hipSuccess) return e;
-    }
     // dX += dZ_c W_c: (hidden x tokens), K = vocabulary of the chunk; W_c is
-    // read dim-contiguous (h contiguous per vocabulary row), dZ K-contiguous
+    // read dim-contiguous (h contiguous per vocabulary row), dZ K-contiguous.
+    // dW rows of the chunk: (hidden x vocabulary), K = tokens; X (h contiguous
+    // per token) and dZ (v contiguous per token) are both read dim-contiguous.
+    // One launch, dX's (longer) tiles first.
     {
-      Operand P{Wc, plan.H, plan.H, vc};
-      Operand Q{dz, plan.ldz, plan.M, vc};
+      Operand PX{Wc, plan.H, plan.H, vc};
+      Operand QX{dz, plan.ldz, plan.M, vc};
       const int mode = (c > 0 ? 1 : 0) | (c + 1 == plan.n_chunks ? 2 : 0);
-      EpiDx::Params ep{dxacc, static_cast<uint16_t*>(a.dX), plan.H, plan.M, mode};
-      hipError_t e = run_gemm<EpiDx, true, false>(P, Q, plan.H, plan.M, vc, ep, stream);
+      EpiDx::Params ex{dxacc, static_cast<uint16_t*>(a.dX), plan.H, plan.M, mode};
+      Operand PW{X, plan.H, plan.H, plan.M};
+      Operand QW{dz, plan.ldz, vc, plan.M};
+      EpiDw::Params ew{static_cast<uint16_t*>(a.dW), plan.H, c0, vc};
+      hipError_t e = run_gemm2<EpiDx, true, false, EpiDw, true, true>(
+          PX, QX, plan.H, plan.M, vc, ex, PW, QW, plan.H, vc, plan.M, ew, stream);
       if (e != hipSuccess) return e;
     }
   }
