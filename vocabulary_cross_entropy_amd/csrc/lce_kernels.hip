@@ -462,12 +462,12 @@ struct EpiF32 {
 // Tree reductions of one accumulator block (16 values): short dependency
 // chains, since one wavefront per SIMD has no other wave to fill the gaps.
 __device__ __forceinline__ float max16(const f32x16_t& v) {
-  float m[8];
+  // three-input maxima (v_max3_f32): 5 + 2 + 1 instructions
+  float m[6];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) m[i] = fmaxf(v[i], v[i + 8]);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) m[i] = fmaxf(m[i], m[i + 4]);
-  return fmaxf(fmaxf(m[0], m[2]), fmaxf(m[1], m[3]));
+  for (int i = 0; i < 5; ++i) m[i] = fmaxf(fmaxf(v[3 * i], v[3 * i + 1]), v[3 * i + 2]);
+  m[5] = v[15];
+  return fmaxf(fmaxf(fmaxf(m[0], m[1]), m[2]), fmaxf(fmaxf(m[3], m[4]), m[5]));
 }
 
 // Register (a, r) = (tl / 32, 4 ((tl / 8) % 4) + tl % 4) of a lane's column
