@@ -118,17 +118,24 @@ def bench_logits(case, steps: int, warmup: int):
     )
 
 
-def bench_linear(case, steps: int, warmup: int):
+def bench_linear(case, steps: int, warmup: int, f32: bool = False):
+    """The linear form's forward + backward steps; with ``f32`` the FP32-input
+    entry points (FP32 X, W, dX, dW)."""
     import torch
     import vocabulary_cross_entropy_amd as vce
     from vocabulary_cross_entropy_amd import accounting
 
     dev = torch.device("cuda:0")
-    X, W = _bf16_dev(case.X, dev), _bf16_dev(case.W, dev)
+    if f32:
+        X, W = torch.from_numpy(case.X).to(dev), torch.from_numpy(case.W).to(dev)
+    else:
+        X, W = _bf16_dev(case.X, dev), _bf16_dev(case.W, dev)
     t = torch.from_numpy(case.targets).to(dev)
     go = torch.ones(1, device=dev)
     M, H, V = case.M, case.H, case.V
-    ws = vce.lce_workspace(M, H, V, dev)
+    ws = vce.lce_workspace(M, H, V, dev, f32)
+    fwd = vce.lce_forward_f32 if f32 else vce.lce_forward
+    bwd = vce.lce_backward_f32 if f32 else vce.lce_backward
     loss = torch.empty(M, device=dev)
     mean = torch.empty((), device=dev)
     stats = torch.empty((M, 4), device=dev)
@@ -139,10 +146,10 @@ def bench_linear(case, steps: int, warmup: int):
 
     def step(ev_f=None, ev_b=None):
         if ev_f: ev_f[0].record()
-        vce.lce_forward(X, W, t, eps, True, workspace=ws, out=out)
+        fwd(X, W, t, eps, True, workspace=ws, out=out)
         if ev_f: ev_f[1].record()
         if ev_b: ev_b[0].record()
-        vce.lce_backward(X, W, t, stats, nv, go, eps, True, workspace=ws, dX=dX, dW=dW)
+        bwd(X, W, t, stats, nv, go, eps, True, workspace=ws, dX=dX, dW=dW)
         if ev_b: ev_b[1].record()
 
     for _ in range(warmup):
@@ -164,6 +171,19 @@ def bench_linear(case, steps: int, warmup: int):
     ms_step = total_ms / steps
     avg_f, avg_b = sum(fwd_ms) / steps, sum(bwd_ms) / steps
     peak = accounting.BF16_MFMA_PEAK_TFLOPS
+    if f32:
+        # FP32 products as three BF16 products: the matrix cores do three
+        # times the nominal 8 M H V flops (plus the split of X and W per call)
+        fb = f_fb / (ms_step * 1e-3) / 1e12
+        return dict(
+            workload=case.name, M=M, H=H, V=V, ms_per_step=ms_step,
+            tokens_per_s=M * steps / (total_ms * 1e-3),
+            fwd_ms_median=statistics.median(fwd_ms), bwd_ms_median=statistics.median(bwd_ms),
+            fb_tflops_fp32_equivalent=fb,
+            fb_frac_of_fp32_mfma_peak=fb / accounting.FP32_MFMA_PEAK_TFLOPS,
+            fb_bf16_mfma_tflops=3 * fb, fb_frac_of_bf16_mfma_peak=3 * fb / peak,
+            workspace_MiB=ws.numel() / 2 ** 20,
+        )
     return dict(
         workload=case.name, M=M, H=H, V=V, ms_per_step=ms_step,
         tokens_per_s=M * steps / (total_ms * 1e-3),
@@ -337,6 +357,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-shard", action="store_true",
                     help="skip the one-shard-of-eight vocabulary-sharded runs")
+    ap.add_argument("--no-f32", action="store_true",
+                    help="skip the FP32-input run of the linear form")
     ap.add_argument("--only", choices=["logits", "linear"], default=None,
                     help="run one form only (for profiling)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -385,6 +407,15 @@ def main():
                                                      min(args.warmup, 3))
             print(f"[bench] linear CE, one shard of 8: "
                   f"{sharded['linear']['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
+        del lcase
+        if not args.no_f32:
+            print("[bench] generating the FP32 linear workload M=4096 H=4096 V=131072",
+                  file=sys.stderr, flush=True)
+            lin["fp32_inputs"] = bench_linear(wl.linear_4k_f32(), max(3, min(args.steps, 5)),
+                                              min(args.warmup, 2), f32=True)
+            print(f"[bench] linear CE, FP32 inputs: "
+                  f"{lin['fp32_inputs']['ms_per_step']:.3f} ms/step", file=sys.stderr,
+                  flush=True)
     if res is None:
         print(json.dumps({"linear_ce": lin}))
         return

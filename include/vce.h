@@ -245,6 +245,39 @@ int lce_backward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * FP32 inputs to the linear form (the cross-entropy API page, Description:
+ * BF16 or FP32 input, FP32 loss and gradient computation).  X (M, H) and W
+ * (V, H) are FP32, row-major, contiguous, 16-byte aligned, H a multiple of 8.
+ * The matrix cores take each operand as two BF16 planes, x = hi + lo with
+ * hi = bf16(x) and lo = bf16(x - hi) (round to nearest even: hi + lo is x to
+ * within 2^-16 of its size), and every product as hi*hi + hi*lo + lo*hi with
+ * FP32 accumulation: each product is off by at most about 3 * 2^-16 of its
+ * size, for three times the BF16 matrix-core work.  The gradient dZ is split
+ * the same way before the dX and dW products.
+ *
+ *  lce_workspace_size_f32: bytes of workspace for an (M, H, V) problem (the
+ *    BF16 planes of X and W, 4 (M + V) H bytes, plus what the BF16 form
+ *    needs, with dZ in two planes); 0 for invalid sizes.
+ *  lce_forward_f32: as lce_forward (all outputs FP32, same layouts).
+ *  lce_backward_f32: as lce_backward, with dX (M, H) and dW (V, H) FP32,
+ *    overwritten.  Each call splits X and W again (the workspace need not
+ *    survive from the forward).
+ */
+size_t lce_workspace_size_f32(int64_t M, int64_t H, int64_t V);
+
+int lce_forward_f32(const float* X, const float* W, int64_t M, int64_t H, int64_t V,
+                    const int64_t* targets, float label_smoothing, int reduce_loss,
+                    int64_t ignore_idx, float* loss_tok, float* loss_mean, float* stats,
+                    int32_t* n_valid, float* entropy, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+int lce_backward_f32(const float* X, const float* W, int64_t M, int64_t H, int64_t V,
+                     const int64_t* targets, const float* stats, const int32_t* n_valid,
+                     const float* grad_output, const float* entropy, const float* grad_entropy,
+                     float label_smoothing, int reduce_loss, int64_t ignore_idx, float* dX,
+                     float* dW, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Vocabulary-sharded linear cross-entropy: the per-shard half of the
  * tensor-parallel forward of the Liger-Kernel PR (Summary: tensor-parallel
  * fused linear cross-entropy; the classifier W sharded by vocabulary rows),

@@ -9,7 +9,7 @@ Liger-Kernel fused linear cross-entropy PR (Summary: classifier GEMM fused
 with NLL/LSE; Backward and Performance methodology: dZ from recomputed
 logits, then dX = dZ W and dW = dZ^T X):
 
-    Z  = X W^T                    (FP64 product of the exact BF16 values)
+    Z  = X W^T                    (FP64 product of the exact BF16 or FP32 values)
     loss, stats = logits cross-entropy of Z   (the C core of this package)
     dZ = g_r (softmax(Z_r) - q_r)             (the C core of this package)
          [+ gH_r dH/dZ_r when an entropy gradient is given]
@@ -31,13 +31,17 @@ def _rows(a: np.ndarray, rows):
 
 
 def _dec(a: np.ndarray) -> np.ndarray:
-    """BF16 bit patterns (uint16) are widened exactly; float64 passes through."""
+    """The exact value of every input: BF16 bit patterns (uint16) and FP32
+    values are widened exactly to float64 (the cross-entropy API page,
+    Description: BF16 or FP32 input); float64 passes through."""
     a = np.asarray(a)
     if a.dtype == np.uint16:
         return bf16_to_f64(a)
+    if a.dtype == np.float32:
+        return a.astype(np.float64)
     if a.dtype == np.float64:
         return a
-    raise TypeError(f"X and W must be BF16 bits (uint16) or float64, got {a.dtype}")
+    raise TypeError(f"X and W must be BF16 bits (uint16), float32 or float64, got {a.dtype}")
 
 
 def logits(X_bits: np.ndarray, W_bits: np.ndarray, rows=None) -> np.ndarray:

@@ -1,12 +1,12 @@
-"""Write the FP64 oracle's per-token results for the two full-size linear
-cross-entropy workloads (M=4096, H=4096, V=131072 and M=16384, H=2304,
-V=256003) to tests/golden/*.npz.
+"""Write the FP64 oracle's per-token results for the full-size linear
+cross-entropy workloads (M=4096, H=4096, V=131072 with BF16 and with FP32
+inputs, and M=16384, H=2304, V=256003) to tests/golden/*.npz.
 
 Calls only the oracle package and the seeded input generators; no value here
 comes from the GPU path.  The stored digest of the inputs lets the tests
 confirm that they regenerated the same bytes.
 
-    python tests/golden/make_linear_golden.py
+    python tests/golden/make_linear_golden.py [linear_4k linear_16k linear_4k_f32]
 """
 import hashlib
 import os
@@ -30,8 +30,10 @@ def digest(case) -> str:
     return h.hexdigest()
 
 
-def main():
-    for fn in (wl.linear_4k, wl.linear_16k):
+def main(names=None):
+    for fn in (wl.linear_4k, wl.linear_16k, wl.linear_4k_f32):
+        if names and fn.__name__ not in names:
+            continue
         t0 = time.time()
         case = fn()
         loss, stats, lse = linear.forward(case.X, case.W, case.targets, case.label_smoothing,
@@ -42,4 +44,4 @@ def main():
 
 
 if __name__ == "__main__":
-    main()
+    main(sys.argv[1:])

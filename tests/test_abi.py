@@ -152,6 +152,55 @@ def test_lce_backward_rejects(L):
     assert call(ent=A, gent=A + 2) == 3
 
 
+def test_lce_workspace_size_f32(L):
+    assert L.lce_workspace_size_f32(-1, 8, 8) == 0
+    assert L.lce_workspace_size_f32(4, 12, 8) == 0
+    M, H, V = 4096, 4096, 131072
+    f32 = L.lce_workspace_size_f32(M, H, V)
+    # BF16 hi and lo planes of X and W (4 (M + V) H bytes) come on top of the
+    # BF16 form's partials, and dZ takes two planes instead of one
+    assert f32 >= 4 * (M + V) * H + L.lce_workspace_size(M, H, V) - M * H * 4
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), 1), (dict(eps=-0.5), 1), (dict(H=12), 7),
+    (dict(X=None), 1), (dict(W=A + 4), 3), (dict(ws=A + 128), 3), (dict(ws_bytes=1), 5),
+    (dict(reduce_loss=2), 1), (dict(stats=A + 8), 3),
+])
+def test_lce_forward_f32_rejects(L, kw, code):
+    a = dict(X=A, W=A, M=64, H=64, V=1000, targets=A, eps=0.0, reduce_loss=1, ignore=-100,
+             loss_tok=A, loss_mean=A, stats=A, n_valid=A, entropy=None, ws=A, ws_bytes=None)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = L.lce_workspace_size_f32(max(a["M"], 0), a["H"], a["V"])
+    assert L.lce_forward_f32(a["X"], a["W"], a["M"], a["H"], a["V"], a["targets"], a["eps"],
+                             a["reduce_loss"], a["ignore"], a["loss_tok"], a["loss_mean"],
+                             a["stats"], a["n_valid"], a["entropy"], a["ws"], a["ws_bytes"],
+                             None) == code
+
+
+def test_lce_backward_f32_rejects(L):
+    ws = L.lce_workspace_size_f32(64, 64, 1000)
+    assert ws > L.lce_workspace_size(64, 64, 1000)
+
+    def call(**kw):
+        a = dict(X=A, W=A, M=64, H=64, V=1000, targets=A, stats=A, n_valid=A, go=A, ent=None,
+                 gent=None, eps=0.0, reduce_loss=1, ignore=-100, dX=A, dW=A, ws=A, ws_bytes=ws)
+        a.update(kw)
+        return L.lce_backward_f32(a["X"], a["W"], a["M"], a["H"], a["V"], a["targets"],
+                                  a["stats"], a["n_valid"], a["go"], a["ent"], a["gent"],
+                                  a["eps"], a["reduce_loss"], a["ignore"], a["dX"], a["dW"],
+                                  a["ws"], a["ws_bytes"], None)
+
+    assert call(dW=None) == 1
+    assert call(dX=A + 4) == 3
+    assert call(dW=A + 8) == 3
+    # the BF16 form's workspace is too small for the FP32 form
+    assert call(ws_bytes=L.lce_workspace_size(64, 64, 1000)) == 5
+    assert call(gent=A) == 1
+    assert call(H=20) == 7
+
+
 def test_gemm_rejects(L):
     g = L.vce_gemm_bf16
 

@@ -140,3 +140,57 @@ def test_sampled_rows_match_full():
     dXc, dWc = linear.backward(X, W, t, g, eps, token_chunk=9)
     np.testing.assert_allclose(dXc, dX, rtol=1e-14, atol=1e-18)
     np.testing.assert_allclose(dWc, dW, rtol=1e-12, atol=1e-15)
+
+
+# --- FP32 inputs ------------------------------------------------------------------
+
+def _case_f32(seed, M, H, V, n_ign=0):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((M, H)).astype(np.float32)
+    W = (rng.standard_normal((V, H)) / np.sqrt(H) * 2.0).astype(np.float32)
+    t = rng.integers(0, V, size=M).astype(np.int64)
+    if n_ign:
+        t[rng.choice(M, n_ign, replace=False)] = IGN
+    return X, W, t
+
+
+@pytest.mark.parametrize("eps", [0.0, 0.2])
+def test_f32_inputs_against_torch_autograd_float64(eps):
+    # FP32 X and W are taken at their exact values: torch float64 autograd on
+    # the widened values gives the same loss, dX and dW (a path that rounded
+    # them to BF16 would be off by ~1e-3 here).
+    X, W, t = _case_f32(31, 10, 24, 53, n_ign=2)
+    Xt = torch.tensor(X.astype(np.float64), requires_grad=True)
+    Wt = torch.tensor(W.astype(np.float64), requires_grad=True)
+    ref = torch.nn.functional.cross_entropy(Xt @ Wt.T, torch.tensor(t), ignore_index=IGN,
+                                            label_smoothing=eps, reduction="sum")
+    ref.backward()
+    loss, _, _ = linear.forward(X, W, t, eps)
+    assert loss.sum() == pytest.approx(ref.item(), rel=1e-12)
+    g = np.where(t == IGN, 0.0, 1.0)
+    dX, dW = linear.backward(X, W, t, g, eps)
+    np.testing.assert_allclose(dX, Xt.grad.numpy(), rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(dW, Wt.grad.numpy(), rtol=1e-11, atol=1e-14)
+
+
+def test_f32_inputs_that_are_bf16_values_match_the_bf16_path():
+    # FP32 arrays holding BF16-representable values give bit-identical results
+    # to the BF16 bit patterns of the same values.
+    Xb, Wb, t = _case(32, 9, 16, 41, n_ign=1, f64=False)
+    Xf = oracle.bf16_to_f64(Xb).astype(np.float32)
+    Wf = oracle.bf16_to_f64(Wb).astype(np.float32)
+    lb, sb, _ = linear.forward(Xb, Wb, t, 0.1)
+    lf, sf, _ = linear.forward(Xf, Wf, t, 0.1)
+    np.testing.assert_array_equal(lf, lb)
+    np.testing.assert_array_equal(sf[t != IGN], sb[t != IGN])
+    g = np.linspace(0.5, 1.5, 9)
+    for a, b in zip(linear.backward(Xf, Wf, t, g, 0.1), linear.backward(Xb, Wb, t, g, 0.1)):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_f32_inputs_pure_python_tiny():
+    X, W, t = _case_f32(33, 3, 5, 6)
+    Z = tiny.matmul_nt(X.astype(np.float64).tolist(), W.astype(np.float64).tolist())
+    loss, _, _ = linear.forward(X, W, t)
+    for r in range(3):
+        assert loss[r] == pytest.approx(tiny.loss_row(Z[r], int(t[r]), 0.0), rel=1e-13)

@@ -16,6 +16,7 @@ from __future__ import annotations
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense BF16 matrix peak (256 CU x 2.4 GHz)
+FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense FP32 matrix peak
 
 
 def ce_bytes(N: int, V: int, elem_bytes: int, n_ignored: int = 0, phase: str = "fb") -> int:

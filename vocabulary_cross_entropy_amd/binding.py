@@ -41,6 +41,11 @@ SIGNATURES = {
                            _VP, _VP, _SZ, _VP]),
     "lce_backward": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _F32, _I32,
                             _I64, _VP, _VP, _VP, _SZ, _VP]),
+    "lce_workspace_size_f32": (_SZ, [_I64, _I64, _I64]),
+    "lce_forward_f32": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _F32, _I32, _I64, _VP, _VP, _VP,
+                               _VP, _VP, _VP, _SZ, _VP]),
+    "lce_backward_f32": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _F32,
+                                _I32, _I64, _VP, _VP, _VP, _SZ, _VP]),
     "lce_forward_shard": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _VP, _SZ,
                                  _VP]),
     "lce_backward_shard": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _VP, _VP,
@@ -293,16 +298,21 @@ def lce_workspace_size(M: int, H: int, V: int) -> int:
     return int(lib().lce_workspace_size(M, H, V))
 
 
-def lce_workspace(M: int, H: int, V: int, device="cuda") -> torch.Tensor:
-    n = lce_workspace_size(M, H, V)
+def lce_workspace_size_f32(M: int, H: int, V: int) -> int:
+    return int(lib().lce_workspace_size_f32(M, H, V))
+
+
+def lce_workspace(M: int, H: int, V: int, device="cuda", f32: bool = False) -> torch.Tensor:
+    """Workspace for the BF16 linear form, or with ``f32`` for the FP32 one."""
+    n = lce_workspace_size_f32(M, H, V) if f32 else lce_workspace_size(M, H, V)
     if n == 0:
         raise ValueError(f"no workspace plan for M={M}, H={H}, V={V}")
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def _check_linear(X, W, targets):
-    if X.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
-        raise TypeError("X and W must be bfloat16")
+def _check_linear(X, W, targets, dtype=torch.bfloat16):
+    if X.dtype != dtype or W.dtype != dtype:
+        raise TypeError(f"X and W must be {dtype}")
     if not (X.is_contiguous() and W.is_contiguous() and targets.is_contiguous()):
         raise ValueError("X, W and targets must be contiguous")
     if X.dim() != 2 or W.dim() != 2 or X.shape[1] != W.shape[1] or targets.numel() != X.shape[0]:
@@ -316,14 +326,29 @@ def lce_forward(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
                 label_smoothing: float = 0.0, reduce_loss: bool = True, ignore_idx: int = -100,
                 *, workspace: torch.Tensor | None = None, stream=None, out=None,
                 with_entropy: bool = False):
-    """Fused linear cross-entropy forward.  Returns (loss_tok, loss_mean, stats, n_valid),
-    plus the per-token entropy with ``with_entropy``."""
-    _check_linear(X, W, targets)
+    """Fused linear cross-entropy forward, BF16 X and W.  Returns (loss_tok,
+    loss_mean, stats, n_valid), plus the per-token entropy with ``with_entropy``."""
+    return _lce_forward(False, X, W, targets, label_smoothing, reduce_loss, ignore_idx,
+                        workspace, stream, out, with_entropy)
+
+
+def lce_forward_f32(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
+                    label_smoothing: float = 0.0, reduce_loss: bool = True,
+                    ignore_idx: int = -100, *, workspace: torch.Tensor | None = None,
+                    stream=None, out=None, with_entropy: bool = False):
+    """As ``lce_forward`` for FP32 X and W (workspace from ``lce_workspace(..., f32=True)``)."""
+    return _lce_forward(True, X, W, targets, label_smoothing, reduce_loss, ignore_idx,
+                        workspace, stream, out, with_entropy)
+
+
+def _lce_forward(f32, X, W, targets, label_smoothing, reduce_loss, ignore_idx, workspace,
+                 stream, out, with_entropy):
+    _check_linear(X, W, targets, torch.float32 if f32 else torch.bfloat16)
     M, H = X.shape
     V = W.shape[0]
     dev = X.device
     if workspace is None:
-        workspace = lce_workspace(M, H, V, dev)
+        workspace = lce_workspace(M, H, V, dev, f32)
     if out is None:
         loss_tok = torch.empty(M, dtype=torch.float32, device=dev)
         stats = torch.empty((M, 4), dtype=torch.float32, device=dev)
@@ -333,11 +358,12 @@ def lce_forward(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
     else:
         loss_tok, loss_mean, stats, n_valid = out[:4]
         ent = out[4] if with_entropy else None
-    rc = lib().lce_forward(_ptr(X), _ptr(W), M, H, V, _ptr(targets), float(label_smoothing),
-                           int(bool(reduce_loss)), int(ignore_idx), _ptr(loss_tok),
-                           _ptr(loss_mean), _ptr(stats), _ptr(n_valid), _ptr(ent),
-                           _ptr(workspace), workspace.numel(), _stream(stream))
-    _check("lce_forward", rc)
+    name = "lce_forward_f32" if f32 else "lce_forward"
+    rc = getattr(lib(), name)(_ptr(X), _ptr(W), M, H, V, _ptr(targets), float(label_smoothing),
+                              int(bool(reduce_loss)), int(ignore_idx), _ptr(loss_tok),
+                              _ptr(loss_mean), _ptr(stats), _ptr(n_valid), _ptr(ent),
+                              _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(name, rc)
     if with_entropy:
         return loss_tok, loss_mean, stats, n_valid, ent
     return loss_tok, loss_mean, stats, n_valid
@@ -352,19 +378,41 @@ def lce_backward(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, stats:
     """Fused linear cross-entropy backward.  Returns (dX, dW), BF16.  With
     ``grad_entropy`` the entropy's gradient is added (``entropy``: the
     forward's entropy output)."""
-    _check_linear(X, W, targets)
+    return _lce_backward(False, X, W, targets, stats, n_valid, grad_output, label_smoothing,
+                         reduce_loss, ignore_idx, workspace, dX, dW, stream, entropy,
+                         grad_entropy)
+
+
+def lce_backward_f32(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
+                     stats: torch.Tensor, n_valid: torch.Tensor | None,
+                     grad_output: torch.Tensor, label_smoothing: float = 0.0,
+                     reduce_loss: bool = True, ignore_idx: int = -100, *,
+                     workspace: torch.Tensor | None = None, dX: torch.Tensor | None = None,
+                     dW: torch.Tensor | None = None, stream=None,
+                     entropy: torch.Tensor | None = None,
+                     grad_entropy: torch.Tensor | None = None):
+    """As ``lce_backward`` for FP32 X and W; (dX, dW) FP32."""
+    return _lce_backward(True, X, W, targets, stats, n_valid, grad_output, label_smoothing,
+                         reduce_loss, ignore_idx, workspace, dX, dW, stream, entropy,
+                         grad_entropy)
+
+
+def _lce_backward(f32, X, W, targets, stats, n_valid, grad_output, label_smoothing,
+                  reduce_loss, ignore_idx, workspace, dX, dW, stream, entropy, grad_entropy):
+    _check_linear(X, W, targets, torch.float32 if f32 else torch.bfloat16)
     M, H = X.shape
     V = W.shape[0]
     if workspace is None:
-        workspace = lce_workspace(M, H, V, X.device)
+        workspace = lce_workspace(M, H, V, X.device, f32)
     dX = torch.empty_like(X) if dX is None else dX
     dW = torch.empty_like(W) if dW is None else dW
-    rc = lib().lce_backward(_ptr(X), _ptr(W), M, H, V, _ptr(targets), _ptr(stats), _ptr(n_valid),
-                            _ptr(grad_output), _ptr(entropy), _ptr(grad_entropy),
-                            float(label_smoothing), int(bool(reduce_loss)), int(ignore_idx),
-                            _ptr(dX), _ptr(dW), _ptr(workspace), workspace.numel(),
-                            _stream(stream))
-    _check("lce_backward", rc)
+    name = "lce_backward_f32" if f32 else "lce_backward"
+    rc = getattr(lib(), name)(_ptr(X), _ptr(W), M, H, V, _ptr(targets), _ptr(stats),
+                              _ptr(n_valid), _ptr(grad_output), _ptr(entropy),
+                              _ptr(grad_entropy), float(label_smoothing),
+                              int(bool(reduce_loss)), int(ignore_idx), _ptr(dX), _ptr(dW),
+                              _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(name, rc)
     return dX, dW
 
 

@@ -331,27 +331,39 @@ __device__ __forceinline__ void loop_slice(LoopState& S, const SliceLoader<PD>& 
 // for wavefront (wr, wc) = (wave / 2, wave % 2).
 // One output tile: tile number b of the problem (P, Q, K), then the epilogue.
 // MASK: K is not a multiple of 2 BK (or is 0): k is masked on every read.
-template <class Epi, bool PD, bool QD, bool MASK>
-__device__ __forceinline__ void gemm_tile(const Operand& P, const Operand& Q, int64_t K, int bid,
-                                          int n_ti, int n_tj, const typename Epi::Params& ep,
-                                          uint16_t* smem) {
-  uint16_t LDS_AS* const sp = (uint16_t LDS_AS*)smem;  // P stages: sp + s * BM * BK
-  uint16_t LDS_AS* const sq = sp + 2 * BM * BK;         // Q stages: sq + s * BN * BK
-
-  int ti, tj;
-  tile_of(bid, n_ti, n_tj, &ti, &tj);
-  const int64_t i0 = (int64_t)ti * BM, j0 = (int64_t)tj * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wr = wave / NWC, wc = wave % NWC;
-
-  LoopState S;
+// Up to three operand pairs whose products one tile sums before its
+// epilogue: C[i][j] = sum_s sum_k P_s(i, k) Q_s(j, k), every pair with the
+// same K.  One pair is the plain GEMM; three carry the FP32-input form, whose
+// operands are each split into two BF16 planes (see split_bf16_kernel).
+template <int NSEG>
+struct Segs {
+  Operand P[NSEG], Q[NSEG];
+  // pair s by value (constant indices only, so the kernel arguments are read
+  // in place and never copied to scratch)
+  __device__ __forceinline__ Operand p(int s) const {
+    Operand r = P[0];
 #pragma unroll
-  for (int a = 0; a < NA; ++a)
+    for (int t = 1; t < NSEG; ++t)
+      if (s == t) r = P[t];
+    return r;
+  }
+  __device__ __forceinline__ Operand q(int s) const {
+    Operand r = Q[0];
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) S.acc[a][b][r] = 0.0f;
+    for (int t = 1; t < NSEG; ++t)
+      if (s == t) r = Q[t];
+    return r;
+  }
+};
 
+// One operand pair's sum over K added to the accumulators in S: loaders,
+// prologue and main loop, then a drain and a barrier, after which both LDS
+// stages are free again (for the next pair or the epilogue).
+template <bool PD, bool QD, bool MASK>
+__device__ __forceinline__ void mainloop(LoopState& S, const Operand& P, const Operand& Q,
+                                         int64_t K, int64_t i0, int64_t j0, int wave, int lane,
+                                         int wr, int wc, uint16_t LDS_AS* sp,
+                                         uint16_t LDS_AS* sq) {
   SliceLoader<PD> lp;
   SliceLoader<QD> lq;
   lp.init(P, i0, wave, lane);
@@ -396,38 +408,68 @@ __device__ __forceinline__ void gemm_tile(const Operand& P, const Operand& Q, in
     loop_slice<0, PD, QD, MASK>(S, lp, lq, sp, sq, k + 1, klast, wr, wc, lane);
   }
   // drain the loads of the slices past the end (zeros, never used) and let
-  // every wave finish with LDS before the epilogue reuses it
+  // every wave finish with LDS before the epilogue (or the next pair) reuses it
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
+}
+
+template <class Epi, bool PD, bool QD, bool MASK, int NSEG>
+__device__ __forceinline__ void gemm_tile(const Segs<NSEG>& G, int64_t K, int bid, int n_ti,
+                                          int n_tj, const typename Epi::Params& ep,
+                                          uint16_t* smem) {
+  uint16_t LDS_AS* const sp = (uint16_t LDS_AS*)smem;  // P stages: sp + s * BM * BK
+  uint16_t LDS_AS* const sq = sp + 2 * BM * BK;         // Q stages: sq + s * BN * BK
+
+  int ti, tj;
+  tile_of(bid, n_ti, n_tj, &ti, &tj);
+  const int64_t i0 = (int64_t)ti * BM, j0 = (int64_t)tj * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave / NWC, wc = wave % NWC;
+
+  LoopState S;
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S.acc[a][b][r] = 0.0f;
+
+  // one copy of the main loop, run once per pair
+#pragma nounroll
+  for (int s = 0; s < NSEG; ++s)
+    mainloop<PD, QD, MASK>(S, G.p(s), G.q(s), K, i0, j0, wave, lane, wr, wc, sp, sq);
   Epi::apply(ep, S.acc, i0, j0, wr, wc, lane, smem);
 }
 
-template <class Epi, bool PD, bool QD, bool MASK>
-__global__ __launch_bounds__(NT, 1) void gemm_kernel(Operand P, Operand Q, int64_t K, int n_ti,
+template <class Epi, bool PD, bool QD, bool MASK, int NSEG>
+__global__ __launch_bounds__(NT, 1) void gemm_kernel(Segs<NSEG> G, int64_t K, int n_ti,
                                                      int n_tj, typename Epi::Params ep) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[kSmemElems];
-  gemm_tile<Epi, PD, QD, MASK>(P, Q, K, blockIdx.x, n_ti, n_tj, ep, smem);
+  gemm_tile<Epi, PD, QD, MASK, NSEG>(G, K, blockIdx.x, n_ti, n_tj, ep, smem);
 }
 
 // Two independent problems in one grid, the first one's tiles first: the
 // backward's dX and dW GEMMs of a chunk (both read only that chunk's dZ), so
 // that the short grid of one fills the last wave of the other.
+template <int NSEG>
 struct GemmProblem {
-  Operand P, Q;
+  Segs<NSEG> G;
   int64_t K;
   int n_ti, n_tj;
 };
 
-template <class EA, bool PA, bool QA, bool MA, class EB, bool PB, bool QB, bool MB>
-__global__ __launch_bounds__(NT, 1) void gemm2_kernel(GemmProblem A, typename EA::Params ea,
-                                                      GemmProblem B, typename EB::Params eb) {
+template <class EA, bool PA, bool QA, bool MA, class EB, bool PB, bool QB, bool MB, int NSEG>
+__global__ __launch_bounds__(NT, 1) void gemm2_kernel(GemmProblem<NSEG> A,
+                                                      typename EA::Params ea,
+                                                      GemmProblem<NSEG> B,
+                                                      typename EB::Params eb) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[kSmemElems];
   const int na = A.n_ti * A.n_tj;
   if ((int)blockIdx.x < na)
-    gemm_tile<EA, PA, QA, MA>(A.P, A.Q, A.K, blockIdx.x, A.n_ti, A.n_tj, ea, smem);
+    gemm_tile<EA, PA, QA, MA, NSEG>(A.G, A.K, blockIdx.x, A.n_ti, A.n_tj, ea, smem);
   else
-    gemm_tile<EB, PB, QB, MB>(B.P, B.Q, B.K, blockIdx.x - na, B.n_ti, B.n_tj, eb, smem);
+    gemm_tile<EB, PB, QB, MB, NSEG>(B.G, B.K, blockIdx.x - na, B.n_ti, B.n_tj, eb, smem);
 }
 
 // ---- epilogues ------------------------------------------------------------------
@@ -624,7 +666,11 @@ struct EpiLseT {
 // consecutive tokens hit distinct banks) and leaves as whole 512-byte token
 // rows, 16 bytes per lane (direct 8-byte stores from the MFMA layout left
 // partial lines: 1.6x the bytes written, measured).
-template <bool ENT>
+// SPLIT (the FP32-input form): dZ leaves as two BF16 planes, hi = bf16(x) at
+// dz and lo = bf16(x - hi) at dz + plane, so hi + lo carries x to about 16
+// significant bits; both planes of 128 tokens fill the stage one plane of
+// 256 tokens fills, so the tile is staged and stored in two halves.
+template <bool ENT, bool SPLIT = false>
 struct EpiDzT {
   struct Params {
     uint16_t* dz;
@@ -639,6 +685,7 @@ struct EpiDzT {
     int reduce_loss;
     int64_t ignore_idx, M, V;
     int64_t v0, Vg;  // W holds vocabulary rows v0 .. v0 + V - 1 of Vg (0, V unless sharded)
+    int64_t plane;   // SPLIT: elements from the hi plane to the lo plane
   };
   __device__ static void apply(const Params& p, f32x16_t (&acc)[NA][NB], int64_t i0, int64_t j0,
                                int wr, int wc, int lane, uint16_t* smem) {
@@ -668,73 +715,137 @@ struct EpiDzT {
     const bool full = p.vc_valid - (i0 + wr * 128) >= 128;
     const int64_t lim64 = p.vc_valid - vrow0;
     const int lim = lim64 > 128 ? 128 : (lim64 < 0 ? 0 : (int)lim64);
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
+    const int tid = threadIdx.x;
+
+    // Terms of token column b.  Rows that give zero (ignored token, padding
+    // column) or NaN (target out of range) are folded into the arithmetic:
+    // g = 0 or NaN, and an exponent pushed to -inf so that exp() is 0 for
+    // every finite logit.
+    struct Tok {
+      int64_t t;
+      float g, lse2, gH, ez;
+      bool live;
+    };
+    auto token = [&](int b) {
       const int64_t j = j0 + wc * WN + b * 32 + (lane & 31);
-      // Rows that give zero (ignored token, padding column) or NaN (target
-      // out of range) are folded into the arithmetic: g = 0 or NaN, and an
-      // exponent pushed to -inf so that exp() is 0 for every finite logit.
-      int64_t t = -1;
-      float g = 0.0f, lse2 = 1e30f;
-      bool live = false;
-      float gH = 0.0f, ez = 0.0f;
+      Tok k{-1, 0.0f, 1e30f, 0.0f, 0.0f, false};
       if (j < p.M) {
-        t = tg[b];
-        if (t != p.ignore_idx) {
-          if (t >= 0 && t < p.Vg) {
-            live = true;
-            g = p.reduce_loss ? gscale : go[b];
-            lse2 = sv[b][0] * kLog2e + log2_hw(sv[b][1]);
+        k.t = tg[b];
+        if (k.t != p.ignore_idx) {
+          if (k.t >= 0 && k.t < p.Vg) {
+            k.live = true;
+            k.g = p.reduce_loss ? gscale : go[b];
+            k.lse2 = sv[b][0] * kLog2e + log2_hw(sv[b][1]);
             if (ENT) {  // dH/dz_v = p_v (E_p[z] - z_v), E_p[z] = lse - H
-              gH = gh[b];
-              ez = lse2 * kLn2 - hv[b];
+              k.gH = gh[b];
+              k.ez = k.lse2 * kLn2 - hv[b];
             }
           } else {
-            g = __builtin_nanf("");
+            k.g = __builtin_nanf("");
           }
         }
       }
-      const float goff = g * (p.eps / (float)p.Vg);
-      const int jl = wc * WN + b * 32 + (lane & 31);
+      return k;
+    };
+    auto value = [&](const Tok& k, float goff, float z) {
+      const float ex = exp2_hw(__builtin_fmaf(z, kLog2e, -k.lse2));
+      return ENT ? ex * __builtin_fmaf(k.gH, k.ez - z, k.g) - goff : ex * k.g - goff;
+    };
+    // The target's element also gets -(1 - eps) g: only a lane whose target
+    // lies in this wave's rows (rarely any) recomputes that one value.
+    auto target_row = [&](const Tok& k) {
+      const int64_t tr64 = k.t - p.v0 - p.c0 - vrow0;
+      return (k.live && tr64 >= 0 && tr64 < 128 && ((tr64 >> 2) & 1) == 0 && tr64 < lim)
+                 ? (int)tr64
+                 : -1;
+    };
+
+    if constexpr (!SPLIT) {
 #pragma unroll
-      for (int a = 0; a < NA; ++a)
+      for (int b = 0; b < NB; ++b) {
+        const Tok k = token(b);
+        const float goff = k.g * (p.eps / (float)p.Vg);
+        const int jl = wc * WN + b * 32 + (lane & 31);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float val[4];
+        for (int a = 0; a < NA; ++a)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float z = acc[a][b][4 * q + e];
-            const float ex = exp2_hw(__builtin_fmaf(z, kLog2e, -lse2));
-            float x = ENT ? ex * __builtin_fmaf(gH, ez - z, g) - goff : ex * g - goff;
-            if (!full) x = (a * 32 + 8 * q + e < lim) ? x : 0.0f;
-            val[e] = x;
+          for (int q = 0; q < 4; ++q) {
+            float val[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float x = value(k, goff, acc[a][b][4 * q + e]);
+              val[e] = (full || a * 32 + 8 * q + e < lim) ? x : 0.0f;
+            }
+            const uint32_t w01 = pack_bf16x2(val[0], val[1]), w23 = pack_bf16x2(val[2], val[3]);
+            const int vl = wr * 128 + 4 * (lane >> 5) + a * 32 + 8 * q;
+            *reinterpret_cast<u32x2_t LDS_AS*>(st + jl * kDzLd + vl) = u32x2_t{w01, w23};
           }
-          const uint32_t w01 = pack_bf16x2(val[0], val[1]), w23 = pack_bf16x2(val[2], val[3]);
-          const int vl = wr * 128 + 4 * (lane >> 5) + a * 32 + 8 * q;
-          *reinterpret_cast<u32x2_t LDS_AS*>(st + jl * kDzLd + vl) = u32x2_t{w01, w23};
+        // overwrite the lane's own earlier LDS write (program order suffices)
+        const int tl = target_row(k);
+        if (tl >= 0) {
+          const float x = value(k, goff, pick(acc, b, tl)) - k.g * (1.0f - p.eps);
+          st[jl * kDzLd + wr * 128 + 4 * (lane >> 5) + tl] = to_bf16(x);
         }
-      // The target's element also gets -(1 - eps) g: only a lane whose target
-      // lies in this wave's rows (rarely any) recomputes that one value and
-      // overwrites it (its own earlier LDS write, so program order suffices).
-      const int64_t tr64 = t - p.v0 - p.c0 - vrow0;
-      if (live && tr64 >= 0 && tr64 < 128 && ((tr64 >> 2) & 1) == 0 && tr64 < lim) {
-        const int tl = (int)tr64;
-        const float z = pick(acc, b, tl);
-        const float ex = exp2_hw(__builtin_fmaf(z, kLog2e, -lse2));
-        const float x = (ENT ? ex * __builtin_fmaf(gH, ez - z, g) - goff : ex * g - goff) -
-                        g * (1.0f - p.eps);
-        st[jl * kDzLd + wr * 128 + 4 * (lane >> 5) + tl] = to_bf16(x);
       }
-    }
-    __syncthreads();
-    // 256 token rows x 32 chunks of 16 B; 512 threads, consecutive threads
-    // take consecutive chunks of a row
-    const int tid = threadIdx.x;
+      __syncthreads();
+      // 256 token rows x 32 chunks of 16 B; 512 threads, consecutive threads
+      // take consecutive chunks of a row
 #pragma unroll 4
-    for (int u = 0; u < (BN * BM / 8) / NT; ++u) {
-      const int idx = u * NT + tid, jl = idx >> 5, ch = idx & 31;
-      const u32x4_t w = *reinterpret_cast<const u32x4_t LDS_AS*>(st + jl * kDzLd + ch * 8);
-      *reinterpret_cast<u32x4_t*>(p.dz + (j0 + jl) * p.ldz + i0 + ch * 8) = w;
+      for (int u = 0; u < (BN * BM / 8) / NT; ++u) {
+        const int idx = u * NT + tid, jl = idx >> 5, ch = idx & 31;
+        const u32x4_t w = *reinterpret_cast<const u32x4_t LDS_AS*>(st + jl * kDzLd + ch * 8);
+        *reinterpret_cast<u32x4_t*>(p.dz + (j0 + jl) * p.ldz + i0 + ch * 8) = w;
+      }
+    } else {
+      uint16_t LDS_AS* const sl = st + 128 * kDzLd;  // lo plane of the half
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        // half h: token columns b = 2h, 2h + 1 of every wave, i.e. tile tokens
+        // wc * 128 + 64 h + [0, 64), staged at rows wc * 64 + [0, 64)
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+          const int b = 2 * h + bb;
+          const Tok k = token(b);
+          const float goff = k.g * (p.eps / (float)p.Vg);
+          const int jl = wc * 64 + bb * 32 + (lane & 31);
+#pragma unroll
+          for (int a = 0; a < NA; ++a)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              float val[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float x = value(k, goff, acc[a][b][4 * q + e]);
+                val[e] = (full || a * 32 + 8 * q + e < lim) ? x : 0.0f;
+              }
+              const uint32_t h01 = pack_bf16x2(val[0], val[1]), h23 = pack_bf16x2(val[2], val[3]);
+              const uint32_t l01 = pack_bf16x2(val[0] - bf16_lo(h01), val[1] - bf16_hi(h01));
+              const uint32_t l23 = pack_bf16x2(val[2] - bf16_lo(h23), val[3] - bf16_hi(h23));
+              const int vl = wr * 128 + 4 * (lane >> 5) + a * 32 + 8 * q;
+              *reinterpret_cast<u32x2_t LDS_AS*>(st + jl * kDzLd + vl) = u32x2_t{h01, h23};
+              *reinterpret_cast<u32x2_t LDS_AS*>(sl + jl * kDzLd + vl) = u32x2_t{l01, l23};
+            }
+          const int tl = target_row(k);
+          if (tl >= 0) {
+            const float x = value(k, goff, pick(acc, b, tl)) - k.g * (1.0f - p.eps);
+            const uint16_t hb = to_bf16(x);
+            const int o = jl * kDzLd + wr * 128 + 4 * (lane >> 5) + tl;
+            st[o] = hb;
+            sl[o] = to_bf16(x - from_bf16(hb));
+          }
+        }
+        __syncthreads();
+        // 2 planes x 128 token rows x 32 chunks of 16 B
+#pragma unroll 4
+        for (int u = 0; u < (2 * 128 * BM / 8) / NT; ++u) {
+          const int idx = u * NT + tid, pl = idx >> 12, jl = (idx >> 5) & 127, ch = idx & 31;
+          const u32x4_t w = *reinterpret_cast<const u32x4_t LDS_AS*>(
+              st + pl * 128 * kDzLd + jl * kDzLd + ch * 8);
+          const int64_t tok = j0 + (jl >> 6) * 128 + 64 * h + (jl & 63);
+          *reinterpret_cast<u32x4_t*>(p.dz + pl * p.plane + tok * p.ldz + i0 + ch * 8) = w;
+        }
+        if (h == 0) __syncthreads();  // the second half reuses the stage
+      }
     }
   }
 };
@@ -769,6 +880,33 @@ struct EpiDw {
 
 // Backward dX: rows = hidden (h), cols = tokens.  mode bit 0: add the FP32
 // accumulator of earlier chunks; bit 1: final chunk, write BF16 dX.
+// dW of a chunk in FP32 (the FP32-input form): rows = hidden, cols = vocabulary.
+struct EpiDwF32 {
+  struct Params {
+    float* dW;
+    int64_t H, c0, vc_valid;
+  };
+  __device__ static void apply(const Params& p, f32x16_t (&acc)[NA][NB], int64_t i0, int64_t j0,
+                               int wr, int wc, int lane, uint16_t*) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int64_t j = j0 + wc * WN + b * 32 + (lane & 31);
+      if (j >= p.vc_valid) continue;
+      float* row = p.dW + (p.c0 + j) * p.H;
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t i = i0 + wr * 128 + a * 32 + 8 * q + 4 * (lane >> 5);
+          if (i < p.H)
+            *reinterpret_cast<f32x4_t*>(row + i) =
+                f32x4_t{acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2],
+                        acc[a][b][4 * q + 3]};
+        }
+    }
+  }
+};
+
 struct EpiDx {
   struct Params {
     float* accbuf;
@@ -879,56 +1017,66 @@ __global__ __launch_bounds__(256) void lce_merge_kernel(MergeParams p) {
 
 // ---- host side ------------------------------------------------------------------
 
-template <class Epi, bool PD, bool QD>
-hipError_t run_gemm(const Operand& P, const Operand& Q, int64_t rows, int64_t cols, int64_t K,
+template <class Epi, bool PD, bool QD, int NSEG>
+hipError_t run_gemm(const Segs<NSEG>& G, int64_t rows, int64_t cols, int64_t K,
                     const typename Epi::Params& ep, hipStream_t stream) {
   const int64_t n_ti = (rows + BM - 1) / BM, n_tj = (cols + BN - 1) / BN;
   const int64_t n = n_ti * n_tj;
   if (n <= 0) return hipSuccess;
   if (n > INT32_MAX / 2) return hipErrorInvalidValue;
-  // both operands have k_limit = K
+  // every operand has k_limit = K
   if (K % (2 * BK) != 0 || K == 0)
-    hipLaunchKernelGGL((gemm_kernel<Epi, PD, QD, true>), dim3((unsigned)n), dim3(NT), 0, stream,
-                       P, Q, K, (int)n_ti, (int)n_tj, ep);
+    hipLaunchKernelGGL((gemm_kernel<Epi, PD, QD, true, NSEG>), dim3((unsigned)n), dim3(NT), 0,
+                       stream, G, K, (int)n_ti, (int)n_tj, ep);
   else
-    hipLaunchKernelGGL((gemm_kernel<Epi, PD, QD, false>), dim3((unsigned)n), dim3(NT), 0, stream,
-                       P, Q, K, (int)n_ti, (int)n_tj, ep);
+    hipLaunchKernelGGL((gemm_kernel<Epi, PD, QD, false, NSEG>), dim3((unsigned)n), dim3(NT), 0,
+                       stream, G, K, (int)n_ti, (int)n_tj, ep);
   return hipGetLastError();
+}
+
+template <class Epi, bool PD, bool QD>
+hipError_t run_gemm(const Operand& P, const Operand& Q, int64_t rows, int64_t cols, int64_t K,
+                    const typename Epi::Params& ep, hipStream_t stream) {
+  return run_gemm<Epi, PD, QD, 1>(Segs<1>{{P}, {Q}}, rows, cols, K, ep, stream);
 }
 
 inline bool needs_mask(int64_t K) { return K % (2 * BK) != 0 || K == 0; }
 
-template <class EA, bool PA, bool QA, bool MA, class EB, bool PB, bool QB, bool MB>
-hipError_t launch2(const GemmProblem& A, const typename EA::Params& ea, const GemmProblem& B,
-                   const typename EB::Params& eb, int64_t n, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm2_kernel<EA, PA, QA, MA, EB, PB, QB, MB>), dim3((unsigned)n), dim3(NT),
-                     0, stream, A, ea, B, eb);
+template <class EA, bool PA, bool QA, bool MA, class EB, bool PB, bool QB, bool MB, int NSEG>
+hipError_t launch2(const GemmProblem<NSEG>& A, const typename EA::Params& ea,
+                   const GemmProblem<NSEG>& B, const typename EB::Params& eb, int64_t n,
+                   hipStream_t stream) {
+  hipLaunchKernelGGL((gemm2_kernel<EA, PA, QA, MA, EB, PB, QB, MB, NSEG>), dim3((unsigned)n),
+                     dim3(NT), 0, stream, A, ea, B, eb);
   return hipGetLastError();
 }
 
 // Problem A (rows x cols, K) and problem B in one launch, A's tiles first.
-template <class EA, bool PA, bool QA, class EB, bool PB, bool QB>
-hipError_t run_gemm2(const Operand& PAo, const Operand& QAo, int64_t rowsA, int64_t colsA,
-                     int64_t KA, const typename EA::Params& ea, const Operand& PBo,
-                     const Operand& QBo, int64_t rowsB, int64_t colsB, int64_t KB,
-                     const typename EB::Params& eb, hipStream_t stream) {
-  GemmProblem A{PAo, QAo, KA, (int)((rowsA + BM - 1) / BM), (int)((colsA + BN - 1) / BN)};
-  GemmProblem B{PBo, QBo, KB, (int)((rowsB + BM - 1) / BM), (int)((colsB + BN - 1) / BN)};
+template <class EA, bool PA, bool QA, class EB, bool PB, bool QB, int NSEG>
+hipError_t run_gemm2(const Segs<NSEG>& GA, int64_t rowsA, int64_t colsA, int64_t KA,
+                     const typename EA::Params& ea, const Segs<NSEG>& GB, int64_t rowsB,
+                     int64_t colsB, int64_t KB, const typename EB::Params& eb,
+                     hipStream_t stream) {
+  GemmProblem<NSEG> A{GA, KA, (int)((rowsA + BM - 1) / BM), (int)((colsA + BN - 1) / BN)};
+  GemmProblem<NSEG> B{GB, KB, (int)((rowsB + BM - 1) / BM), (int)((colsB + BN - 1) / BN)};
   const int64_t n = (int64_t)A.n_ti * A.n_tj + (int64_t)B.n_ti * B.n_tj;
   if (n <= 0) return hipSuccess;
   if (n > INT32_MAX / 2) return hipErrorInvalidValue;
   const bool ma = needs_mask(KA), mb = needs_mask(KB);
-  if (!ma && !mb) return launch2<EA, PA, QA, false, EB, PB, QB, false>(A, ea, B, eb, n, stream);
-  if (!ma && mb) return launch2<EA, PA, QA, false, EB, PB, QB, true>(A, ea, B, eb, n, stream);
-  if (ma && !mb) return launch2<EA, PA, QA, true, EB, PB, QB, false>(A, ea, B, eb, n, stream);
-  return launch2<EA, PA, QA, true, EB, PB, QB, true>(A, ea, B, eb, n, stream);
+  if (!ma && !mb)
+    return launch2<EA, PA, QA, false, EB, PB, QB, false, NSEG>(A, ea, B, eb, n, stream);
+  if (!ma && mb)
+    return launch2<EA, PA, QA, false, EB, PB, QB, true, NSEG>(A, ea, B, eb, n, stream);
+  if (ma && !mb)
+    return launch2<EA, PA, QA, true, EB, PB, QB, false, NSEG>(A, ea, B, eb, n, stream);
+  return launch2<EA, PA, QA, true, EB, PB, QB, true, NSEG>(A, ea, B, eb, n, stream);
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
-bool lce_make_plan(int64_t M, int64_t H, int64_t V, LcePlan* plan) {
+bool lce_make_plan(int64_t M, int64_t H, int64_t V, LcePlan* plan, bool f32) {
   if (M < 0 || H <= 0 || V <= 0 || H % 8 != 0) return false;
   // Every buffer offset a GEMM load forms (256 rows x leading dimension x 2 B)
   // stays below 2^31.
@@ -944,19 +1092,92 @@ bool lce_make_plan(int64_t M, int64_t H, int64_t V, LcePlan* plan) {
   p.chunk = vr < kChunk ? vr : kChunk;
   p.n_chunks = (V + p.chunk - 1) / p.chunk;
   p.ldz = p.chunk;
+  p.f32 = f32;
+  // FP32 inputs: hi and lo planes of X, then of W
+  p.xplane = f32 ? align256((size_t)M * H * 2) : 0;
+  p.wplane = f32 ? align256((size_t)V * H * 2) : 0;
+  p.off_xs = 0;
+  p.off_ws = 2 * p.xplane;
+  const size_t split = 2 * p.xplane + 2 * p.wplane;
   const size_t part = align256((size_t)p.n_vtiles * p.Mp * 4);
-  const size_t fwd = 4 * part + align256((size_t)p.Mp * 4);
-  // backward: dZ of one chunk (Mp x chunk, token-major) and the dX accumulator
+  const size_t fwd = split + 4 * part + align256((size_t)p.Mp * 4);
+  // backward: dZ of one chunk (Mp x chunk, token-major; two planes with FP32
+  // inputs) and the dX accumulator (BF16 output over several chunks only)
   const size_t dz = align256((size_t)p.Mp * p.chunk * 2);
-  const size_t dx = p.n_chunks > 1 ? align256((size_t)p.Mp * H * 4) : 0;
-  p.off_part = 0;
-  p.off_dz = 0;
-  p.off_dx = dz;
+  p.dzplane = f32 ? (int64_t)(dz / 2) : 0;
+  const size_t dx = (!f32 && p.n_chunks > 1) ? align256((size_t)p.Mp * H * 4) : 0;
+  p.off_part = split;
+  p.off_dz = split;
+  p.off_dx = split + (f32 ? 2 : 1) * dz;
   const size_t bwd = p.off_dx + dx;
   p.total = fwd > bwd ? fwd : bwd;
   *plan = p;
   return true;
 }
+
+namespace {
+
+// hi = bf16(x) and lo = bf16(x - hi), both rounded to nearest even; x - hi is
+// exact in FP32, so hi + lo carries x to about 16 significant bits (the
+// FP32-input form runs its GEMMs on these planes: x y ~ xh yh + xh yl + xl yh).
+// n4 groups of four elements; every thread takes up to four groups, a grid
+// stride apart, with their loads in flight together.
+__global__ __launch_bounds__(256) void split_bf16_kernel(const f32x4_t* in, u32x2_t* hi,
+                                                         u32x2_t* lo, int64_t n4) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x; i0 < n4; i0 += 4 * stride) {
+    f32x4_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + u * stride;
+      v[u] = i < n4 ? __builtin_nontemporal_load(in + i) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + u * stride;
+      if (i >= n4) break;
+      const uint32_t h01 = pack_bf16x2(v[u][0], v[u][1]), h23 = pack_bf16x2(v[u][2], v[u][3]);
+      hi[i] = u32x2_t{h01, h23};
+      lo[i] = u32x2_t{pack_bf16x2(v[u][0] - bf16_lo(h01), v[u][1] - bf16_hi(h01)),
+                      pack_bf16x2(v[u][2] - bf16_lo(h23), v[u][3] - bf16_hi(h23))};
+    }
+  }
+}
+
+// Split n FP32 elements (n a multiple of 4) into planes hi and lo.
+hipError_t run_split(const float* in, uint16_t* hi, uint16_t* lo, int64_t n, hipStream_t stream) {
+  const int64_t n4 = n / 4;
+  if (n4 == 0) return hipSuccess;
+  const int64_t want = (n4 + 4 * 256 - 1) / (4 * 256);
+  const unsigned blocks = (unsigned)(want < 8192 ? want : 8192);
+  hipLaunchKernelGGL(split_bf16_kernel, dim3(blocks), dim3(256), 0, stream,
+                     reinterpret_cast<const f32x4_t*>(in), reinterpret_cast<u32x2_t*>(hi),
+                     reinterpret_cast<u32x2_t*>(lo), n4);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+namespace {
+
+// The BF16 planes of FP32 inputs in the workspace, filled from X and W.
+struct SplitOps {
+  const uint16_t *Xh, *Xl, *Wh, *Wl;
+};
+
+SplitOps split_inputs(const LcePlan& plan, const void* X, const void* W, char* ws,
+                      hipStream_t stream, hipError_t* err) {
+  uint16_t* xh = reinterpret_cast<uint16_t*>(ws + plan.off_xs);
+  uint16_t* xl = reinterpret_cast<uint16_t*>(ws + plan.off_xs + plan.xplane);
+  uint16_t* wh = reinterpret_cast<uint16_t*>(ws + plan.off_ws);
+  uint16_t* wl = reinterpret_cast<uint16_t*>(ws + plan.off_ws + plan.wplane);
+  *err = run_split(static_cast<const float*>(X), xh, xl, plan.M * plan.H, stream);
+  if (*err == hipSuccess)
+    *err = run_split(static_cast<const float*>(W), wh, wl, plan.V * plan.H, stream);
+  return SplitOps{xh, xl, wh, wl};
+}
+
+}  // namespace
 
 hipError_t launch_lce_forward(const LcePlan& plan, const LceFwdArgs& a, hipStream_t stream) {
   const size_t part = align256((size_t)plan.n_vtiles * plan.Mp * 4);
@@ -965,20 +1186,32 @@ hipError_t launch_lce_forward(const LcePlan& plan, const LceFwdArgs& a, hipStrea
   float* ps = reinterpret_cast<float*>(a.ws + plan.off_part + 2 * part);
   float* pw = reinterpret_cast<float*>(a.ws + plan.off_part + 3 * part);
   float* zt = reinterpret_cast<float*>(a.ws + plan.off_part + 4 * part);
-  const uint16_t* X = static_cast<const uint16_t*>(a.X);
-  const uint16_t* W = static_cast<const uint16_t*>(a.W);
-
-  Operand P{W, plan.H, plan.V, plan.H};
-  Operand Q{X, plan.H, plan.M, plan.H};
   hipError_t e;
-  if (a.entropy) {
-    EpiLseT<true>::Params ep{pm, pd, ps, pw, zt, a.targets, plan.M, plan.V, plan.Mp,
-                             a.ignore_idx, a.v0};
-    e = run_gemm<EpiLseT<true>, false, false>(P, Q, plan.V, plan.Mp, plan.H, ep, stream);
+  const EpiLseT<true>::Params ept{pm, pd, ps, pw, zt, a.targets, plan.M, plan.V, plan.Mp,
+                                  a.ignore_idx, a.v0};
+  const EpiLseT<false>::Params epf{pm, pd, ps, pw, zt, a.targets, plan.M, plan.V, plan.Mp,
+                                   a.ignore_idx, a.v0};
+  if (!plan.f32) {
+    const uint16_t* X = static_cast<const uint16_t*>(a.X);
+    const uint16_t* W = static_cast<const uint16_t*>(a.W);
+    Operand P{W, plan.H, plan.V, plan.H};
+    Operand Q{X, plan.H, plan.M, plan.H};
+    e = a.entropy
+            ? run_gemm<EpiLseT<true>, false, false>(P, Q, plan.V, plan.Mp, plan.H, ept, stream)
+            : run_gemm<EpiLseT<false>, false, false>(P, Q, plan.V, plan.Mp, plan.H, epf, stream);
   } else {
-    EpiLseT<false>::Params ep{pm, pd, ps, pw, zt, a.targets, plan.M, plan.V, plan.Mp,
-                              a.ignore_idx, a.v0};
-    e = run_gemm<EpiLseT<false>, false, false>(P, Q, plan.V, plan.Mp, plan.H, ep, stream);
+    // Z = Xh Wh^T + Xh Wl^T + Xl Wh^T, one tile summing the three products
+    const SplitOps o = split_inputs(plan, a.X, a.W, a.ws, stream, &e);
+    if (e != hipSuccess) return e;
+    const Segs<3> G{{{o.Wh, plan.H, plan.V, plan.H},
+                     {o.Wl, plan.H, plan.V, plan.H},
+                     {o.Wh, plan.H, plan.V, plan.H}},
+                    {{o.Xh, plan.H, plan.M, plan.H},
+                     {o.Xh, plan.H, plan.M, plan.H},
+                     {o.Xl, plan.H, plan.M, plan.H}}};
+    e = a.entropy
+            ? run_gemm<EpiLseT<true>, false, false, 3>(G, plan.V, plan.Mp, plan.H, ept, stream)
+            : run_gemm<EpiLseT<false>, false, false, 3>(G, plan.V, plan.Mp, plan.H, epf, stream);
   }
   if (e != hipSuccess) return e;
   MergeParams mp{pm, pd, ps, pw, zt, a.targets, plan.M, plan.Mp, plan.V, plan.n_vtiles,
@@ -998,14 +1231,63 @@ __global__ __launch_bounds__(256) void lce_zero_kernel(u32x4_t* out, int64_t n) 
     out[i] = u32x4_t{0u, 0u, 0u, 0u};
 }
 
+namespace {
+
+// The FP32-input backward: per vocabulary chunk, dZ in two BF16 planes from
+// the three-product logits, then dX += dZ W_c and dW_c = dZ^T X each as one
+// tile summing three products of the planes (dZh Wh + dZh Wl + dZl Wh, and
+// likewise with X), FP32 outputs.
+template <bool ENT>
+hipError_t backward_f32(const LcePlan& plan, const LceBwdArgs& a, hipStream_t stream) {
+  hipError_t e;
+  const SplitOps o = split_inputs(plan, a.X, a.W, a.ws, stream, &e);
+  if (e != hipSuccess) return e;
+  uint16_t* dzh = reinterpret_cast<uint16_t*>(a.ws + plan.off_dz);
+  const uint16_t* dzl = dzh + plan.dzplane;
+  const int64_t H = plan.H, M = plan.M;
+  for (int64_t c = 0; c < plan.n_chunks; ++c) {
+    const int64_t c0 = c * plan.chunk;
+    const int64_t vc = (plan.V - c0) < plan.chunk ? (plan.V - c0) : plan.chunk;
+    const uint16_t* Whc = o.Wh + c0 * H;
+    const uint16_t* Wlc = o.Wl + c0 * H;
+    {
+      const Segs<3> G{{{Whc, H, vc, H}, {Wlc, H, vc, H}, {Whc, H, vc, H}},
+                      {{o.Xh, H, M, H}, {o.Xh, H, M, H}, {o.Xl, H, M, H}}};
+      typename EpiDzT<ENT, true>::Params ep{dzh, plan.ldz, c0, vc, a.stats, a.targets,
+                                            a.grad_output, a.n_valid, a.entropy, a.grad_entropy,
+                                            a.eps, a.reduce_loss, a.ignore_idx, M, plan.V,
+                                            a.v0, a.Vg, plan.dzplane};
+      e = run_gemm<EpiDzT<ENT, true>, false, false, 3>(G, vc, plan.Mp, H, ep, stream);
+      if (e != hipSuccess) return e;
+    }
+    {
+      const Segs<3> GX{{{Whc, H, H, vc}, {Wlc, H, H, vc}, {Whc, H, H, vc}},
+                       {{dzh, plan.ldz, M, vc}, {dzh, plan.ldz, M, vc}, {dzl, plan.ldz, M, vc}}};
+      EpiDx::Params ex{static_cast<float*>(a.dX), nullptr, H, M, c > 0 ? 1 : 0};
+      const Segs<3> GW{{{o.Xh, H, H, M}, {o.Xl, H, H, M}, {o.Xh, H, H, M}},
+                       {{dzh, plan.ldz, vc, M}, {dzh, plan.ldz, vc, M}, {dzl, plan.ldz, vc, M}}};
+      EpiDwF32::Params ew{static_cast<float*>(a.dW), H, c0, vc};
+      e = run_gemm2<EpiDx, true, false, EpiDwF32, true, true, 3>(GX, H, M, vc, ex, GW, H, vc, M,
+                                                                 ew, stream);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
 hipError_t launch_lce_backward(const LcePlan& plan, const LceBwdArgs& a, hipStream_t stream) {
   if (plan.M == 0) {  // no token: dW = 0 (H is a multiple of 8, dW 16-byte aligned)
-    const int64_t n = plan.V * plan.H / 8;
+    const int64_t n = plan.V * plan.H / (plan.f32 ? 4 : 8);
     const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
     hipLaunchKernelGGL(lce_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<u32x4_t*>(a.dW), n);
     return hipGetLastError();
   }
+  if (plan.f32)
+    return a.grad_entropy ? backward_f32<true>(plan, a, stream)
+                          : backward_f32<false>(plan, a, stream);
   uint16_t* dz = reinterpret_cast<uint16_t*>(a.ws + plan.off_dz);
   float* dxacc = reinterpret_cast<float*>(a.ws + plan.off_dx);
   const uint16_t* X = static_cast<const uint16_t*>(a.X);
@@ -1045,8 +1327,9 @@ hipError_t launch_lce_backward(const LcePlan& plan, const LceBwdArgs& a, hipStre
       Operand PW{X, plan.H, plan.H, plan.M};
       Operand QW{dz, plan.ldz, vc, plan.M};
       EpiDw::Params ew{static_cast<uint16_t*>(a.dW), plan.H, c0, vc};
-      hipError_t e = run_gemm2<EpiDx, true, false, EpiDw, true, true>(
-          PX, QX, plan.H, plan.M, vc, ex, PW, QW, plan.H, vc, plan.M, ew, stream);
+      hipError_t e = run_gemm2<EpiDx, true, false, EpiDw, true, true, 1>(
+          Segs<1>{{PX}, {QX}}, plan.H, plan.M, vc, ex, Segs<1>{{PW}, {QW}}, plan.H, vc, plan.M,
+          ew, stream);
       if (e != hipSuccess) return e;
     }
   }

@@ -347,16 +347,22 @@ size_t lce_workspace_size(int64_t M, int64_t H, int64_t V) {
   return plan.total;
 }
 
+size_t lce_workspace_size_f32(int64_t M, int64_t H, int64_t V) {
+  vce::LcePlan plan;
+  if (!vce::lce_make_plan(M, H, V, &plan, true)) return 0;
+  return plan.total;
+}
+
 namespace {
 
 int check_lce_common(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
                      const int64_t* targets, float eps, int reduce_loss, void* workspace,
-                     size_t workspace_bytes, vce::LcePlan* plan) {
+                     size_t workspace_bytes, vce::LcePlan* plan, bool f32 = false) {
   if (M < 0 || H <= 0 || V <= 0) return VCE_EINVAL;
   if (!(eps >= 0.0f && eps <= 1.0f)) return VCE_EINVAL;
   if (reduce_loss != 0 && reduce_loss != 1) return VCE_EINVAL;
   if (H % 8 != 0) return VCE_EUNSUPPORTED;
-  if (!vce::lce_make_plan(M, H, V, plan)) return VCE_EUNSUPPORTED;
+  if (!vce::lce_make_plan(M, H, V, plan, f32)) return VCE_EUNSUPPORTED;
   if (M == 0) return VCE_OK;
   if (!X || !W || !targets || !workspace) return VCE_EINVAL;
   if (!aligned(X, 16) || !aligned(W, 16) || !aligned(targets, 8) || !aligned(workspace, 256))
@@ -365,16 +371,14 @@ int check_lce_common(const void* X, const void* W, int64_t M, int64_t H, int64_t
   return VCE_OK;
 }
 
-}  // namespace
-
-int lce_forward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
-                const int64_t* targets, float label_smoothing, int reduce_loss,
-                int64_t ignore_idx, float* loss_tok, float* loss_mean, float* stats,
-                int32_t* n_valid, float* entropy, void* workspace, size_t workspace_bytes,
-                void* stream) {
+int lce_forward_impl(bool f32, const void* X, const void* W, int64_t M, int64_t H, int64_t V,
+                     const int64_t* targets, float label_smoothing, int reduce_loss,
+                     int64_t ignore_idx, float* loss_tok, float* loss_mean, float* stats,
+                     int32_t* n_valid, float* entropy, void* workspace, size_t workspace_bytes,
+                     void* stream) {
   vce::LcePlan plan;
   int rc = check_lce_common(X, W, M, H, V, targets, label_smoothing, reduce_loss, workspace,
-                            workspace_bytes, &plan);
+                            workspace_bytes, &plan, f32);
   if (rc != VCE_OK) return rc;
   if (reduce_loss && (!loss_mean || !n_valid)) return VCE_EINVAL;
   if (M > 0 && (!loss_tok || !stats)) return VCE_EINVAL;
@@ -418,14 +422,14 @@ int lce_forward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
   return rc;
 }
 
-int lce_backward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
-                 const int64_t* targets, const float* stats, const int32_t* n_valid,
-                 const float* grad_output, const float* entropy, const float* grad_entropy,
-                 float label_smoothing, int reduce_loss, int64_t ignore_idx, void* dX, void* dW,
-                 void* workspace, size_t workspace_bytes, void* stream) {
+int lce_backward_impl(bool f32, const void* X, const void* W, int64_t M, int64_t H, int64_t V,
+                      const int64_t* targets, const float* stats, const int32_t* n_valid,
+                      const float* grad_output, const float* entropy, const float* grad_entropy,
+                      float label_smoothing, int reduce_loss, int64_t ignore_idx, void* dX,
+                      void* dW, void* workspace, size_t workspace_bytes, void* stream) {
   vce::LcePlan plan;
   int rc = check_lce_common(X, W, M, H, V, targets, label_smoothing, reduce_loss, workspace,
-                            workspace_bytes, &plan);
+                            workspace_bytes, &plan, f32);
   if (rc != VCE_OK) return rc;
   if (!dW) return VCE_EINVAL;
   if (!aligned(dW, 16)) return VCE_EALIGN;
@@ -455,6 +459,48 @@ int lce_backward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
   a.v0 = 0;
   a.Vg = V;
   return launch_status(vce::launch_lce_backward(plan, a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+int lce_forward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
+                const int64_t* targets, float label_smoothing, int reduce_loss,
+                int64_t ignore_idx, float* loss_tok, float* loss_mean, float* stats,
+                int32_t* n_valid, float* entropy, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  return lce_forward_impl(false, X, W, M, H, V, targets, label_smoothing, reduce_loss,
+                          ignore_idx, loss_tok, loss_mean, stats, n_valid, entropy, workspace,
+                          workspace_bytes, stream);
+}
+
+int lce_forward_f32(const float* X, const float* W, int64_t M, int64_t H, int64_t V,
+                    const int64_t* targets, float label_smoothing, int reduce_loss,
+                    int64_t ignore_idx, float* loss_tok, float* loss_mean, float* stats,
+                    int32_t* n_valid, float* entropy, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return lce_forward_impl(true, X, W, M, H, V, targets, label_smoothing, reduce_loss,
+                          ignore_idx, loss_tok, loss_mean, stats, n_valid, entropy, workspace,
+                          workspace_bytes, stream);
+}
+
+int lce_backward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
+                 const int64_t* targets, const float* stats, const int32_t* n_valid,
+                 const float* grad_output, const float* entropy, const float* grad_entropy,
+                 float label_smoothing, int reduce_loss, int64_t ignore_idx, void* dX, void* dW,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  return lce_backward_impl(false, X, W, M, H, V, targets, stats, n_valid, grad_output, entropy,
+                           grad_entropy, label_smoothing, reduce_loss, ignore_idx, dX, dW,
+                           workspace, workspace_bytes, stream);
+}
+
+int lce_backward_f32(const float* X, const float* W, int64_t M, int64_t H, int64_t V,
+                     const int64_t* targets, const float* stats, const int32_t* n_valid,
+                     const float* grad_output, const float* entropy, const float* grad_entropy,
+                     float label_smoothing, int reduce_loss, int64_t ignore_idx, float* dX,
+                     float* dW, void* workspace, size_t workspace_bytes, void* stream) {
+  return lce_backward_impl(true, X, W, M, H, V, targets, stats, n_valid, grad_output, entropy,
+                           grad_entropy, label_smoothing, reduce_loss, ignore_idx, dX, dW,
+                           workspace, workspace_bytes, stream);
 }
 
 int lce_forward_shard(const void* X, const void* W, int64_t M, int64_t H, int64_t V_local,

@@ -82,9 +82,16 @@ struct LcePlan {
   size_t off_part;     // forward: per-tile partials and target logits
   size_t off_dz, off_dx;  // backward: dZ of one chunk, FP32 dX accumulator
   size_t total;
+  // FP32 inputs: X and W split into BF16 hi and lo planes in the workspace
+  // (lo plane right after its hi plane), dZ in two planes, no accumulator
+  // (dX is FP32 and accumulates in place)
+  bool f32;
+  size_t off_xs, off_ws;  // hi planes of X and W
+  size_t xplane, wplane;  // bytes per plane
+  int64_t dzplane;        // elements from the hi plane of dZ to its lo plane
 };
 
-bool lce_make_plan(int64_t M, int64_t H, int64_t V, LcePlan* plan);
+bool lce_make_plan(int64_t M, int64_t H, int64_t V, LcePlan* plan, bool f32 = false);
 
 struct LceFwdArgs {
   const void* X;

@@ -198,12 +198,14 @@ def make_linear(seed: int, M: int, H: int, V: int, *, ignore_frac: float | None 
                 ignore_count: int | None = None, targets: str = "uniform", zipf_s: float = 1.1,
                 label_smoothing: float = 0.0, reduce_loss: bool = True,
                 grad_output: str = "ones", w_sigma: float | None = None,
-                name: str = "custom") -> LinearCase:
-    """Draw X ~ N(0,1) and W ~ N(0, 1/H) (unless ``w_sigma``), both BF16."""
+                name: str = "custom", fp32: bool = False) -> LinearCase:
+    """Draw X ~ N(0,1) and W ~ N(0, 1/H) (unless ``w_sigma``), both BF16
+    (RNE from the FP32 draw), or with ``fp32`` the FP32 draws themselves."""
     rng = np.random.default_rng(seed)
-    X = f32_to_bf16_bits(_normal_f32(rng, (M, H), 1.0))
+    cast = (lambda a: a) if fp32 else f32_to_bf16_bits
+    X = cast(_normal_f32(rng, (M, H), 1.0))
     ws = (1.0 / np.sqrt(H)) if w_sigma is None else w_sigma
-    W = f32_to_bf16_bits(_normal_f32(rng, (V, H), ws))
+    W = cast(_normal_f32(rng, (V, H), ws))
     if targets == "zipf":
         t = zipf_targets(rng, M, V, zipf_s)
     else:
@@ -251,6 +253,12 @@ def linear_4k() -> LinearCase:
     """X 4096 x 4096, W 131072 x 4096, 3% ignored, eps 0, mean."""
     return make_linear(1004, 4096, 4096, 131072, ignore_frac=0.03, label_smoothing=0.0,
                        reduce_loss=True, name="linear_m4096_h4096_v131072")
+
+
+def linear_4k_f32() -> LinearCase:
+    """linear_4k's shapes and recipe with FP32 X and W (the FP32 draws)."""
+    return make_linear(1004, 4096, 4096, 131072, ignore_frac=0.03, label_smoothing=0.0,
+                       reduce_loss=True, name="linear_f32_m4096_h4096_v131072", fp32=True)
 
 
 def linear_16k() -> LinearCase:
