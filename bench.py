@@ -357,6 +357,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-shard", action="store_true",
                     help="skip the one-shard-of-eight vocabulary-sharded runs")
+    ap.add_argument("--no-other", action="store_true",
+                    help="skip the (B,SQ,V) = (4,1024,32000) logits and the M=16384 H=2304 "
+                         "V=256003 linear workloads")
     ap.add_argument("--no-f32", action="store_true",
                     help="skip the FP32-input run of the linear form")
     ap.add_argument("--only", choices=["logits", "linear"], default=None,
@@ -395,6 +398,20 @@ def main():
         sharded["logits"] = bench_sharded_logits(case, 8, args.steps, min(args.warmup, 5))
         print(f"[bench] logits CE, one shard of 8: {sharded['logits']['ms_per_step']:.3f} ms/step",
               file=sys.stderr, flush=True)
+    other = {}
+    if res is not None and not args.no_other:
+        mcase = wl.medium_logits()
+        r = bench_logits(mcase, args.steps, args.warmup)
+        other[mcase.name] = {
+            "ms_per_step": round(r["ms_per_step"], 4),
+            "tokens_per_s": round(r["tokens_per_s"], 1),
+            "fwd_ms_median": round(r["fwd_ms_median"], 4),
+            "bwd_ms_median": round(r["bwd_ms_median"], 4),
+            "fb_GBs": round(r["fb_GBs"], 1),
+            "fb_frac_of_hbm_peak": round(r["fb_GBs"] / accounting.HBM_PEAK_GBS, 4)}
+        print(f"[bench] logits CE {mcase.name}: {r['ms_per_step']:.3f} ms/step", file=sys.stderr,
+              flush=True)
+        del mcase
     lin = None
     if not args.no_linear and args.only in (None, "linear"):
         print("[bench] generating the linear workload M=4096 H=4096 V=131072", file=sys.stderr,
@@ -408,6 +425,18 @@ def main():
             print(f"[bench] linear CE, one shard of 8: "
                   f"{sharded['linear']['ms_per_step']:.3f} ms/step", file=sys.stderr, flush=True)
         del lcase
+        if not args.no_other:
+            print("[bench] generating the linear workload M=16384 H=2304 V=256003",
+                  file=sys.stderr, flush=True)
+            l5 = bench_linear(wl.linear_16k(), max(3, min(args.steps, 5)), min(args.warmup, 2))
+            other[l5["workload"]] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                     for k, v in l5.items()
+                                     if k in ("ms_per_step", "tokens_per_s", "fwd_ms_median",
+                                              "bwd_ms_median", "fb_tflops", "bwd_tflops",
+                                              "fb_frac_of_peak", "workspace_MiB")}
+            other[l5["workload"]]["fwd_tflops"] = l5["roofline"]["achieved"]
+            print(f"[bench] linear CE {l5['workload']}: {l5['ms_per_step']:.3f} ms/step",
+                  file=sys.stderr, flush=True)
         if not args.no_f32:
             print("[bench] generating the FP32 linear workload M=4096 H=4096 V=131072",
                   file=sys.stderr, flush=True)
@@ -452,6 +481,7 @@ def main():
                    "fb_frac_of_hbm_peak": round(res["fb_GBs"] / peak, 4)},
         "linear_ce": lin,
         "vocab_sharded_one_of_8": sharded or None,
+        "other_configs": other or None,
     }
     print(json.dumps(line))
 

@@ -636,8 +636,10 @@ struct EpiLseT {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int64_t j = j0 + wc * WN + b * 32 + lane;
-        const f32x4_t e0 = *reinterpret_cast<const f32x4_t*>(sh + (((0 * NWC + wc) * NB + b) * 32 + lane) * 4);
-        const f32x4_t e1 = *reinterpret_cast<const f32x4_t*>(sh + (((1 * NWC + wc) * NB + b) * 32 + lane) * 4);
+        const f32x4_t e0 =
+            *reinterpret_cast<const f32x4_t*>(sh + (((0 * NWC + wc) * NB + b) * 32 + lane) * 4);
+        const f32x4_t e1 =
+            *reinterpret_cast<const f32x4_t*>(sh + (((1 * NWC + wc) * NB + b) * 32 + lane) * 4);
         if (j >= p.M) continue;
         if (ENT) {
           LseEntState st{e0[0], e0[1], e0[2], e0[3]};
@@ -819,8 +821,10 @@ struct EpiDzT {
                 val[e] = (full || a * 32 + 8 * q + e < lim) ? x : 0.0f;
               }
               const uint32_t h01 = pack_bf16x2(val[0], val[1]), h23 = pack_bf16x2(val[2], val[3]);
-              const uint32_t l01 = pack_bf16x2(val[0] - bf16_lo(h01), val[1] - bf16_hi(h01));
-              const uint32_t l23 = pack_bf16x2(val[2] - bf16_lo(h23), val[3] - bf16_hi(h23));
+              const uint32_t l01 =
+                  pack_bf16x2(val[0] - bf16_lo(h01), val[1] - bf16_hi(h01));
+              const uint32_t l23 =
+                  pack_bf16x2(val[2] - bf16_lo(h23), val[3] - bf16_hi(h23));
               const int vl = wr * 128 + 4 * (lane >> 5) + a * 32 + 8 * q;
               *reinterpret_cast<u32x2_t LDS_AS*>(st + jl * kDzLd + vl) = u32x2_t{h01, h23};
               *reinterpret_cast<u32x2_t LDS_AS*>(sl + jl * kDzLd + vl) = u32x2_t{l01, l23};
