@@ -24,10 +24,11 @@
 //    three MFMAs (loads issued in one burst after each barrier, as with
 //    direct-to-LDS loads into two stages, left the MFMAs waiting: measured
 //    1150-1200 TFLOP/s against 1470-1600 with the loads taken out).
-//  * One barrier per slice, before its last k-step: it publishes the next
-//    slice's LDS writes and frees the stage just read.  The fragment reads of
-//    the next k-step go out right after the second MFMA of each k-step, in
-//    the order the MFMAs consume them.
+//  * One barrier per slice, two MFMAs into its last k-step (those two keep
+//    the MFMA pipe busy while the wave waits): it publishes the next slice's
+//    LDS writes and frees the stage just read.  The fragment reads of the
+//    next k-step go out right after the second MFMA of each k-step, in the
+//    order the MFMAs consume them.
 //  * Tile order: hardware workgroup ids go round-robin over the 8 XCDs, so
 //    each XCD is given a contiguous range of tiles, walked in bands of 8 row
 //    tiles so the 32 workgroups an XCD runs at once share both operands in
@@ -262,12 +263,14 @@ struct LoopState {
 // Slice k of the main loop (its data in stage k & 1, its first k-step's
 // fragments in FA and FB[0]).  During k-steps 0..2 the wave writes slice
 // k + 1 from register buffer B1 = (k + 1) & 1 to the other stage and refills
-// the buffer with slice k + 3.  The barrier before k-step 3 publishes slice
-// k + 1 (every wave waited for its own writes) and tells that stage k is no
-// longer read (every wave's fragments of k-step 3 are in registers), so the
-// next round of writes may go there.  MFMAs run a-major: P fragment a dies
+// the buffer with slice k + 3.  The barrier early in k-step 3 (after its
+// first two MFMAs, before any read of the other stage) publishes slice k + 1
+// (every wave waited for its own writes) and tells that stage k is no longer
+// read (every wave's fragments of k-step 3 are in registers), so the next
+// round of writes may go there.  MFMAs run a-major: P fragment a dies
 // after MFMA 4 a + 3 and is refilled with the next k-step's right then; the
-// next Q fragments go to the other buffer after MFMA 1.  Waits: the compiler
+// next Q fragments go to the other buffer after MFMA 1 (MFMA 2 in k-step
+// 3, behind the barrier).  Waits: the compiler
 // places s_waitcnt vmcnt before each LDS write (its load was issued 32 loads
 // earlier) and lgkmcnt before the MFMAs that use fresh fragments.
 template <int B1, bool PD, bool QD, bool MASK>
@@ -286,20 +289,25 @@ __device__ __forceinline__ void loop_slice(LoopState& S, const SliceLoader<PD>& 
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const int f = ks & 1;
-    if (ks == 3) {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-    }
 #pragma unroll
     for (int a = 0; a < NA; ++a) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
+        const int m = a * NB + b;
+        // the barrier goes in after two MFMAs of k-step 3 (their operands are
+        // in registers), so the MFMA pipe stays busy while the wave waits for
+        // its last fragment read and for the other waves
+        if (ks == 3 && m == 2) {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+        }
         S.acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(S.FA[a], S.FB[f][b], S.acc[a][b],
                                                               0, 0, 0);
-        const int m = a * NB + b;
-        if (m == 1) {
+        // next k-step's Q fragments (at k-step 3: of the next slice, from the
+        // stage the barrier has just published)
+        if (m == (ks == 3 ? 2 : 1)) {
 #pragma unroll
           for (int r = 0; r < NB; ++r)
             S.FB[f ^ 1][r] = ks < 3 ? frag<QD>(cq, wc * WN + 32 * r, ks + 1, lane)
