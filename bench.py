@@ -42,6 +42,31 @@ def _event_pairs(n):
             for _ in range(n)]
 
 
+def _graph_step_ms(step, steps: int, warmup: int) -> float:
+    """Average time of `step` replayed from a HIP graph captured on a side
+    stream (every call of the library is stream-ordered and capture-safe)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        step()  # warm the side stream once outside the capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e = _event_pairs(1)[0]
+    e[0].record()
+    for _ in range(steps):
+        g.replay()
+    e[1].record()
+    torch.cuda.synchronize()
+    return e[0].elapsed_time(e[1]) / steps
+
+
 def bench_logits(case, steps: int, warmup: int):
     import torch
     import vocabulary_cross_entropy_amd as vce
@@ -88,6 +113,10 @@ def bench_logits(case, steps: int, warmup: int):
     fwd_ms = [a.elapsed_time(b) for a, b in ev_f]
     bwd_ms = [a.elapsed_time(b) for a, b in ev_b]
 
+    # the same step captured once in a HIP graph and replayed: the GPU time of
+    # the step without the host's per-call launch work between kernels
+    graph_ms = _graph_step_ms(step, steps, warmup)
+
     # in-place backward: logits restored before each launch, outside its events
     zin = torch.empty_like(z)
     ip_ms = []
@@ -113,7 +142,7 @@ def bench_logits(case, steps: int, warmup: int):
         bwd_ms_median=statistics.median(bwd_ms), bwd_inplace_ms_median=statistics.median(ip_ms),
         fwd_GBs=b_fwd / (avg_f * 1e-3) / 1e9, bwd_GBs=b_bwd / (avg_b * 1e-3) / 1e9,
         fb_GBs=(b_fwd + b_bwd) / (ms_step * 1e-3) / 1e9,
-        bytes_fwd=b_fwd, bytes_bwd=b_bwd,
+        bytes_fwd=b_fwd, bytes_bwd=b_bwd, graph_ms_per_step=graph_ms,
         bytes_fb_nominal=accounting.ce_bytes_nominal(N, V, es, "fb"),
     )
 
@@ -408,7 +437,8 @@ def main():
             "fwd_ms_median": round(r["fwd_ms_median"], 4),
             "bwd_ms_median": round(r["bwd_ms_median"], 4),
             "fb_GBs": round(r["fb_GBs"], 1),
-            "fb_frac_of_hbm_peak": round(r["fb_GBs"] / accounting.HBM_PEAK_GBS, 4)}
+            "fb_frac_of_hbm_peak": round(r["fb_GBs"] / accounting.HBM_PEAK_GBS, 4),
+            "graph_replay_ms_per_step": round(r["graph_ms_per_step"], 4)}
         print(f"[bench] logits CE {mcase.name}: {r['ms_per_step']:.3f} ms/step", file=sys.stderr,
               flush=True)
         del mcase
@@ -478,7 +508,8 @@ def main():
                    "bwd_inplace_ms_median": round(res["bwd_inplace_ms_median"], 4),
                    "fwd_GBs": round(res["fwd_GBs"], 1), "bwd_GBs": round(res["bwd_GBs"], 1),
                    "fb_GBs": round(res["fb_GBs"], 1),
-                   "fb_frac_of_hbm_peak": round(res["fb_GBs"] / peak, 4)},
+                   "fb_frac_of_hbm_peak": round(res["fb_GBs"] / peak, 4),
+                   "graph_replay_ms_per_step": round(res["graph_ms_per_step"], 4)},
         "linear_ce": lin,
         "vocab_sharded_one_of_8": sharded or None,
         "other_configs": other or None,
