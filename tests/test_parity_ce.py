@@ -121,9 +121,16 @@ def test_sqbv_v128256_bf16_in_place_equals_separate(headline):
 
 
 @pytest.mark.parametrize("V,dtype", [(1, "fp32"), (7, "bf16"), (9, "fp32"), (1001, "bf16"),
-                                     (1003, "fp32"), (4099, "bf16"), (33333, "bf16")])
+                                     (1003, "fp32"), (4099, "bf16"), (33333, "bf16"),
+                                     (16383, "bf16"), (16385, "bf16"), (32767, "bf16"),
+                                     (32769, "bf16"), (8191, "fp32"), (8193, "fp32"),
+                                     (16385, "fp32")])
 def test_ragged_vocab(V, dtype):
     # V not a multiple of the vector width: rows start at every 16-byte phase.
+    # Widths around one pass of the forward's 512 threads (4 loads of 16 B
+    # each: 16384 BF16 or 8192 FP32 elements) and of the backward's 1024
+    # (32768 BF16, 16384 FP32) leave 0, 1 or all-but-one vectors in the last
+    # partial chunk.
     case = wl.make_logits(2000 + V, 3, 5, V, dtype=dtype, sigma=3.0, ignore_count=2,
                           label_smoothing=0.05, reduce_loss=False, grad_output="random")
     _say(f"ragged V={V} {dtype}")

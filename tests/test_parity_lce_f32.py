@@ -105,6 +105,7 @@ def test_f32_small(eps, reduce_loss):
     (520, 136, 9000),      # ragged tokens, K not a multiple of 128, ragged vocabulary
     (257, 2304, 4000),     # the second workload's hidden size
     (700, 264, 70001),     # three vocabulary chunks, the last ragged
+    (300, 128, 65536),     # exactly two full vocabulary chunks
 ])
 def test_f32_shapes(M, H, V):
     case = wl.make_linear(3200 + M, M, H, V, ignore_count=min(5, M - 1), label_smoothing=0.1,
