@@ -18,6 +18,15 @@ the statistics, so this follows the plainest reading:
           I/O Contract; label smoothing spreads eps over all V classes)
   grad    on shard k's columns: g_r (exp(z - m - ln d) - q), q as unsharded.
 
+The optional entropy H = -sum_v p_v ln p_v (the Liger-Kernel PR's tensor-
+parallel forward offers it; Summary: "optional entropy") needs one more local
+statistic, the un-normalised mean log-ratio in bits,
+  w_k = sum_v exp(z_v - m_k) (z_v - m_k) / ln 2,
+moved to the global max like d:  W = sum_k exp(m_k - m) (ln 2 w_k + d_k (m_k - m)),
+  H = ln d - W / d,
+since -sum p ln p = ln d - sum_v exp(z_v - m) (z_v - m) / d.  Its gradient on a
+shard is the unsharded one, g_H p_v (H + ln p_v) with the global statistics.
+
 Plain NumPy in float64, one row at a time where that reads clearest.
 """
 from __future__ import annotations
@@ -55,6 +64,47 @@ def shard_partials(logits_shard: np.ndarray, targets: np.ndarray, vocab_start: i
         out[r, 2] = row.sum()
         c = t[r] - vocab_start
         out[r, 3] = row[c] if 0 <= c < vl else 0.0
+    return out
+
+
+def shard_partials_w(logits_shard: np.ndarray, targets: np.ndarray,
+                     ignore_idx: int = -100) -> np.ndarray:
+    """Local entropy statistic (N,) w_k = sum_v exp(z - m_k)(z - m_k) / ln 2 of
+    one shard (see the module docstring); 0 for ignored rows."""
+    z = _f64(logits_shard).reshape(-1, np.asarray(logits_shard).shape[-1])
+    t = np.asarray(targets, np.int64).reshape(-1)
+    out = np.zeros(z.shape[0])
+    for r in range(z.shape[0]):
+        if t[r] == ignore_idx:
+            continue
+        row = z[r]
+        m = row.max()
+        if not np.isfinite(m):
+            continue
+        e = np.exp(row - m)
+        fin = np.isfinite(row)          # exp(-inf) (-inf) contributes 0
+        out[r] = float(np.sum(e[fin] * (row[fin] - m))) / np.log(2.0)
+    return out
+
+
+def merge_entropy(partials, partials_w, targets: np.ndarray, ignore_idx: int = -100):
+    """Per-row entropy (N,) from every shard's (m_k, d_k) and w_k; 0 for
+    ignored rows."""
+    P = np.stack([np.asarray(p, np.float64) for p in partials])          # (K, N, 4)
+    Wk = np.stack([np.asarray(w, np.float64) for w in partials_w])       # (K, N)
+    t = np.asarray(targets, np.int64).reshape(-1)
+    out = np.zeros(t.size)
+    ln2 = np.log(2.0)
+    for r in range(t.size):
+        if t[r] == ignore_idx:
+            continue
+        mk, dk, wk = P[:, r, 0], P[:, r, 1], Wk[:, r]
+        m = mk.max()
+        live = dk > 0
+        f = np.exp(mk[live] - m)
+        d = float(np.sum(dk[live] * f))
+        W = float(np.sum(f * (ln2 * wk[live] + dk[live] * (mk[live] - m))))
+        out[r] = np.log(d) - W / d
     return out
 
 

@@ -199,3 +199,49 @@ def test_linear_shard_against_pure_python():
             for h in range(4):
                 ref = sum(dZ[r][v] * Xf[r][h] for r in range(3))
                 assert dWk[v - a, h] == pytest.approx(ref, rel=1e-12, abs=1e-14)
+
+
+# --- entropy over shards -----------------------------------------------------------
+
+@pytest.mark.parametrize("k", [1, 2, 5])
+def test_sharded_entropy_equals_unsharded(k):
+    z, t = _case(40 + k, 30, 777, n_ign=4)
+    b = _split(777, k, k + 3)
+    parts = [shard.shard_partials(z[:, a:e], t, a, IGN) for a, e in b]
+    ws = [shard.shard_partials_w(z[:, a:e], t, IGN) for a, e in b]
+    H = shard.merge_entropy(parts, ws, t, IGN)
+    ref = oracle.entropy(z, t, IGN)
+    np.testing.assert_allclose(H, ref, rtol=1e-12, atol=1e-12)
+    assert np.all(H[t == IGN] == 0.0)
+
+
+def test_sharded_entropy_closed_forms():
+    # uniform logits: H = ln V whatever the split; a one-hot-like row (one logit
+    # far above the rest) has H ~ 0; a shard of -inf columns adds nothing
+    V = 96
+    z = np.zeros((3, V))
+    z[1, 7] = 80.0
+    z[2, 64:] = -np.inf
+    t = np.array([0, 1, 2])
+    b = [(0, 40), (40, 64), (64, 96)]
+    parts = [shard.shard_partials(z[:, a:e], t, a, IGN) for a, e in b]
+    ws = [shard.shard_partials_w(z[:, a:e], t, IGN) for a, e in b]
+    H = shard.merge_entropy(parts, ws, t, IGN)
+    assert H[0] == pytest.approx(np.log(V), rel=1e-14)
+    assert abs(H[1]) < 1e-30 + 96 * 80 * np.exp(-80)
+    assert H[2] == pytest.approx(np.log(64), rel=1e-14)
+
+
+def test_sharded_entropy_against_pure_python():
+    z, t = _case(44, 5, 11)
+    b = _split(11, 3, 9)
+    parts = [shard.shard_partials(z[:, a:e], t, a, IGN) for a, e in b]
+    ws = [shard.shard_partials_w(z[:, a:e], t, IGN) for a, e in b]
+    H = shard.merge_entropy(parts, ws, t, IGN)
+    import math
+    for r in range(5):
+        row = list(z[r])
+        mx = max(row)
+        den = sum(math.exp(v - mx) for v in row)
+        h = -sum((math.exp(v - mx) / den) * math.log(math.exp(v - mx) / den) for v in row)
+        assert H[r] == pytest.approx(h, rel=1e-12)
