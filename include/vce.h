@@ -150,10 +150,15 @@ int ce_backward(const void* logits, void* grad, int dtype, int64_t d0, int64_t d
  *    columns; ignored rows hold zeros.  logits, dtype, d0, d1, ls0, ls1,
  *    targets, ts0, ts1, ignore_idx as in ce_forward with V = V_local; targets
  *    are indices into the full vocabulary.  partial: 16-byte aligned.
+ *    partial_w (N) FP32 or NULL: when given, also the shard's entropy
+ *    statistic w_k = sum_v exp(z_v - m_k) (z_v - m_k) / ln 2 (0 for ignored
+ *    rows), for the entropy output of ce_merge_shards (the Liger-Kernel PR's
+ *    tensor-parallel forward offers the entropy, Summary).
  */
 int ce_forward_shard(const void* logits, int dtype, int64_t d0, int64_t d1, int64_t V_local,
                      int64_t ls0, int64_t ls1, const int64_t* targets, int64_t ts0, int64_t ts1,
-                     int64_t vocab_start, int64_t ignore_idx, float* partial, void* stream);
+                     int64_t vocab_start, int64_t ignore_idx, float* partial, float* partial_w,
+                     void* stream);
 
 /*
  *  ce_merge_shards: partials (n_shards, N, 4), the shards' partial outputs
@@ -163,24 +168,31 @@ int ce_forward_shard(const void* logits, int dtype, int64_t d0, int64_t d1, int6
  *    n_valid exactly as ce_forward would for the whole (N, V) logits, the
  *    label smoothing eps / V and the mean logit taken over the full V.  A
  *    target neither ignore_idx nor in [0, V) gives NaN, as in ce_forward.
+ *    entropy (N) FP32 or NULL: when given, the per-row entropy of the full
+ *    row, as ce_forward's, from partials_w (n_shards, N), the shards'
+ *    partial_w outputs in the same order (required then; otherwise unread):
+ *    W = sum_k exp(m_k - m) (ln 2 w_k + d_k (m_k - m)), H = ln d - W / d.
  */
-int ce_merge_shards(const float* partials, int64_t n_shards, int64_t d0, int64_t d1,
-                    const int64_t* targets, int64_t ts0, int64_t ts1, int64_t V,
+int ce_merge_shards(const float* partials, const float* partials_w, int64_t n_shards, int64_t d0,
+                    int64_t d1, const int64_t* targets, int64_t ts0, int64_t ts1, int64_t V,
                     float label_smoothing, int reduce_loss, int64_t ignore_idx, float* loss_tok,
-                    float* loss_mean, float* stats, int32_t* n_valid, void* stream);
+                    float* loss_mean, float* stats, int32_t* n_valid, float* entropy,
+                    void* stream);
 
 /*
  *  ce_backward_shard: ce_backward for the shard's columns of the gradient,
  *    from the merged stats and n_valid of ce_merge_shards: V is the full
  *    vocabulary (vocab_start + V_local <= V), and only the shard holding the
- *    target subtracts (1 - eps) g there.  Other arguments as in ce_backward.
+ *    target subtracts (1 - eps) g there.  entropy, grad_entropy: the merged
+ *    entropy of ce_merge_shards and its upstream gradient, as in ce_backward.
+ *    Other arguments as in ce_backward.
  */
 int ce_backward_shard(const void* logits, void* grad, int dtype, int64_t d0, int64_t d1,
                       int64_t V_local, int64_t ls0, int64_t ls1, const int64_t* targets,
                       int64_t ts0, int64_t ts1, int64_t vocab_start, int64_t V,
                       const float* stats, const int32_t* n_valid, const float* grad_output,
-                      float label_smoothing, int reduce_loss, int64_t ignore_idx,
-                      int overwrite_input, void* stream);
+                      const float* entropy, const float* grad_entropy, float label_smoothing,
+                      int reduce_loss, int64_t ignore_idx, int overwrite_input, void* stream);
 
 /*
  * vce_shift_targets: causal label shift, the optional token shifting of the
@@ -286,26 +298,30 @@ int lce_backward_f32(const float* X, const float* W, int64_t M, int64_t H, int64
  * [vocab_start, vocab_start + V_local) of the full classifier.  The
  * workspace is sized by lce_workspace_size(M, H, V_local).
  *
- *  lce_forward_shard: partial (M, 4) FP32 as in ce_forward_shard, for the
- *    logits X W_local^T, which are never stored.  Other arguments as in
- *    lce_forward.
+ *  lce_forward_shard: partial (M, 4) FP32 and optional partial_w (M) as in
+ *    ce_forward_shard, for the logits X W_local^T, which are never stored.
+ *    Other arguments as in lce_forward.
  */
 int lce_forward_shard(const void* X, const void* W, int64_t M, int64_t H, int64_t V_local,
                       const int64_t* targets, int64_t vocab_start, int64_t ignore_idx,
-                      float* partial, void* workspace, size_t workspace_bytes, void* stream);
+                      float* partial, float* partial_w, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 /*
  *  lce_backward_shard: from the merged stats and n_valid (ce_merge_shards
  *    over every shard, V the full vocabulary), dW_local (V_local, H) of this
  *    shard and this shard's share of dX, dZ_k W_local (M, H): the full dX is
  *    the sum of the shards' shares (the caller's reduction across shards).
- *    BF16 outputs, overwritten.  Other arguments as in lce_backward.
+ *    BF16 outputs, overwritten.  entropy, grad_entropy: the merged entropy
+ *    and its upstream gradient, as in ce_backward_shard.  Other arguments as
+ *    in lce_backward.
  */
 int lce_backward_shard(const void* X, const void* W, int64_t M, int64_t H, int64_t V_local,
                        const int64_t* targets, int64_t vocab_start, int64_t V,
                        const float* stats, const int32_t* n_valid, const float* grad_output,
-                       float label_smoothing, int reduce_loss, int64_t ignore_idx, void* dX,
-                       void* dW, void* workspace, size_t workspace_bytes, void* stream);
+                       const float* entropy, const float* grad_entropy, float label_smoothing,
+                       int reduce_loss, int64_t ignore_idx, void* dX, void* dW, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /*
  * vce_gemm_bf16: the matrix-core building block of the linear form, exported

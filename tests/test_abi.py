@@ -223,15 +223,15 @@ def test_gemm_rejects(L):
 
 
 def fshard(L, logits=A, dtype=1, d0=2, d1=3, V=1000, ls0=3000, ls1=1000, targets=A, ts0=3, ts1=1,
-           v0=0, ignore=-100, partial=A):
+           v0=0, ignore=-100, partial=A, partial_w=None):
     return L.ce_forward_shard(logits, dtype, d0, d1, V, ls0, ls1, targets, ts0, ts1, v0, ignore,
-                              partial, None)
+                              partial, partial_w, None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=3), 2), (dict(V=0), 1), (dict(v0=-1), 1), (dict(v0=(1 << 63) - 10), 1),
     (dict(partial=None), 1), (dict(logits=None), 1), (dict(partial=A + 8), 3),
-    (dict(logits=A + 1), 3), (dict(d0=1 << 20, d1=1 << 12), 1),
+    (dict(logits=A + 1), 3), (dict(d0=1 << 20, d1=1 << 12), 1), (dict(partial_w=A + 2), 3),
 ])
 def test_ce_forward_shard_rejects(L, kw, code):
     assert fshard(L, **kw) == code
@@ -242,9 +242,11 @@ def test_ce_forward_shard_empty_is_a_no_op(L):
 
 
 def merge(L, partials=A, k=4, d0=2, d1=3, targets=A, ts0=3, ts1=1, V=1000, eps=0.0,
-          reduce_loss=0, ignore=-100, loss_tok=A, loss_mean=A, stats=A, n_valid=A):
-    return L.ce_merge_shards(partials, k, d0, d1, targets, ts0, ts1, V, eps, reduce_loss, ignore,
-                             loss_tok, loss_mean, stats, n_valid, None)
+          reduce_loss=0, ignore=-100, loss_tok=A, loss_mean=A, stats=A, n_valid=A,
+          partials_w=None, entropy=None):
+    return L.ce_merge_shards(partials, partials_w, k, d0, d1, targets, ts0, ts1, V, eps,
+                             reduce_loss, ignore, loss_tok, loss_mean, stats, n_valid, entropy,
+                             None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -254,16 +256,19 @@ def merge(L, partials=A, k=4, d0=2, d1=3, targets=A, ts0=3, ts1=1, V=1000, eps=0
     (dict(loss_tok=None), 1), (dict(targets=None), 1),
     (dict(partials=A + 4), 3), (dict(stats=A + 8), 3), (dict(targets=A + 4), 3),
     (dict(k=1 << 40, d0=1 << 15, d1=1 << 15), 1),
+    (dict(entropy=A), 1),                         # entropy without the shards' statistics
+    (dict(entropy=A + 2, partials_w=A), 3), (dict(entropy=A, partials_w=A + 1), 3),
 ])
 def test_ce_merge_shards_rejects(L, kw, code):
     assert merge(L, **kw) == code
 
 
 def bshard(L, logits=A, grad=A + (1 << 30), dtype=1, d0=2, d1=3, VL=1000, ls0=3000, ls1=1000,
-           targets=A, ts0=3, ts1=1, v0=0, V=8000, stats=A, n_valid=A, go=A, eps=0.0,
-           reduce_loss=0, ignore=-100, overwrite=0):
+           targets=A, ts0=3, ts1=1, v0=0, V=8000, stats=A, n_valid=A, go=A, ent=None, gent=None,
+           eps=0.0, reduce_loss=0, ignore=-100, overwrite=0):
     return L.ce_backward_shard(logits, grad, dtype, d0, d1, VL, ls0, ls1, targets, ts0, ts1, v0, V,
-                               stats, n_valid, go, eps, reduce_loss, ignore, overwrite, None)
+                               stats, n_valid, go, ent, gent, eps, reduce_loss, ignore, overwrite,
+                               None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -272,7 +277,7 @@ def bshard(L, logits=A, grad=A + (1 << 30), dtype=1, d0=2, d1=3, VL=1000, ls0=30
     (dict(eps=-1.0), 1), (dict(overwrite=3), 1), (dict(grad=None), 1), (dict(stats=None), 1),
     (dict(go=None), 1), (dict(reduce_loss=1, n_valid=None), 1),
     (dict(overwrite=1), 4), (dict(grad=A + 4096), 4), (dict(grad=A + (1 << 30) + 2), 3),
-    (dict(stats=A + 4), 3),
+    (dict(stats=A + 4), 3), (dict(gent=A), 1), (dict(ent=A, gent=A + 2), 3),
 ])
 def test_ce_backward_shard_rejects(L, kw, code):
     assert bshard(L, **kw) == code
@@ -282,11 +287,11 @@ def test_lce_shard_rejects(L):
     ws = L.lce_workspace_size(64, 64, 1000)
 
     def fwd_(**kw):
-        a = dict(X=A, W=A, M=64, H=64, VL=1000, targets=A, v0=0, ignore=-100, part=A, ws=A,
-                 ws_bytes=ws)
+        a = dict(X=A, W=A, M=64, H=64, VL=1000, targets=A, v0=0, ignore=-100, part=A, pw=None,
+                 ws=A, ws_bytes=ws)
         a.update(kw)
         return L.lce_forward_shard(a["X"], a["W"], a["M"], a["H"], a["VL"], a["targets"], a["v0"],
-                                   a["ignore"], a["part"], a["ws"], a["ws_bytes"], None)
+                                   a["ignore"], a["part"], a["pw"], a["ws"], a["ws_bytes"], None)
 
     assert fwd_(v0=-1) == 1
     assert fwd_(part=None) == 1
@@ -295,15 +300,17 @@ def test_lce_shard_rejects(L):
     assert fwd_(ws_bytes=ws - 1) == 5
     assert fwd_(X=A + 2) == 3
     assert fwd_(M=0, part=None) == 0
+    assert fwd_(pw=A + 1) == 3
 
     def bwd_(**kw):
         a = dict(X=A, W=A, M=64, H=64, VL=1000, targets=A, v0=0, V=4000, stats=A, n_valid=A,
-                 go=A, eps=0.0, reduce_loss=1, ignore=-100, dX=A, dW=A, ws=A, ws_bytes=ws)
+                 go=A, ent=None, gent=None, eps=0.0, reduce_loss=1, ignore=-100, dX=A, dW=A,
+                 ws=A, ws_bytes=ws)
         a.update(kw)
         return L.lce_backward_shard(a["X"], a["W"], a["M"], a["H"], a["VL"], a["targets"],
-                                    a["v0"], a["V"], a["stats"], a["n_valid"], a["go"], a["eps"],
-                                    a["reduce_loss"], a["ignore"], a["dX"], a["dW"], a["ws"],
-                                    a["ws_bytes"], None)
+                                    a["v0"], a["V"], a["stats"], a["n_valid"], a["go"], a["ent"],
+                                    a["gent"], a["eps"], a["reduce_loss"], a["ignore"], a["dX"],
+                                    a["dW"], a["ws"], a["ws_bytes"], None)
 
     assert bwd_(V=999) == 1
     assert bwd_(v0=3001) == 1
@@ -314,6 +321,8 @@ def test_lce_shard_rejects(L):
     assert bwd_(n_valid=A + 2) == 3
     assert bwd_(ws_bytes=ws - 1) == 5
     assert bwd_(eps=2.0) == 1
+    assert bwd_(gent=A) == 1
+    assert bwd_(ent=A + 2, gent=A) == 3
 
 
 def test_shift_targets_rejects(L):

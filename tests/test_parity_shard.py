@@ -339,3 +339,102 @@ def test_linear_empty_batch_zeroes_dW():
     vce.lce_backward_shard(X, W, t, 0, 2 * V, st, nv, go, workspace=ws, dW=dW2)
     torch.cuda.synchronize()
     assert torch.count_nonzero(dW).item() == 0 and torch.count_nonzero(dW2).item() == 0
+
+
+# --- entropy over shards (the optional entropy of the tensor-parallel forward) ---------
+
+def _stack_entropy_logits(case, bounds, zd, t):
+    parts = torch.empty((len(bounds), case.d0, case.d1, 4), dtype=torch.float32, device="cuda")
+    pws = torch.empty((len(bounds), case.d0, case.d1), dtype=torch.float32, device="cuda")
+    shards = [zd[:, :, a:b].contiguous() for a, b in bounds]
+    for k, ((a, b), zk) in enumerate(zip(bounds, shards)):
+        vce.ce_forward_shard(zk, t, a, case.ignore_idx, out=parts[k], with_entropy=True,
+                             out_w=pws[k])
+    return shards, parts, pws
+
+
+@pytest.mark.parametrize("dtype,V,k", [("bf16", 9000, 3), ("fp32", 4099, 4), ("bf16", 128256, 8)])
+def test_sharded_entropy_logits(dtype, V, k):
+    case = wl.make_logits(4100 + k, 4, 64, V, dtype=dtype, sigma=3.0, ignore_count=9,
+                          label_smoothing=0.1, reduce_loss=True)
+    bounds = _bounds(V, k, 17)
+    _say(f"sharded entropy {dtype} V={V} shards={len(bounds)}")
+    zd = to_device(case.logits, dtype)
+    t = torch.from_numpy(case.targets).cuda()
+    shards, parts, pws = _stack_entropy_logits(case, bounds, zd, t)
+    loss, mean, stats, nv, ent = vce.ce_merge_shards(parts, t, V, 0.1, True, case.ignore_idx,
+                                                     partials_w=pws)
+    # the shards' w against the oracle's local statistic
+    N = case.N
+    lg = case.logits.reshape(N, V)
+    valid = case.targets.reshape(-1) != case.ignore_idx
+    for kk, (a, b) in enumerate(bounds):
+        ref_w = oshard.shard_partials_w(lg[:, a:b], case.targets, case.ignore_idx)
+        got_w = pws[kk].cpu().numpy().reshape(-1).astype(np.float64)
+        assert np.all(got_w[~valid] == 0.0)
+        np.testing.assert_allclose(got_w[valid], ref_w[valid], rtol=2e-5, atol=2e-3)
+    # merged entropy against the unsharded oracle, at the loss bar
+    H = ent.cpu().numpy().reshape(-1).astype(np.float64)
+    ref_H = oracle.entropy(case.logits, case.targets, case.ignore_idx)
+    assert_loss_close(H, ref_H)
+    # the gradient with an entropy term: every shard's columns are bitwise the
+    # unsharded backward's from the same merged statistics and entropy
+    gH = (np.random.default_rng(5).standard_normal((case.d0, case.d1)) * 0.7).astype(np.float32)
+    gHd = torch.from_numpy(gH).cuda()
+    go = torch.ones(1, device="cuda")
+    full = vce.ce_backward(zd, t, stats, nv, go, 0.1, True, case.ignore_idx, entropy=ent,
+                           grad_entropy=gHd)
+    for (a, b), zk in zip(bounds, shards):
+        gk = vce.ce_backward_shard(zk, t, a, V, stats, nv, go, 0.1, True, case.ignore_idx,
+                                   entropy=ent, grad_entropy=gHd)
+        assert torch.equal(gk, full[:, :, a:b].contiguous()), (a, b)
+    torch.cuda.synchronize()
+
+
+def test_one_shard_entropy_is_bitwise_the_unsharded_one():
+    case = wl.make_logits(4200, 8, 32, 5003, dtype="bf16", sigma=3.0, ignore_count=7,
+                          label_smoothing=0.0, reduce_loss=False)
+    zd = to_device(case.logits, "bf16")
+    t = torch.from_numpy(case.targets).cuda()
+    part, pw = vce.ce_forward_shard(zd, t, 0, IGN, with_entropy=True)
+    l2, _, s2, _, e2 = vce.ce_merge_shards(part.unsqueeze(0), t, case.V, 0.0, False, IGN,
+                                           partials_w=pw.unsqueeze(0))
+    l1, _, s1, _, e1 = vce.ce_forward(zd, t, 0.0, False, IGN, with_entropy=True)
+    torch.cuda.synchronize()
+    assert torch.equal(e1, e2) and torch.equal(l1, l2) and torch.equal(s1, s2)
+
+
+def test_linear_sharded_entropy():
+    case = wl.make_linear(4300, 300, 192, 6000, ignore_count=9, label_smoothing=0.1,
+                          reduce_loss=True)
+    bounds = [(0, 2500), (2500, 6000)]
+    X = to_device(case.X, "bf16")
+    t = torch.from_numpy(case.targets).cuda()
+    Ws = [to_device(np.ascontiguousarray(case.W[a:b]), "bf16") for a, b in bounds]
+    parts = torch.empty((2, case.M, 4), dtype=torch.float32, device="cuda")
+    pws = torch.empty((2, case.M), dtype=torch.float32, device="cuda")
+    for k, ((a, b), Wk) in enumerate(zip(bounds, Ws)):
+        vce.lce_forward_shard(X, Wk, t, a, IGN, out=parts[k], with_entropy=True, out_w=pws[k])
+    loss, mean, stats, nv, ent = vce.ce_merge_shards(parts, t, case.V, 0.1, True, IGN,
+                                                     partials_w=pws)
+    gH = (np.random.default_rng(6).standard_normal(case.M) * 0.7).astype(np.float32)
+    gHd = torch.from_numpy(gH).cuda()
+    go = torch.ones(1, device="cuda")
+    outs = [vce.lce_backward_shard(X, Wk, t, a, case.V, stats, nv, go, 0.1, True, IGN,
+                                   entropy=ent, grad_entropy=gHd)
+            for (a, b), Wk in zip(bounds, Ws)]
+    torch.cuda.synchronize()
+    valid = case.targets != IGN
+    H = ent.cpu().numpy().reshape(-1).astype(np.float64)
+    ref_H = linear.entropy(case.X, case.W, case.targets, IGN)
+    assert np.all(H[~valid] == 0.0)
+    rel = np.abs(H[valid] - ref_H[valid]) / np.abs(ref_H[valid])
+    assert rel.max() <= LINEAR_LOSS_RTOL, rel.max()
+    g = oracle.row_scale(case.grad_output, case.targets, True, IGN)
+    rdX, rdW = linear.backward(case.X, case.W, case.targets, g, 0.1, IGN,
+                               grad_entropy=gH.astype(np.float64))
+    dX = sum(oracle.bf16_to_f64(to_host_bits(o[0])) for o in outs)
+    dW = np.concatenate([oracle.bf16_to_f64(to_host_bits(o[1])) for o in outs])
+    fx, fw = rel_frobenius(dX, rdX), rel_frobenius(dW, rdW)
+    _say(f"linear sharded entropy: H rel {rel.max():.2e}, dX frob {fx:.2e}, dW frob {fw:.2e}")
+    assert fx <= LINEAR_FROB_RTOL and fw <= LINEAR_FROB_RTOL

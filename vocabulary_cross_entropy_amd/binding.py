@@ -30,11 +30,12 @@ SIGNATURES = {
     "ce_backward": (_I32, [_VP, _VP, _I32, _I64, _I64, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _VP,
                            _VP, _VP, _VP, _F32, _I32, _I64, _I32, _VP]),
     "ce_forward_shard": (_I32, [_VP, _I32, _I64, _I64, _I64, _I64, _I64, _VP, _I64, _I64, _I64,
-                                _I64, _VP, _VP]),
-    "ce_merge_shards": (_I32, [_VP, _I64, _I64, _I64, _VP, _I64, _I64, _I64, _F32, _I32, _I64,
-                               _VP, _VP, _VP, _VP, _VP]),
+                                _I64, _VP, _VP, _VP]),
+    "ce_merge_shards": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _I64, _I64, _I64, _F32, _I32,
+                               _I64, _VP, _VP, _VP, _VP, _VP, _VP]),
     "ce_backward_shard": (_I32, [_VP, _VP, _I32, _I64, _I64, _I64, _I64, _I64, _VP, _I64, _I64,
-                                 _I64, _I64, _VP, _VP, _VP, _F32, _I32, _I64, _I32, _VP]),
+                                 _I64, _I64, _VP, _VP, _VP, _VP, _VP, _F32, _I32, _I64, _I32,
+                                 _VP]),
     "vce_shift_targets": (_I32, [_VP, _I64, _I64, _I64, _I64, _I32, _I64, _VP, _VP]),
     "lce_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "lce_forward": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _F32, _I32, _I64, _VP, _VP, _VP, _VP,
@@ -46,10 +47,10 @@ SIGNATURES = {
                                _VP, _VP, _VP, _SZ, _VP]),
     "lce_backward_f32": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _F32,
                                 _I32, _I64, _VP, _VP, _VP, _SZ, _VP]),
-    "lce_forward_shard": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _VP, _SZ,
-                                 _VP]),
+    "lce_forward_shard": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _VP, _VP,
+                                 _SZ, _VP]),
     "lce_backward_shard": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _VP, _VP,
-                                  _F32, _I32, _I64, _VP, _VP, _VP, _SZ, _VP]),
+                                  _VP, _VP, _F32, _I32, _I64, _VP, _VP, _VP, _SZ, _VP]),
     "vce_gemm_bf16": (_I32, [_VP, _I64, _I32, _VP, _I64, _I32, _I64, _I64, _I64, _VP, _I64, _VP]),
 }
 
@@ -195,28 +196,38 @@ def ce_backward(logits: torch.Tensor, targets: torch.Tensor, stats: torch.Tensor
 
 
 def ce_forward_shard(logits: torch.Tensor, targets: torch.Tensor, vocab_start: int,
-                     ignore_idx: int = -100, *, stream=None, out=None) -> torch.Tensor:
+                     ignore_idx: int = -100, *, stream=None, out=None, with_entropy: bool = False,
+                     out_w=None):
     """Partial statistics (d0, d1, 4) of one vocabulary shard: ``logits`` holds
-    columns vocab_start .. vocab_start + V_local - 1 of the full vocabulary."""
+    columns vocab_start .. vocab_start + V_local - 1 of the full vocabulary.
+    With ``with_entropy`` also the shard's entropy statistic (d0, d1), returned
+    second."""
     logits, targets = _logits3d(logits, targets)
     _need_cuda(logits, targets)
     d0, d1, V = logits.shape
     part = torch.empty((d0, d1, 4), dtype=torch.float32, device=logits.device) if out is None \
         else out
+    pw = None
+    if with_entropy:
+        pw = torch.empty((d0, d1), dtype=torch.float32, device=logits.device) if out_w is None \
+            else out_w
     rc = lib().ce_forward_shard(_ptr(logits), _dtype_code(logits), d0, d1, V, logits.stride(0),
                                 logits.stride(1), _ptr(targets), targets.stride(0),
                                 targets.stride(1), int(vocab_start), int(ignore_idx), _ptr(part),
-                                _stream(stream))
+                                _ptr(pw), _stream(stream))
     _check("ce_forward_shard", rc)
-    return part
+    return (part, pw) if with_entropy else part
 
 
 def ce_merge_shards(partials: torch.Tensor, targets: torch.Tensor, V: int,
                     label_smoothing: float = 0.0, reduce_loss: bool = False,
-                    ignore_idx: int = -100, *, stream=None, out=None):
+                    ignore_idx: int = -100, *, stream=None, out=None,
+                    partials_w: torch.Tensor | None = None, out_entropy=None):
     """Merge stacked shard partials (n_shards, d0, d1, 4) (or (n_shards, N, 4)
     with targets (N)) into (loss_tok, loss_mean, stats, n_valid) over the full
-    vocabulary of V columns, as ce_forward returns them."""
+    vocabulary of V columns, as ce_forward returns them.  With ``partials_w``
+    (the shards' entropy statistics stacked the same way) the per-row entropy
+    is appended."""
     if targets.dim() == 1:
         targets = targets.unsqueeze(0)
     if targets.dtype != torch.int64:
@@ -234,12 +245,21 @@ def ce_merge_shards(partials: torch.Tensor, targets: torch.Tensor, V: int,
         n_valid = torch.empty((), dtype=torch.int32, device=dev) if reduce_loss else None
     else:
         loss_tok, loss_mean, stats, n_valid = out
-    rc = lib().ce_merge_shards(_ptr(partials), partials.shape[0], d0, d1, _ptr(targets),
-                               targets.stride(0), targets.stride(1), int(V),
+    ent = None
+    if partials_w is not None:
+        if not partials_w.is_contiguous() or partials_w.dtype != torch.float32 or \
+                partials_w.numel() != partials.shape[0] * d0 * d1:
+            raise ValueError("partials_w must be contiguous float32 (n_shards, d0, d1)")
+        ent = torch.empty((d0, d1), dtype=torch.float32, device=dev) if out_entropy is None \
+            else out_entropy
+    rc = lib().ce_merge_shards(_ptr(partials), _ptr(partials_w), partials.shape[0], d0, d1,
+                               _ptr(targets), targets.stride(0), targets.stride(1), int(V),
                                float(label_smoothing), int(bool(reduce_loss)), int(ignore_idx),
                                _ptr(loss_tok), _ptr(loss_mean), _ptr(stats), _ptr(n_valid),
-                               _stream(stream))
+                               _ptr(ent), _stream(stream))
     _check("ce_merge_shards", rc)
+    if ent is not None:
+        return loss_tok, loss_mean, stats, n_valid, ent
     return loss_tok, loss_mean, stats, n_valid
 
 
@@ -248,8 +268,10 @@ def ce_backward_shard(logits: torch.Tensor, targets: torch.Tensor, vocab_start: 
                       grad_output: torch.Tensor, label_smoothing: float = 0.0,
                       reduce_loss: bool = False, ignore_idx: int = -100,
                       overwrite_input: bool = False, *, grad: torch.Tensor | None = None,
-                      stream=None):
-    """Gradient of one vocabulary shard's logits from the merged ``stats``."""
+                      stream=None, entropy: torch.Tensor | None = None,
+                      grad_entropy: torch.Tensor | None = None):
+    """Gradient of one vocabulary shard's logits from the merged ``stats``
+    (with ``grad_entropy``, plus the entropy's, ``entropy`` the merged one)."""
     logits, targets = _logits3d(logits, targets)
     _need_cuda(logits, targets, stats, grad_output)
     d0, d1, VL = logits.shape
@@ -264,8 +286,9 @@ def ce_backward_shard(logits: torch.Tensor, targets: torch.Tensor, vocab_start: 
     rc = lib().ce_backward_shard(_ptr(logits), _ptr(grad), _dtype_code(logits), d0, d1, VL,
                                  logits.stride(0), logits.stride(1), _ptr(targets),
                                  targets.stride(0), targets.stride(1), int(vocab_start), int(V),
-                                 _ptr(stats), _ptr(n_valid), _ptr(grad_output),
-                                 float(label_smoothing), int(bool(reduce_loss)), int(ignore_idx),
+                                 _ptr(stats), _ptr(n_valid), _ptr(grad_output), _ptr(entropy),
+                                 _ptr(grad_entropy), float(label_smoothing),
+                                 int(bool(reduce_loss)), int(ignore_idx),
                                  int(bool(overwrite_input)), _stream(stream))
     _check("ce_backward_shard", rc)
     return grad
@@ -418,20 +441,24 @@ def _lce_backward(f32, X, W, targets, stats, n_valid, grad_output, label_smoothi
 
 def lce_forward_shard(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, vocab_start: int,
                       ignore_idx: int = -100, *, workspace: torch.Tensor | None = None,
-                      stream=None, out=None) -> torch.Tensor:
+                      stream=None, out=None, with_entropy: bool = False, out_w=None):
     """Partial statistics (M, 4) of the vocabulary shard W (V_local, H) holding
-    rows vocab_start .. vocab_start + V_local - 1 of the full classifier."""
+    rows vocab_start .. vocab_start + V_local - 1 of the full classifier; with
+    ``with_entropy`` also its entropy statistic (M), returned second."""
     _check_linear(X, W, targets)
     M, H = X.shape
     V = W.shape[0]
     if workspace is None:
         workspace = lce_workspace(M, H, V, X.device)
     part = torch.empty((M, 4), dtype=torch.float32, device=X.device) if out is None else out
+    pw = None
+    if with_entropy:
+        pw = torch.empty(M, dtype=torch.float32, device=X.device) if out_w is None else out_w
     rc = lib().lce_forward_shard(_ptr(X), _ptr(W), M, H, V, _ptr(targets), int(vocab_start),
-                                 int(ignore_idx), _ptr(part), _ptr(workspace), workspace.numel(),
-                                 _stream(stream))
+                                 int(ignore_idx), _ptr(part), _ptr(pw), _ptr(workspace),
+                                 workspace.numel(), _stream(stream))
     _check("lce_forward_shard", rc)
-    return part
+    return (part, pw) if with_entropy else part
 
 
 def lce_backward_shard(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, vocab_start: int,
@@ -439,9 +466,12 @@ def lce_backward_shard(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, 
                        grad_output: torch.Tensor, label_smoothing: float = 0.0,
                        reduce_loss: bool = True, ignore_idx: int = -100, *,
                        workspace: torch.Tensor | None = None, dX: torch.Tensor | None = None,
-                       dW: torch.Tensor | None = None, stream=None):
+                       dW: torch.Tensor | None = None, stream=None,
+                       entropy: torch.Tensor | None = None,
+                       grad_entropy: torch.Tensor | None = None):
     """(dX share, dW) of one vocabulary shard from the merged ``stats``; the
-    shards' dX shares sum to the full dX."""
+    shards' dX shares sum to the full dX.  ``entropy``, ``grad_entropy`` as in
+    ``ce_backward_shard``."""
     _check_linear(X, W, targets)
     M, H = X.shape
     VL = W.shape[0]
@@ -451,6 +481,7 @@ def lce_backward_shard(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, 
     dW = torch.empty_like(W) if dW is None else dW
     rc = lib().lce_backward_shard(_ptr(X), _ptr(W), M, H, VL, _ptr(targets), int(vocab_start),
                                   int(V), _ptr(stats), _ptr(n_valid), _ptr(grad_output),
+                                  _ptr(entropy), _ptr(grad_entropy),
                                   float(label_smoothing), int(bool(reduce_loss)),
                                   int(ignore_idx), _ptr(dX), _ptr(dW), _ptr(workspace),
                                   workspace.numel(), _stream(stream))

@@ -194,6 +194,7 @@ __global__ __launch_bounds__(kFwdThreads) void ce_fwd_kernel(CeFwdParams p) {
     if (tid == 0) {
       if (SHARD) {
         *reinterpret_cast<f32x4_t*>(p.partial + 4 * r) = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        if (ENT) p.partial_w[r] = 0.0f;
       } else {
         p.loss_tok[r] = 0.0f;
         *reinterpret_cast<f32x4_t*>(p.stats + 4 * r) = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -244,8 +245,10 @@ __global__ __launch_bounds__(kFwdThreads) void ce_fwd_kernel(CeFwdParams p) {
   }
   const S tot = block_reduce(st, sh);
   if (SHARD) {
-    if (tid == 0)
+    if (tid == 0) {
       *reinterpret_cast<f32x4_t*>(p.partial + 4 * r) = f32x4_t{tot.m, tot.d, tot.s, zt};
+      if constexpr (ENT) p.partial_w[r] = tot.w;
+    }
     return;
   }
   if (tid == 0) {
@@ -442,7 +445,9 @@ __global__ __launch_bounds__(kBwdThreads) void ce_bwd_kernel(CeBwdParams p) {
 // z_t from the shard holding the target (the others contribute 0); then the
 // loss and the saved statistics as ce_fwd_kernel writes them, with the mean
 // logit and eps / V over the full vocabulary.
+template <bool ENT>
 __global__ __launch_bounds__(256) void ce_merge_shards_kernel(CeMergeParams p) {
+  using S = typename StateOf<ENT>::T;
   const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (r >= p.N) return;
   const int64_t i0 = r / p.d1, i1 = r - i0 * p.d1;
@@ -450,13 +455,23 @@ __global__ __launch_bounds__(256) void ce_merge_shards_kernel(CeMergeParams p) {
   if (t == p.ignore_idx) {
     p.loss_tok[r] = 0.0f;
     *reinterpret_cast<f32x4_t*>(p.stats + 4 * r) = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    if (ENT) p.entropy[r] = 0.0f;
     return;
   }
-  LseState st = {kNegInf, 0.0f, 0.0f};
+  S st;
+  st.m = kNegInf;
+  st.d = 0.0f;
+  st.s = 0.0f;
+  if constexpr (ENT) st.w = 0.0f;
   float zt = 0.0f;
   for (int64_t k = 0; k < p.n_shards; ++k) {
     const f32x4_t q = *reinterpret_cast<const f32x4_t*>(p.partials + (k * p.N + r) * 4);
-    lse_merge(st, LseState{q[0], q[1], q[2]});
+    S b;
+    b.m = q[0];
+    b.d = q[1];
+    b.s = q[2];
+    if constexpr (ENT) b.w = p.partials_w[k * p.N + r];
+    lse_merge(st, b);
     zt += q[3];
   }
   const bool t_ok = t >= 0 && t < p.V;
@@ -465,6 +480,7 @@ __global__ __launch_bounds__(256) void ce_merge_shards_kernel(CeMergeParams p) {
   const float loss = ce_row_loss(st.m, st.d, zt, mean, p.eps);
   p.loss_tok[r] = t_ok ? loss : __builtin_nanf("");
   *reinterpret_cast<f32x4_t*>(p.stats + 4 * r) = f32x4_t{st.m, st.d, zt, mean};
+  if constexpr (ENT) p.entropy[r] = entropy_of(st.d, st.w);
 }
 
 // Causal label shift: out[r] = the target one position later along the
@@ -491,10 +507,15 @@ hipError_t launch_ce_forward(const CeFwdParams& p, int dtype, int64_t N, hipStre
   if (N <= 0) return hipSuccess;
   const dim3 g((unsigned)N), b(kFwdThreads);
   if (p.partial) {
-    if (dtype == 0)
+    const bool ent = p.partial_w != nullptr;
+    if (dtype == 0 && !ent)
       hipLaunchKernelGGL((ce_fwd_kernel<0, false, true>), g, b, 0, stream, p);
-    else
+    else if (dtype == 0)
+      hipLaunchKernelGGL((ce_fwd_kernel<0, true, true>), g, b, 0, stream, p);
+    else if (!ent)
       hipLaunchKernelGGL((ce_fwd_kernel<1, false, true>), g, b, 0, stream, p);
+    else
+      hipLaunchKernelGGL((ce_fwd_kernel<1, true, true>), g, b, 0, stream, p);
     return hipGetLastError();
   }
   const bool ent = p.entropy != nullptr;
@@ -511,8 +532,11 @@ hipError_t launch_ce_forward(const CeFwdParams& p, int dtype, int64_t N, hipStre
 
 hipError_t launch_ce_merge_shards(const CeMergeParams& p, hipStream_t stream) {
   if (p.N <= 0) return hipSuccess;
-  hipLaunchKernelGGL(ce_merge_shards_kernel, dim3((unsigned)((p.N + 255) / 256)), dim3(256), 0,
-                     stream, p);
+  const dim3 g((unsigned)((p.N + 255) / 256)), b(256);
+  if (p.entropy)
+    hipLaunchKernelGGL(ce_merge_shards_kernel<true>, g, b, 0, stream, p);
+  else
+    hipLaunchKernelGGL(ce_merge_shards_kernel<false>, g, b, 0, stream, p);
   return hipGetLastError();
 }
 

@@ -970,6 +970,7 @@ struct MergeParams {
   float* entropy;  // optional
   int64_t v0;      // vocabulary index of W's first row (0 unless sharded)
   float* partial;  // shard mode: (M, 4) = (m, d, sum z, z_t or 0) instead of loss/stats
+  float* partial_w;  // shard mode with ENT: (M) entropy statistic w
 };
 
 // ENT: the partials carry the entropy accumulator too (and the entropy is written).
@@ -1010,6 +1011,7 @@ __global__ __launch_bounds__(256) void lce_merge_kernel(MergeParams p) {
       q = f32x4_t{st.m, st.d, st.s, (c >= 0 && c < p.V) ? p.zt[j] : 0.0f};
     }
     *reinterpret_cast<f32x4_t*>(p.partial + 4 * j) = q;
+    if constexpr (ENT) p.partial_w[j] = t != p.ignore_idx ? st.w : 0.0f;
     return;
   }
   if (t == p.ignore_idx) {
@@ -1199,6 +1201,8 @@ hipError_t launch_lce_forward(const LcePlan& plan, const LceFwdArgs& a, hipStrea
   float* pw = reinterpret_cast<float*>(a.ws + plan.off_part + 3 * part);
   float* zt = reinterpret_cast<float*>(a.ws + plan.off_part + 4 * part);
   hipError_t e;
+  // the entropy accumulator: for the entropy output, or a shard's entropy statistic
+  const bool ent = a.entropy != nullptr || a.partial_w != nullptr;
   const EpiLseT<true>::Params ept{pm, pd, ps, pw, zt, a.targets, plan.M, plan.V, plan.Mp,
                                   a.ignore_idx, a.v0};
   const EpiLseT<false>::Params epf{pm, pd, ps, pw, zt, a.targets, plan.M, plan.V, plan.Mp,
@@ -1208,7 +1212,7 @@ hipError_t launch_lce_forward(const LcePlan& plan, const LceFwdArgs& a, hipStrea
     const uint16_t* W = static_cast<const uint16_t*>(a.W);
     Operand P{W, plan.H, plan.V, plan.H};
     Operand Q{X, plan.H, plan.M, plan.H};
-    e = a.entropy
+    e = ent
             ? run_gemm<EpiLseT<true>, false, false>(P, Q, plan.V, plan.Mp, plan.H, ept, stream)
             : run_gemm<EpiLseT<false>, false, false>(P, Q, plan.V, plan.Mp, plan.H, epf, stream);
   } else {
@@ -1221,14 +1225,15 @@ hipError_t launch_lce_forward(const LcePlan& plan, const LceFwdArgs& a, hipStrea
                     {{o.Xh, plan.H, plan.M, plan.H},
                      {o.Xh, plan.H, plan.M, plan.H},
                      {o.Xl, plan.H, plan.M, plan.H}}};
-    e = a.entropy
+    e = ent
             ? run_gemm<EpiLseT<true>, false, false, 3>(G, plan.V, plan.Mp, plan.H, ept, stream)
             : run_gemm<EpiLseT<false>, false, false, 3>(G, plan.V, plan.Mp, plan.H, epf, stream);
   }
   if (e != hipSuccess) return e;
   MergeParams mp{pm, pd, ps, pw, zt, a.targets, plan.M, plan.Mp, plan.V, plan.n_vtiles,
-                 a.ignore_idx, a.eps, a.loss_tok, a.stats, a.entropy, a.v0, a.partial};
-  if (a.entropy)
+                 a.ignore_idx, a.eps, a.loss_tok, a.stats, a.entropy, a.v0, a.partial,
+                 a.partial_w};
+  if (ent)
     hipLaunchKernelGGL(lce_merge_kernel<true>, dim3((unsigned)((plan.M + 31) / 32)), dim3(256), 0,
                        stream, mp);
   else

@@ -112,6 +112,7 @@ int ce_forward(const void* logits, int dtype, int64_t d0, int64_t d1, int64_t V,
   p.entropy = entropy;
   p.v0 = 0;
   p.partial = nullptr;
+  p.partial_w = nullptr;
   rc = launch_status(vce::launch_ce_forward(p, dtype, sh.N, s));
   if (rc != VCE_OK) return rc;
   if (reduce_loss || n_valid) {
@@ -182,7 +183,8 @@ int ce_backward(const void* logits, void* grad, int dtype, int64_t d0, int64_t d
 
 int ce_forward_shard(const void* logits, int dtype, int64_t d0, int64_t d1, int64_t V_local,
                      int64_t ls0, int64_t ls1, const int64_t* targets, int64_t ts0, int64_t ts1,
-                     int64_t vocab_start, int64_t ignore_idx, float* partial, void* stream) {
+                     int64_t vocab_start, int64_t ignore_idx, float* partial, float* partial_w,
+                     void* stream) {
   CeShape sh;
   int rc = check_ce_common(logits, dtype, d0, d1, V_local, ls0, ls1, targets, ts0, ts1, 0.0f, 0,
                            &sh);
@@ -190,7 +192,7 @@ int ce_forward_shard(const void* logits, int dtype, int64_t d0, int64_t d1, int6
   if (vocab_start < 0 || vocab_start > INT64_MAX - V_local) return VCE_EINVAL;
   if (sh.N == 0) return VCE_OK;
   if (!partial) return VCE_EINVAL;
-  if (!aligned(partial, 16)) return VCE_EALIGN;
+  if (!aligned(partial, 16) || (partial_w && !aligned(partial_w, 4))) return VCE_EALIGN;
   vce::CeFwdParams p;
   p.logits = logits;
   p.d1 = d1;
@@ -207,13 +209,15 @@ int ce_forward_shard(const void* logits, int dtype, int64_t d0, int64_t d1, int6
   p.entropy = nullptr;
   p.v0 = vocab_start;
   p.partial = partial;
+  p.partial_w = partial_w;
   return launch_status(vce::launch_ce_forward(p, dtype, sh.N, static_cast<hipStream_t>(stream)));
 }
 
-int ce_merge_shards(const float* partials, int64_t n_shards, int64_t d0, int64_t d1,
-                    const int64_t* targets, int64_t ts0, int64_t ts1, int64_t V,
+int ce_merge_shards(const float* partials, const float* partials_w, int64_t n_shards, int64_t d0,
+                    int64_t d1, const int64_t* targets, int64_t ts0, int64_t ts1, int64_t V,
                     float label_smoothing, int reduce_loss, int64_t ignore_idx, float* loss_tok,
-                    float* loss_mean, float* stats, int32_t* n_valid, void* stream) {
+                    float* loss_mean, float* stats, int32_t* n_valid, float* entropy,
+                    void* stream) {
   if (n_shards <= 0 || d0 < 0 || d1 < 0 || V <= 0 || ts0 < 0 || ts1 < 0) return VCE_EINVAL;
   if (!(label_smoothing >= 0.0f && label_smoothing <= 1.0f)) return VCE_EINVAL;
   if (reduce_loss != 0 && reduce_loss != 1) return VCE_EINVAL;
@@ -222,6 +226,9 @@ int ce_merge_shards(const float* partials, int64_t n_shards, int64_t d0, int64_t
   if (!mul_ok(n_shards, N, &tot) || tot > INT64_MAX / 16) return VCE_EINVAL;
   if (reduce_loss && (!loss_mean || !n_valid)) return VCE_EINVAL;
   if (N > 0 && (!partials || !targets || !loss_tok || !stats)) return VCE_EINVAL;
+  if (N > 0 && entropy && !partials_w) return VCE_EINVAL;
+  if ((partials_w && !aligned(partials_w, 4)) || (entropy && !aligned(entropy, 4)))
+    return VCE_EALIGN;
   if ((partials && !aligned(partials, 16)) || (stats && !aligned(stats, 16)) ||
       (targets && !aligned(targets, 8)) || (loss_tok && !aligned(loss_tok, 4)) ||
       (loss_mean && !aligned(loss_mean, 4)) || (n_valid && !aligned(n_valid, 4)))
@@ -231,6 +238,8 @@ int ce_merge_shards(const float* partials, int64_t n_shards, int64_t d0, int64_t
   if (N > 0) {
     vce::CeMergeParams mp;
     mp.partials = partials;
+    mp.partials_w = entropy ? partials_w : nullptr;
+    mp.entropy = entropy;
     mp.n_shards = n_shards;
     mp.N = N;
     mp.d1 = d1;
@@ -265,8 +274,8 @@ int ce_backward_shard(const void* logits, void* grad, int dtype, int64_t d0, int
                       int64_t V_local, int64_t ls0, int64_t ls1, const int64_t* targets,
                       int64_t ts0, int64_t ts1, int64_t vocab_start, int64_t V,
                       const float* stats, const int32_t* n_valid, const float* grad_output,
-                      float label_smoothing, int reduce_loss, int64_t ignore_idx,
-                      int overwrite_input, void* stream) {
+                      const float* entropy, const float* grad_entropy, float label_smoothing,
+                      int reduce_loss, int64_t ignore_idx, int overwrite_input, void* stream) {
   CeShape sh;
   int rc = check_ce_common(logits, dtype, d0, d1, V_local, ls0, ls1, targets, ts0, ts1,
                            label_smoothing, reduce_loss, &sh);
@@ -275,7 +284,9 @@ int ce_backward_shard(const void* logits, void* grad, int dtype, int64_t d0, int
   if (vocab_start < 0 || V < V_local || vocab_start > V - V_local) return VCE_EINVAL;
   if (sh.N == 0) return VCE_OK;
   if (!grad || !stats || !grad_output || (reduce_loss && !n_valid)) return VCE_EINVAL;
-  if (!aligned(stats, 16) || !aligned(grad_output, 4) || (n_valid && !aligned(n_valid, 4)))
+  if (grad_entropy && !entropy) return VCE_EINVAL;
+  if (!aligned(stats, 16) || !aligned(grad_output, 4) || (n_valid && !aligned(n_valid, 4)) ||
+      (entropy && !aligned(entropy, 4)) || (grad_entropy && !aligned(grad_entropy, 4)))
     return VCE_EALIGN;
   if (overwrite_input) {
     if (grad != logits) return VCE_EALIAS;
@@ -300,8 +311,8 @@ int ce_backward_shard(const void* logits, void* grad, int dtype, int64_t d0, int
   p.stats = stats;
   p.n_valid = n_valid;
   p.grad_output = grad_output;
-  p.entropy = nullptr;
-  p.grad_entropy = nullptr;
+  p.entropy = grad_entropy ? entropy : nullptr;
+  p.grad_entropy = grad_entropy;
   p.eps = label_smoothing;
   p.reduce_loss = reduce_loss;
   p.ignore_idx = ignore_idx;
@@ -403,6 +414,7 @@ int lce_forward_impl(bool f32, const void* X, const void* W, int64_t M, int64_t 
     a.ws = static_cast<char*>(workspace);
     a.v0 = 0;
     a.partial = nullptr;
+    a.partial_w = nullptr;
     rc = launch_status(vce::launch_lce_forward(plan, a, s));
     if (rc != VCE_OK) return rc;
   }
@@ -505,7 +517,8 @@ int lce_backward_f32(const float* X, const float* W, int64_t M, int64_t H, int64
 
 int lce_forward_shard(const void* X, const void* W, int64_t M, int64_t H, int64_t V_local,
                       const int64_t* targets, int64_t vocab_start, int64_t ignore_idx,
-                      float* partial, void* workspace, size_t workspace_bytes, void* stream) {
+                      float* partial, float* partial_w, void* workspace, size_t workspace_bytes,
+                      void* stream) {
   vce::LcePlan plan;
   int rc = check_lce_common(X, W, M, H, V_local, targets, 0.0f, 0, workspace, workspace_bytes,
                             &plan);
@@ -513,7 +526,7 @@ int lce_forward_shard(const void* X, const void* W, int64_t M, int64_t H, int64_
   if (vocab_start < 0 || vocab_start > INT64_MAX - V_local) return VCE_EINVAL;
   if (M == 0) return VCE_OK;
   if (!partial) return VCE_EINVAL;
-  if (!aligned(partial, 16)) return VCE_EALIGN;
+  if (!aligned(partial, 16) || (partial_w && !aligned(partial_w, 4))) return VCE_EALIGN;
   vce::LceFwdArgs a;
   a.X = X;
   a.W = W;
@@ -529,14 +542,16 @@ int lce_forward_shard(const void* X, const void* W, int64_t M, int64_t H, int64_
   a.ws = static_cast<char*>(workspace);
   a.v0 = vocab_start;
   a.partial = partial;
+  a.partial_w = partial_w;
   return launch_status(vce::launch_lce_forward(plan, a, static_cast<hipStream_t>(stream)));
 }
 
 int lce_backward_shard(const void* X, const void* W, int64_t M, int64_t H, int64_t V_local,
                        const int64_t* targets, int64_t vocab_start, int64_t V,
                        const float* stats, const int32_t* n_valid, const float* grad_output,
-                       float label_smoothing, int reduce_loss, int64_t ignore_idx, void* dX,
-                       void* dW, void* workspace, size_t workspace_bytes, void* stream) {
+                       const float* entropy, const float* grad_entropy, float label_smoothing,
+                       int reduce_loss, int64_t ignore_idx, void* dX, void* dW, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   vce::LcePlan plan;
   int rc = check_lce_common(X, W, M, H, V_local, targets, label_smoothing, reduce_loss, workspace,
                             workspace_bytes, &plan);
@@ -546,8 +561,10 @@ int lce_backward_shard(const void* X, const void* W, int64_t M, int64_t H, int64
   if (!aligned(dW, 16)) return VCE_EALIGN;
   if (M > 0) {
     if (!dX || !stats || !grad_output || (reduce_loss && !n_valid)) return VCE_EINVAL;
+    if (grad_entropy && !entropy) return VCE_EINVAL;
     if (!aligned(dX, 16) || !aligned(stats, 16) || !aligned(grad_output, 4) ||
-        (n_valid && !aligned(n_valid, 4)))
+        (n_valid && !aligned(n_valid, 4)) || (entropy && !aligned(entropy, 4)) ||
+        (grad_entropy && !aligned(grad_entropy, 4)))
       return VCE_EALIGN;
   }
   vce::LceBwdArgs a;
@@ -557,8 +574,8 @@ int lce_backward_shard(const void* X, const void* W, int64_t M, int64_t H, int64
   a.stats = stats;
   a.n_valid = n_valid;
   a.grad_output = grad_output;
-  a.entropy = nullptr;
-  a.grad_entropy = nullptr;
+  a.entropy = grad_entropy ? entropy : nullptr;
+  a.grad_entropy = grad_entropy;
   a.eps = label_smoothing;
   a.reduce_loss = reduce_loss;
   a.ignore_idx = ignore_idx;

@@ -19,16 +19,19 @@ struct CeFwdParams {
   float* entropy;  // optional (N)
   int64_t v0;      // first vocabulary column of the row (0 unless sharded)
   float* partial;  // shard mode: (N, 4) partial statistics instead of loss/stats
+  float* partial_w;  // shard mode, optional: (N) entropy statistic w of the shard
 };
 
 struct CeMergeParams {
-  const float* partials;  // (n_shards, N, 4)
+  const float* partials;    // (n_shards, N, 4)
+  const float* partials_w;  // with entropy: (n_shards, N)
   int64_t n_shards, N, d1;
   const int64_t* targets;
   int64_t ts0, ts1, V, ignore_idx;  // V: the full vocabulary
   float eps;
   float* loss_tok;
   float* stats;
+  float* entropy;  // optional (N), needs partials_w
 };
 
 struct CeMeanParams {
@@ -108,6 +111,7 @@ struct LceFwdArgs {
   char* ws;
   int64_t v0;      // vocabulary index of W's first row (0 unless sharded)
   float* partial;  // shard mode: (M, 4) local statistics instead of loss/stats
+  float* partial_w;  // shard mode, optional: (M) entropy statistic w of the shard
 };
 
 struct LceBwdArgs {
