@@ -117,6 +117,22 @@ def bench_logits(case, steps: int, warmup: int):
     # the step without the host's per-call launch work between kernels
     graph_ms = _graph_step_ms(step, steps, warmup)
 
+    # the one-pass forward + backward (grad_output known up front): the same
+    # outputs, the logits read once
+    def step_fb():
+        vce.ce_forward_backward(z, t, go, eps, red, grad=grad, out=out)
+
+    for _ in range(warmup):
+        step_fb()
+    torch.cuda.synchronize()
+    efb = _event_pairs(1)[0]
+    efb[0].record()
+    for _ in range(steps):
+        step_fb()
+    efb[1].record()
+    torch.cuda.synchronize()
+    fb_ms = efb[0].elapsed_time(efb[1]) / steps
+
     # in-place backward: logits restored before each launch, outside its events
     zin = torch.empty_like(z)
     ip_ms = []
@@ -142,7 +158,7 @@ def bench_logits(case, steps: int, warmup: int):
         bwd_ms_median=statistics.median(bwd_ms), bwd_inplace_ms_median=statistics.median(ip_ms),
         fwd_GBs=b_fwd / (avg_f * 1e-3) / 1e9, bwd_GBs=b_bwd / (avg_b * 1e-3) / 1e9,
         fb_GBs=(b_fwd + b_bwd) / (ms_step * 1e-3) / 1e9,
-        bytes_fwd=b_fwd, bytes_bwd=b_bwd, graph_ms_per_step=graph_ms,
+        bytes_fwd=b_fwd, bytes_bwd=b_bwd, graph_ms_per_step=graph_ms, one_pass_ms=fb_ms,
         bytes_fb_nominal=accounting.ce_bytes_nominal(N, V, es, "fb"),
     )
 
@@ -438,7 +454,9 @@ def main():
             "bwd_ms_median": round(r["bwd_ms_median"], 4),
             "fb_GBs": round(r["fb_GBs"], 1),
             "fb_frac_of_hbm_peak": round(r["fb_GBs"] / accounting.HBM_PEAK_GBS, 4),
-            "graph_replay_ms_per_step": round(r["graph_ms_per_step"], 4)}
+            "graph_replay_ms_per_step": round(r["graph_ms_per_step"], 4),
+            "one_pass_ms_per_step": round(r["one_pass_ms"], 4),
+            "one_pass_tokens_per_s": round(mcase.N / (r["one_pass_ms"] * 1e-3), 1)}
         print(f"[bench] logits CE {mcase.name}: {r['ms_per_step']:.3f} ms/step", file=sys.stderr,
               flush=True)
         del mcase
@@ -509,7 +527,11 @@ def main():
                    "fwd_GBs": round(res["fwd_GBs"], 1), "bwd_GBs": round(res["bwd_GBs"], 1),
                    "fb_GBs": round(res["fb_GBs"], 1),
                    "fb_frac_of_hbm_peak": round(res["fb_GBs"] / peak, 4),
-                   "graph_replay_ms_per_step": round(res["graph_ms_per_step"], 4)},
+                   "graph_replay_ms_per_step": round(res["graph_ms_per_step"], 4),
+                   "one_pass_ms_per_step": round(res["one_pass_ms"], 4),
+                   "one_pass_tokens_per_s": round(case.N / (res["one_pass_ms"] * 1e-3), 1),
+                   "one_pass_GBs": round(res["bytes_bwd"] / (res["one_pass_ms"] * 1e-3) / 1e9,
+                                         1)},
         "linear_ce": lin,
         "vocab_sharded_one_of_8": sharded or None,
         "other_configs": other or None,

@@ -135,6 +135,29 @@ int ce_backward(const void* logits, void* grad, int dtype, int64_t d0, int64_t d
                 int reduce_loss, int64_t ignore_idx, int overwrite_input, void* stream);
 
 /*
+ * ce_forward_backward: ce_forward and ce_backward in one call, for a loss whose
+ * upstream gradient is known when the loss is asked for (the loss is the last
+ * operation, e.g. grad_output = 1).  The outputs are those of ce_forward
+ * followed by ce_backward with the same arguments (no entropy), bit for bit;
+ * the logits are read once instead of twice: each row is held on chip between
+ * its statistics and its gradient (rows of up to 256 KB: 131072 BF16 or 65536
+ * FP32 logits, at most; longer rows take the two sweeps inside this call).  The
+ * flow the TransformerEngine PR replaced also formed the derivative in the
+ * forward (Changes), as an FP32 buffer for a later multiply by the incoming
+ * gradient; here grad_output is applied at once and the gradient is stored in
+ * the input dtype, in a separate buffer or over the logits.
+ *
+ *  Arguments as in ce_forward and ce_backward; loss_tok, loss_mean, stats,
+ *  n_valid are written as ce_forward writes them, grad as ce_backward does.
+ */
+int ce_forward_backward(const void* logits, void* grad, int dtype, int64_t d0, int64_t d1,
+                        int64_t V, int64_t ls0, int64_t ls1, const int64_t* targets, int64_t ts0,
+                        int64_t ts1, const float* grad_output, float label_smoothing,
+                        int reduce_loss, int64_t ignore_idx, int overwrite_input,
+                        float* loss_tok, float* loss_mean, float* stats, int32_t* n_valid,
+                        void* stream);
+
+/*
  * Vocabulary-sharded logits cross-entropy.  The per-shard half of the
  * tensor-parallel flow of the TransformerEngine PR "Minimize the memory usage
  * of the fused cross entropy kernel" (Changes: the multi-GPU path with two

@@ -339,3 +339,30 @@ def test_shift_targets_rejects(L):
     assert call(targets=A + 4) == 3
     assert call(out=A + 8) == 4           # overlaps the targets it reads
     assert call(d0=0, targets=None, out=None) == 0
+
+
+def test_ce_forward_backward_rejects(L):
+    def call(**kw):
+        a = dict(logits=A, grad=A + (1 << 30), dtype=1, d0=2, d1=3, V=1000, ls0=3000, ls1=1000,
+                 targets=A, ts0=3, ts1=1, go=A, eps=0.0, reduce_loss=1, ignore=-100,
+                 overwrite=0, loss_tok=A, loss_mean=A, stats=A, n_valid=A)
+        a.update(kw)
+        return L.ce_forward_backward(a["logits"], a["grad"], a["dtype"], a["d0"], a["d1"],
+                                     a["V"], a["ls0"], a["ls1"], a["targets"], a["ts0"],
+                                     a["ts1"], a["go"], a["eps"], a["reduce_loss"], a["ignore"],
+                                     a["overwrite"], a["loss_tok"], a["loss_mean"], a["stats"],
+                                     a["n_valid"], None)
+
+    assert call(dtype=4) == 2
+    assert call(V=0) == 1
+    assert call(eps=1.5) == 1
+    assert call(overwrite=2) == 1
+    assert call(reduce_loss=1, loss_mean=None) == 1
+    assert call(go=None) == 1
+    assert call(grad=None) == 1
+    assert call(stats=None) == 1
+    assert call(stats=A + 4) == 3
+    assert call(go=A + 2) == 3
+    assert call(overwrite=1) == 4                   # overwrite needs grad == logits
+    assert call(grad=A + 4096) == 4                 # overlapping buffers
+    assert call(grad=A + (1 << 30) + 2) == 3        # rows split at different 16 B phases

@@ -1,0 +1,134 @@
+"""Parity of the one-pass forward + backward (ce_forward_backward): its
+outputs are, bit for bit, those of ce_forward followed by ce_backward with the
+same arguments (which the other logits tests hold to the FP64 oracle), and
+one case is also checked against the oracle directly."""
+import numpy as np
+import pytest
+import torch
+
+import vocabulary_cross_entropy_amd as vce
+from vocabulary_cross_entropy_amd import workloads as wl
+from vce_testutil import to_device, to_host_bits
+from test_parity_ce import check_backward, check_forward
+
+pytestmark = pytest.mark.gpu
+IGN = wl.IGNORE_INDEX
+
+
+def _say(msg):
+    print(f"[parity-fb] {msg}", flush=True)
+
+
+def two_call(z, t, go, eps, red, overwrite):
+    zc = z.clone() if overwrite else z
+    loss, mean, stats, nv = vce.ce_forward(zc, t, eps, red, IGN)
+    grad = vce.ce_backward(zc, t, stats, nv, go, eps, red, IGN, overwrite_input=overwrite)
+    return loss, mean, stats, nv, grad
+
+
+def one_pass(z, t, go, eps, red, overwrite):
+    zc = z.clone() if overwrite else z
+    return vce.ce_forward_backward(zc, t, go, eps, red, IGN, overwrite_input=overwrite)
+
+
+def assert_same(a, b, red):
+    names = ("loss", "mean", "stats", "n_valid", "grad")
+    for name, x, y in zip(names, a, b):
+        if x is None and y is None:
+            continue
+        if name in ("mean", "n_valid") and not red:
+            continue
+        assert torch.equal(x, y) or (torch.isnan(x).equal(torch.isnan(y)) and
+                                     torch.equal(torch.nan_to_num(x), torch.nan_to_num(y))), name
+
+
+def _case(seed, d0, d1, V, dtype, eps, red, layout="B,SQ", n_ign=3, sigma=3.0):
+    return wl.make_logits(seed, d0, d1, V, dtype=dtype, sigma=sigma, ignore_count=n_ign,
+                          label_smoothing=eps, reduce_loss=red, grad_output="random",
+                          layout=layout)
+
+
+@pytest.mark.parametrize("dtype,V", [("fp32", 1000), ("bf16", 7), ("bf16", 1001),
+                                     ("fp32", 4099), ("bf16", 32000), ("bf16", 65537),
+                                     ("fp32", 65536), ("bf16", 131072),
+                                     ("bf16", 131080), ("fp32", 70000)])
+@pytest.mark.parametrize("eps,red", [(0.0, False), (0.1, True)])
+@pytest.mark.parametrize("overwrite", [False, True])
+def test_one_pass_equals_two_calls(dtype, V, eps, red, overwrite):
+    # 131080 BF16 and 70000 FP32 exceed the on-chip row and take the two sweeps
+    case = _case(5000 + V, 3, 17, V, dtype, eps, red)
+    z = to_device(case.logits, dtype)
+    t = torch.from_numpy(case.targets).cuda()
+    go = torch.from_numpy(case.grad_output).cuda()
+    go = go.reshape(-1) if red else go
+    a = two_call(z, t, go, eps, red, overwrite)
+    b = one_pass(z, t, go, eps, red, overwrite)
+    torch.cuda.synchronize()
+    assert_same(a, b, red)
+
+
+def test_one_pass_edge_targets_and_infinite_columns():
+    V = 3000
+    case = _case(5101, 2, 40, V, "bf16", 0.1, False, n_ign=5)
+    lg = case.logits.reshape(-1, V)
+    lg[:, 2500:] = np.uint16(0xFF80)          # -inf padding columns (BF16 bits)
+    tt = case.targets.reshape(-1)
+    tt[:] = np.minimum(tt, 2499)
+    tt[0], tt[1], tt[2] = V, -3, 2499         # out of range (twice) and the last live column
+    z = to_device(case.logits, "bf16")
+    t = torch.from_numpy(case.targets).cuda()
+    go = torch.from_numpy(case.grad_output).cuda()
+    for overwrite in (False, True):
+        a = two_call(z, t, go, 0.1, False, overwrite)
+        b = one_pass(z, t, go, 0.1, False, overwrite)
+        torch.cuda.synchronize()
+        assert_same(a, b, False)
+        assert torch.isnan(b[0].reshape(-1)[:2]).all()
+
+
+def test_one_pass_strided_view():
+    # (SQ,B,V) storage used as a (B,SQ,V) view
+    case = _case(5102, 64, 4, 5000, "bf16", 0.1, True, layout="SQ,B")
+    zs = to_device(case.logits, "bf16")
+    ts = torch.from_numpy(case.targets).cuda()
+    zv, tv = zs.transpose(0, 1), ts.transpose(0, 1)
+    go = torch.ones(1, device="cuda")
+    a = two_call(zv, tv, go, 0.1, True, False)
+    b = one_pass(zv, tv, go, 0.1, True, False)
+    torch.cuda.synchronize()
+    assert_same(a, b, True)
+
+
+def test_one_pass_headline_shape_against_oracle():
+    """The (SQ,B,V) = (2048, 2, 128256) BF16 workload, in place, against the
+    FP64 oracle (loss and statistics; gradient rows checked in full) and
+    bitwise against the two calls."""
+    case = wl.headline_logits()
+    _say(case.name)
+    z = to_device(case.logits, "bf16")
+    t = torch.from_numpy(case.targets).cuda()
+    go = torch.from_numpy(case.grad_output).cuda()
+    a = two_call(z, t, go, 0.0, False, True)
+    b = one_pass(z, t, go, 0.0, False, True)
+    torch.cuda.synchronize()
+    assert_same(a, b, False)
+    out = dict(loss=b[0].cpu().numpy(), stats=b[2].cpu().numpy().reshape(-1, 4),
+               grad=to_host_bits(b[4]))
+    check_forward(case, out)
+    check_backward(case, out, chunk=512)
+
+
+def test_one_pass_all_ignored_and_empty():
+    case = _case(5103, 2, 8, 900, "fp32", 0.0, True, n_ign=16)
+    z = to_device(case.logits, "fp32")
+    t = torch.from_numpy(case.targets).cuda()
+    go = torch.ones(1, device="cuda")
+    loss, mean, stats, nv, grad = one_pass(z, t, go, 0.0, True, False)
+    torch.cuda.synchronize()
+    assert float(mean.item()) == 0.0 and int(nv.item()) == 0
+    assert torch.count_nonzero(grad).item() == 0 and torch.count_nonzero(loss).item() == 0
+    ze = torch.empty((0, 4, 900), device="cuda")
+    te = torch.empty((0, 4), dtype=torch.int64, device="cuda")
+    loss, mean, stats, nv, grad = vce.ce_forward_backward(ze, te, go, 0.0, True)
+    torch.cuda.synchronize()
+    assert float(mean.item()) == 0.0 and int(nv.item()) == 0

@@ -29,6 +29,8 @@ SIGNATURES = {
                           _VP, _VP, _VP, _VP, _VP, _VP]),
     "ce_backward": (_I32, [_VP, _VP, _I32, _I64, _I64, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _VP,
                            _VP, _VP, _VP, _F32, _I32, _I64, _I32, _VP]),
+    "ce_forward_backward": (_I32, [_VP, _VP, _I32, _I64, _I64, _I64, _I64, _I64, _VP, _I64, _I64,
+                                   _VP, _F32, _I32, _I64, _I32, _VP, _VP, _VP, _VP, _VP]),
     "ce_forward_shard": (_I32, [_VP, _I32, _I64, _I64, _I64, _I64, _I64, _VP, _I64, _I64, _I64,
                                 _I64, _VP, _VP, _VP]),
     "ce_merge_shards": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _I64, _I64, _I64, _F32, _I32,
@@ -193,6 +195,41 @@ def ce_backward(logits: torch.Tensor, targets: torch.Tensor, stats: torch.Tensor
                            _stream(stream))
     _check("ce_backward", rc)
     return grad
+
+
+def ce_forward_backward(logits: torch.Tensor, targets: torch.Tensor, grad_output: torch.Tensor,
+                        label_smoothing: float = 0.0, reduce_loss: bool = False,
+                        ignore_idx: int = -100, overwrite_input: bool = False, *,
+                        grad: torch.Tensor | None = None, stream=None, out=None):
+    """``ce_forward`` then ``ce_backward`` with the same arguments, in one pass
+    over the logits.  Returns (loss_tok, loss_mean, stats, n_valid, grad)."""
+    logits, targets = _logits3d(logits, targets)
+    _need_cuda(logits, targets, grad_output)
+    d0, d1, V = logits.shape
+    dev = logits.device
+    if out is None:
+        loss_tok = torch.empty((d0, d1), dtype=torch.float32, device=dev)
+        stats = torch.empty((d0, d1, 4), dtype=torch.float32, device=dev)
+        loss_mean = torch.empty((), dtype=torch.float32, device=dev) if reduce_loss else None
+        n_valid = torch.empty((), dtype=torch.int32, device=dev) if reduce_loss else None
+    else:
+        loss_tok, loss_mean, stats, n_valid = out
+    if overwrite_input:
+        grad = logits
+    elif grad is None:
+        grad = _grad_like(logits)
+    elif grad.dim() == 2:
+        grad = grad.unsqueeze(0)
+    if tuple(grad.stride()) != tuple(logits.stride()) or grad.dtype != logits.dtype:
+        raise ValueError("grad must have the dtype and strides of logits")
+    rc = lib().ce_forward_backward(_ptr(logits), _ptr(grad), _dtype_code(logits), d0, d1, V,
+                                   logits.stride(0), logits.stride(1), _ptr(targets),
+                                   targets.stride(0), targets.stride(1), _ptr(grad_output),
+                                   float(label_smoothing), int(bool(reduce_loss)),
+                                   int(ignore_idx), int(bool(overwrite_input)), _ptr(loss_tok),
+                                   _ptr(loss_mean), _ptr(stats), _ptr(n_valid), _stream(stream))
+    _check("ce_forward_backward", rc)
+    return loss_tok, loss_mean, stats, n_valid, grad
 
 
 def ce_forward_shard(logits: torch.Tensor, targets: torch.Tensor, vocab_start: int,

@@ -31,6 +31,7 @@ namespace {
 constexpr int kFwdThreads = 512;
 constexpr int kFwdWaves = kFwdThreads / 64;
 constexpr int kBwdThreads = 1024;
+constexpr int kFbVecs = 32;  // most 16-byte vectors per thread the one-pass kernel holds
 constexpr int kUnroll = 4;
 
 template <int DT>
@@ -270,7 +271,7 @@ __global__ __launch_bounds__(1024) void ce_mean_kernel(CeMeanParams p) {
   for (int64_t r = threadIdx.x; r < p.N; r += 1024) {
     const int64_t i0 = r / p.d1, i1 = r - i0 * p.d1;
     if (p.targets[i0 * p.ts0 + i1 * p.ts1] != p.ignore_idx) {
-      sum += (double)p.loss_tok[r];
+      if (p.loss_tok) sum += (double)p.loss_tok[r];
       ++cnt;
     }
   }
@@ -440,6 +441,171 @@ __global__ __launch_bounds__(kBwdThreads) void ce_bwd_kernel(CeBwdParams p) {
 
 }  // namespace
 
+// Forward and backward of one row in one pass, for a caller that knows
+// grad_output when it asks for the loss (a terminal loss): the row is read
+// once into registers (NV 16-byte vectors per thread, at most 512 x 32 x 16 B
+// = 256 KB), its statistics are reduced exactly as ce_fwd_kernel reduces them
+// (same threads, same chunks of four vectors, same order), loss and stats are
+// written as ce_fwd_kernel writes them, and the gradient is written from the
+// registers exactly as ce_bwd_kernel computes it from those statistics: one
+// read and one write of the logits instead of two reads and one write.
+template <int DT, int NV>
+__global__ __launch_bounds__(kFwdThreads) void ce_fb_kernel(CeFwdParams f, CeBwdParams b) {
+  using T = typename Elem<DT>::T;
+  constexpr int vec = Elem<DT>::kVec;
+  constexpr int NC = NV / kUnroll;  // chunks of four vectors per thread
+  __shared__ LseState sh[kFwdWaves];
+  const int64_t r = blockIdx.x;
+  const int64_t i0 = r / f.d1, i1 = r - i0 * f.d1;
+  const int64_t t = f.targets[i0 * f.ts0 + i1 * f.ts1];
+  const int tid = threadIdx.x;
+  const int64_t V = f.V;
+  const int64_t off = i0 * f.ls0 + i1 * f.ls1;
+  const T* row = static_cast<const T*>(f.logits) + off;
+  T* grow = static_cast<T*>(b.grad) + off;
+  const RowSplit rs = split_row<DT>(row, V);
+  u32x4_t* gvec = reinterpret_cast<u32x4_t*>(grow + rs.head);
+  const int64_t nscal = rs.head + (V - rs.tail0);
+  const bool t_ok = (t >= 0 && t < V);
+
+  if (t == f.ignore_idx || !t_ok) {
+    // ignored: loss 0, zero stats, zero gradient, the row is not read; a
+    // target outside [0, V): the statistics as ce_fwd_kernel forms them,
+    // NaN loss and a NaN gradient row
+    const float fill = (t == f.ignore_idx) ? 0.0f : __builtin_nanf("");
+    if (t != f.ignore_idx) {
+      // statistics still come from the whole row (same order as the forward)
+      LseState st{kNegInf, 0.0f, 0.0f};
+      if (tid < nscal) {
+        const int64_t idx = tid < rs.head ? tid : rs.tail0 + (tid - rs.head);
+        const float z = Elem<DT>::load(row + idx);
+        st = LseState{z, (z == kNegInf) ? 0.0f : 1.0f, z};
+      }
+      const u32x4_t* vrow = reinterpret_cast<const u32x4_t*>(row + rs.head);
+      int64_t j = tid;
+      for (; j + (kUnroll - 1) * kFwdThreads < rs.nvec; j += kUnroll * kFwdThreads) {
+        u32x4_t w[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) w[u] = vrow[j + u * kFwdThreads];
+        fold<DT, kUnroll>(st, w);
+      }
+      if (j < rs.nvec) {
+        const int nvalid = (int)((rs.nvec - j + kFwdThreads - 1) / kFwdThreads);
+        u32x4_t w[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+          w[u] = u < nvalid ? vrow[j + u * kFwdThreads] : u32x4_t{0, 0, 0, 0};
+        fold<DT, kUnroll>(st, w, nvalid);
+      }
+      const LseState tot = block_reduce(st, sh);
+      if (tid == 0) {
+        f.loss_tok[r] = __builtin_nanf("");
+        *reinterpret_cast<f32x4_t*>(f.stats + 4 * r) =
+            f32x4_t{tot.m, tot.d, __builtin_nanf(""), tot.s / (float)V};
+      }
+      __syncthreads();  // every read of the row is done before it may be overwritten
+    } else if (tid == 0) {
+      f.loss_tok[r] = 0.0f;
+      *reinterpret_cast<f32x4_t*>(f.stats + 4 * r) = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    float fv[vec];
+#pragma unroll
+    for (int i = 0; i < vec; ++i) fv[i] = fill;
+    if (tid < nscal) {
+      const int64_t idx = tid < rs.head ? tid : rs.tail0 + (tid - rs.head);
+      store_one<DT>(grow + idx, fill);
+    }
+    for (int64_t j = tid; j < rs.nvec; j += kFwdThreads) store_vec<DT>(gvec + j, fv);
+    return;
+  }
+
+  // ---- forward: read the row into registers, reduce its statistics ----------
+  float zt = __builtin_nanf("");
+  if (tid == 0) zt = Elem<DT>::load(row + t);
+  LseState st{kNegInf, 0.0f, 0.0f};
+  float zs = 0.0f;  // this thread's scalar (head or tail) element, if any
+  int64_t sidx = -1;
+  if (tid < nscal) {
+    sidx = tid < rs.head ? tid : rs.tail0 + (tid - rs.head);
+    zs = Elem<DT>::load(row + sidx);
+    st = LseState{zs, (zs == kNegInf) ? 0.0f : 1.0f, zs};
+  }
+  const u32x4_t* vrow = reinterpret_cast<const u32x4_t*>(row + rs.head);
+  u32x4_t w[NV];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int64_t j = tid + (int64_t)c * kUnroll * kFwdThreads;
+    if (j + (kUnroll - 1) * kFwdThreads < rs.nvec) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        w[c * kUnroll + u] = __builtin_nontemporal_load(vrow + j + u * kFwdThreads);
+      fold<DT, kUnroll>(st, &w[c * kUnroll]);
+    } else if (j < rs.nvec) {
+      const int nvalid = (int)((rs.nvec - j + kFwdThreads - 1) / kFwdThreads);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        w[c * kUnroll + u] = u < nvalid ? __builtin_nontemporal_load(vrow + j + u * kFwdThreads)
+                                        : u32x4_t{0, 0, 0, 0};
+      fold<DT, kUnroll>(st, &w[c * kUnroll], nvalid);
+    }
+  }
+  const LseState tot = block_reduce(st, sh);
+  if (tid == 0) {
+    const float mean = tot.s / (float)V;
+    f.loss_tok[r] = ce_row_loss(tot.m, tot.d, zt, mean, f.eps);
+    *reinterpret_cast<f32x4_t*>(f.stats + 4 * r) = f32x4_t{tot.m, tot.d, zt, mean};
+  }
+  // every read of the row (the target logit included) is done before the
+  // gradient may overwrite it
+  __syncthreads();
+
+  // ---- backward from the registers (the expressions of ce_bwd_kernel) --------
+  float g;
+  if (b.reduce_loss) {
+    const int32_t nv = b.n_valid[0];
+    g = b.grad_output[0] / (float)(nv > 0 ? nv : 1);
+  } else {
+    g = b.grad_output[r];
+  }
+  const float m = tot.m, d = tot.d;
+  const float mref = (m == kNegInf) ? 0.0f : m;
+  const float mL = mref * kLog2e;
+  const float gs = g / d;
+  const float goff = g * (b.eps / (float)V);
+  const float gt = g * (1.0f - b.eps);
+  auto gval = [&](float z) -> float {
+    const float e = exp2_hw(__builtin_fmaf(z, kLog2e, -mL));
+    return e * gs - goff;
+  };
+  if (sidx >= 0) {
+    float gv = gval(zs);
+    if (sidx == t) gv -= gt;
+    store_one<DT>(grow + sidx, gv);
+  }
+  const int64_t tv = t - rs.head;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t j = tid + (int64_t)(c * kUnroll + u) * kFwdThreads;
+      if (j < rs.nvec) {
+        float z[vec];
+        unpack<DT>(w[c * kUnroll + u], z);
+        float gv[vec];
+#pragma unroll
+        for (int i = 0; i < vec; ++i) gv[i] = gval(z[i]);
+        const int64_t base = j * vec;
+        if (tv >= base && tv < base + vec) {
+#pragma unroll
+          for (int i = 0; i < vec; ++i)
+            if (base + i == tv) gv[i] -= gt;
+        }
+        store_vec<DT>(gvec + j, gv);
+      }
+    }
+  }
+}
+
 // Per-row merge of vocabulary-shard statistics, shards in fixed order
 // (bitwise reproducible): m = max m_k, d = sum d_k exp(m_k - m), sum z, and
 // z_t from the shard holding the target (the others contribute 0); then the
@@ -543,6 +709,37 @@ hipError_t launch_ce_merge_shards(const CeMergeParams& p, hipStream_t stream) {
 hipError_t launch_ce_mean(const CeMeanParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(ce_mean_kernel, dim3(1), dim3(1024), 0, stream, p);
   return hipGetLastError();
+}
+
+namespace {
+
+template <int DT>
+bool launch_fb_dt(const CeFwdParams& f, const CeBwdParams& b, int64_t N, hipStream_t stream) {
+  // vectors per thread to hold the row (the 16-byte head/tail are scalars)
+  const int64_t nvec = f.V / Elem<DT>::kVec;
+  const dim3 g((unsigned)N), blk(kFwdThreads);
+  if (nvec <= 8 * kFwdThreads)
+    hipLaunchKernelGGL((ce_fb_kernel<DT, 8>), g, blk, 0, stream, f, b);
+  else if (nvec <= 16 * kFwdThreads)
+    hipLaunchKernelGGL((ce_fb_kernel<DT, 16>), g, blk, 0, stream, f, b);
+  else if (nvec <= kFbVecs * kFwdThreads)
+    hipLaunchKernelGGL((ce_fb_kernel<DT, kFbVecs>), g, blk, 0, stream, f, b);
+  else
+    return false;
+  return true;
+}
+
+}  // namespace
+
+bool ce_fb_fits(int dtype, int64_t V) {
+  return V / (dtype == 0 ? 4 : 8) <= (int64_t)kFbVecs * kFwdThreads;
+}
+
+hipError_t launch_ce_forward_backward(const CeFwdParams& f, const CeBwdParams& b, int dtype,
+                                      int64_t N, hipStream_t stream) {
+  if (N <= 0) return hipSuccess;
+  const bool ok = dtype == 0 ? launch_fb_dt<0>(f, b, N, stream) : launch_fb_dt<1>(f, b, N, stream);
+  return ok ? hipGetLastError() : hipErrorInvalidValue;
 }
 
 hipError_t launch_ce_backward(const CeBwdParams& p, int dtype, int64_t N, hipStream_t stream) {

@@ -181,6 +181,105 @@ int ce_backward(const void* logits, void* grad, int dtype, int64_t d0, int64_t d
   return launch_status(vce::launch_ce_backward(p, dtype, sh.N, static_cast<hipStream_t>(stream)));
 }
 
+int ce_forward_backward(const void* logits, void* grad, int dtype, int64_t d0, int64_t d1,
+                        int64_t V, int64_t ls0, int64_t ls1, const int64_t* targets, int64_t ts0,
+                        int64_t ts1, const float* grad_output, float label_smoothing,
+                        int reduce_loss, int64_t ignore_idx, int overwrite_input,
+                        float* loss_tok, float* loss_mean, float* stats, int32_t* n_valid,
+                        void* stream) {
+  CeShape sh;
+  int rc = check_ce_common(logits, dtype, d0, d1, V, ls0, ls1, targets, ts0, ts1,
+                           label_smoothing, reduce_loss, &sh);
+  if (rc != VCE_OK) return rc;
+  if (overwrite_input != 0 && overwrite_input != 1) return VCE_EINVAL;
+  if (reduce_loss && (!loss_mean || !n_valid)) return VCE_EINVAL;
+  if (sh.N > 0 && (!loss_tok || !stats || !grad || !grad_output)) return VCE_EINVAL;
+  if ((stats && !aligned(stats, 16)) || (loss_tok && !aligned(loss_tok, 4)) ||
+      (loss_mean && !aligned(loss_mean, 4)) || (n_valid && !aligned(n_valid, 4)) ||
+      (grad_output && !aligned(grad_output, 4)))
+    return VCE_EALIGN;
+  if (sh.N > 0) {
+    if (overwrite_input) {
+      if (grad != logits) return VCE_EALIAS;
+    } else {
+      uintptr_t a0, a1, b0, b1;
+      extent(logits, d0, d1, V, ls0, ls1, sh.es, &a0, &a1);
+      extent(grad, d0, d1, V, ls0, ls1, sh.es, &b0, &b1);
+      if (a0 < b1 && b0 < a1) return VCE_EALIAS;
+      if ((reinterpret_cast<uintptr_t>(logits) - reinterpret_cast<uintptr_t>(grad)) % 16 != 0)
+        return VCE_EALIGN;
+    }
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  vce::CeMeanParams mp;
+  mp.loss_tok = nullptr;
+  mp.targets = targets;
+  mp.N = sh.N;
+  mp.d1 = d1 > 0 ? d1 : 1;
+  mp.ts0 = ts0;
+  mp.ts1 = ts1;
+  mp.ignore_idx = ignore_idx;
+  mp.loss_mean = nullptr;
+  mp.n_valid = n_valid;
+  if (sh.N > 0) {
+    // the mean's denominator is needed before the gradient: count first
+    if (reduce_loss) {
+      rc = launch_status(vce::launch_ce_mean(mp, s));
+      if (rc != VCE_OK) return rc;
+    }
+    vce::CeFwdParams f;
+    f.logits = logits;
+    f.d1 = d1;
+    f.ls0 = ls0;
+    f.ls1 = ls1;
+    f.V = V;
+    f.targets = targets;
+    f.ts0 = ts0;
+    f.ts1 = ts1;
+    f.eps = label_smoothing;
+    f.ignore_idx = ignore_idx;
+    f.loss_tok = loss_tok;
+    f.stats = stats;
+    f.entropy = nullptr;
+    f.v0 = 0;
+    f.partial = nullptr;
+    f.partial_w = nullptr;
+    vce::CeBwdParams b;
+    b.logits = logits;
+    b.grad = grad;
+    b.d1 = d1;
+    b.ls0 = ls0;
+    b.ls1 = ls1;
+    b.V = V;
+    b.targets = targets;
+    b.ts0 = ts0;
+    b.ts1 = ts1;
+    b.stats = stats;
+    b.n_valid = n_valid;
+    b.grad_output = grad_output;
+    b.entropy = nullptr;
+    b.grad_entropy = nullptr;
+    b.eps = label_smoothing;
+    b.reduce_loss = reduce_loss;
+    b.ignore_idx = ignore_idx;
+    b.v0 = 0;
+    b.Vg = V;
+    if (vce::ce_fb_fits(dtype, V)) {
+      rc = launch_status(vce::launch_ce_forward_backward(f, b, dtype, sh.N, s));
+    } else {  // rows too long to hold on chip: the two sweeps
+      rc = launch_status(vce::launch_ce_forward(f, dtype, sh.N, s));
+      if (rc == VCE_OK) rc = launch_status(vce::launch_ce_backward(b, dtype, sh.N, s));
+    }
+    if (rc != VCE_OK) return rc;
+  }
+  if (reduce_loss || n_valid) {
+    mp.loss_tok = loss_tok;
+    mp.loss_mean = reduce_loss ? loss_mean : nullptr;
+    rc = launch_status(vce::launch_ce_mean(mp, s));
+  }
+  return rc;
+}
+
 int ce_forward_shard(const void* logits, int dtype, int64_t d0, int64_t d1, int64_t V_local,
                      int64_t ls0, int64_t ls1, const int64_t* targets, int64_t ts0, int64_t ts1,
                      int64_t vocab_start, int64_t ignore_idx, float* partial, float* partial_w,

@@ -71,6 +71,10 @@ struct ShiftParams {
 };
 hipError_t launch_shift_targets(const ShiftParams& p, hipStream_t stream);
 hipError_t launch_ce_backward(const CeBwdParams& p, int dtype, int64_t N, hipStream_t stream);
+// One-pass forward + backward (rows of at most 512 x 32 16-byte vectors: see ce_fb_fits).
+bool ce_fb_fits(int dtype, int64_t V);
+hipError_t launch_ce_forward_backward(const CeFwdParams& f, const CeBwdParams& b, int dtype,
+                                      int64_t N, hipStream_t stream);
 
 // ---- fused linear cross-entropy ----------------------------------------------
 
