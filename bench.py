@@ -146,6 +146,19 @@ def bench_logits(case, steps: int, warmup: int):
         torch.cuda.synchronize()
         ip_ms.append(e[0].elapsed_time(e[1]))
 
+    # context only: a plain device-to-device copy of the same tensor (torch's
+    # copy kernel), read + write of the logits' bytes, as a practical ceiling
+    # for a read-and-write sweep; never the roofline's denominator
+    cp_ms = []
+    for _ in range(max(3, min(steps, 10))):
+        e = _event_pairs(1)[0]
+        e[0].record()
+        zin.copy_(z)
+        e[1].record()
+        torch.cuda.synchronize()
+        cp_ms.append(e[0].elapsed_time(e[1]))
+    copy_GBs = 2 * z.numel() * z.element_size() / (statistics.median(cp_ms) * 1e-3) / 1e9
+
     n_ign = int(case.meta["n_ignored"])
     es = case.elem_bytes
     b_fwd = accounting.ce_bytes(N, V, es, n_ign, "fwd")
@@ -159,7 +172,7 @@ def bench_logits(case, steps: int, warmup: int):
         fwd_GBs=b_fwd / (avg_f * 1e-3) / 1e9, bwd_GBs=b_bwd / (avg_b * 1e-3) / 1e9,
         fb_GBs=(b_fwd + b_bwd) / (ms_step * 1e-3) / 1e9,
         bytes_fwd=b_fwd, bytes_bwd=b_bwd, graph_ms_per_step=graph_ms, one_pass_ms=fb_ms,
-        bytes_fb_nominal=accounting.ce_bytes_nominal(N, V, es, "fb"),
+        bytes_fb_nominal=accounting.ce_bytes_nominal(N, V, es, "fb"), copy_GBs=copy_GBs,
     )
 
 
@@ -531,7 +544,9 @@ def main():
                    "one_pass_ms_per_step": round(res["one_pass_ms"], 4),
                    "one_pass_tokens_per_s": round(case.N / (res["one_pass_ms"] * 1e-3), 1),
                    "one_pass_GBs": round(res["bytes_bwd"] / (res["one_pass_ms"] * 1e-3) / 1e9,
-                                         1)},
+                                         1),
+                   "copy_ceiling_GBs": round(res["copy_GBs"], 1),
+                   "bwd_frac_of_copy_ceiling": round(res["bwd_GBs"] / res["copy_GBs"], 4)},
         "linear_ce": lin,
         "vocab_sharded_one_of_8": sharded or None,
         "other_configs": other or None,
