@@ -132,3 +132,62 @@ def test_one_pass_all_ignored_and_empty():
     loss, mean, stats, nv, grad = vce.ce_forward_backward(ze, te, go, 0.0, True)
     torch.cuda.synchronize()
     assert float(mean.item()) == 0.0 and int(nv.item()) == 0
+
+
+def test_one_pass_and_shards_graph_capture_replay():
+    # The one-pass call and the three shard calls only enqueue kernels on the
+    # given stream, so they are captured and replayed like the others; every
+    # replay (with eager work and synchronisation between them) must give the
+    # eager outputs bit for bit.
+    d0, d1, V, S = 2, 384, 12000, 3
+    case = _case(5104, d0, d1, V, "bf16", 0.1, True)
+    z = to_device(case.logits, "bf16")
+    t = torch.from_numpy(case.targets).cuda()
+    go = torch.ones(1, device="cuda")
+    loss = torch.empty((d0, d1), device="cuda")
+    mean = torch.empty((), device="cuda")
+    stats = torch.empty((d0, d1, 4), device="cuda")
+    nv = torch.empty((), dtype=torch.int32, device="cuda")
+    grad = torch.empty_like(z)
+    out = (loss, mean, stats, nv)
+    bounds = [0, 4000, 8000, V]
+    parts = torch.empty((S, d0, d1, 4), device="cuda")
+    sl = torch.empty((d0, d1), device="cuda")
+    smean = torch.empty((), device="cuda")
+    sst = torch.empty((d0, d1, 4), device="cuda")
+    snv = torch.empty((), dtype=torch.int32, device="cuda")
+    sgrad = [torch.empty((d0, d1, bounds[k + 1] - bounds[k]), dtype=torch.bfloat16,
+                         device="cuda") for k in range(S)]
+    zs = [z[:, :, bounds[k]:bounds[k + 1]].contiguous() for k in range(S)]
+
+    def work(stream=None):
+        vce.ce_forward_backward(z, t, go, 0.1, True, IGN, grad=grad, out=out, stream=stream)
+        for k in range(S):
+            vce.ce_forward_shard(zs[k], t, bounds[k], IGN, out=parts[k], stream=stream)
+        vce.ce_merge_shards(parts, t, V, 0.1, True, IGN, out=(sl, smean, sst, snv), stream=stream)
+        for k in range(S):
+            vce.ce_backward_shard(zs[k], t, bounds[k], V, sst, snv, go, 0.1, True, IGN,
+                                  grad=sgrad[k], stream=stream)
+
+    work()
+    torch.cuda.synchronize()
+    outs = [loss, mean, stats, nv, grad, sl, smean, sst, snv] + sgrad
+    ref = [x.clone() for x in outs]
+    s = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            work(stream=s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for x in outs:
+            x.zero_()
+        work()                      # eager work between the replays
+        torch.cuda.synchronize()
+        for x in outs:
+            x.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs, ref)):
+            assert torch.equal(a, b), f"replay {rep}: output {i} differs"
