@@ -27,10 +27,15 @@ namespace {
 // 32000 BF16 the forward takes 46-48 us with 512 threads and 58-61 us with
 // 1024 (more rows in flight per CU, shorter reductions), and the same at
 // 128256 columns; the backward is fastest with 1024 (85 vs 89 us at 32000,
-// 364 vs 397 us at 128256).
+// 364 vs 397 us at 128256) on rows over 32 KB, and with 512 on shorter ones,
+// where 1024 threads leave most lanes one vector or none (4096 rows of 8000
+// BF16: 22.5 against 35.7 us; of 16032: 45.5-46.8 against 47.0-48.0 us;
+// 256 threads are slower still at 16032).
 constexpr int kFwdThreads = 512;
 constexpr int kFwdWaves = kFwdThreads / 64;
 constexpr int kBwdThreads = 1024;
+constexpr int kBwdThreadsShort = 512;
+constexpr int64_t kBwdShortRowBytes = 32768;
 constexpr int kFbVecs = 32;  // most 16-byte vectors per thread the one-pass kernel holds
 constexpr int kUnroll = 4;
 
@@ -316,8 +321,8 @@ __device__ __forceinline__ void store_one<1>(uint16_t* dst, float g) { *dst = to
 
 // ENT: adds grad_entropy[r] dH/dz_v = grad_entropy[r] p_v (E_p[z] - z_v), with
 // E_p[z] = lse - H from the forward's entropy.
-template <int DT, bool ENT>
-__global__ __launch_bounds__(kBwdThreads) void ce_bwd_kernel(CeBwdParams p) {
+template <int DT, bool ENT, int NT>
+__global__ __launch_bounds__(NT) void ce_bwd_kernel(CeBwdParams p) {
   using T = typename Elem<DT>::T;
   constexpr int vec = Elem<DT>::kVec;
   const int64_t r = blockIdx.x;
@@ -344,7 +349,7 @@ __global__ __launch_bounds__(kBwdThreads) void ce_bwd_kernel(CeBwdParams p) {
       const int64_t idx = tid < rs.head ? tid : rs.tail0 + (tid - rs.head);
       store_one<DT>(grow + idx, fill);
     }
-    for (int64_t j = tid; j < rs.nvec; j += kBwdThreads) store_vec<DT>(gvec + j, f);
+    for (int64_t j = tid; j < rs.nvec; j += NT) store_vec<DT>(gvec + j, f);
     return;
   }
 
@@ -394,10 +399,10 @@ __global__ __launch_bounds__(kBwdThreads) void ce_bwd_kernel(CeBwdParams p) {
   const u32x4_t* vrow = reinterpret_cast<const u32x4_t*>(row + rs.head);
   const int64_t tv = tl - rs.head;  // target position inside the vector body
   int64_t j = tid;
-  for (; j + (kUnroll - 1) * kBwdThreads < rs.nvec; j += kUnroll * kBwdThreads) {
+  for (; j + (kUnroll - 1) * NT < rs.nvec; j += kUnroll * NT) {
     u32x4_t w[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) w[u] = __builtin_nontemporal_load(vrow + j + u * kBwdThreads);
+    for (int u = 0; u < kUnroll; ++u) w[u] = __builtin_nontemporal_load(vrow + j + u * NT);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       float z[vec];
@@ -405,21 +410,21 @@ __global__ __launch_bounds__(kBwdThreads) void ce_bwd_kernel(CeBwdParams p) {
       float gv[vec];
 #pragma unroll
       for (int i = 0; i < vec; ++i) gv[i] = gval(z[i]);
-      const int64_t base = (j + u * kBwdThreads) * vec;
+      const int64_t base = (j + u * NT) * vec;
       if (tv >= base && tv < base + vec) {
 #pragma unroll
         for (int i = 0; i < vec; ++i)
           if (base + i == tv) gv[i] -= gt;
       }
-      store_vec<DT>(gvec + j + u * kBwdThreads, gv);
+      store_vec<DT>(gvec + j + u * NT, gv);
     }
   }
   if (j < rs.nvec) {  // last partial chunk: all its loads in flight together
-    const int nvalid = (int)((rs.nvec - j + kBwdThreads - 1) / kBwdThreads);
+    const int nvalid = (int)((rs.nvec - j + NT - 1) / NT);
     u32x4_t w[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
-      if (u < nvalid) w[u] = __builtin_nontemporal_load(vrow + j + u * kBwdThreads);
+      if (u < nvalid) w[u] = __builtin_nontemporal_load(vrow + j + u * NT);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       if (u >= nvalid) break;
@@ -428,13 +433,13 @@ __global__ __launch_bounds__(kBwdThreads) void ce_bwd_kernel(CeBwdParams p) {
       float gv[vec];
 #pragma unroll
       for (int i = 0; i < vec; ++i) gv[i] = gval(z[i]);
-      const int64_t base = (j + u * kBwdThreads) * vec;
+      const int64_t base = (j + u * NT) * vec;
       if (tv >= base && tv < base + vec) {
 #pragma unroll
         for (int i = 0; i < vec; ++i)
           if (base + i == tv) gv[i] -= gt;
       }
-      store_vec<DT>(gvec + j + u * kBwdThreads, gv);
+      store_vec<DT>(gvec + j + u * NT, gv);
     }
   }
 }
@@ -742,21 +747,29 @@ hipError_t launch_ce_forward_backward(const CeFwdParams& f, const CeBwdParams& b
   return ok ? hipGetLastError() : hipErrorInvalidValue;
 }
 
+// One workgroup per row; rows of at most kBwdShortRowBytes take the smaller
+// workgroup.
+template <int DT, bool ENT>
+void launch_bwd(const CeBwdParams& p, int64_t N, hipStream_t stream) {
+  if (p.V * (DT == 0 ? 4 : 2) <= kBwdShortRowBytes)
+    hipLaunchKernelGGL((ce_bwd_kernel<DT, ENT, kBwdThreadsShort>), dim3((unsigned)N),
+                       dim3(kBwdThreadsShort), 0, stream, p);
+  else
+    hipLaunchKernelGGL((ce_bwd_kernel<DT, ENT, kBwdThreads>), dim3((unsigned)N),
+                       dim3(kBwdThreads), 0, stream, p);
+}
+
 hipError_t launch_ce_backward(const CeBwdParams& p, int dtype, int64_t N, hipStream_t stream) {
   if (N <= 0) return hipSuccess;
   const bool ent = p.grad_entropy != nullptr;
   if (dtype == 0 && !ent)
-    hipLaunchKernelGGL((ce_bwd_kernel<0, false>), dim3((unsigned)N), dim3(kBwdThreads), 0,
-                       stream, p);
+    launch_bwd<0, false>(p, N, stream);
   else if (dtype == 0)
-    hipLaunchKernelGGL((ce_bwd_kernel<0, true>), dim3((unsigned)N), dim3(kBwdThreads), 0,
-                       stream, p);
+    launch_bwd<0, true>(p, N, stream);
   else if (!ent)
-    hipLaunchKernelGGL((ce_bwd_kernel<1, false>), dim3((unsigned)N), dim3(kBwdThreads), 0,
-                       stream, p);
+    launch_bwd<1, false>(p, N, stream);
   else
-    hipLaunchKernelGGL((ce_bwd_kernel<1, true>), dim3((unsigned)N), dim3(kBwdThreads), 0,
-                       stream, p);
+    launch_bwd<1, true>(p, N, stream);
   return hipGetLastError();
 }
 
