@@ -26,13 +26,17 @@ namespace {
 // the backward reads and writes it.  Measured on MI355X: at 4096 rows of
 // 32000 BF16 the forward takes 46-48 us with 512 threads and 58-61 us with
 // 1024 (more rows in flight per CU, shorter reductions), and the same at
-// 128256 columns; the backward is fastest with 1024 (85 vs 89 us at 32000,
+// 128256 columns, while rows of at most 48 KB are read faster by 256 (4096
+// rows of 8000 BF16: 17.7 against 24.2 us; of 16032: 25.5 against 30 us; of
+// 24000: 34.6 against 40 us; at 32000, 44.8 against 44.0 us); the backward is
+// fastest with 1024 (85 vs 89 us at 32000,
 // 364 vs 397 us at 128256) on rows over 32 KB, and with 512 on shorter ones,
 // where 1024 threads leave most lanes one vector or none (4096 rows of 8000
 // BF16: 22.5 against 35.7 us; of 16032: 45.5-46.8 against 47.0-48.0 us;
 // 256 threads are slower still at 16032).
 constexpr int kFwdThreads = 512;
-constexpr int kFwdWaves = kFwdThreads / 64;
+constexpr int kFwdThreadsShort = 256;
+constexpr int64_t kFwdShortRowBytes = 49152;
 constexpr int kBwdThreads = 1024;
 constexpr int kBwdThreadsShort = 512;
 constexpr int64_t kBwdShortRowBytes = 32768;
@@ -162,7 +166,7 @@ __device__ __forceinline__ void fold(S& st, const u32x4_t* w, int nvalid = N) {
   st.m = m_new;
 }
 
-template <class S>
+template <int NW, class S>
 __device__ __forceinline__ S block_reduce(S st, S* sh) {
   lse_wave_reduce(st);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -170,7 +174,7 @@ __device__ __forceinline__ S block_reduce(S st, S* sh) {
   __syncthreads();
   S r = sh[0];
 #pragma unroll
-  for (int w = 1; w < kFwdWaves; ++w) lse_merge(r, sh[w]);
+  for (int w = 1; w < NW; ++w) lse_merge(r, sh[w]);
   return r;
 }
 
@@ -187,11 +191,11 @@ struct StateOf<true> {
 // SHARD: the row holds vocabulary columns v0 .. v0 + V - 1 of a larger
 // vocabulary; instead of the loss, write the shard's partial statistics
 // (m, d, sum z, z_t if this shard holds the target else 0) for a later merge.
-template <int DT, bool ENT, bool SHARD>
-__global__ __launch_bounds__(kFwdThreads) void ce_fwd_kernel(CeFwdParams p) {
+template <int DT, bool ENT, bool SHARD, int NT>
+__global__ __launch_bounds__(NT) void ce_fwd_kernel(CeFwdParams p) {
   using T = typename Elem<DT>::T;
   using S = typename StateOf<ENT>::T;
-  __shared__ S sh[kFwdWaves];
+  __shared__ S sh[NT / 64];
   const int64_t r = blockIdx.x;
   const int64_t i0 = r / p.d1, i1 = r - i0 * p.d1;
   const int64_t t = p.targets[i0 * p.ts0 + i1 * p.ts1];
@@ -234,22 +238,22 @@ __global__ __launch_bounds__(kFwdThreads) void ce_fwd_kernel(CeFwdParams p) {
   }
   const u32x4_t* vrow = reinterpret_cast<const u32x4_t*>(row + rs.head);
   int64_t j = tid;
-  for (; j + (kUnroll - 1) * kFwdThreads < rs.nvec; j += kUnroll * kFwdThreads) {
+  for (; j + (kUnroll - 1) * NT < rs.nvec; j += kUnroll * NT) {
     u32x4_t w[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) w[u] = __builtin_nontemporal_load(vrow + j + u * kFwdThreads);
+    for (int u = 0; u < kUnroll; ++u) w[u] = __builtin_nontemporal_load(vrow + j + u * NT);
     fold<DT, kUnroll>(st, w);
   }
   if (j < rs.nvec) {  // last partial chunk: all its loads in flight together
-    const int nvalid = (int)((rs.nvec - j + kFwdThreads - 1) / kFwdThreads);
+    const int nvalid = (int)((rs.nvec - j + NT - 1) / NT);
     u32x4_t w[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
-      w[u] = u < nvalid ? __builtin_nontemporal_load(vrow + j + u * kFwdThreads)
+      w[u] = u < nvalid ? __builtin_nontemporal_load(vrow + j + u * NT)
                         : u32x4_t{0, 0, 0, 0};
     fold<DT, kUnroll>(st, w, nvalid);
   }
-  const S tot = block_reduce(st, sh);
+  const S tot = block_reduce<NT / 64>(st, sh);
   if (SHARD) {
     if (tid == 0) {
       *reinterpret_cast<f32x4_t*>(p.partial + 4 * r) = f32x4_t{tot.m, tot.d, tot.s, zt};
@@ -454,12 +458,12 @@ __global__ __launch_bounds__(NT) void ce_bwd_kernel(CeBwdParams p) {
 // written as ce_fwd_kernel writes them, and the gradient is written from the
 // registers exactly as ce_bwd_kernel computes it from those statistics: one
 // read and one write of the logits instead of two reads and one write.
-template <int DT, int NV>
-__global__ __launch_bounds__(kFwdThreads) void ce_fb_kernel(CeFwdParams f, CeBwdParams b) {
+template <int DT, int NV, int NT>
+__global__ __launch_bounds__(NT) void ce_fb_kernel(CeFwdParams f, CeBwdParams b) {
   using T = typename Elem<DT>::T;
   constexpr int vec = Elem<DT>::kVec;
   constexpr int NC = NV / kUnroll;  // chunks of four vectors per thread
-  __shared__ LseState sh[kFwdWaves];
+  __shared__ LseState sh[NT / 64];
   const int64_t r = blockIdx.x;
   const int64_t i0 = r / f.d1, i1 = r - i0 * f.d1;
   const int64_t t = f.targets[i0 * f.ts0 + i1 * f.ts1];
@@ -488,21 +492,21 @@ __global__ __launch_bounds__(kFwdThreads) void ce_fb_kernel(CeFwdParams f, CeBwd
       }
       const u32x4_t* vrow = reinterpret_cast<const u32x4_t*>(row + rs.head);
       int64_t j = tid;
-      for (; j + (kUnroll - 1) * kFwdThreads < rs.nvec; j += kUnroll * kFwdThreads) {
+      for (; j + (kUnroll - 1) * NT < rs.nvec; j += kUnroll * NT) {
         u32x4_t w[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) w[u] = vrow[j + u * kFwdThreads];
+        for (int u = 0; u < kUnroll; ++u) w[u] = vrow[j + u * NT];
         fold<DT, kUnroll>(st, w);
       }
       if (j < rs.nvec) {
-        const int nvalid = (int)((rs.nvec - j + kFwdThreads - 1) / kFwdThreads);
+        const int nvalid = (int)((rs.nvec - j + NT - 1) / NT);
         u32x4_t w[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-          w[u] = u < nvalid ? vrow[j + u * kFwdThreads] : u32x4_t{0, 0, 0, 0};
+          w[u] = u < nvalid ? vrow[j + u * NT] : u32x4_t{0, 0, 0, 0};
         fold<DT, kUnroll>(st, w, nvalid);
       }
-      const LseState tot = block_reduce(st, sh);
+      const LseState tot = block_reduce<NT / 64>(st, sh);
       if (tid == 0) {
         f.loss_tok[r] = __builtin_nanf("");
         *reinterpret_cast<f32x4_t*>(f.stats + 4 * r) =
@@ -520,7 +524,7 @@ __global__ __launch_bounds__(kFwdThreads) void ce_fb_kernel(CeFwdParams f, CeBwd
       const int64_t idx = tid < rs.head ? tid : rs.tail0 + (tid - rs.head);
       store_one<DT>(grow + idx, fill);
     }
-    for (int64_t j = tid; j < rs.nvec; j += kFwdThreads) store_vec<DT>(gvec + j, fv);
+    for (int64_t j = tid; j < rs.nvec; j += NT) store_vec<DT>(gvec + j, fv);
     return;
   }
 
@@ -539,22 +543,22 @@ __global__ __launch_bounds__(kFwdThreads) void ce_fb_kernel(CeFwdParams f, CeBwd
   u32x4_t w[NV];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    const int64_t j = tid + (int64_t)c * kUnroll * kFwdThreads;
-    if (j + (kUnroll - 1) * kFwdThreads < rs.nvec) {
+    const int64_t j = tid + (int64_t)c * kUnroll * NT;
+    if (j + (kUnroll - 1) * NT < rs.nvec) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u)
-        w[c * kUnroll + u] = __builtin_nontemporal_load(vrow + j + u * kFwdThreads);
+        w[c * kUnroll + u] = __builtin_nontemporal_load(vrow + j + u * NT);
       fold<DT, kUnroll>(st, &w[c * kUnroll]);
     } else if (j < rs.nvec) {
-      const int nvalid = (int)((rs.nvec - j + kFwdThreads - 1) / kFwdThreads);
+      const int nvalid = (int)((rs.nvec - j + NT - 1) / NT);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u)
-        w[c * kUnroll + u] = u < nvalid ? __builtin_nontemporal_load(vrow + j + u * kFwdThreads)
+        w[c * kUnroll + u] = u < nvalid ? __builtin_nontemporal_load(vrow + j + u * NT)
                                         : u32x4_t{0, 0, 0, 0};
       fold<DT, kUnroll>(st, &w[c * kUnroll], nvalid);
     }
   }
-  const LseState tot = block_reduce(st, sh);
+  const LseState tot = block_reduce<NT / 64>(st, sh);
   if (tid == 0) {
     const float mean = tot.s / (float)V;
     f.loss_tok[r] = ce_row_loss(tot.m, tot.d, zt, mean, f.eps);
@@ -592,7 +596,7 @@ __global__ __launch_bounds__(kFwdThreads) void ce_fb_kernel(CeFwdParams f, CeBwd
   for (int c = 0; c < NC; ++c) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t j = tid + (int64_t)(c * kUnroll + u) * kFwdThreads;
+      const int64_t j = tid + (int64_t)(c * kUnroll + u) * NT;
       if (j < rs.nvec) {
         float z[vec];
         unpack<DT>(w[c * kUnroll + u], z);
@@ -674,30 +678,46 @@ hipError_t launch_shift_targets(const ShiftParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Rows of at most kFwdShortRowBytes take the smaller workgroup (the one-pass
+// kernel follows the same rule, so that its statistics are reduced in the
+// same order).
+static inline bool fwd_short_row(int dtype, int64_t V) {
+  return V * (dtype == 0 ? 4 : 2) <= kFwdShortRowBytes;
+}
+
+template <int DT, bool ENT, bool SHARD>
+void launch_fwd(const CeFwdParams& p, int64_t N, hipStream_t stream) {
+  if (fwd_short_row(DT, p.V))
+    hipLaunchKernelGGL((ce_fwd_kernel<DT, ENT, SHARD, kFwdThreadsShort>), dim3((unsigned)N),
+                       dim3(kFwdThreadsShort), 0, stream, p);
+  else
+    hipLaunchKernelGGL((ce_fwd_kernel<DT, ENT, SHARD, kFwdThreads>), dim3((unsigned)N),
+                       dim3(kFwdThreads), 0, stream, p);
+}
+
 hipError_t launch_ce_forward(const CeFwdParams& p, int dtype, int64_t N, hipStream_t stream) {
   if (N <= 0) return hipSuccess;
-  const dim3 g((unsigned)N), b(kFwdThreads);
   if (p.partial) {
     const bool ent = p.partial_w != nullptr;
     if (dtype == 0 && !ent)
-      hipLaunchKernelGGL((ce_fwd_kernel<0, false, true>), g, b, 0, stream, p);
+      launch_fwd<0, false, true>(p, N, stream);
     else if (dtype == 0)
-      hipLaunchKernelGGL((ce_fwd_kernel<0, true, true>), g, b, 0, stream, p);
+      launch_fwd<0, true, true>(p, N, stream);
     else if (!ent)
-      hipLaunchKernelGGL((ce_fwd_kernel<1, false, true>), g, b, 0, stream, p);
+      launch_fwd<1, false, true>(p, N, stream);
     else
-      hipLaunchKernelGGL((ce_fwd_kernel<1, true, true>), g, b, 0, stream, p);
+      launch_fwd<1, true, true>(p, N, stream);
     return hipGetLastError();
   }
   const bool ent = p.entropy != nullptr;
   if (dtype == 0 && !ent)
-    hipLaunchKernelGGL((ce_fwd_kernel<0, false, false>), g, b, 0, stream, p);
+    launch_fwd<0, false, false>(p, N, stream);
   else if (dtype == 0)
-    hipLaunchKernelGGL((ce_fwd_kernel<0, true, false>), g, b, 0, stream, p);
+    launch_fwd<0, true, false>(p, N, stream);
   else if (!ent)
-    hipLaunchKernelGGL((ce_fwd_kernel<1, false, false>), g, b, 0, stream, p);
+    launch_fwd<1, false, false>(p, N, stream);
   else
-    hipLaunchKernelGGL((ce_fwd_kernel<1, true, false>), g, b, 0, stream, p);
+    launch_fwd<1, true, false>(p, N, stream);
   return hipGetLastError();
 }
 
@@ -720,15 +740,25 @@ namespace {
 
 template <int DT>
 bool launch_fb_dt(const CeFwdParams& f, const CeBwdParams& b, int64_t N, hipStream_t stream) {
-  // vectors per thread to hold the row (the 16-byte head/tail are scalars)
+  // vectors per thread to hold the row (the 16-byte head/tail are scalars);
+  // the workgroup size is the forward's for the same row
   const int64_t nvec = f.V / Elem<DT>::kVec;
-  const dim3 g((unsigned)N), blk(kFwdThreads);
+  const dim3 g((unsigned)N);
+  if (fwd_short_row(DT, f.V)) {
+    const dim3 blk(kFwdThreadsShort);
+    if (nvec <= 8 * kFwdThreadsShort)
+      hipLaunchKernelGGL((ce_fb_kernel<DT, 8, kFwdThreadsShort>), g, blk, 0, stream, f, b);
+    else
+      hipLaunchKernelGGL((ce_fb_kernel<DT, 16, kFwdThreadsShort>), g, blk, 0, stream, f, b);
+    return true;
+  }
+  const dim3 blk(kFwdThreads);
   if (nvec <= 8 * kFwdThreads)
-    hipLaunchKernelGGL((ce_fb_kernel<DT, 8>), g, blk, 0, stream, f, b);
+    hipLaunchKernelGGL((ce_fb_kernel<DT, 8, kFwdThreads>), g, blk, 0, stream, f, b);
   else if (nvec <= 16 * kFwdThreads)
-    hipLaunchKernelGGL((ce_fb_kernel<DT, 16>), g, blk, 0, stream, f, b);
+    hipLaunchKernelGGL((ce_fb_kernel<DT, 16, kFwdThreads>), g, blk, 0, stream, f, b);
   else if (nvec <= kFbVecs * kFwdThreads)
-    hipLaunchKernelGGL((ce_fb_kernel<DT, kFbVecs>), g, blk, 0, stream, f, b);
+    hipLaunchKernelGGL((ce_fb_kernel<DT, kFbVecs, kFwdThreads>), g, blk, 0, stream, f, b);
   else
     return false;
   return true;
