@@ -124,13 +124,17 @@ def test_sqbv_v128256_bf16_in_place_equals_separate(headline):
                                      (1003, "fp32"), (4099, "bf16"), (33333, "bf16"),
                                      (16383, "bf16"), (16385, "bf16"), (32767, "bf16"),
                                      (32769, "bf16"), (8191, "fp32"), (8193, "fp32"),
-                                     (16385, "fp32")])
+                                     (16385, "fp32"), (16384, "bf16"), (24576, "bf16"),
+                                     (24577, "bf16"), (8192, "fp32"), (12288, "fp32"),
+                                     (12289, "fp32")])
 def test_ragged_vocab(V, dtype):
     # V not a multiple of the vector width: rows start at every 16-byte phase.
     # Widths around one pass of the forward's 512 threads (4 loads of 16 B
     # each: 16384 BF16 or 8192 FP32 elements) and of the backward's 1024
     # (32768 BF16, 16384 FP32) leave 0, 1 or all-but-one vectors in the last
-    # partial chunk.
+    # partial chunk.  Rows of at most 32 KB (16384 BF16, 8192 FP32) take the
+    # backward's smaller workgroup and rows of at most 48 KB (24576 BF16,
+    # 12288 FP32) the forward's: both sides of each limit are here.
     case = wl.make_logits(2000 + V, 3, 5, V, dtype=dtype, sigma=3.0, ignore_count=2,
                           label_smoothing=0.05, reduce_loss=False, grad_output="random")
     _say(f"ragged V={V} {dtype}")
