@@ -72,8 +72,13 @@ def bench_logits(case, steps: int, warmup: int):
     import vocabulary_cross_entropy_amd as vce
     from vocabulary_cross_entropy_amd import accounting
 
+    from vocabulary_cross_entropy_amd import workloads as wl
+
     dev = torch.device("cuda:0")
-    z = _bf16_dev(case.logits, dev)
+    if case.dtype == wl.DTYPE_BF16:
+        z = _bf16_dev(case.logits, dev)
+    else:
+        z = torch.from_numpy(np.ascontiguousarray(case.logits)).to(dev)
     t = torch.from_numpy(case.targets).to(dev)
     go = torch.from_numpy(case.grad_output).to(dev)
     if case.reduce_loss:
@@ -473,6 +478,19 @@ def main():
         print(f"[bench] logits CE {mcase.name}: {r['ms_per_step']:.3f} ms/step", file=sys.stderr,
               flush=True)
         del mcase
+        # the tiny correctness workload (B=2, SQ=4, V=1000 FP32) in its four
+        # label-smoothing x reduction settings: launch-bound, so only its step
+        # time is reported (a roofline fraction would mean nothing here)
+        for eps_, red_ in ((0.0, False), (0.0, True), (0.1, False), (0.1, True)):
+            tcase = wl.tiny_logits(eps_, red_)
+            r = bench_logits(tcase, args.steps, args.warmup)
+            other[tcase.name] = {"ms_per_step": round(r["ms_per_step"], 4),
+                                 "tokens_per_s": round(r["tokens_per_s"], 1),
+                                 "one_pass_ms_per_step": round(r["one_pass_ms"], 4),
+                                 "bound": "launch latency"}
+        print(f"[bench] logits CE tiny workloads: "
+              f"{', '.join(str(v['ms_per_step']) for k, v in other.items() if k.startswith('tiny'))}"
+              f" ms/step", file=sys.stderr, flush=True)
     lin = None
     if not args.no_linear and args.only in (None, "linear"):
         print("[bench] generating the linear workload M=4096 H=4096 V=131072", file=sys.stderr,
