@@ -98,8 +98,9 @@ const char* vce_strerror(int status);
  *  stats    (N, 4) FP32 saved statistics (see above), always written.
  *  n_valid  1 int32: count of non-ignored rows; required iff reduce_loss
  *           (the backward of the averaged loss reads it), else may be NULL.
- *  Kernels: one row sweep (one 1024-thread workgroup per row), plus one
- *  single-workgroup deterministic mean when reduce_loss or n_valid is given.
+ *  Kernels: one row sweep (one workgroup per row: 512 threads, 256 for rows
+ *  of at most 48 KB), plus one single-workgroup deterministic mean when
+ *  reduce_loss or n_valid is given.
  *  entropy  (N) FP32, or NULL: written iff non-NULL (costs one more FMA per
  *           logit; the path without it is unchanged).
  */
