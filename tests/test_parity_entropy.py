@@ -4,8 +4,9 @@ logits and the linear form, through the C-ABI.
 
 Entropy values are held to the loss bar (1e-4 abs + 1e-5 rel; the linear form
 to its loss bar, 1e-3 rel).  The gradient with an entropy term: BF16 to 1 ulp
-of the rounded oracle value outside the cancellation band, where the band's
-terms now include the entropy term's T_H = |gH| p (|E_p[z]| + |z|); FP32 to
+of the rounded oracle value outside the cancellation band, which the entropy
+term's size T_H = |gH| p (|E_p[z]| + |z|) widens by 2^-10 T_H (2^8 times its
+error bound 2^-18 T_H, see below); FP32 to
 1e-6 + 2^-18 T_H (the term multiplies E_p[z] - z, formed in FP32 from values
 of magnitude |E_p[z]| + |z|, so a few of their ulps carry through; the plain
 bar 1e-6 is kept where gH = 0); dX and dW of the linear form to 5e-3 relative
@@ -34,7 +35,8 @@ def _grad_entropy(seed, shape):
 
 
 def _terms(z_rows, ref_stats, H, g, gH, targets, eps, ignore_idx):
-    """Per-element magnitude of the summands of g (p - q) + gH p (E_p[z] - z)."""
+    """Per-element magnitudes of the summands of g (p - q) + gH p (E_p[z] - z):
+    T = |g| (p + q) and T_H = |gH| p (|E_p[z]| + |z|)."""
     V = z_rows.shape[1]
     with np.errstate(invalid="ignore", divide="ignore", over="ignore"):
         lse = ref_stats[:, 0] + np.log(ref_stats[:, 1])
@@ -45,9 +47,11 @@ def _terms(z_rows, ref_stats, H, g, gH, targets, eps, ignore_idx):
     q[r, targets[r]] += 1.0 - eps
     E = (lse - H)[:, None]
     zf = np.where(np.isfinite(z_rows), np.abs(z_rows), 0.0)
-    T = np.abs(g)[:, None] * (p + q) + np.abs(gH)[:, None] * p * (np.abs(E) + zf)
+    T = np.abs(g)[:, None] * (p + q)
+    T_H = np.abs(gH)[:, None] * p * (np.abs(E) + zf)
     T[~valid] = 0.0
-    return np.nan_to_num(T)
+    T_H[~valid] = 0.0
+    return np.nan_to_num(T), np.nan_to_num(T_H)
 
 
 def _assert_grad_fp32_entropy(gpu, ref, T_H, what):
@@ -118,9 +122,9 @@ def test_entropy_logits(dtype, V, eps, reduce_loss):
         worst = _assert_grad_fp32_entropy(gpu, ref, T_H, "grad with entropy")
     else:
         z = oracle.bf16_to_f64(case.logits.reshape(case.N, V))
-        T = _terms(z, st, ref_H, g, gH.astype(np.float64), case.targets.reshape(-1), eps,
-                   case.ignore_idx)
-        worst = assert_grad_bf16(gpu, ref, T, "grad with entropy")
+        T, T_H = _terms(z, st, ref_H, g, gH.astype(np.float64), case.targets.reshape(-1), eps,
+                        case.ignore_idx)
+        worst = assert_grad_bf16(gpu, ref, T, "grad with entropy", extra_terms=T_H)
     _say(f"entropy max abs err {err:.2e}; gradient worst {worst}")
 
 

@@ -15,6 +15,8 @@
 // element); the row state is merged across the wavefront with butterfly
 // shuffles and across wavefronts in LDS.  The workgroup sizes were measured
 // on MI355X (see kFwdThreads).
+#include <type_traits>
+
 #include "vce_device.h"
 #include "vce_internal.h"
 
@@ -131,14 +133,21 @@ __device__ __forceinline__ void fold(S& st, const u32x4_t* w, int nvalid = N) {
     for (int i = 0; i < vec; ++i) cm = fmaxf(cm, z[u][i]);
   const float m_new = fmaxf(st.m, cm);
   const float mref = (m_new == kNegInf) ? 0.0f : m_new;
+  // (z - m) log2(e) as z log2(e) - mL with mL = fl(m log2(e)): one FMA per
+  // logit.  Every term of the chunk then carries the factor 2^rho of the
+  // rounding rho = m log2(e) - mL (exact by an FMA), taken back out of the
+  // chunk's sum below; what remains per term is the rounding of the FMA,
+  // relative to (z - m) log2(e), so the terms near the maximum, which make
+  // up d, are the most accurate.  A NaN logit makes d NaN.
   const float mL = mref * kLog2e;
+  const float rho = __builtin_fmaf(mref, kLog2e, -mL);
   float dpart[N], wpart[N];
 #pragma unroll
   for (int u = 0; u < N; ++u) {
     float acc = 0.0f, accw = 0.0f;
 #pragma unroll
     for (int i = 0; i < vec; ++i) {
-      const float t = __builtin_fmaf(z[u][i], kLog2e, -mL);  // (z - m) log2(e)
+      const float t = __builtin_fmaf(z[u][i], kLog2e, -mL);
       const float e = exp2_hw(t);
       acc += e;
       // -inf logits: e = 0 and t = -inf; the clamp keeps 0 * t finite
@@ -150,7 +159,11 @@ __device__ __forceinline__ void fold(S& st, const u32x4_t* w, int nvalid = N) {
   float dsum = dpart[0];
 #pragma unroll
   for (int u = 1; u < N; ++u) dsum += dpart[u];
-  const float f = exp2_hw((st.m - mref) * kLog2e);
+  // 2^-rho = 1 - rho ln 2 to within (rho ln 2)^2 / 2: |rho| is half an FP32 ulp
+  // of m log2(e) at most, below 2^-10 for |m| < 2^13; beyond, the exponential
+  const float corr = fabsf(rho) < 0x1p-10f ? -rho * kLn2 : exp2_hw(-rho) - 1.0f;
+  dsum = __builtin_fmaf(dsum, corr, dsum);
+  const float f = exp_diff(st.m - mref);
   if constexpr (kEnt) {
     float wsum = wpart[0];
 #pragma unroll
@@ -367,7 +380,6 @@ __global__ __launch_bounds__(NT) void ce_bwd_kernel(CeBwdParams p) {
   const f32x4_t sv = *reinterpret_cast<const f32x4_t*>(p.stats + 4 * r);
   const float m = sv[0], d = sv[1];
   const float mref = (m == kNegInf) ? 0.0f : m;
-  const float mL = mref * kLog2e;
   const float gs = g / d;
   const float goff = g * (p.eps / (float)p.Vg);
   const int64_t tl = t - p.v0;  // target column within this row (may lie outside)
@@ -377,75 +389,87 @@ __global__ __launch_bounds__(NT) void ce_bwd_kernel(CeBwdParams p) {
     gHd = p.grad_entropy[r] / d;
     ez = mref + kLn2 * log2_hw(d) - p.entropy[r];  // E_p[z] = lse - H
   }
-  // gradient of one logit, before the target correction; -inf logits (p = 0)
-  // are clamped so that p (E_p[z] - z) stays 0
-  auto gval = [&](float z) -> float {
-    const float e = exp2_hw(__builtin_fmaf(z, kLog2e, -mL));
-    if constexpr (ENT)
-      return e * __builtin_fmaf(gHd, ez - fmaxf(z, -1e30f), gs) - goff;
-    else
-      return e * gs - goff;
+  // Gradient of one logit, before the target correction: e^(z - m) from the
+  // exact difference (its error does not grow with |z| or |m|, so elements
+  // where p and the smoothing term nearly cancel keep their BF16 rounding).
+  // A row with a finite mean logit holds no infinite or NaN logit, and with
+  // |m| <= 2^100 no z - m can overflow, so it skips the clamp that -inf
+  // logits (p = 0) need; the entropy term always clamps, so that
+  // p (E_p[z] - z) stays 0 there.  A NaN logit has made d NaN in the
+  // forward, hence the whole row.
+  const bool finite_row = !ENT && __builtin_isfinite(sv[3]) && fabsf(m) <= 0x1p100f;
+  auto sweep = [&](auto clamp) {
+    auto gval = [&](float z) -> float {
+      const float e = decltype(clamp)::value ? exp_diff(z - mref) : exp_diff_finite(z - mref);
+      if constexpr (ENT)
+        return e * __builtin_fmaf(gHd, ez - fmaxf(z, -1e30f), gs) - goff;
+      else
+        return e * gs - goff;
+    };
+    {
+      const int64_t nscal = rs.head + (V - rs.tail0);
+      if (tid < nscal) {
+        const int64_t idx = tid < rs.head ? tid : rs.tail0 + (tid - rs.head);
+        const float z = Elem<DT>::load(row + idx);
+        float gv = gval(z);
+        if (idx == tl) gv -= gt;
+        store_one<DT>(grow + idx, gv);
+      }
+    }
+    // The logits row and the gradient row share their alignment within 16
+    // bytes only if their base offsets agree; the host guarantees it (same
+    // strides and equal base alignment), so the same split serves both.
+    const u32x4_t* vrow = reinterpret_cast<const u32x4_t*>(row + rs.head);
+    const int64_t tv = tl - rs.head;  // target position inside the vector body
+    int64_t j = tid;
+    for (; j + (kUnroll - 1) * NT < rs.nvec; j += kUnroll * NT) {
+      u32x4_t w[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) w[u] = __builtin_nontemporal_load(vrow + j + u * NT);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        float z[vec];
+        unpack<DT>(w[u], z);
+        float gv[vec];
+#pragma unroll
+        for (int i = 0; i < vec; ++i) gv[i] = gval(z[i]);
+        const int64_t base = (j + u * NT) * vec;
+        if (tv >= base && tv < base + vec) {
+#pragma unroll
+          for (int i = 0; i < vec; ++i)
+            if (base + i == tv) gv[i] -= gt;
+        }
+        store_vec<DT>(gvec + j + u * NT, gv);
+      }
+    }
+    if (j < rs.nvec) {  // last partial chunk: all its loads in flight together
+      const int nvalid = (int)((rs.nvec - j + NT - 1) / NT);
+      u32x4_t w[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        if (u < nvalid) w[u] = __builtin_nontemporal_load(vrow + j + u * NT);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        if (u >= nvalid) break;
+        float z[vec];
+        unpack<DT>(w[u], z);
+        float gv[vec];
+#pragma unroll
+        for (int i = 0; i < vec; ++i) gv[i] = gval(z[i]);
+        const int64_t base = (j + u * NT) * vec;
+        if (tv >= base && tv < base + vec) {
+#pragma unroll
+          for (int i = 0; i < vec; ++i)
+            if (base + i == tv) gv[i] -= gt;
+        }
+        store_vec<DT>(gvec + j + u * NT, gv);
+      }
+    }
   };
-
-  {
-    const int64_t nscal = rs.head + (V - rs.tail0);
-    if (tid < nscal) {
-      const int64_t idx = tid < rs.head ? tid : rs.tail0 + (tid - rs.head);
-      const float z = Elem<DT>::load(row + idx);
-      float gv = gval(z);
-      if (idx == tl) gv -= gt;
-      store_one<DT>(grow + idx, gv);
-    }
-  }
-  // The logits row and the gradient row share their alignment within 16 bytes
-  // only if their base offsets agree; the host guarantees it (same strides and
-  // equal base alignment), so the same split serves both.
-  const u32x4_t* vrow = reinterpret_cast<const u32x4_t*>(row + rs.head);
-  const int64_t tv = tl - rs.head;  // target position inside the vector body
-  int64_t j = tid;
-  for (; j + (kUnroll - 1) * NT < rs.nvec; j += kUnroll * NT) {
-    u32x4_t w[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) w[u] = __builtin_nontemporal_load(vrow + j + u * NT);
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      float z[vec];
-      unpack<DT>(w[u], z);
-      float gv[vec];
-#pragma unroll
-      for (int i = 0; i < vec; ++i) gv[i] = gval(z[i]);
-      const int64_t base = (j + u * NT) * vec;
-      if (tv >= base && tv < base + vec) {
-#pragma unroll
-        for (int i = 0; i < vec; ++i)
-          if (base + i == tv) gv[i] -= gt;
-      }
-      store_vec<DT>(gvec + j + u * NT, gv);
-    }
-  }
-  if (j < rs.nvec) {  // last partial chunk: all its loads in flight together
-    const int nvalid = (int)((rs.nvec - j + NT - 1) / NT);
-    u32x4_t w[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      if (u < nvalid) w[u] = __builtin_nontemporal_load(vrow + j + u * NT);
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if (u >= nvalid) break;
-      float z[vec];
-      unpack<DT>(w[u], z);
-      float gv[vec];
-#pragma unroll
-      for (int i = 0; i < vec; ++i) gv[i] = gval(z[i]);
-      const int64_t base = (j + u * NT) * vec;
-      if (tv >= base && tv < base + vec) {
-#pragma unroll
-        for (int i = 0; i < vec; ++i)
-          if (base + i == tv) gv[i] -= gt;
-      }
-      store_vec<DT>(gvec + j + u * NT, gv);
-    }
-  }
+  if (finite_row)
+    sweep(std::false_type{});
+  else
+    sweep(std::true_type{});
 }
 
 }  // namespace
@@ -578,41 +602,48 @@ __global__ __launch_bounds__(NT) void ce_fb_kernel(CeFwdParams f, CeBwdParams b)
   }
   const float m = tot.m, d = tot.d;
   const float mref = (m == kNegInf) ? 0.0f : m;
-  const float mL = mref * kLog2e;
   const float gs = g / d;
   const float goff = g * (b.eps / (float)V);
   const float gt = g * (1.0f - b.eps);
-  auto gval = [&](float z) -> float {
-    const float e = exp2_hw(__builtin_fmaf(z, kLog2e, -mL));
-    return e * gs - goff;
-  };
-  if (sidx >= 0) {
-    float gv = gval(zs);
-    if (sidx == t) gv -= gt;
-    store_one<DT>(grow + sidx, gv);
-  }
-  const int64_t tv = t - rs.head;
+  // the clamp rule of ce_bwd_kernel, from the same statistics
+  const bool finite_row = __builtin_isfinite(tot.s / (float)V) && fabsf(m) <= 0x1p100f;
+  auto sweep = [&](auto clamp) {
+    auto gval = [&](float z) -> float {
+      const float e = decltype(clamp)::value ? exp_diff(z - mref) : exp_diff_finite(z - mref);
+      return e * gs - goff;
+    };
+    if (sidx >= 0) {
+      float gv = gval(zs);
+      if (sidx == t) gv -= gt;
+      store_one<DT>(grow + sidx, gv);
+    }
+    const int64_t tv = t - rs.head;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
+    for (int c = 0; c < NC; ++c) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t j = tid + (int64_t)(c * kUnroll + u) * NT;
-      if (j < rs.nvec) {
-        float z[vec];
-        unpack<DT>(w[c * kUnroll + u], z);
-        float gv[vec];
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t j = tid + (int64_t)(c * kUnroll + u) * NT;
+        if (j < rs.nvec) {
+          float z[vec];
+          unpack<DT>(w[c * kUnroll + u], z);
+          float gv[vec];
 #pragma unroll
-        for (int i = 0; i < vec; ++i) gv[i] = gval(z[i]);
-        const int64_t base = j * vec;
-        if (tv >= base && tv < base + vec) {
+          for (int i = 0; i < vec; ++i) gv[i] = gval(z[i]);
+          const int64_t base = j * vec;
+          if (tv >= base && tv < base + vec) {
 #pragma unroll
-          for (int i = 0; i < vec; ++i)
-            if (base + i == tv) gv[i] -= gt;
+            for (int i = 0; i < vec; ++i)
+              if (base + i == tv) gv[i] -= gt;
+          }
+          store_vec<DT>(gvec + j, gv);
         }
-        store_vec<DT>(gvec + j, gv);
       }
     }
-  }
+  };
+  if (finite_row)
+    sweep(std::false_type{});
+  else
+    sweep(std::true_type{});
 }
 
 // Per-row merge of vocabulary-shard statistics, shards in fixed order

@@ -8,6 +8,10 @@ namespace vce {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// ln 2 in two parts: kLn2Hi is ln 2 rounded to FP32, kLn2Lo the FP32 value
+// nearest the remainder (ln 2 - kLn2Hi, about -1.9e-9).
+constexpr float kLn2Hi = 0.693147182464599609375f;
+constexpr float kLn2Lo = -1.9046542121259336e-09f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -21,6 +25,36 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 // log2(x) on the transcendental unit (v_log_f32).
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+// e^r for r <= 0 (r = z - m, a logit less its row maximum, formed exactly in
+// FP32: for BF16 inputs and any FP32 pair within a factor of two the
+// difference is exact).  t = fl(r log2 e) goes to the transcendental unit
+// unchanged, and the rounding left in t is put back as the factor 1 + c with
+// c = r - t ln 2, taken with ln 2 in two parts (the Cody-Waite reduction): the
+// result carries the exponential unit's own error and about one FP32 rounding,
+// independent of the size of z or m.  exp_diff_finite takes a finite r;
+// exp_diff also takes -inf, giving 0 (the clamp keeps t finite: e^-256 is 0
+// in FP32), and gives 0 for a NaN r too, so callers that must propagate NaN
+// logits do so through the row statistics.
+__device__ __forceinline__ float exp_diff_finite(float r) {
+  const float t = r * kLog2e;
+  float c = __builtin_fmaf(-t, kLn2Hi, r);
+  c = __builtin_fmaf(-t, kLn2Lo, c);
+  const float e0 = exp2_hw(t);
+  return __builtin_fmaf(e0, c, e0);
+}
+__device__ __forceinline__ float exp_diff(float r) { return exp_diff_finite(fmaxf(r, -256.0f)); }
+
+// Rescale factors of an online-softmax merge of two partial states with
+// maxima am and bm: the side with the larger maximum keeps factor 1 (exactly
+// exp_diff(0)), the other gets e^(m_small - m_big).  One exponential per
+// merge; two empty sides (both -inf) give factors 1 and 0 on zero sums.
+__device__ __forceinline__ void merge_factors(float am, float bm, float& fa, float& fb) {
+  const bool a_big = am >= bm;
+  const float f = exp_diff(a_big ? bm - am : am - bm);
+  fa = a_big ? 1.0f : f;
+  fb = a_big ? f : 1.0f;
+}
 
 // BF16 pair packed in one dword -> two floats (exact widening).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -57,10 +91,9 @@ struct LseState {
 // products are written as explicit FMAs so that every kernel rounds them the
 // same way (the compiler would otherwise pick which product to fuse).
 __device__ __forceinline__ void lse_merge(LseState& a, const LseState& b) {
-  float m = fmaxf(a.m, b.m);
-  float mref = (m == kNegInf) ? 0.0f : m;
-  float fa = exp2_hw((a.m - mref) * kLog2e);
-  float fb = exp2_hw((b.m - mref) * kLog2e);
+  const float m = fmaxf(a.m, b.m);
+  float fa, fb;
+  merge_factors(a.m, b.m, fa, fb);
   a.d = __builtin_fmaf(a.d, fa, b.d * fb);
   a.s = a.s + b.s;
   a.m = m;
@@ -93,8 +126,8 @@ struct LseEntState {
 __device__ __forceinline__ void lse_merge(LseEntState& a, const LseEntState& b) {
   const float m = fmaxf(a.m, b.m);
   const float mref = (m == kNegInf) ? 0.0f : m;
-  const float fa = exp2_hw((a.m - mref) * kLog2e);
-  const float fb = exp2_hw((b.m - mref) * kLog2e);
+  float fa, fb;
+  merge_factors(a.m, b.m, fa, fb);
   const float wa = a.d > 0.0f ? fa * __builtin_fmaf((a.m - mref) * kLog2e, a.d, a.w) : 0.0f;
   const float wb = b.d > 0.0f ? fb * __builtin_fmaf((b.m - mref) * kLog2e, b.d, b.w) : 0.0f;
   a.d = __builtin_fmaf(a.d, fa, b.d * fb);
