@@ -2,6 +2,7 @@
 and of its matrix-core GEMM building block with the FP64 oracle."""
 import hashlib
 import os
+import time
 
 import numpy as np
 import pytest
@@ -208,7 +209,7 @@ def test_linear_deterministic():
 
 
 # --- the full-size workloads: every token's loss against stored oracle values,
-# --- sampled rows of dX and dW computed by the oracle, and invariants ----------------
+# --- sampled rows of dX and dW, invariants, then the whole dX and dW --------------
 
 def _digest(case):
     h = hashlib.sha256()
@@ -256,6 +257,30 @@ def full_size(case):
          f"max |colsum dW| / bound {ratio:.2f}")
     assert fx <= LINEAR_FROB_RTOL and fw <= LINEAR_FROB_RTOL
     assert ratio <= 1.0
+    # The whole dX and dW against the FP64 oracle (the Liger-Kernel PR reports
+    # its error over whole tensors, Correctness).  The oracle runs over token
+    # ranges to bound host memory: each range gives its dX rows and its share
+    # of dW = sum over tokens of dZ_r^T X_r, summed here.
+    dWg = oracle.bf16_to_f64(to_host_bits(dW))
+    del dW, out["dW_dev"]
+    t0 = time.perf_counter()
+    ref_dW = np.zeros(dWg.shape)
+    num_x = den_x = 0.0
+    step = 2048
+    for s in range(0, case.M, step):
+        e = min(case.M, s + step)
+        rdx_s, rdw_s = linear.backward(case.X[s:e], case.W, case.targets[s:e], g[s:e],
+                                       case.label_smoothing, case.ignore_idx)
+        num_x += float(np.sum((out["dX"][s:e] - rdx_s) ** 2))
+        den_x += float(np.sum(rdx_s ** 2))
+        ref_dW += rdw_s
+        del rdx_s, rdw_s
+        _say(f"  oracle dX/dW over tokens {s}..{e - 1}: {time.perf_counter() - t0:.0f} s")
+    fxw = (num_x / den_x) ** 0.5
+    fww = rel_frobenius(dWg, ref_dW)
+    _say(f"{case.name}: whole-matrix relative Frobenius error dX {fxw:.2e}, dW {fww:.2e} "
+         f"(oracle {time.perf_counter() - t0:.0f} s)")
+    assert fxw <= LINEAR_FROB_RTOL and fww <= LINEAR_FROB_RTOL
 
 
 def test_linear_m4096_h4096_v131072():

@@ -25,8 +25,9 @@ STATUS = {0: "VCE_OK", 1: "VCE_EINVAL", 2: "VCE_EDTYPE", 3: "VCE_EALIGN", 4: "VC
 _I64, _I32, _F32, _VP, _SZ = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 SIGNATURES = {
     "vce_strerror": (ctypes.c_char_p, [_I32]),
+    "ce_workspace_size": (_SZ, []),
     "ce_forward": (_I32, [_VP, _I32, _I64, _I64, _I64, _I64, _I64, _VP, _I64, _I64, _F32, _I32, _I64,
-                          _VP, _VP, _VP, _VP, _VP, _VP]),
+                          _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "ce_backward": (_I32, [_VP, _VP, _I32, _I64, _I64, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _VP,
                            _VP, _VP, _VP, _F32, _I32, _I64, _I32, _VP]),
     "ce_forward_backward": (_I32, [_VP, _VP, _I32, _I64, _I64, _I64, _I64, _I64, _VP, _I64, _I64,
@@ -113,6 +114,38 @@ def _need_cuda(*ts):
             raise RuntimeError("libvce runs on the GPU only: tensors must be on a HIP device")
 
 
+def _check_buf(t, name: str, numel: int, dtype=torch.float32, *, one_ok: bool = False,
+               like: torch.Tensor | None = None):
+    """A tensor handed to the library as a flat buffer: its dtype, element
+    count (``numel``, or 1 with ``one_ok``), contiguity (the library reads it
+    in flattened row order) and device (that of ``like``).  None passes."""
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.numel() != numel and not (one_ok and t.numel() == 1):
+        want = f"{numel}" + (" or 1" if one_ok else "")
+        raise ValueError(f"{name} must hold {want} elements, got {t.numel()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if like is not None and t.device != like.device:
+        raise ValueError(f"{name} must be on {like.device}, got {t.device}")
+
+
+def _check_rows(N: int, like: torch.Tensor, *, stats=None, n_valid=None, grad_output=None,
+                reduce_loss=False, loss_tok=None, loss_mean=None, entropy=None,
+                grad_entropy=None):
+    """The per-row buffers of a logits or linear call with N rows."""
+    _check_buf(stats, "stats", 4 * N, like=like)
+    _check_buf(n_valid, "n_valid", 1, torch.int32, like=like)
+    if grad_output is not None:
+        _check_buf(grad_output, "grad_output", 1 if reduce_loss else N, like=like)
+    _check_buf(loss_tok, "loss_tok", N, like=like)
+    _check_buf(loss_mean, "loss_mean", 1, like=like)
+    _check_buf(entropy, "entropy", N, like=like)
+    _check_buf(grad_entropy, "grad_entropy", N, like=like)
+
+
 def _logits3d(logits: torch.Tensor, targets: torch.Tensor):
     if logits.dim() == 2:
         logits = logits.unsqueeze(0)
@@ -126,6 +159,14 @@ def _logits3d(logits: torch.Tensor, targets: torch.Tensor):
     return logits, targets
 
 
+def _check_grad(grad: torch.Tensor, logits: torch.Tensor):
+    if tuple(grad.shape) != tuple(logits.shape) or tuple(grad.stride()) != tuple(logits.stride()) \
+            or grad.dtype != logits.dtype:
+        raise ValueError("grad must have the shape, dtype and strides of logits")
+    if grad.device != logits.device:
+        raise ValueError(f"grad must be on {logits.device}, got {grad.device}")
+
+
 def _grad_like(logits: torch.Tensor) -> torch.Tensor:
     """An uninitialised tensor with the dtype and strides of ``logits`` whose
     rows start at the same offset within 16 bytes (the backward splits the
@@ -137,14 +178,26 @@ def _grad_like(logits: torch.Tensor) -> torch.Tensor:
     return buf.as_strided(logits.shape, logits.stride(), pad)
 
 
+def ce_workspace_size() -> int:
+    return int(lib().ce_workspace_size())
+
+
+def ce_workspace(device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for ``ce_forward``: with it the averaged loss and
+    the count come out of the forward's own launch.  Every call leaves it
+    zero-filled, so calls in order on one stream may share it; calls that may
+    overlap need one each."""
+    return torch.zeros(ce_workspace_size(), dtype=torch.uint8, device=device)
+
+
 def ce_forward(logits: torch.Tensor, targets: torch.Tensor, label_smoothing: float = 0.0,
                reduce_loss: bool = False, ignore_idx: int = -100, *, stream=None, out=None,
-               with_entropy: bool = False):
+               with_entropy: bool = False, workspace: torch.Tensor | None = None):
     """Forward of logits cross-entropy.  Returns (loss_tok, loss_mean, stats, n_valid),
     plus the per-row entropy with ``with_entropy``; loss_mean and n_valid are None
-    unless reduce_loss.  ``out`` gives the output tensors in the same order."""
+    unless reduce_loss.  ``out`` gives the output tensors in the same order.
+    ``workspace`` (from ``ce_workspace``) folds the mean into the forward's launch."""
     logits, targets = _logits3d(logits, targets)
-    _need_cuda(logits, targets)
     d0, d1, V = logits.shape
     dev = logits.device
     if out is None:
@@ -156,10 +209,16 @@ def ce_forward(logits: torch.Tensor, targets: torch.Tensor, label_smoothing: flo
     else:
         loss_tok, loss_mean, stats, n_valid = out[:4]
         ent = out[4] if with_entropy else None
+    _check_rows(d0 * d1, logits, stats=stats, n_valid=n_valid, loss_tok=loss_tok,
+                loss_mean=loss_mean, entropy=ent)
+    if workspace is not None:
+        _check_buf(workspace, "workspace", workspace.numel(), torch.uint8, like=logits)
+    _need_cuda(logits, targets)
     rc = lib().ce_forward(_ptr(logits), _dtype_code(logits), d0, d1, V, logits.stride(0),
                           logits.stride(1), _ptr(targets), targets.stride(0), targets.stride(1),
                           float(label_smoothing), int(bool(reduce_loss)), int(ignore_idx),
                           _ptr(loss_tok), _ptr(loss_mean), _ptr(stats), _ptr(n_valid), _ptr(ent),
+                          _ptr(workspace), 0 if workspace is None else workspace.numel(),
                           _stream(stream))
     _check("ce_forward", rc)
     if with_entropy:
@@ -177,16 +236,18 @@ def ce_backward(logits: torch.Tensor, targets: torch.Tensor, stats: torch.Tensor
     ``grad_entropy`` (per row) the entropy's gradient is added; ``entropy`` is
     then the forward's entropy output."""
     logits, targets = _logits3d(logits, targets)
-    _need_cuda(logits, targets, stats, grad_output)
     d0, d1, V = logits.shape
+    _check_rows(d0 * d1, logits, stats=stats, n_valid=n_valid if reduce_loss else None,
+                grad_output=grad_output, reduce_loss=reduce_loss, entropy=entropy,
+                grad_entropy=grad_entropy)
     if overwrite_input:
         grad = logits
     elif grad is None:
         grad = _grad_like(logits)
     elif grad.dim() == 2:
         grad = grad.unsqueeze(0)
-    if tuple(grad.stride()) != tuple(logits.stride()) or grad.dtype != logits.dtype:
-        raise ValueError("grad must have the dtype and strides of logits")
+    _check_grad(grad, logits)
+    _need_cuda(logits, targets, stats, grad_output)
     rc = lib().ce_backward(_ptr(logits), _ptr(grad), _dtype_code(logits), d0, d1, V,
                            logits.stride(0), logits.stride(1), _ptr(targets), targets.stride(0),
                            targets.stride(1), _ptr(stats), _ptr(n_valid), _ptr(grad_output),
@@ -204,7 +265,6 @@ def ce_forward_backward(logits: torch.Tensor, targets: torch.Tensor, grad_output
     """``ce_forward`` then ``ce_backward`` with the same arguments, in one pass
     over the logits.  Returns (loss_tok, loss_mean, stats, n_valid, grad)."""
     logits, targets = _logits3d(logits, targets)
-    _need_cuda(logits, targets, grad_output)
     d0, d1, V = logits.shape
     dev = logits.device
     if out is None:
@@ -214,14 +274,16 @@ def ce_forward_backward(logits: torch.Tensor, targets: torch.Tensor, grad_output
         n_valid = torch.empty((), dtype=torch.int32, device=dev) if reduce_loss else None
     else:
         loss_tok, loss_mean, stats, n_valid = out
+    _check_rows(d0 * d1, logits, stats=stats, n_valid=n_valid, grad_output=grad_output,
+                reduce_loss=reduce_loss, loss_tok=loss_tok, loss_mean=loss_mean)
     if overwrite_input:
         grad = logits
     elif grad is None:
         grad = _grad_like(logits)
     elif grad.dim() == 2:
         grad = grad.unsqueeze(0)
-    if tuple(grad.stride()) != tuple(logits.stride()) or grad.dtype != logits.dtype:
-        raise ValueError("grad must have the dtype and strides of logits")
+    _check_grad(grad, logits)
+    _need_cuda(logits, targets, grad_output)
     rc = lib().ce_forward_backward(_ptr(logits), _ptr(grad), _dtype_code(logits), d0, d1, V,
                                    logits.stride(0), logits.stride(1), _ptr(targets),
                                    targets.stride(0), targets.stride(1), _ptr(grad_output),
@@ -240,7 +302,6 @@ def ce_forward_shard(logits: torch.Tensor, targets: torch.Tensor, vocab_start: i
     With ``with_entropy`` also the shard's entropy statistic (d0, d1), returned
     second."""
     logits, targets = _logits3d(logits, targets)
-    _need_cuda(logits, targets)
     d0, d1, V = logits.shape
     part = torch.empty((d0, d1, 4), dtype=torch.float32, device=logits.device) if out is None \
         else out
@@ -248,6 +309,9 @@ def ce_forward_shard(logits: torch.Tensor, targets: torch.Tensor, vocab_start: i
     if with_entropy:
         pw = torch.empty((d0, d1), dtype=torch.float32, device=logits.device) if out_w is None \
             else out_w
+    _check_buf(part, "partial", 4 * d0 * d1, like=logits)
+    _check_buf(pw, "partial_w", d0 * d1, like=logits)
+    _need_cuda(logits, targets)
     rc = lib().ce_forward_shard(_ptr(logits), _dtype_code(logits), d0, d1, V, logits.stride(0),
                                 logits.stride(1), _ptr(targets), targets.stride(0),
                                 targets.stride(1), int(vocab_start), int(ignore_idx), _ptr(part),
@@ -273,7 +337,6 @@ def ce_merge_shards(partials: torch.Tensor, targets: torch.Tensor, V: int,
     if not partials.is_contiguous() or partials.dtype != torch.float32 or \
             partials.numel() != partials.shape[0] * d0 * d1 * 4:
         raise ValueError("partials must be contiguous float32 (n_shards, d0, d1, 4)")
-    _need_cuda(partials, targets)
     dev = partials.device
     if out is None:
         loss_tok = torch.empty((d0, d1), dtype=torch.float32, device=dev)
@@ -282,6 +345,9 @@ def ce_merge_shards(partials: torch.Tensor, targets: torch.Tensor, V: int,
         n_valid = torch.empty((), dtype=torch.int32, device=dev) if reduce_loss else None
     else:
         loss_tok, loss_mean, stats, n_valid = out
+    _check_rows(d0 * d1, partials, stats=stats, n_valid=n_valid, loss_tok=loss_tok,
+                loss_mean=loss_mean, entropy=out_entropy)
+    _need_cuda(partials, targets)
     ent = None
     if partials_w is not None:
         if not partials_w.is_contiguous() or partials_w.dtype != torch.float32 or \
@@ -310,16 +376,18 @@ def ce_backward_shard(logits: torch.Tensor, targets: torch.Tensor, vocab_start: 
     """Gradient of one vocabulary shard's logits from the merged ``stats``
     (with ``grad_entropy``, plus the entropy's, ``entropy`` the merged one)."""
     logits, targets = _logits3d(logits, targets)
-    _need_cuda(logits, targets, stats, grad_output)
     d0, d1, VL = logits.shape
+    _check_rows(d0 * d1, logits, stats=stats, n_valid=n_valid if reduce_loss else None,
+                grad_output=grad_output, reduce_loss=reduce_loss, entropy=entropy,
+                grad_entropy=grad_entropy)
     if overwrite_input:
         grad = logits
     elif grad is None:
         grad = _grad_like(logits)
     elif grad.dim() == 2:
         grad = grad.unsqueeze(0)
-    if tuple(grad.stride()) != tuple(logits.stride()) or grad.dtype != logits.dtype:
-        raise ValueError("grad must have the dtype and strides of logits")
+    _check_grad(grad, logits)
+    _need_cuda(logits, targets, stats, grad_output)
     rc = lib().ce_backward_shard(_ptr(logits), _ptr(grad), _dtype_code(logits), d0, d1, VL,
                                  logits.stride(0), logits.stride(1), _ptr(targets),
                                  targets.stride(0), targets.stride(1), int(vocab_start), int(V),
@@ -379,7 +447,20 @@ def _check_linear(X, W, targets, dtype=torch.bfloat16):
         raise ValueError("X (M,H), W (V,H), targets (M)")
     if targets.dtype != torch.int64:
         raise TypeError("targets must be int64")
-    _need_cuda(X, W, targets)
+    if W.device != X.device or targets.device != X.device:
+        raise ValueError("X, W and targets must be on one device")
+
+
+def _check_like(t, name: str, ref: torch.Tensor):
+    """An output with the shape and dtype of ``ref`` (dX like X, dW like W)."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(ref.shape) or t.dtype != ref.dtype:
+        raise ValueError(f"{name} must be {ref.dtype} of shape {tuple(ref.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != ref.device:
+        raise ValueError(f"{name} must be on {ref.device}, got {t.device}")
 
 
 def lce_forward(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
@@ -418,6 +499,10 @@ def _lce_forward(f32, X, W, targets, label_smoothing, reduce_loss, ignore_idx, w
     else:
         loss_tok, loss_mean, stats, n_valid = out[:4]
         ent = out[4] if with_entropy else None
+    _check_rows(M, X, stats=stats, n_valid=n_valid, loss_tok=loss_tok, loss_mean=loss_mean,
+                entropy=ent)
+    _check_buf(workspace, "workspace", workspace.numel(), torch.uint8, like=X)
+    _need_cuda(X, W, targets)
     name = "lce_forward_f32" if f32 else "lce_forward"
     rc = getattr(lib(), name)(_ptr(X), _ptr(W), M, H, V, _ptr(targets), float(label_smoothing),
                               int(bool(reduce_loss)), int(ignore_idx), _ptr(loss_tok),
@@ -466,6 +551,13 @@ def _lce_backward(f32, X, W, targets, stats, n_valid, grad_output, label_smoothi
         workspace = lce_workspace(M, H, V, X.device, f32)
     dX = torch.empty_like(X) if dX is None else dX
     dW = torch.empty_like(W) if dW is None else dW
+    _check_rows(M, X, stats=stats, n_valid=n_valid if reduce_loss else None,
+                grad_output=grad_output, reduce_loss=reduce_loss, entropy=entropy,
+                grad_entropy=grad_entropy)
+    _check_like(dX, "dX", X)
+    _check_like(dW, "dW", W)
+    _check_buf(workspace, "workspace", workspace.numel(), torch.uint8, like=X)
+    _need_cuda(X, W, targets, stats, grad_output)
     name = "lce_backward_f32" if f32 else "lce_backward"
     rc = getattr(lib(), name)(_ptr(X), _ptr(W), M, H, V, _ptr(targets), _ptr(stats),
                               _ptr(n_valid), _ptr(grad_output), _ptr(entropy),
@@ -491,6 +583,9 @@ def lce_forward_shard(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, v
     pw = None
     if with_entropy:
         pw = torch.empty(M, dtype=torch.float32, device=X.device) if out_w is None else out_w
+    _check_buf(part, "partial", 4 * M, like=X)
+    _check_buf(pw, "partial_w", M, like=X)
+    _need_cuda(X, W, targets)
     rc = lib().lce_forward_shard(_ptr(X), _ptr(W), M, H, V, _ptr(targets), int(vocab_start),
                                  int(ignore_idx), _ptr(part), _ptr(pw), _ptr(workspace),
                                  workspace.numel(), _stream(stream))
@@ -516,6 +611,12 @@ def lce_backward_shard(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, 
         workspace = lce_workspace(M, H, VL, X.device)
     dX = torch.empty_like(X) if dX is None else dX
     dW = torch.empty_like(W) if dW is None else dW
+    _check_rows(M, X, stats=stats, n_valid=n_valid if reduce_loss else None,
+                grad_output=grad_output, reduce_loss=reduce_loss, entropy=entropy,
+                grad_entropy=grad_entropy)
+    _check_like(dX, "dX", X)
+    _check_like(dW, "dW", W)
+    _need_cuda(X, W, targets, stats, grad_output)
     rc = lib().lce_backward_shard(_ptr(X), _ptr(W), M, H, VL, _ptr(targets), int(vocab_start),
                                   int(V), _ptr(stats), _ptr(n_valid), _ptr(grad_output),
                                   _ptr(entropy), _ptr(grad_entropy),
