@@ -83,12 +83,6 @@ enum vce_dtype { VCE_DTYPE_FP32 = 0, VCE_DTYPE_BF16 = 1 };
 const char* vce_strerror(int status);
 
 /*
- * ce_workspace_size: bytes of the optional ce_forward workspace (256; a
- * completion counter).  The same for every problem size.
- */
-size_t ce_workspace_size(void);
-
-/*
  * ce_forward: single-pass online-softmax forward of logits cross-entropy.
  *
  *  logits   (d0, d1, V) elements of `dtype` (FP32 or BF16).  Row (i0, i1)
@@ -104,26 +98,17 @@ size_t ce_workspace_size(void);
  *  stats    (N, 4) FP32 saved statistics (see above), always written.
  *  n_valid  1 int32: count of non-ignored rows; required iff reduce_loss
  *           (the backward of the averaged loss reads it), else may be NULL.
+ *  Kernels: one row sweep (one workgroup per row: 512 threads, 256 for rows
+ *  of at most 48 KB), plus one single-workgroup deterministic mean when
+ *  reduce_loss or n_valid is given.
  *  entropy  (N) FP32, or NULL: written iff non-NULL (costs one more FMA per
  *           logit; the path without it is unchanged).
- *  workspace  NULL, or at least ce_workspace_size() bytes of device memory,
- *           256-byte aligned (VCE_EALIGN), holding zeros before its first
- *           use (e.g. hipMemset once); every call leaves it holding zeros
- *           again.  VCE_EWORKSPACE if workspace_bytes is too small.  Calls
- *           that may run at the same time (other streams, other graphs) need
- *           distinct workspaces; calls in order on one stream may share one.
- *  Kernels: one row sweep (one workgroup per row: 512 threads, 256 for rows
- *  of at most 48 KB).  The averaged loss and n_valid (when reduce_loss or
- *  n_valid is given) are formed in a fixed order, the same bits either way:
- *  with a workspace by the row sweep's last workgroup inside the same launch
- *  (the workspace holds its completion counter), without one by a second,
- *  one-workgroup kernel.
  */
 int ce_forward(const void* logits, int dtype, int64_t d0, int64_t d1, int64_t V,
                int64_t ls0, int64_t ls1, const int64_t* targets, int64_t ts0, int64_t ts1,
                float label_smoothing, int reduce_loss, int64_t ignore_idx,
                float* loss_tok, float* loss_mean, float* stats, int32_t* n_valid,
-               float* entropy, void* workspace, size_t workspace_bytes, void* stream);
+               float* entropy, void* stream);
 
 /*
  * ce_backward: rebuild the logits gradient from the saved statistics.

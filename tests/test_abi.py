@@ -55,9 +55,9 @@ def test_strerror(L):
 
 def fwd(L, logits=A, dtype=1, d0=2, d1=3, V=1000, ls0=3000, ls1=1000, targets=A, ts0=3, ts1=1,
         eps=0.0, reduce_loss=0, ignore=-100, loss_tok=A, loss_mean=A, stats=A, n_valid=A,
-        entropy=None, ws=None, ws_bytes=0):
+        entropy=None):
     return L.ce_forward(logits, dtype, d0, d1, V, ls0, ls1, targets, ts0, ts1, eps, reduce_loss,
-                        ignore, loss_tok, loss_mean, stats, n_valid, entropy, ws, ws_bytes, None)
+                        ignore, loss_tok, loss_mean, stats, n_valid, entropy, None)
 
 
 def bwd(L, logits=A, grad=A + (1 << 30), dtype=1, d0=2, d1=3, V=1000, ls0=3000, ls1=1000, targets=A,
@@ -78,15 +78,9 @@ def bwd(L, logits=A, grad=A + (1 << 30), dtype=1, d0=2, d1=3, V=1000, ls0=3000, 
     (dict(stats=A + 4), 3), (dict(entropy=A + 2), 3),
     (dict(d0=1 << 32, d1=1 << 32), 1),
     (dict(d0=1 << 20, d1=1 << 12), 1),  # N above INT32_MAX rows
-    (dict(ws=A + 4, ws_bytes=256), 3),  # workspace not 256-byte aligned
-    (dict(ws=A, ws_bytes=255), 5),      # workspace smaller than ce_workspace_size()
 ])
 def test_ce_forward_rejects(L, kw, code):
     assert fwd(L, **kw) == code
-
-
-def test_ce_workspace_size(L):
-    assert L.ce_workspace_size() == 256
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -64,8 +64,6 @@ def test_ce_forward_rejects_malformed_outputs():
     bad_loss = (torch.empty((N_D1, N_D0)).t(), None, good[2], None)
     with pytest.raises(ValueError):
         vce.ce_forward(z, t, out=bad_loss)
-    with pytest.raises(ValueError):
-        vce.ce_forward(z, t, out=good, workspace=torch.zeros((16, 16), dtype=torch.uint8).t())
 
 
 def test_ce_forward_backward_rejects_malformed_grad_output():

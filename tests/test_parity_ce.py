@@ -265,95 +265,3 @@ def test_graph_capture_replay():
         torch.cuda.synchronize()
         assert torch.equal(loss, ref[0]) and torch.equal(mean, ref[1]) and torch.equal(grad, ref[2])
 
-
-# --- the averaged loss inside the forward's launch (caller workspace) -------------
-
-def _mean_cases():
-    return [wl.tiny_logits(0.1, True), wl.medium_logits(),
-            wl.make_logits(2201, 3, 5, 1001, dtype="bf16", sigma=3.0, ignore_count=2,
-                           label_smoothing=0.05, reduce_loss=True),
-            wl.make_logits(2202, 70, 1000, 64, dtype="bf16", sigma=2.0, ignore_frac=0.1,
-                           label_smoothing=0.2, reduce_loss=True),
-            wl.make_logits(2203, 1, 1, 5000, dtype="fp32", sigma=2.0, reduce_loss=True),
-            wl.make_logits(2204, 2, 16, 300, dtype="bf16", sigma=1.0, ignore_count=32,
-                           reduce_loss=True),
-            wl.make_logits(2205, 7, 3, 128256, dtype="bf16", sigma=4.0, ignore_count=1,
-                           reduce_loss=True)]
-
-
-def test_forward_workspace_mean_is_the_two_kernel_mean():
-    # One workspace serves every call in turn (grids of 1 to 70000
-    # workgroups): each call's mean and count equal the separate kernel's bit
-    # for bit and the oracle's, and the call leaves the workspace zero.
-    ws = vce.ce_workspace()
-    for case in _mean_cases():
-        z = to_device(case.logits, case.dtype)
-        t = torch.from_numpy(case.targets).cuda()
-        a = vce.ce_forward(z, t, case.label_smoothing, True, case.ignore_idx)
-        b = vce.ce_forward(z, t, case.label_smoothing, True, case.ignore_idx, workspace=ws)
-        torch.cuda.synchronize()
-        for i in range(4):
-            assert torch.equal(a[i], b[i]), f"{case.name}: output {i} differs"
-        assert torch.count_nonzero(ws) == 0, f"{case.name}: workspace not reset"
-        ref_loss, _, _ = oracle.ce_forward(case.logits, case.targets, case.label_smoothing,
-                                           case.ignore_idx)
-        ref_mean = oracle.mean_loss(ref_loss, case.targets, case.ignore_idx)
-        assert abs(b[1].item() - ref_mean) <= 1e-4 + 1e-5 * abs(ref_mean)
-        assert b[3].item() == oracle.n_valid(case.targets, case.ignore_idx)
-        _say(f"{case.name}: in-launch mean {b[1].item():.6f} = two-kernel mean, "
-             f"n_valid {b[3].item()}")
-
-
-def test_forward_workspace_count_without_mean():
-    # n_valid requested for a per-token loss: counted inside the launch too
-    case = wl.make_logits(2206, 4, 300, 3000, dtype="bf16", sigma=3.0, ignore_count=17)
-    z = to_device(case.logits, "bf16")
-    t = torch.from_numpy(case.targets).cuda()
-    ws = vce.ce_workspace()
-    out = (torch.empty((4, 300), device="cuda"), None, torch.empty((4, 300, 4), device="cuda"),
-           torch.full((), -1, dtype=torch.int32, device="cuda"))
-    vce.ce_forward(z, t, 0.0, False, out=out, workspace=ws)
-    torch.cuda.synchronize()
-    assert out[3].item() == 1200 - 17
-    assert torch.count_nonzero(ws) == 0
-
-
-def test_forward_workspace_graph_replay():
-    # forward (mean in the launch) + backward captured once, replayed three
-    # times with eager calls on the same workspace in between
-    case = wl.make_logits(2207, 4, 256, 8000, dtype="bf16", sigma=3.0, ignore_frac=0.05,
-                          label_smoothing=0.1, reduce_loss=True)
-    z = to_device(case.logits, "bf16")
-    t = torch.from_numpy(case.targets).cuda()
-    go = torch.ones(1, device="cuda")
-    ws = vce.ce_workspace()
-    out = (torch.empty((4, 256), device="cuda"), torch.empty((), device="cuda"),
-           torch.empty((4, 256, 4), device="cuda"), torch.empty((), dtype=torch.int32,
-                                                                device="cuda"))
-    grad = torch.empty_like(z)
-    vce.ce_forward(z, t, 0.1, True, out=out)
-    vce.ce_backward(z, t, out[2], out[3], go, 0.1, True, grad=grad)
-    torch.cuda.synchronize()
-    ref = [x.clone() for x in out] + [grad.clone()]
-    s = torch.cuda.Stream()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(s):
-        with torch.cuda.graph(graph, stream=s):
-            vce.ce_forward(z, t, 0.1, True, out=out, stream=s, workspace=ws)
-            vce.ce_backward(z, t, out[2], out[3], go, 0.1, True, grad=grad, stream=s)
-    torch.cuda.synchronize()
-    other = wl.make_logits(2208, 2, 100, 3000, dtype="bf16", sigma=2.0, ignore_count=3,
-                           reduce_loss=True)
-    zo = to_device(other.logits, "bf16")
-    to = torch.from_numpy(other.targets).cuda()
-    for rep in range(3):
-        for x in list(out) + [grad]:
-            x.zero_()
-        eager = vce.ce_forward(zo, to, 0.0, True, workspace=ws)  # the same workspace, eagerly
-        torch.cuda.synchronize()
-        assert eager[3].item() == 197 and torch.count_nonzero(ws) == 0
-        graph.replay()
-        torch.cuda.synchronize()
-        for i, (a, b) in enumerate(zip(list(out) + [grad], ref)):
-            assert torch.equal(a, b), f"replay {rep}: output {i} differs"
-        assert torch.count_nonzero(ws) == 0

@@ -89,28 +89,3 @@ def test_linear_calls_on_two_streams():
         for i, (x, y) in enumerate(zip(got_b, ref_b)):
             assert torch.equal(x, y), f"stream b, rep {rep}, output {i}"
     _say("linear: 3 concurrent repetitions equal the serial results")
-
-
-def test_logits_forward_workspaces_on_two_streams():
-    # the in-launch mean keeps its completion counter in the caller's
-    # workspace: one workspace per stream, and every result equals the serial
-    # one and the two-kernel path's
-    a = _logits_inputs(7005, 30000, 0.1, True)
-    b = _logits_inputs(7006, 5003, 0.05, True)
-    wa, wb = vce.ce_workspace(), vce.ce_workspace()
-    ref_a = vce.ce_forward(a[0], a[1], 0.1, True, IGN)
-    ref_b = vce.ce_forward(b[0], b[1], 0.05, True, IGN)
-    torch.cuda.synchronize()
-    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
-    for rep in range(3):
-        with torch.cuda.stream(sa):
-            got_a = vce.ce_forward(a[0], a[1], 0.1, True, IGN, stream=sa, workspace=wa)
-        with torch.cuda.stream(sb):
-            got_b = vce.ce_forward(b[0], b[1], 0.05, True, IGN, stream=sb, workspace=wb)
-        torch.cuda.synchronize()
-        for i, (x, y) in enumerate(zip(got_a, ref_a)):
-            assert torch.equal(x, y), f"stream a, rep {rep}, output {i}"
-        for i, (x, y) in enumerate(zip(got_b, ref_b)):
-            assert torch.equal(x, y), f"stream b, rep {rep}, output {i}"
-        assert torch.count_nonzero(wa) == 0 and torch.count_nonzero(wb) == 0
-    _say("logits forward with workspaces: 3 concurrent repetitions equal the serial results")

@@ -25,9 +25,8 @@ STATUS = {0: "VCE_OK", 1: "VCE_EINVAL", 2: "VCE_EDTYPE", 3: "VCE_EALIGN", 4: "VC
 _I64, _I32, _F32, _VP, _SZ = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 SIGNATURES = {
     "vce_strerror": (ctypes.c_char_p, [_I32]),
-    "ce_workspace_size": (_SZ, []),
     "ce_forward": (_I32, [_VP, _I32, _I64, _I64, _I64, _I64, _I64, _VP, _I64, _I64, _F32, _I32, _I64,
-                          _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+                          _VP, _VP, _VP, _VP, _VP, _VP]),
     "ce_backward": (_I32, [_VP, _VP, _I32, _I64, _I64, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _VP,
                            _VP, _VP, _VP, _F32, _I32, _I64, _I32, _VP]),
     "ce_forward_backward": (_I32, [_VP, _VP, _I32, _I64, _I64, _I64, _I64, _I64, _VP, _I64, _I64,
@@ -178,25 +177,12 @@ def _grad_like(logits: torch.Tensor) -> torch.Tensor:
     return buf.as_strided(logits.shape, logits.stride(), pad)
 
 
-def ce_workspace_size() -> int:
-    return int(lib().ce_workspace_size())
-
-
-def ce_workspace(device="cuda") -> torch.Tensor:
-    """A zero-filled workspace for ``ce_forward``: with it the averaged loss and
-    the count come out of the forward's own launch.  Every call leaves it
-    zero-filled, so calls in order on one stream may share it; calls that may
-    overlap need one each."""
-    return torch.zeros(ce_workspace_size(), dtype=torch.uint8, device=device)
-
-
 def ce_forward(logits: torch.Tensor, targets: torch.Tensor, label_smoothing: float = 0.0,
                reduce_loss: bool = False, ignore_idx: int = -100, *, stream=None, out=None,
-               with_entropy: bool = False, workspace: torch.Tensor | None = None):
+               with_entropy: bool = False):
     """Forward of logits cross-entropy.  Returns (loss_tok, loss_mean, stats, n_valid),
     plus the per-row entropy with ``with_entropy``; loss_mean and n_valid are None
-    unless reduce_loss.  ``out`` gives the output tensors in the same order.
-    ``workspace`` (from ``ce_workspace``) folds the mean into the forward's launch."""
+    unless reduce_loss.  ``out`` gives the output tensors in the same order."""
     logits, targets = _logits3d(logits, targets)
     d0, d1, V = logits.shape
     dev = logits.device
@@ -211,14 +197,11 @@ def ce_forward(logits: torch.Tensor, targets: torch.Tensor, label_smoothing: flo
         ent = out[4] if with_entropy else None
     _check_rows(d0 * d1, logits, stats=stats, n_valid=n_valid, loss_tok=loss_tok,
                 loss_mean=loss_mean, entropy=ent)
-    if workspace is not None:
-        _check_buf(workspace, "workspace", workspace.numel(), torch.uint8, like=logits)
     _need_cuda(logits, targets)
     rc = lib().ce_forward(_ptr(logits), _dtype_code(logits), d0, d1, V, logits.stride(0),
                           logits.stride(1), _ptr(targets), targets.stride(0), targets.stride(1),
                           float(label_smoothing), int(bool(reduce_loss)), int(ignore_idx),
                           _ptr(loss_tok), _ptr(loss_mean), _ptr(stats), _ptr(n_valid), _ptr(ent),
-                          _ptr(workspace), 0 if workspace is None else workspace.numel(),
                           _stream(stream))
     _check("ce_forward", rc)
     if with_entropy:

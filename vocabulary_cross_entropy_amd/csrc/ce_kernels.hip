@@ -200,80 +200,12 @@ struct StateOf<true> {
   using T = LseEntState;
 };
 
-// Averaged loss over the non-ignored rows [0, N) and their count, in a fixed
-// order: kMeanLanes virtual lanes, lane v sums the losses of rows v,
-// v + kMeanLanes, ... in FP64 in row order, then a pairwise tree over the
-// lanes.  Every workgroup size that divides kMeanLanes performs the same
-// additions in the same order, so the separate mean kernel and the forward's
-// last workgroup write the same bits.  loss_tok may be null (count only).
-constexpr int kMeanLanes = 1024;
-struct MeanScratch {
-  double sum[kMeanLanes];
-  int32_t cnt[kMeanLanes];
-};
-
-template <int NT>
-__device__ __forceinline__ void mean_and_count(const float* loss_tok, const int64_t* targets,
-                                               int64_t N, int64_t d1, int64_t ts0, int64_t ts1,
-                                               int64_t ignore_idx, float* loss_mean,
-                                               int32_t* n_valid, MeanScratch& sh) {
-  static_assert(kMeanLanes % NT == 0, "the workgroup size must divide the lane count");
-  for (int v = threadIdx.x; v < kMeanLanes; v += NT) {
-    double sum = 0.0;
-    int32_t cnt = 0;
-    for (int64_t r = v; r < N; r += kMeanLanes) {
-      const int64_t i0 = r / d1, i1 = r - i0 * d1;
-      if (targets[i0 * ts0 + i1 * ts1] != ignore_idx) {
-        if (loss_tok) sum += (double)loss_tok[r];
-        ++cnt;
-      }
-    }
-    sh.sum[v] = sum;
-    sh.cnt[v] = cnt;
-  }
-  __syncthreads();
-  for (int s = kMeanLanes / 2; s > 0; s >>= 1) {
-    for (int i = threadIdx.x; i < s; i += NT) {
-      sh.sum[i] += sh.sum[i + s];
-      sh.cnt[i] += sh.cnt[i + s];
-    }
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    const int32_t c = sh.cnt[0];
-    if (loss_mean) loss_mean[0] = (float)(sh.sum[0] / (double)(c > 0 ? c : 1));
-    if (n_valid) n_valid[0] = c;
-  }
-}
-
-// The averaged loss inside the forward's launch: every workgroup counts itself
-// done on p.done once its row's loss is written (release: the loss is visible
-// device-wide before the count, across the XCDs' L2 caches); the workgroup
-// that counts last (acquire) reads every row's loss and forms the mean and
-// the count, then resets the counter to zero for the next call.
-template <int NT>
-__device__ __forceinline__ void mean_if_last(const CeFwdParams& p, int64_t N) {
-  __shared__ MeanScratch ms;
-  __shared__ int last;
-  if (threadIdx.x == 0) {
-    const unsigned old =
-        __hip_atomic_fetch_add(p.done, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    last = (old == gridDim.x - 1u);
-  }
-  __syncthreads();
-  if (!last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  mean_and_count<NT>(p.loss_tok, p.targets, N, p.d1, p.ts0, p.ts1, p.ignore_idx, p.loss_mean,
-                     p.n_valid, ms);
-  if (threadIdx.x == 0) __hip_atomic_store(p.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // ENT: also the entropy of softmax(z) per row (0 for ignored rows).
 // SHARD: the row holds vocabulary columns v0 .. v0 + V - 1 of a larger
 // vocabulary; instead of the loss, write the shard's partial statistics
 // (m, d, sum z, z_t if this shard holds the target else 0) for a later merge.
 template <int DT, bool ENT, bool SHARD, int NT>
-__device__ __forceinline__ void fwd_row(const CeFwdParams& p) {
+__global__ __launch_bounds__(NT) void ce_fwd_kernel(CeFwdParams p) {
   using T = typename Elem<DT>::T;
   using S = typename StateOf<ENT>::T;
   __shared__ S sh[NT / 64];
@@ -351,21 +283,35 @@ __device__ __forceinline__ void fwd_row(const CeFwdParams& p) {
   }
 }
 
-template <int DT, bool ENT, bool SHARD, int NT>
-__global__ __launch_bounds__(NT) void ce_fwd_kernel(CeFwdParams p) {
-  fwd_row<DT, ENT, SHARD, NT>(p);
-  if constexpr (!SHARD) {
-    if (p.done) mean_if_last<NT>(p, (int64_t)gridDim.x);
-  }
-}
-
 // Averaged loss over non-ignored rows and their count, one workgroup, fixed
-// summation order (bitwise reproducible, and the same bits as the forward's
-// in-launch mean).
-__global__ __launch_bounds__(kMeanLanes) void ce_mean_kernel(CeMeanParams p) {
-  __shared__ MeanScratch ms;
-  mean_and_count<kMeanLanes>(p.loss_tok, p.targets, p.N, p.d1, p.ts0, p.ts1, p.ignore_idx,
-                             p.loss_mean, p.n_valid, ms);
+// summation order (bitwise reproducible).
+__global__ __launch_bounds__(1024) void ce_mean_kernel(CeMeanParams p) {
+  __shared__ double ssum[1024];
+  __shared__ int64_t scnt[1024];
+  double sum = 0.0;
+  int64_t cnt = 0;
+  for (int64_t r = threadIdx.x; r < p.N; r += 1024) {
+    const int64_t i0 = r / p.d1, i1 = r - i0 * p.d1;
+    if (p.targets[i0 * p.ts0 + i1 * p.ts1] != p.ignore_idx) {
+      if (p.loss_tok) sum += (double)p.loss_tok[r];
+      ++cnt;
+    }
+  }
+  ssum[threadIdx.x] = sum;
+  scnt[threadIdx.x] = cnt;
+  __syncthreads();
+  for (int s = 512; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) {
+      ssum[threadIdx.x] += ssum[threadIdx.x + s];
+      scnt[threadIdx.x] += scnt[threadIdx.x + s];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int64_t c = scnt[0];
+    if (p.loss_mean) p.loss_mean[0] = (float)(ssum[0] / (double)(c > 0 ? c : 1));
+    if (p.n_valid) p.n_valid[0] = (int32_t)c;
+  }
 }
 
 template <int DT>
@@ -817,7 +763,7 @@ hipError_t launch_ce_merge_shards(const CeMergeParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_ce_mean(const CeMeanParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(ce_mean_kernel, dim3(1), dim3(kMeanLanes), 0, stream, p);
+  hipLaunchKernelGGL(ce_mean_kernel, dim3(1), dim3(1024), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -25,9 +25,6 @@ inline bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 
 inline int launch_status(hipError_t e) { return e == hipSuccess ? VCE_OK : VCE_EHIP; }
 
-// ce_forward's workspace: a completion counter (4 bytes) in a 256-byte block.
-constexpr size_t kCeWorkspaceBytes = 256;
-
 // Byte extent [lo, hi) touched by a (d0, d1, V) strided tensor.
 inline void extent(const void* base, int64_t d0, int64_t d1, int64_t V, int64_t s0, int64_t s1,
                    int64_t es, uintptr_t* lo, uintptr_t* hi) {
@@ -83,13 +80,10 @@ const char* vce_strerror(int status) {
   }
 }
 
-size_t ce_workspace_size(void) { return kCeWorkspaceBytes; }
-
 int ce_forward(const void* logits, int dtype, int64_t d0, int64_t d1, int64_t V, int64_t ls0,
                int64_t ls1, const int64_t* targets, int64_t ts0, int64_t ts1,
                float label_smoothing, int reduce_loss, int64_t ignore_idx, float* loss_tok,
-               float* loss_mean, float* stats, int32_t* n_valid, float* entropy, void* workspace,
-               size_t workspace_bytes, void* stream) {
+               float* loss_mean, float* stats, int32_t* n_valid, float* entropy, void* stream) {
   CeShape sh;
   int rc = check_ce_common(logits, dtype, d0, d1, V, ls0, ls1, targets, ts0, ts1,
                            label_smoothing, reduce_loss, &sh);
@@ -100,14 +94,7 @@ int ce_forward(const void* logits, int dtype, int64_t d0, int64_t d1, int64_t V,
   if ((loss_tok && !aligned(loss_tok, 4)) || (loss_mean && !aligned(loss_mean, 4)) ||
       (n_valid && !aligned(n_valid, 4)) || (entropy && !aligned(entropy, 4)))
     return VCE_EALIGN;
-  if (workspace) {
-    if (!aligned(workspace, 256)) return VCE_EALIGN;
-    if (workspace_bytes < kCeWorkspaceBytes) return VCE_EWORKSPACE;
-  }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // with a workspace (and rows to sweep) the mean and the count come out of
-  // the row sweep's own launch; otherwise a second, one-workgroup kernel
-  const bool fold_mean = workspace && sh.N > 0 && (reduce_loss || n_valid);
 
   vce::CeFwdParams p;
   p.logits = logits;
@@ -126,12 +113,9 @@ int ce_forward(const void* logits, int dtype, int64_t d0, int64_t d1, int64_t V,
   p.v0 = 0;
   p.partial = nullptr;
   p.partial_w = nullptr;
-  p.done = fold_mean ? static_cast<unsigned*>(workspace) : nullptr;
-  p.loss_mean = reduce_loss ? loss_mean : nullptr;
-  p.n_valid = n_valid;
   rc = launch_status(vce::launch_ce_forward(p, dtype, sh.N, s));
   if (rc != VCE_OK) return rc;
-  if ((reduce_loss || n_valid) && !fold_mean) {
+  if (reduce_loss || n_valid) {
     vce::CeMeanParams mp;
     mp.loss_tok = loss_tok;
     mp.targets = targets;
@@ -260,9 +244,6 @@ int ce_forward_backward(const void* logits, void* grad, int dtype, int64_t d0, i
     f.v0 = 0;
     f.partial = nullptr;
     f.partial_w = nullptr;
-    f.done = nullptr;
-    f.loss_mean = nullptr;
-    f.n_valid = nullptr;
     vce::CeBwdParams b;
     b.logits = logits;
     b.grad = grad;
@@ -328,9 +309,6 @@ int ce_forward_shard(const void* logits, int dtype, int64_t d0, int64_t d1, int6
   p.v0 = vocab_start;
   p.partial = partial;
   p.partial_w = partial_w;
-  p.done = nullptr;
-  p.loss_mean = nullptr;
-  p.n_valid = nullptr;
   return launch_status(vce::launch_ce_forward(p, dtype, sh.N, static_cast<hipStream_t>(stream)));
 }
 

@@ -20,12 +20,6 @@ struct CeFwdParams {
   int64_t v0;      // first vocabulary column of the row (0 unless sharded)
   float* partial;  // shard mode: (N, 4) partial statistics instead of loss/stats
   float* partial_w;  // shard mode, optional: (N) entropy statistic w of the shard
-  // Optional: the averaged loss and the count formed inside the launch by the
-  // workgroup that finishes last.  done is a completion counter in caller
-  // memory, zero on entry and reset to zero by that workgroup.
-  unsigned* done;
-  float* loss_mean;  // written iff non-null (with done)
-  int32_t* n_valid;  // written iff non-null (with done)
 };
 
 struct CeMergeParams {
