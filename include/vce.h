@@ -349,7 +349,10 @@ int lce_backward_shard(const void* X, const void* W, int64_t M, int64_t H, int64
 
 /*
  * vce_gemm_bf16: the matrix-core building block of the linear form, exported
- * so it can be checked and timed on its own.  C (rows, cols) FP32 row-major
+ * so it can be checked and timed on its own, as the Liger-Kernel PR "Add SM100
+ * tensor-parallel fused scaled cross entropy" validates its classifier GEMM
+ * apart from the fused loss (SM90 regression validation: standalone forward
+ * GEMM numerical cases).  C (rows, cols) FP32 row-major
  * with leading dimension ldc:  C[i][j] = sum_k P(i, k) Q(j, k), BF16 operands,
  * FP32 accumulation.  Each operand is stored
  *   K-contiguous   (p_dim / q_dim = 0): P(i, k) = P[i * ldp + k]

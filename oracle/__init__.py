@@ -40,21 +40,35 @@ DT_FP32, DT_BF16, DT_FP64 = 0, 1, 2
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile the C core with gcc (IEEE math, OpenMP)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                  "-fno-omit-frame-pointer", "-g"]
+
+
+def build(force: bool = True, sanitize: bool = False, out: str | None = None) -> str:
+    """Compile the C core with gcc (IEEE math, OpenMP).  With ``sanitize`` the
+    build carries AddressSanitizer and UndefinedBehaviorSanitizer (any finding
+    aborts); a process loads such a build only with the sanitizer runtime
+    preloaded, through the VCE_ORACLE_LIB environment variable."""
+    lib = out or _LIB
+    if force or not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(_SRC):
+        tmp = lib + ".tmp%d" % os.getpid()
+        extra = SANITIZE_FLAGS if sanitize else []
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", *extra, _SRC, "-o",
+                               tmp, "-lm"])
+        os.replace(tmp, lib)
+    return lib
 
 
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build(force=True)
-        lib = ctypes.CDLL(_LIB)
+        alt = os.environ.get("VCE_ORACLE_LIB")
+        if alt:
+            lib = ctypes.CDLL(alt)
+        else:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB)
         i64, dbl, vp = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
         lib.vce_oracle_forward.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, i64, vp, i64, i64,
                                            dbl, i64, vp, i64, vp, vp, vp]
