@@ -74,7 +74,8 @@ enum vce_status {
   VCE_EALIAS = 4,       /* overwrite_input set but grad != logits, or buffers overlap */
   VCE_EWORKSPACE = 5,   /* workspace too small (see lce_workspace_size) */
   VCE_EHIP = 6,         /* a kernel launch failed */
-  VCE_EUNSUPPORTED = 7  /* a size this build does not handle (see the entry point) */
+  VCE_EUNSUPPORTED = 7, /* a size this build does not handle (see the entry point) */
+  VCE_ESCRATCH = 8      /* beyond the static scratch of lce_forward_noalloc */
 };
 
 enum vce_dtype { VCE_DTYPE_FP32 = 0, VCE_DTYPE_BF16 = 1 };
@@ -263,6 +264,30 @@ int lce_forward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
                 int64_t ignore_idx, float* loss_tok, float* loss_mean, float* stats,
                 int32_t* n_valid, float* entropy, void* workspace, size_t workspace_bytes,
                 void* stream);
+
+/*
+ * lce_forward_noalloc: lce_forward without a caller workspace, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments, outputs
+ * and kernels as lce_forward (BF16 X and W), bit for bit the same results;
+ * the forward's per-tile partials live in a static device array of the
+ * library, LCE_NOALLOC_SCRATCH_BYTES (64 MiB) per device, held from the
+ * library's first use on a device until the process ends.  That bounds the
+ * problem: 16 * ceil(V / 256) * Mp + 4 * Mp bytes, Mp = M rounded up to a
+ * multiple of 256, must fit (M = 4096, V = 131072 takes 32 MiB; M = 4096
+ * fits V up to 261888); larger problems return VCE_ESCRATCH and launch
+ * nothing.  Nothing in the scratch
+ * needs to start at zero.  Every call on one device shares its scratch:
+ * calls that may overlap on one device (concurrent streams, graphs replayed
+ * on other streams) race and must be serialised by the caller.  The device
+ * is the stream's own (the current device for the NULL stream); no call
+ * allocates, frees or synchronises.
+ */
+#define LCE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int lce_forward_noalloc(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
+                        const int64_t* targets, float label_smoothing, int reduce_loss,
+                        int64_t ignore_idx, float* loss_tok, float* loss_mean, float* stats,
+                        int32_t* n_valid, float* entropy, void* stream);
 
 /*
  * lce_backward: dX (M, H) and dW (V, H), BF16, overwritten (not accumulated).

@@ -366,3 +366,25 @@ def test_ce_forward_backward_rejects(L):
     assert call(overwrite=1) == 4                   # overwrite needs grad == logits
     assert call(grad=A + 4096) == 4                 # overlapping buffers
     assert call(grad=A + (1 << 30) + 2) == 3        # rows split at different 16 B phases
+
+
+def noalloc(L, X=A, W=A, M=64, H=64, V=1000, targets=A, eps=0.0, reduce_loss=0, ignore=-100,
+            loss_tok=A, loss_mean=A, stats=A, n_valid=A, entropy=None):
+    return L.lce_forward_noalloc(X, W, M, H, V, targets, eps, reduce_loss, ignore, loss_tok,
+                                 loss_mean, stats, n_valid, entropy, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), 1), (dict(V=0), 1), (dict(eps=2.0), 1), (dict(H=12), 7),
+    (dict(X=None), 1), (dict(targets=None), 1), (dict(stats=None), 1),
+    (dict(X=A + 8), 3), (dict(stats=A + 4), 3),
+    # the forward's partials beyond the 64 MiB static scratch: 16 * 1001 tiles * 16384
+    (dict(M=16384, H=2304, V=256003), 8),
+    # just past the limit: 16 * 1025 * 4096 + 4 * 4096 bytes > 64 MiB
+    (dict(M=4096, H=64, V=262145), 8),
+])
+def test_lce_forward_noalloc_rejects(L, kw, code):
+    # every rejection comes from the host checks: nothing is launched and the
+    # static scratch is not looked up
+    assert noalloc(L, **kw) == code
+    assert L.vce_strerror(code)

@@ -19,7 +19,7 @@ DTYPE_FP32 = 0
 DTYPE_BF16 = 1
 
 STATUS = {0: "VCE_OK", 1: "VCE_EINVAL", 2: "VCE_EDTYPE", 3: "VCE_EALIGN", 4: "VCE_EALIAS",
-          5: "VCE_EWORKSPACE", 6: "VCE_EHIP", 7: "VCE_EUNSUPPORTED"}
+          5: "VCE_EWORKSPACE", 6: "VCE_EHIP", 7: "VCE_EUNSUPPORTED", 8: "VCE_ESCRATCH"}
 
 # (name, restype, argtypes) for every symbol include/vce.h declares.
 _I64, _I32, _F32, _VP, _SZ = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -42,6 +42,8 @@ SIGNATURES = {
     "lce_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "lce_forward": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _F32, _I32, _I64, _VP, _VP, _VP, _VP,
                            _VP, _VP, _SZ, _VP]),
+    "lce_forward_noalloc": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _F32, _I32, _I64, _VP, _VP,
+                                   _VP, _VP, _VP, _VP]),
     "lce_backward": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _F32, _I32,
                             _I64, _VP, _VP, _VP, _SZ, _VP]),
     "lce_workspace_size_f32": (_SZ, [_I64, _I64, _I64]),
@@ -454,6 +456,39 @@ def lce_forward(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
     loss_mean, stats, n_valid), plus the per-token entropy with ``with_entropy``."""
     return _lce_forward(False, X, W, targets, label_smoothing, reduce_loss, ignore_idx,
                         workspace, stream, out, with_entropy)
+
+
+def lce_forward_noalloc(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
+                        label_smoothing: float = 0.0, reduce_loss: bool = True,
+                        ignore_idx: int = -100, *, stream=None, out=None,
+                        with_entropy: bool = False):
+    """``lce_forward`` with the library's static scratch instead of a workspace
+    (no device allocation by the library; ``out`` lets the caller supply the
+    outputs too).  Problems beyond the scratch raise (VCE_ESCRATCH)."""
+    _check_linear(X, W, targets)
+    M, H = X.shape
+    V = W.shape[0]
+    dev = X.device
+    if out is None:
+        loss_tok = torch.empty(M, dtype=torch.float32, device=dev)
+        stats = torch.empty((M, 4), dtype=torch.float32, device=dev)
+        loss_mean = torch.empty((), dtype=torch.float32, device=dev) if reduce_loss else None
+        n_valid = torch.empty((), dtype=torch.int32, device=dev) if reduce_loss else None
+        ent = torch.empty(M, dtype=torch.float32, device=dev) if with_entropy else None
+    else:
+        loss_tok, loss_mean, stats, n_valid = out[:4]
+        ent = out[4] if with_entropy else None
+    _check_rows(M, X, stats=stats, n_valid=n_valid, loss_tok=loss_tok, loss_mean=loss_mean,
+                entropy=ent)
+    _need_cuda(X, W, targets)
+    rc = lib().lce_forward_noalloc(_ptr(X), _ptr(W), M, H, V, _ptr(targets),
+                                   float(label_smoothing), int(bool(reduce_loss)),
+                                   int(ignore_idx), _ptr(loss_tok), _ptr(loss_mean), _ptr(stats),
+                                   _ptr(n_valid), _ptr(ent), _stream(stream))
+    _check("lce_forward_noalloc", rc)
+    if with_entropy:
+        return loss_tok, loss_mean, stats, n_valid, ent
+    return loss_tok, loss_mean, stats, n_valid
 
 
 def lce_forward_f32(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,

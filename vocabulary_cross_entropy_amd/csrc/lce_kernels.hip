@@ -1124,6 +1124,7 @@ bool lce_make_plan(int64_t M, int64_t H, int64_t V, LcePlan* plan, bool f32) {
   p.off_dz = split;
   p.off_dx = split + (f32 ? 2 : 1) * dz;
   const size_t bwd = p.off_dx + dx;
+  p.fwd_bytes = fwd;
   p.total = fwd > bwd ? fwd : bwd;
   *plan = p;
   return true;

@@ -7,6 +7,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "vce.h"
 #include "vce_internal.h"
 
@@ -76,6 +78,9 @@ const char* vce_strerror(int status) {
     case VCE_EWORKSPACE: return "workspace too small";
     case VCE_EHIP: return "HIP kernel launch failed";
     case VCE_EUNSUPPORTED: return "size not supported by this build";
+    case VCE_ESCRATCH:
+      return "problem larger than the static scratch of lce_forward_noalloc "
+             "(LCE_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -465,19 +470,62 @@ size_t lce_workspace_size_f32(int64_t M, int64_t H, int64_t V) {
 
 namespace {
 
+// static_ws: the forward runs in the library's static scratch (no workspace
+// argument; the forward alone must fit in it, VCE_ESCRATCH otherwise).
 int check_lce_common(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
                      const int64_t* targets, float eps, int reduce_loss, void* workspace,
-                     size_t workspace_bytes, vce::LcePlan* plan, bool f32 = false) {
+                     size_t workspace_bytes, vce::LcePlan* plan, bool f32 = false,
+                     bool static_ws = false) {
   if (M < 0 || H <= 0 || V <= 0) return VCE_EINVAL;
   if (!(eps >= 0.0f && eps <= 1.0f)) return VCE_EINVAL;
   if (reduce_loss != 0 && reduce_loss != 1) return VCE_EINVAL;
   if (H % 8 != 0) return VCE_EUNSUPPORTED;
   if (!vce::lce_make_plan(M, H, V, plan, f32)) return VCE_EUNSUPPORTED;
+  if (static_ws && M > 0 && plan->fwd_bytes > LCE_NOALLOC_SCRATCH_BYTES) return VCE_ESCRATCH;
   if (M == 0) return VCE_OK;
-  if (!X || !W || !targets || !workspace) return VCE_EINVAL;
-  if (!aligned(X, 16) || !aligned(W, 16) || !aligned(targets, 8) || !aligned(workspace, 256))
-    return VCE_EALIGN;
+  if (!X || !W || !targets) return VCE_EINVAL;
+  if (!aligned(X, 16) || !aligned(W, 16) || !aligned(targets, 8)) return VCE_EALIGN;
+  if (static_ws) return VCE_OK;
+  if (!workspace) return VCE_EINVAL;
+  if (!aligned(workspace, 256)) return VCE_EALIGN;
   if (workspace_bytes < plan->total) return VCE_EWORKSPACE;
+  return VCE_OK;
+}
+
+// ---- the static scratch of lce_forward_noalloc -------------------------------------
+// The forward's per-tile partials for callers that cannot allocate: a file-scope
+// device array (each device holds its own copy once the library's code is
+// loaded there, until the process ends).  Its name is a host-side stand-in in
+// host code; the device address comes from hipGetSymbolAddress, once per
+// device with that device current, and only that address is used.
+static __device__ __align__(256) char scratch[LCE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the stream's device (the current device
+// for the NULL stream).
+int scratch_for_stream(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (stream) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return VCE_EHIP;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return VCE_EHIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return VCE_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return VCE_EHIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return VCE_EHIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return VCE_EHIP;
+    if (e != hipSuccess || !p) return VCE_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return VCE_OK;
 }
 
@@ -485,10 +533,10 @@ int lce_forward_impl(bool f32, const void* X, const void* W, int64_t M, int64_t 
                      const int64_t* targets, float label_smoothing, int reduce_loss,
                      int64_t ignore_idx, float* loss_tok, float* loss_mean, float* stats,
                      int32_t* n_valid, float* entropy, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+                     void* stream, bool static_ws = false) {
   vce::LcePlan plan;
   int rc = check_lce_common(X, W, M, H, V, targets, label_smoothing, reduce_loss, workspace,
-                            workspace_bytes, &plan, f32);
+                            workspace_bytes, &plan, f32, static_ws);
   if (rc != VCE_OK) return rc;
   if (reduce_loss && (!loss_mean || !n_valid)) return VCE_EINVAL;
   if (M > 0 && (!loss_tok || !stats)) return VCE_EINVAL;
@@ -497,6 +545,10 @@ int lce_forward_impl(bool f32, const void* X, const void* W, int64_t M, int64_t 
       (n_valid && !aligned(n_valid, 4)) || (entropy && !aligned(entropy, 4)))
     return VCE_EALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (static_ws && M > 0) {
+    rc = scratch_for_stream(s, &workspace);
+    if (rc != VCE_OK) return rc;
+  }
   if (M > 0) {
     vce::LceFwdArgs a;
     a.X = X;
@@ -582,6 +634,15 @@ int lce_forward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
   return lce_forward_impl(false, X, W, M, H, V, targets, label_smoothing, reduce_loss,
                           ignore_idx, loss_tok, loss_mean, stats, n_valid, entropy, workspace,
                           workspace_bytes, stream);
+}
+
+int lce_forward_noalloc(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
+                        const int64_t* targets, float label_smoothing, int reduce_loss,
+                        int64_t ignore_idx, float* loss_tok, float* loss_mean, float* stats,
+                        int32_t* n_valid, float* entropy, void* stream) {
+  return lce_forward_impl(false, X, W, M, H, V, targets, label_smoothing, reduce_loss,
+                          ignore_idx, loss_tok, loss_mean, stats, n_valid, entropy, nullptr, 0,
+                          stream, /*static_ws=*/true);
 }
 
 int lce_forward_f32(const float* X, const float* W, int64_t M, int64_t H, int64_t V,
