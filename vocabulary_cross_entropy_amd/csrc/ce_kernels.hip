@@ -490,7 +490,6 @@ __global__ __launch_bounds__(NT) void ce_fb_kernel(CeFwdParams f, CeBwdParams b)
   __shared__ LseState sh[NT / 64];
   const int64_t r = blockIdx.x;
   const int64_t i0 = r / f.d1, i1 = r - i0 * f.d1;
-  const int64_t t = f.targets[i0 * f.ts0 + i1 * f.ts1];
   const int tid = threadIdx.x;
   const int64_t V = f.V;
   const int64_t off = i0 * f.ls0 + i1 * f.ls1;
@@ -499,6 +498,17 @@ __global__ __launch_bounds__(NT) void ce_fb_kernel(CeFwdParams f, CeBwdParams b)
   const RowSplit rs = split_row<DT>(row, V);
   u32x4_t* gvec = reinterpret_cast<u32x4_t*>(grow + rs.head);
   const int64_t nscal = rs.head + (V - rs.tail0);
+  // every load of this thread's share of the row goes out at once, before
+  // the target is known (an ignored row drops them); vectors past the row
+  // hold zeros
+  const u32x4_t* vrow = reinterpret_cast<const u32x4_t*>(row + rs.head);
+  u32x4_t w[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int64_t j = tid + (int64_t)v * NT;
+    w[v] = j < rs.nvec ? __builtin_nontemporal_load(vrow + j) : u32x4_t{0, 0, 0, 0};
+  }
+  const int64_t t = f.targets[i0 * f.ts0 + i1 * f.ts1];
   const bool t_ok = (t >= 0 && t < V);
 
   if (t == f.ignore_idx || !t_ok) {
@@ -514,21 +524,20 @@ __global__ __launch_bounds__(NT) void ce_fb_kernel(CeFwdParams f, CeBwdParams b)
         const float z = Elem<DT>::load(row + idx);
         st = LseState{z, (z == kNegInf) ? 0.0f : 1.0f, z};
       }
-      const u32x4_t* vrow = reinterpret_cast<const u32x4_t*>(row + rs.head);
       int64_t j = tid;
       for (; j + (kUnroll - 1) * NT < rs.nvec; j += kUnroll * NT) {
-        u32x4_t w[kUnroll];
+        u32x4_t wc[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) w[u] = vrow[j + u * NT];
-        fold<DT, kUnroll>(st, w);
+        for (int u = 0; u < kUnroll; ++u) wc[u] = vrow[j + u * NT];
+        fold<DT, kUnroll>(st, wc);
       }
       if (j < rs.nvec) {
         const int nvalid = (int)((rs.nvec - j + NT - 1) / NT);
-        u32x4_t w[kUnroll];
+        u32x4_t wc[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-          w[u] = u < nvalid ? vrow[j + u * NT] : u32x4_t{0, 0, 0, 0};
-        fold<DT, kUnroll>(st, w, nvalid);
+          wc[u] = u < nvalid ? vrow[j + u * NT] : u32x4_t{0, 0, 0, 0};
+        fold<DT, kUnroll>(st, wc, nvalid);
       }
       const LseState tot = block_reduce<NT / 64>(st, sh);
       if (tid == 0) {
@@ -563,22 +572,15 @@ __global__ __launch_bounds__(NT) void ce_fb_kernel(CeFwdParams f, CeBwdParams b)
     zs = Elem<DT>::load(row + sidx);
     st = LseState{zs, (zs == kNegInf) ? 0.0f : 1.0f, zs};
   }
-  const u32x4_t* vrow = reinterpret_cast<const u32x4_t*>(row + rs.head);
-  u32x4_t w[NV];
+  // chunks of four vectors in the forward's order (its partial chunk folds
+  // only its loaded vectors)
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int64_t j = tid + (int64_t)c * kUnroll * NT;
     if (j + (kUnroll - 1) * NT < rs.nvec) {
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
-        w[c * kUnroll + u] = __builtin_nontemporal_load(vrow + j + u * NT);
       fold<DT, kUnroll>(st, &w[c * kUnroll]);
     } else if (j < rs.nvec) {
       const int nvalid = (int)((rs.nvec - j + NT - 1) / NT);
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
-        w[c * kUnroll + u] = u < nvalid ? __builtin_nontemporal_load(vrow + j + u * NT)
-                                        : u32x4_t{0, 0, 0, 0};
       fold<DT, kUnroll>(st, &w[c * kUnroll], nvalid);
     }
   }
