@@ -699,7 +699,6 @@ struct EpiDzT {
   };
   __device__ static void apply(const Params& p, f32x16_t (&acc)[NA][NB], int64_t i0, int64_t j0,
                                int wr, int wc, int lane, uint16_t* smem) {
-    uint16_t LDS_AS* const st = (uint16_t LDS_AS*)smem;  // [256 tokens][kDzLd]
     // every per-token input of the lane's four tokens first, so that they
     // share one memory round trip
     int64_t tg[NB];
@@ -771,42 +770,55 @@ struct EpiDzT {
     };
 
     if constexpr (!SPLIT) {
+      // Straight from the accumulators to memory, no LDS round trip: lanes l
+      // and l + 32 hold rows 8 q + [0, 4) and 8 q + [4, 8) of block a for the
+      // same token, so one v_permlane32_swap per dword pair gives lane l rows
+      // [0, 8) and [16, 24) of the block and lane l + 32 rows [8, 16) and
+      // [24, 32): two 16-byte stores per lane and block, 32 consecutive bytes
+      // of a token row from each lane pair.
+      const int64_t row0 = i0 + wr * 128 + 8 * (lane >> 5);  // chunk of r = 0 after the swap
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const Tok k = token(b);
         const float goff = k.g * (p.eps / (float)p.Vg);
-        const int jl = wc * WN + b * 32 + (lane & 31);
+        const int tl = target_row(k);
+        uint16_t* const drow = p.dz + (j0 + wc * WN + b * 32 + (lane & 31)) * p.ldz + row0;
 #pragma unroll
-        for (int a = 0; a < NA; ++a)
+        for (int a = 0; a < NA; ++a) {
+          float val[16];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float val[4];
+          for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const float x = value(k, goff, acc[a][b][4 * q + e]);
-              val[e] = (full || a * 32 + 8 * q + e < lim) ? x : 0.0f;
+              val[4 * q + e] = (full || a * 32 + 8 * q + e < lim) ? x : 0.0f;
             }
-            const uint32_t w01 = pack_bf16x2(val[0], val[1]), w23 = pack_bf16x2(val[2], val[3]);
-            const int vl = wr * 128 + 4 * (lane >> 5) + a * 32 + 8 * q;
-            *reinterpret_cast<u32x2_t LDS_AS*>(st + jl * kDzLd + vl) = u32x2_t{w01, w23};
+          // the target's element (rarely in this block): the same value less
+          // (1 - eps) g
+          if (tl >= 0 && (tl >> 5) == a) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (tl == a * 32 + 8 * (r >> 2) + (r & 3))
+                val[r] = value(k, goff, acc[a][b][r]) - k.g * (1.0f - p.eps);
           }
-        // overwrite the lane's own earlier LDS write (program order suffices)
-        const int tl = target_row(k);
-        if (tl >= 0) {
-          const float x = value(k, goff, pick(acc, b, tl)) - k.g * (1.0f - p.eps);
-          st[jl * kDzLd + wr * 128 + 4 * (lane >> 5) + tl] = to_bf16(x);
+          uint32_t w[8];
+#pragma unroll
+          for (int r = 0; r < 8; ++r) w[r] = pack_bf16x2(val[2 * r], val[2 * r + 1]);
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+              const auto sw = __builtin_amdgcn_permlane32_swap(w[4 * h + d], w[4 * h + 2 + d],
+                                                               false, false);
+              w[4 * h + d] = sw[0];
+              w[4 * h + 2 + d] = sw[1];
+            }
+          *reinterpret_cast<u32x4_t*>(drow + a * 32) = u32x4_t{w[0], w[1], w[2], w[3]};
+          *reinterpret_cast<u32x4_t*>(drow + a * 32 + 16) = u32x4_t{w[4], w[5], w[6], w[7]};
         }
       }
-      __syncthreads();
-      // 256 token rows x 32 chunks of 16 B; 512 threads, consecutive threads
-      // take consecutive chunks of a row
-#pragma unroll 4
-      for (int u = 0; u < (BN * BM / 8) / NT; ++u) {
-        const int idx = u * NT + tid, jl = idx >> 5, ch = idx & 31;
-        const u32x4_t w = *reinterpret_cast<const u32x4_t LDS_AS*>(st + jl * kDzLd + ch * 8);
-        *reinterpret_cast<u32x4_t*>(p.dz + (j0 + jl) * p.ldz + i0 + ch * 8) = w;
-      }
     } else {
+      uint16_t LDS_AS* const st = (uint16_t LDS_AS*)smem;  // [256 tokens][kDzLd]
       uint16_t LDS_AS* const sl = st + 128 * kDzLd;  // lo plane of the half
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
