@@ -85,6 +85,38 @@ def _loop_ms(fn, steps: int) -> float:
     return e[0].elapsed_time(e[1]) / steps
 
 
+def _inplace_memory(vce, zin, z, t, eps, red, out, stats, go) -> dict:
+    """Device memory of a forward + in-place backward, measured rather than
+    assumed: what the saved state occupies (per-row loss and the four row
+    statistics) against the logits, and how much device memory the two calls
+    take beyond their arguments -- the device's free bytes (hipMemGetInfo,
+    which also sees allocations made outside torch) and torch's allocator,
+    before and after, one warm call first."""
+    import torch
+
+    def call():
+        zin.copy_(z)
+        vce.ce_forward(zin, t, eps, red, out=out)
+        vce.ce_backward(zin, t, stats, out[3], go, eps, red, overwrite_input=True)
+
+    call()
+    torch.cuda.synchronize()
+    free0, torch0 = torch.cuda.mem_get_info()[0], torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    call()
+    torch.cuda.synchronize()
+    free1, peak = torch.cuda.mem_get_info()[0], torch.cuda.max_memory_allocated()
+    saved = out[0].numel() * out[0].element_size() + stats.numel() * stats.element_size()
+    return dict(
+        logits_bytes=z.numel() * z.element_size(),
+        saved_state_bytes=saved,
+        saved_state_bytes_per_token=saved / out[0].numel(),
+        fp32_gradient_bytes=z.numel() * 4,
+        inplace_fwd_bwd_device_bytes_taken=free0 - free1,
+        inplace_fwd_bwd_torch_peak_extra_bytes=peak - torch0,
+    )
+
+
 def bench_logits(case, steps: int, warmup: int):
     """One step = ce_forward (statistics, loss; the averaged loss and the count
     by a one-workgroup kernel when the loss is reduced) then ce_backward into a
@@ -158,6 +190,7 @@ def bench_logits(case, steps: int, warmup: int):
 
     # in-place backward: logits restored before each launch, outside its events
     zin = torch.empty_like(z)
+    mem = _inplace_memory(vce, zin, z, t, eps, red, out, stats, go)
     ip_ms = []
     for i in range(max(3, min(steps, 10))):
         zin.copy_(z)
@@ -194,6 +227,7 @@ def bench_logits(case, steps: int, warmup: int):
         fb_GBs=(b_fwd + b_bwd) / (ms_step * 1e-3) / 1e9,
         bytes_fwd=b_fwd, bytes_bwd=b_bwd, graph_ms_per_step=graph_ms, one_pass_ms=fb_ms,
         bytes_fb_nominal=accounting.ce_bytes_nominal(N, V, es, "fb"), copy_GBs=copy_GBs,
+        memory=mem,
     )
 
 
@@ -620,6 +654,7 @@ def main():
                                          1),
                    "copy_ceiling_GBs": round(res["copy_GBs"], 1),
                    "bwd_frac_of_copy_ceiling": round(res["bwd_GBs"] / res["copy_GBs"], 4)},
+        "memory": res["memory"],
         "linear_ce": lin,
         "vocab_sharded_one_of_8": sharded or None,
         "other_configs": other or None,

@@ -120,6 +120,46 @@ def test_sqbv_v128256_bf16_in_place_equals_separate(headline):
     np.testing.assert_array_equal(inp["loss"], sep["loss"])
 
 
+def test_in_place_takes_no_device_memory(headline):
+    """The memory claim of the statistics-saving design, measured at the
+    (2048, 2, 128256) BF16 shape (TransformerEngine PR "Minimize the memory
+    usage of the fused cross entropy kernel", downstream validation: the
+    in-place backward needs no additional allocation): the saved state is 20
+    bytes per token (the loss and four row statistics), and a forward plus an
+    in-place backward take no device memory beyond their arguments -- the
+    device's free bytes (which see allocations made outside torch too) and
+    torch's allocator are unchanged across the two calls, after one warm call."""
+    c = headline
+    z = to_device(c.logits, c.dtype)
+    t = torch.from_numpy(c.targets).cuda()
+    go = torch.from_numpy(c.grad_output).cuda()
+    assert not c.reduce_loss
+    loss = torch.empty((c.d0, c.d1), device="cuda")
+    stats = torch.empty((c.d0, c.d1, 4), device="cuda")
+    out = (loss, None, stats, None)
+
+    def call():
+        vce.ce_forward(z, t, c.label_smoothing, False, c.ignore_idx, out=out)
+        g = vce.ce_backward(z, t, stats, None, go, c.label_smoothing, False, c.ignore_idx,
+                            overwrite_input=True)
+        assert g.data_ptr() == z.data_ptr()
+
+    call()
+    torch.cuda.synchronize()
+    free0, alloc0 = torch.cuda.mem_get_info()[0], torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    call()
+    torch.cuda.synchronize()
+    free1, peak = torch.cuda.mem_get_info()[0], torch.cuda.max_memory_allocated()
+    saved = loss.numel() * loss.element_size() + stats.numel() * stats.element_size()
+    _say(f"logits {z.numel() * z.element_size()} B, saved state {saved} B "
+         f"({saved / c.N:.0f} B/token); device bytes taken {free0 - free1}, torch peak extra "
+         f"{peak - alloc0}")
+    assert saved == 20 * c.N
+    assert free1 == free0
+    assert peak == alloc0
+
+
 @pytest.mark.parametrize("V,dtype", [(1, "fp32"), (7, "bf16"), (9, "fp32"), (1001, "bf16"),
                                      (1003, "fp32"), (4099, "bf16"), (33333, "bf16"),
                                      (16383, "bf16"), (16385, "bf16"), (32767, "bf16"),

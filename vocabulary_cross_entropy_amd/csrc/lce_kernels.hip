@@ -39,7 +39,9 @@
 //    wavefronts that share the tokens.  Per-tile partials are merged per
 //    token by a second kernel in a fixed order.
 //  * Backward, per vocabulary chunk: recompute the logits and write dZ (BF16,
-//    token-major); dW rows of the chunk are finished by one GEMM over all
+//    token-major) straight from the accumulators (a lane swap turns the MFMA
+//    layout into 16-byte pieces of token rows; staging the tile in LDS and
+//    storing whole rows was measured slower); dW rows of the chunk are finished by one GEMM over all
 //    tokens (written once, never accumulated); dX accumulates chunk by chunk
 //    in FP32, the last chunk writes BF16.
 #include <type_traits>
@@ -65,8 +67,7 @@ constexpr int UPW = UNITS / (NT / 64);             // units per wave per operand
 constexpr int GROUP_I = 8;                         // row tiles per band of the tile order
 constexpr int64_t kChunk = 32768;                  // backward vocabulary chunk
 constexpr uint32_t kOob = 0x80000000u;             // buffer offset that reads as 0
-constexpr int kDzLd = BM + 4;   // LDS row (elements) of the staged dZ tile: 520 B, conflict-free
-constexpr int kSmemElems = (2 * (BM + BN) * BK > BN * kDzLd) ? 2 * (BM + BN) * BK : BN * kDzLd;
+constexpr int kSmemElems = 2 * (BM + BN) * BK;  // two stages of both operands (128 KB)
 
 static_assert(BM == BN, "one loader shape serves both operands");
 static_assert(NA == 4 && NB == 4 && UPW == 8, "the schedule below assumes these");
@@ -724,7 +725,6 @@ struct EpiDzT {
     const bool full = p.vc_valid - (i0 + wr * 128) >= 128;
     const int64_t lim64 = p.vc_valid - vrow0;
     const int lim = lim64 > 128 ? 128 : (lim64 < 0 ? 0 : (int)lim64);
-    const int tid = threadIdx.x;
 
     // Terms of token column b.  Rows that give zero (ignored token, padding
     // column) or NaN (target out of range) are folded into the arithmetic:
@@ -769,106 +769,62 @@ struct EpiDzT {
                  : -1;
     };
 
-    if constexpr (!SPLIT) {
-      // Straight from the accumulators to memory, no LDS round trip: lanes l
-      // and l + 32 hold rows 8 q + [0, 4) and 8 q + [4, 8) of block a for the
-      // same token, so one v_permlane32_swap per dword pair gives lane l rows
-      // [0, 8) and [16, 24) of the block and lane l + 32 rows [8, 16) and
-      // [24, 32): two 16-byte stores per lane and block, 32 consecutive bytes
-      // of a token row from each lane pair.
-      const int64_t row0 = i0 + wr * 128 + 8 * (lane >> 5);  // chunk of r = 0 after the swap
+    // Straight from the accumulators to memory, no LDS round trip: lanes l
+    // and l + 32 hold rows 8 q + [0, 4) and 8 q + [4, 8) of block a for the
+    // same token, so one v_permlane32_swap per dword pair gives lane l rows
+    // [0, 8) and [16, 24) of the block and lane l + 32 rows [8, 16) and
+    // [24, 32): two 16-byte stores per lane and block (per plane), 32
+    // consecutive bytes of a token row from each lane pair.
+    const int64_t row0 = i0 + wr * 128 + 8 * (lane >> 5);  // chunk of r = 0 after the swap
+    auto swap_store = [&](uint32_t (&w)[8], uint16_t* dst) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const Tok k = token(b);
-        const float goff = k.g * (p.eps / (float)p.Vg);
-        const int tl = target_row(k);
-        uint16_t* const drow = p.dz + (j0 + wc * WN + b * 32 + (lane & 31)) * p.ldz + row0;
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int a = 0; a < NA; ++a) {
-          float val[16];
+        for (int d = 0; d < 2; ++d) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(w[4 * h + d], w[4 * h + 2 + d], false,
+                                                           false);
+          w[4 * h + d] = sw[0];
+          w[4 * h + 2 + d] = sw[1];
+        }
+      *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{w[0], w[1], w[2], w[3]};
+      *reinterpret_cast<u32x4_t*>(dst + 16) = u32x4_t{w[4], w[5], w[6], w[7]};
+    };
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
+    for (int b = 0; b < NB; ++b) {
+      const Tok k = token(b);
+      const float goff = k.g * (p.eps / (float)p.Vg);
+      const int tl = target_row(k);
+      uint16_t* const drow = p.dz + (j0 + wc * WN + b * 32 + (lane & 31)) * p.ldz + row0;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float x = value(k, goff, acc[a][b][4 * q + e]);
-              val[4 * q + e] = (full || a * 32 + 8 * q + e < lim) ? x : 0.0f;
-            }
-          // the target's element (rarely in this block): the same value less
-          // (1 - eps) g
-          if (tl >= 0 && (tl >> 5) == a) {
+      for (int a = 0; a < NA; ++a) {
+        float val[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (tl == a * 32 + 8 * (r >> 2) + (r & 3))
-                val[r] = value(k, goff, acc[a][b][r]) - k.g * (1.0f - p.eps);
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = value(k, goff, acc[a][b][4 * q + e]);
+            val[4 * q + e] = (full || a * 32 + 8 * q + e < lim) ? x : 0.0f;
           }
-          uint32_t w[8];
+        // the target's element (rarely in this block): the same value less
+        // (1 - eps) g
+        if (tl >= 0 && (tl >> 5) == a) {
 #pragma unroll
-          for (int r = 0; r < 8; ++r) w[r] = pack_bf16x2(val[2 * r], val[2 * r + 1]);
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int d = 0; d < 2; ++d) {
-              const auto sw = __builtin_amdgcn_permlane32_swap(w[4 * h + d], w[4 * h + 2 + d],
-                                                               false, false);
-              w[4 * h + d] = sw[0];
-              w[4 * h + 2 + d] = sw[1];
-            }
-          *reinterpret_cast<u32x4_t*>(drow + a * 32) = u32x4_t{w[0], w[1], w[2], w[3]};
-          *reinterpret_cast<u32x4_t*>(drow + a * 32 + 16) = u32x4_t{w[4], w[5], w[6], w[7]};
+          for (int r = 0; r < 16; ++r)
+            if (tl == a * 32 + 8 * (r >> 2) + (r & 3))
+              val[r] = value(k, goff, acc[a][b][r]) - k.g * (1.0f - p.eps);
         }
-      }
-    } else {
-      uint16_t LDS_AS* const st = (uint16_t LDS_AS*)smem;  // [256 tokens][kDzLd]
-      uint16_t LDS_AS* const sl = st + 128 * kDzLd;  // lo plane of the half
+        uint32_t w[8];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        // half h: token columns b = 2h, 2h + 1 of every wave, i.e. tile tokens
-        // wc * 128 + 64 h + [0, 64), staged at rows wc * 64 + [0, 64)
+        for (int r = 0; r < 8; ++r) w[r] = pack_bf16x2(val[2 * r], val[2 * r + 1]);
+        if constexpr (SPLIT) {
+          // the lo plane: what the BF16 hi value leaves of each FP32 value
+          uint32_t wl[8];
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-          const int b = 2 * h + bb;
-          const Tok k = token(b);
-          const float goff = k.g * (p.eps / (float)p.Vg);
-          const int jl = wc * 64 + bb * 32 + (lane & 31);
-#pragma unroll
-          for (int a = 0; a < NA; ++a)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              float val[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float x = value(k, goff, acc[a][b][4 * q + e]);
-                val[e] = (full || a * 32 + 8 * q + e < lim) ? x : 0.0f;
-              }
-              const uint32_t h01 = pack_bf16x2(val[0], val[1]), h23 = pack_bf16x2(val[2], val[3]);
-              const uint32_t l01 =
-                  pack_bf16x2(val[0] - bf16_lo(h01), val[1] - bf16_hi(h01));
-              const uint32_t l23 =
-                  pack_bf16x2(val[2] - bf16_lo(h23), val[3] - bf16_hi(h23));
-              const int vl = wr * 128 + 4 * (lane >> 5) + a * 32 + 8 * q;
-              *reinterpret_cast<u32x2_t LDS_AS*>(st + jl * kDzLd + vl) = u32x2_t{h01, h23};
-              *reinterpret_cast<u32x2_t LDS_AS*>(sl + jl * kDzLd + vl) = u32x2_t{l01, l23};
-            }
-          const int tl = target_row(k);
-          if (tl >= 0) {
-            const float x = value(k, goff, pick(acc, b, tl)) - k.g * (1.0f - p.eps);
-            const uint16_t hb = to_bf16(x);
-            const int o = jl * kDzLd + wr * 128 + 4 * (lane >> 5) + tl;
-            st[o] = hb;
-            sl[o] = to_bf16(x - from_bf16(hb));
-          }
+          for (int r = 0; r < 8; ++r)
+            wl[r] = pack_bf16x2(val[2 * r] - bf16_lo(w[r]), val[2 * r + 1] - bf16_hi(w[r]));
+          swap_store(wl, drow + p.plane + a * 32);
         }
-        __syncthreads();
-        // 2 planes x 128 token rows x 32 chunks of 16 B
-#pragma unroll 4
-        for (int u = 0; u < (2 * 128 * BM / 8) / NT; ++u) {
-          const int idx = u * NT + tid, pl = idx >> 12, jl = (idx >> 5) & 127, ch = idx & 31;
-          const u32x4_t w = *reinterpret_cast<const u32x4_t LDS_AS*>(
-              st + pl * 128 * kDzLd + jl * kDzLd + ch * 8);
-          const int64_t tok = j0 + (jl >> 6) * 128 + 64 * h + (jl & 63);
-          *reinterpret_cast<u32x4_t*>(p.dz + pl * p.plane + tok * p.ldz + i0 + ch * 8) = w;
-        }
-        if (h == 0) __syncthreads();  // the second half reuses the stage
+        swap_store(w, drow + a * 32);
       }
     }
   }
