@@ -52,12 +52,18 @@ def _case(seed, d0, d1, V, dtype, eps, red, layout="B,SQ", n_ign=3, sigma=3.0):
                                      ("fp32", 4099), ("bf16", 32000), ("bf16", 65537),
                                      ("fp32", 65536), ("bf16", 131072),
                                      ("bf16", 131080), ("fp32", 70000),
-                                     ("bf16", 24576), ("bf16", 24577), ("fp32", 12289)])
+                                     ("bf16", 24576), ("bf16", 24577), ("fp32", 12289),
+                                     ("bf16", 40000), ("bf16", 90001), ("bf16", 100003),
+                                     ("bf16", 128256),
+                                     ("fp32", 45000)])
 @pytest.mark.parametrize("eps,red", [(0.0, False), (0.1, True)])
 @pytest.mark.parametrize("overwrite", [False, True])
 def test_one_pass_equals_two_calls(dtype, V, eps, red, overwrite):
     # 131080 BF16 and 70000 FP32 exceed the on-chip row and take the two sweeps;
-    # 24576 / 24577 BF16 and 12289 FP32 sit at the forward's workgroup-size limit
+    # 24576 / 24577 BF16 and 12289 FP32 sit at the forward's workgroup-size limit;
+    # 65537 .. 131072 BF16 and 32769 .. 65536 FP32 keep part of the row in LDS
+    # (90001: none of it, the registers hold the whole row; 100003 and 45000:
+    # rows that start off a 16-byte boundary)
     case = _case(5000 + V, 3, 17, V, dtype, eps, red)
     z = to_device(case.logits, dtype)
     t = torch.from_numpy(case.targets).cuda()

@@ -22,6 +22,8 @@
 
 namespace vce {
 
+#define LDS_AS __attribute__((address_space(3)))
+
 namespace {
 
 // Threads per row: the forward reads each element once and reduces the row,
@@ -176,6 +178,53 @@ __device__ __forceinline__ void fold(S& st, const u32x4_t* w, int nvalid = N) {
 #pragma unroll
   for (int u = 0; u < N; ++u)
     if (u < nvalid) st.s = vec_sum<DT>(w[u], z[u], st.s);
+  st.m = m_new;
+}
+
+// fold() for a chunk of N vectors without the unpacked copy of the chunk:
+// the same arithmetic in the same order (bitwise the same state), with each
+// logit unpacked again where it is used instead of being held in registers
+// between the chunk's max and its sum of exponentials (the one-pass kernel
+// keeps the whole row in VGPRs and cannot spare 8 N more).
+template <int DT, int N>
+__device__ __forceinline__ void fold_lean(LseState& st, u32x4_t* w, int nvalid = N) {
+  constexpr int vec = Elem<DT>::kVec;
+  auto elem = [&](int u, int i) -> float {
+    float z[vec];
+    unpack<DT>(w[u], z);
+    return u < nvalid ? z[i] : kNegInf;
+  };
+  float cm = elem(0, 0);
+#pragma unroll
+  for (int u = 0; u < N; ++u)
+#pragma unroll
+    for (int i = 0; i < vec; ++i) cm = fmaxf(cm, elem(u, i));
+  // the unpacked values are not kept for the sums below
+#pragma unroll
+  for (int u = 0; u < N; ++u) asm volatile("" : "+v"(w[u]));
+  const float m_new = fmaxf(st.m, cm);
+  const float mref = (m_new == kNegInf) ? 0.0f : m_new;
+  const float mL = mref * kLog2e;
+  const float rho = __builtin_fmaf(mref, kLog2e, -mL);
+  float dsum = 0.0f;
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < vec; ++i) acc += exp2_hw(__builtin_fmaf(elem(u, i), kLog2e, -mL));
+    dsum = u == 0 ? acc : dsum + acc;
+  }
+  const float corr = fabsf(rho) < 0x1p-10f ? -rho * kLn2 : exp2_hw(-rho) - 1.0f;
+  dsum = __builtin_fmaf(dsum, corr, dsum);
+  const float f = exp_diff(st.m - mref);
+  st.d = __builtin_fmaf(st.d, f, dsum);
+#pragma unroll
+  for (int u = 0; u < N; ++u)
+    if (u < nvalid) {
+      float z[vec];
+      unpack<DT>(w[u], z);
+      st.s = vec_sum<DT>(w[u], z, st.s);
+    }
   st.m = m_new;
 }
 
@@ -648,6 +697,248 @@ __global__ __launch_bounds__(NT) void ce_fb_kernel(CeFwdParams f, CeBwdParams b)
     sweep(std::true_type{});
 }
 
+// A wave-uniform 64-bit value moved to scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Buffer descriptor of `bytes` bytes at p, built from wave-uniform scalars
+// (the row is the workgroup's, but the compiler cannot always tell, and a
+// descriptor it thinks divergent costs a loop around every access).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  void* q = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(q, (short)0, __builtin_amdgcn_readfirstlane(bytes),
+                                           0x00020000);
+}
+
+// The same descriptor as four scalar words, for store16_nt.
+__device__ __forceinline__ u32x4_t row_rsrc_words(const void* p, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  return u32x4_t{(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) & 0xffffu,
+                 (uint32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
+}
+
+// 16 bytes per lane to the buffer at voff + soff, non-temporal, then two wait
+// states before anything may write the data registers.  Written out because
+// the compiler puts no wait state behind a 16-byte buffer store with a scalar
+// offset, and a data register written right after it lost a dword in some
+// lanes (measured on gfx950: lanes 12..15 of each 16 kept the next value).
+__device__ __forceinline__ void store16_nt(const u32x4_t& v, uint32_t voff, const u32x4_t& rs,
+                                           int soff) {
+  asm volatile("buffer_store_dwordx4 %0, %1, %2, %3 offen nt\n\ts_nop 1"
+               :
+               : "v"(v), "v"(voff), "s"(rs), "s"(soff)
+               : "memory");
+}
+
+// One vector's gradient values packed as stored: FP32 bits, or BF16 pairs
+// rounded to nearest even.
+template <int DT>
+__device__ __forceinline__ u32x4_t pack_vec(const float* g);
+template <>
+__device__ __forceinline__ u32x4_t pack_vec<0>(const float* g) {
+  return u32x4_t{__float_as_uint(g[0]), __float_as_uint(g[1]), __float_as_uint(g[2]),
+                 __float_as_uint(g[3])};
+}
+template <>
+__device__ __forceinline__ u32x4_t pack_vec<1>(const float* g) {
+  return u32x4_t{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]), pack_bf16x2(g[4], g[5]),
+                 pack_bf16x2(g[6], g[7])};
+}
+
+// The one-pass kernel for rows of more than 8 vectors per thread (BF16 rows
+// of 32769 .. 131072 logits): held in registers alone, 16 or 32 vectors take
+// about 165 or 250 VGPRs a lane, one workgroup per CU, and each CU alternates
+// between reading a row and computing on it.  Here the first NR vectors of a
+// thread's share stay in VGPRs and the rest (if any) go straight from memory
+// into LDS (buffer_load ... lds, read back by the same thread), so a lane
+// fits in 128 VGPRs and a workgroup in under 80 KB of LDS at 128256 logits
+// (measured 0.449 -> 0.390 ms per headline step): two workgroups share a
+// CU and one's arithmetic overlaps the other's memory traffic.  Loads and
+// stores go through buffer descriptors that end at the row's vector body (a
+// read past it gives 0, a write past it is dropped: on gfx950 the range check
+// covers the scalar offset too, measured), so the vector index goes in the
+// scalar offset and no per-vector bounds branches or addresses are needed.  Same threads, chunks, order and
+// expressions as ce_fb_kernel: bitwise the same outputs.
+template <int DT, int NR, int NV, int NT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT / 128)))
+void ce_fb_split_kernel(CeFwdParams f, CeBwdParams b) {
+  using T = typename Elem<DT>::T;
+  constexpr int vec = Elem<DT>::kVec;
+  constexpr int NC = NV / kUnroll;
+  constexpr uint32_t kNt = 2;  // cache policy of the row's loads and stores: non-temporal
+  extern __shared__ u32x4_t lrow[];  // vector j >= NR NT of the row at lrow[j - NR NT]
+  __shared__ LseState sh[NT / 64];
+  const int64_t r = blockIdx.x;
+  // the row's coordinates as scalars (the division runs on the vector unit)
+  const int64_t i0 = uniform64(r / f.d1), i1 = r - i0 * f.d1;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int64_t V = f.V;
+  const int64_t off = uniform64(i0 * f.ls0 + i1 * f.ls1);
+  const T* row = static_cast<const T*>(f.logits) + off;
+  T* grow = static_cast<T*>(b.grad) + off;
+  const RowSplit rs = split_row<DT>(row, V);
+  const int64_t nscal = rs.head + (V - rs.tail0);
+  const int nvec = (int)rs.nvec;
+  const __amdgpu_buffer_rsrc_t src = row_rsrc(row + rs.head, nvec * 16);
+  const uint32_t voff = (uint32_t)tid * 16;
+  // every load of this thread's share goes out at once, before the target is
+  // known (an ignored row drops them)
+  u32x4_t w[NR];
+#pragma unroll
+  for (int v = 0; v < NR; ++v)
+    w[v] = __builtin_bit_cast(
+        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(src, voff, v * NT * 16, kNt));
+#pragma unroll
+  for (int v = NR; v < NV; ++v)
+    if (v * NT + 64 * wave < nvec)  // the wave's 64 vectors start inside the row
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          src, (void LDS_AS*)(lrow + (v - NR) * NT + 64 * wave), 16, voff, v * NT * 16, 0, kNt);
+  // vector slot v of this thread: from the registers or from LDS, 0 past the row
+  auto vec_at = [&](int v) -> u32x4_t {
+    if (v < NR) return w[v];
+    return tid + v * NT < nvec ? lrow[(v - NR) * NT + tid] : u32x4_t{0, 0, 0, 0};
+  };
+  const int64_t t = f.targets[i0 * f.ts0 + i1 * f.ts1];
+  const bool t_ok = (t >= 0 && t < V);
+
+  if (t == f.ignore_idx || !t_ok) {
+    // the LDS writes of the loads above land before the workgroup may end
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const float fill = (t == f.ignore_idx) ? 0.0f : __builtin_nanf("");
+    if (t != f.ignore_idx) {
+      // statistics still come from the whole row (same order as the forward)
+      LseState st{kNegInf, 0.0f, 0.0f};
+      if (tid < nscal) {
+        const int64_t idx = tid < rs.head ? tid : rs.tail0 + (tid - rs.head);
+        const float z = Elem<DT>::load(row + idx);
+        st = LseState{z, (z == kNegInf) ? 0.0f : 1.0f, z};
+      }
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int j = tid + c * kUnroll * NT;
+        if (j >= nvec) break;
+        u32x4_t wc[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) wc[u] = vec_at(c * kUnroll + u);
+        if (j + (kUnroll - 1) * NT < nvec)
+          fold_lean<DT, kUnroll>(st, wc);
+        else
+          fold_lean<DT, kUnroll>(st, wc, (nvec - j + NT - 1) / NT);
+      }
+      const LseState tot = block_reduce<NT / 64>(st, sh);
+      if (tid == 0) {
+        f.loss_tok[r] = __builtin_nanf("");
+        *reinterpret_cast<f32x4_t*>(f.stats + 4 * r) =
+            f32x4_t{tot.m, tot.d, __builtin_nanf(""), tot.s / (float)V};
+      }
+      __syncthreads();  // every read of the row is done before it may be overwritten
+    } else if (tid == 0) {
+      f.loss_tok[r] = 0.0f;
+      *reinterpret_cast<f32x4_t*>(f.stats + 4 * r) = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    float fv[vec];
+#pragma unroll
+    for (int i = 0; i < vec; ++i) fv[i] = fill;
+    if (tid < nscal) {
+      const int64_t idx = tid < rs.head ? tid : rs.tail0 + (tid - rs.head);
+      store_one<DT>(grow + idx, fill);
+    }
+    u32x4_t* gvec = reinterpret_cast<u32x4_t*>(grow + rs.head);
+    for (int j = tid; j < nvec; j += NT) store_vec<DT>(gvec + j, fv);
+    return;
+  }
+
+  // ---- forward: reduce the statistics (the chunks of ce_fwd_kernel) -------
+  float zt = __builtin_nanf("");
+  if (tid == 0) zt = Elem<DT>::load(row + t);
+  LseState st{kNegInf, 0.0f, 0.0f};
+  float zs = 0.0f;  // this thread's scalar (head or tail) element, if any
+  int64_t sidx = -1;
+  if (tid < nscal) {
+    sidx = tid < rs.head ? tid : rs.tail0 + (tid - rs.head);
+    zs = Elem<DT>::load(row + sidx);
+    st = LseState{zs, (zs == kNegInf) ? 0.0f : 1.0f, zs};
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int j = tid + c * kUnroll * NT;
+    if (j < nvec) {
+      u32x4_t wc[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) wc[u] = vec_at(c * kUnroll + u);
+      if (j + (kUnroll - 1) * NT < nvec)
+        fold_lean<DT, kUnroll>(st, wc);
+      else
+        fold_lean<DT, kUnroll>(st, wc, (nvec - j + NT - 1) / NT);
+    }
+  }
+  const LseState tot = block_reduce<NT / 64>(st, sh);
+  if (tid == 0) {
+    const float mean = tot.s / (float)V;
+    f.loss_tok[r] = ce_row_loss(tot.m, tot.d, zt, mean, f.eps);
+    *reinterpret_cast<f32x4_t*>(f.stats + 4 * r) = f32x4_t{tot.m, tot.d, zt, mean};
+  }
+  // every read of the row (the target logit included) is done before the
+  // gradient may overwrite it
+  __syncthreads();
+
+  // ---- backward from registers and LDS (the expressions of ce_bwd_kernel) --
+  float g;
+  if (b.reduce_loss) {
+    const int32_t nv = b.n_valid[0];
+    g = b.grad_output[0] / (float)(nv > 0 ? nv : 1);
+  } else {
+    g = b.grad_output[r];
+  }
+  const float m = tot.m, d = tot.d;
+  const float mref = (m == kNegInf) ? 0.0f : m;
+  const float gs = g / d;
+  const float goff = g * (b.eps / (float)V);
+  const float gt = g * (1.0f - b.eps);
+  const bool finite_row = __builtin_isfinite(tot.s / (float)V) && fabsf(m) <= 0x1p100f;
+  const u32x4_t dst = row_rsrc_words(grow + rs.head, nvec * 16);
+  auto sweep = [&](auto clamp) {
+    auto gval = [&](float z) -> float {
+      const float e = decltype(clamp)::value ? exp_diff(z - mref) : exp_diff_finite(z - mref);
+      return e * gs - goff;
+    };
+    if (sidx >= 0) {
+      float gv = gval(zs);
+      if (sidx == t) gv -= gt;
+      store_one<DT>(grow + sidx, gv);
+    }
+    const int64_t tv = t - rs.head;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int j = tid + v * NT;
+      if (v >= NR && v * NT >= nvec) break;  // nothing of this slot or later is in the row
+      float z[vec];
+      unpack<DT>(vec_at(v), z);
+      float gv[vec];
+#pragma unroll
+      for (int i = 0; i < vec; ++i) gv[i] = gval(z[i]);
+      const int64_t base = (int64_t)j * vec;
+      if (tv >= base && tv < base + vec) {
+#pragma unroll
+        for (int i = 0; i < vec; ++i)
+          if (base + i == tv) gv[i] -= gt;
+      }
+      store16_nt(pack_vec<DT>(gv), voff, dst, v * NT * 16);
+    }
+  };
+  if (finite_row)
+    sweep(std::false_type{});
+  else
+    sweep(std::true_type{});
+}
+
 // Per-row merge of vocabulary-shard statistics, shards in fixed order
 // (bitwise reproducible): m = max m_k, d = sum d_k exp(m_k - m), sum z, and
 // z_t from the shard holding the target (the others contribute 0); then the
@@ -771,6 +1062,27 @@ hipError_t launch_ce_mean(const CeMeanParams& p, hipStream_t stream) {
 
 namespace {
 
+// Rows of 8 .. 32 vectors per thread take ce_fb_split_kernel at 128 VGPRs:
+// up to 16 all in VGPRs, beyond that kFbRegVecs in VGPRs and the rest in
+// LDS, sized for the longest row of this V (no head elements).
+constexpr int kFbRegVecs = 22;
+
+template <int DT, int NR, int NV>
+void launch_fb_split(const CeFwdParams& f, const CeBwdParams& b, dim3 g, int64_t nvec,
+                     hipStream_t stream) {
+  auto kern = ce_fb_split_kernel<DT, NR, NV, kFwdThreads>;
+  static const bool attr = [kern] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (NV - NR) * kFwdThreads * 16);
+    return true;
+  }();
+  (void)attr;
+  const int64_t in_lds = (nvec + 63) / 64 * 64 - (int64_t)NR * kFwdThreads;
+  const size_t lds = in_lds > 0 ? (size_t)in_lds * 16 : 0;
+  hipLaunchKernelGGL(kern, g, dim3(kFwdThreads), lds, stream, f, b);
+}
+
 template <int DT>
 bool launch_fb_dt(const CeFwdParams& f, const CeBwdParams& b, int64_t N, hipStream_t stream) {
   // vectors per thread to hold the row (the 16-byte head/tail are scalars);
@@ -789,9 +1101,9 @@ bool launch_fb_dt(const CeFwdParams& f, const CeBwdParams& b, int64_t N, hipStre
   if (nvec <= 8 * kFwdThreads)
     hipLaunchKernelGGL((ce_fb_kernel<DT, 8, kFwdThreads>), g, blk, 0, stream, f, b);
   else if (nvec <= 16 * kFwdThreads)
-    hipLaunchKernelGGL((ce_fb_kernel<DT, 16, kFwdThreads>), g, blk, 0, stream, f, b);
+    launch_fb_split<DT, 16, 16>(f, b, g, nvec, stream);
   else if (nvec <= kFbVecs * kFwdThreads)
-    hipLaunchKernelGGL((ce_fb_kernel<DT, kFbVecs, kFwdThreads>), g, blk, 0, stream, f, b);
+    launch_fb_split<DT, kFbRegVecs, kFbVecs>(f, b, g, nvec, stream);
   else
     return false;
   return true;
