@@ -75,14 +75,17 @@ def test_one_pass_equals_two_calls(dtype, V, eps, red, overwrite):
     assert_same(a, b, red)
 
 
-def test_one_pass_edge_targets_and_infinite_columns():
-    V = 3000
+@pytest.mark.parametrize("V", [3000, 100001])
+def test_one_pass_edge_targets_and_infinite_columns(V):
+    # 100001 takes the kernel that keeps part of the row in LDS (and rows that
+    # start off a 16-byte boundary)
+    live = V * 5 // 6
     case = _case(5101, 2, 40, V, "bf16", 0.1, False, n_ign=5)
     lg = case.logits.reshape(-1, V)
-    lg[:, 2500:] = np.uint16(0xFF80)          # -inf padding columns (BF16 bits)
+    lg[:, live:] = np.uint16(0xFF80)          # -inf padding columns (BF16 bits)
     tt = case.targets.reshape(-1)
-    tt[:] = np.minimum(tt, 2499)
-    tt[0], tt[1], tt[2] = V, -3, 2499         # out of range (twice) and the last live column
+    tt[:] = np.minimum(tt, live - 1)
+    tt[0], tt[1], tt[2] = V, -3, live - 1     # out of range (twice) and the last live column
     z = to_device(case.logits, "bf16")
     t = torch.from_numpy(case.targets).cuda()
     go = torch.from_numpy(case.grad_output).cuda()
@@ -94,9 +97,10 @@ def test_one_pass_edge_targets_and_infinite_columns():
         assert torch.isnan(b[0].reshape(-1)[:2]).all()
 
 
-def test_one_pass_strided_view():
+@pytest.mark.parametrize("V", [5000, 70001])
+def test_one_pass_strided_view(V):
     # (SQ,B,V) storage used as a (B,SQ,V) view
-    case = _case(5102, 64, 4, 5000, "bf16", 0.1, True, layout="SQ,B")
+    case = _case(5102, 64, 4, V, "bf16", 0.1, True, layout="SQ,B")
     zs = to_device(case.logits, "bf16")
     ts = torch.from_numpy(case.targets).cuda()
     zv, tv = zs.transpose(0, 1), ts.transpose(0, 1)
@@ -142,12 +146,14 @@ def test_one_pass_all_ignored_and_empty():
     assert float(mean.item()) == 0.0 and int(nv.item()) == 0
 
 
-def test_one_pass_and_shards_graph_capture_replay():
+@pytest.mark.parametrize("V", [12000, 70001])
+def test_one_pass_and_shards_graph_capture_replay(V):
     # The one-pass call and the three shard calls only enqueue kernels on the
     # given stream, so they are captured and replayed like the others; every
     # replay (with eager work and synchronisation between them) must give the
-    # eager outputs bit for bit.
-    d0, d1, V, S = 2, 384, 12000, 3
+    # eager outputs bit for bit.  70001 takes the one-pass kernel with part of
+    # the row in LDS (dynamic LDS, set at launch).
+    d0, d1, S = 2, 384, 3
     case = _case(5104, d0, d1, V, "bf16", 0.1, True)
     z = to_device(case.logits, "bf16")
     t = torch.from_numpy(case.targets).cuda()
