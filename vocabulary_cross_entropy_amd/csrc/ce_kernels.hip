@@ -764,8 +764,9 @@ __device__ __forceinline__ u32x4_t pack_vec<1>(const float* g) {
 // stores go through buffer descriptors that end at the row's vector body (a
 // read past it gives 0, a write past it is dropped: on gfx950 the range check
 // covers the scalar offset too, measured), so the vector index goes in the
-// scalar offset and no per-vector bounds branches or addresses are needed.  Same threads, chunks, order and
-// expressions as ce_fb_kernel: bitwise the same outputs.
+// scalar offset and no per-vector bounds branches or addresses are needed.
+// Same threads, chunks, order and expressions as ce_fb_kernel: bitwise the
+// same outputs.
 template <int DT, int NR, int NV, int NT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT / 128)))
 void ce_fb_split_kernel(CeFwdParams f, CeBwdParams b) {

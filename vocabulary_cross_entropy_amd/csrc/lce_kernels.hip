@@ -41,9 +41,9 @@
 //  * Backward, per vocabulary chunk: recompute the logits and write dZ (BF16,
 //    token-major) straight from the accumulators (a lane swap turns the MFMA
 //    layout into 16-byte pieces of token rows; staging the tile in LDS and
-//    storing whole rows was measured slower); dW rows of the chunk are finished by one GEMM over all
-//    tokens (written once, never accumulated); dX accumulates chunk by chunk
-//    in FP32, the last chunk writes BF16.
+//    storing whole rows was measured slower); dW rows of the chunk are
+//    finished by one GEMM over all tokens (written once, never accumulated);
+//    dX accumulates chunk by chunk in FP32, the last chunk writes BF16.
 #include <type_traits>
 
 #include "vce_device.h"
