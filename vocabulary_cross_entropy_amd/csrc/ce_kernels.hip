@@ -386,9 +386,12 @@ template <>
 __device__ __forceinline__ void store_one<1>(uint16_t* dst, float g) { *dst = to_bf16(g); }
 
 // ENT: adds grad_entropy[r] dH/dz_v = grad_entropy[r] p_v (E_p[z] - z_v), with
-// E_p[z] = lse - H from the forward's entropy.
-template <int DT, bool ENT, int NT>
-__global__ __launch_bounds__(NT) void ce_bwd_kernel(CeBwdParams p) {
+// E_p[z] = lse - H from the forward's entropy.  W: the fewest waves per SIMD
+// the register budget must allow (8 lets two 1024-thread workgroups share a
+// CU, which pays off only for rows of 32..64 KB, measured).
+template <int DT, bool ENT, int NT, int W = 1>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(W)))
+void ce_bwd_kernel(CeBwdParams p) {
   using T = typename Elem<DT>::T;
   constexpr int vec = Elem<DT>::kVec;
   // workgroup (r, s): part s of p.splits of row r's vectors
@@ -1133,8 +1136,10 @@ hipError_t launch_ce_forward_backward(const CeFwdParams& f, const CeBwdParams& b
 // kBwdShortRowBytes take the smaller workgroup; longer rows are cut into
 // parts of about 8 vectors a lane (measured on 4096 rows of BF16: 128256
 // columns in two parts 0.370 -> 0.355 ms, 65536 columns in two parts 0.5%
-// faster, 32000 columns in two parts 30% slower, four parts of 128256 4%
-// slower).
+// faster, 32000 columns in two parts 30% slower, three parts of 128256 4%
+// slower, four 8% slower).  Rows of 32..64 KB run two workgroups per CU:
+// 32000 columns 1.5-3% faster in two A/B runs (90.2-93.2 -> 88.9-90.5 us);
+// at 65536 columns it was 4% slower, at 16032 and 128256 no faster.
 template <int DT, bool ENT>
 void launch_bwd(const CeBwdParams& p0, int64_t N, hipStream_t stream) {
   CeBwdParams p = p0;
@@ -1149,8 +1154,13 @@ void launch_bwd(const CeBwdParams& p0, int64_t N, hipStream_t stream) {
     if (splits < 1) splits = 1;
     if (N * splits > (int64_t)INT32_MAX) splits = 1;
     p.splits = (int)splits;
-    hipLaunchKernelGGL((ce_bwd_kernel<DT, ENT, kBwdThreads>), dim3((unsigned)(N * splits)),
-                       dim3(kBwdThreads), 0, stream, p);
+    const dim3 g((unsigned)(N * splits));
+    if (p.V * (DT == 0 ? 4 : 2) <= 2 * kBwdShortRowBytes)
+      hipLaunchKernelGGL((ce_bwd_kernel<DT, ENT, kBwdThreads, 8>), g, dim3(kBwdThreads), 0,
+                         stream, p);
+    else
+      hipLaunchKernelGGL((ce_bwd_kernel<DT, ENT, kBwdThreads>), g, dim3(kBwdThreads), 0, stream,
+                         p);
   }
 }
 
