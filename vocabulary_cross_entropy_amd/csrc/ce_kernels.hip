@@ -759,23 +759,25 @@ __device__ __forceinline__ u32x4_t pack_vec<1>(const float* g) {
                  pack_bf16x2(g[6], g[7])};
 }
 
-// The one-pass kernel for rows of more than 8 vectors per thread (BF16 rows
-// of 32769 .. 131072 logits): held in registers alone, 16 or 32 vectors take
-// about 165 or 250 VGPRs a lane, one workgroup per CU, and each CU alternates
-// between reading a row and computing on it.  Here the first NR vectors of a
-// thread's share stay in VGPRs and the rest (if any) go straight from memory
-// into LDS (buffer_load ... lds, read back by the same thread), so a lane
-// fits in 128 VGPRs and a workgroup in under 80 KB of LDS at 128256 logits
-// (measured 0.449 -> 0.390 ms per headline step): two workgroups share a
-// CU and one's arithmetic overlaps the other's memory traffic.  Loads and
+// The one-pass kernel for rows over 48 KB (BF16 rows of 24577 .. 131072
+// logits): held in registers alone, 8, 16 or 32 vectors a lane take about
+// 120, 165 or 250 VGPRs, so two or one workgroups fit per CU, and each CU
+// alternates between reading a row and computing on it.  Here the first NR
+// vectors of a thread's share stay in VGPRs and the rest (if any) go straight
+// from memory into LDS (buffer_load ... lds, read back by the same thread),
+// so a lane fits in W waves' share of the register file (8 vectors: 70 VGPRs,
+// three workgroups per CU; 16 or 32: 128, two) and a workgroup in under 80 KB
+// of LDS at 128256 logits (measured 0.449 -> 0.390 ms per headline step,
+// 124-129 -> 116-120 us at 4096 rows of 32000): one workgroup's arithmetic
+// overlaps another's memory traffic.  Loads and
 // stores go through buffer descriptors that end at the row's vector body (a
 // read past it gives 0, a write past it is dropped: on gfx950 the range check
 // covers the scalar offset too, measured), so the vector index goes in the
 // scalar offset and no per-vector bounds branches or addresses are needed.
 // Same threads, chunks, order and expressions as ce_fb_kernel: bitwise the
 // same outputs.
-template <int DT, int NR, int NV, int NT>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT / 128)))
+template <int DT, int NR, int NV, int NT, int W = NT / 128>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(W)))
 void ce_fb_split_kernel(CeFwdParams f, CeBwdParams b) {
   using T = typename Elem<DT>::T;
   constexpr int vec = Elem<DT>::kVec;
@@ -1070,15 +1072,16 @@ hipError_t launch_ce_mean(const CeMeanParams& p, hipStream_t stream) {
 
 namespace {
 
-// Rows of 8 .. 32 vectors per thread take ce_fb_split_kernel at 128 VGPRs:
-// up to 16 all in VGPRs, beyond that kFbRegVecs in VGPRs and the rest in
-// LDS, sized for the longest row of this V (no head elements).
+// Rows over 48 KB take ce_fb_split_kernel: up to 8 vectors a lane all in
+// VGPRs at 6 waves per SIMD, up to 16 all in VGPRs at 4, beyond that
+// kFbRegVecs in VGPRs and the rest in LDS, sized for the longest row of this
+// V (no head elements).
 constexpr int kFbRegVecs = 22;
 
-template <int DT, int NR, int NV>
+template <int DT, int NR, int NV, int W = kFwdThreads / 128>
 void launch_fb_split(const CeFwdParams& f, const CeBwdParams& b, dim3 g, int64_t nvec,
                      hipStream_t stream) {
-  auto kern = ce_fb_split_kernel<DT, NR, NV, kFwdThreads>;
+  auto kern = ce_fb_split_kernel<DT, NR, NV, kFwdThreads, W>;
   static const bool attr = [kern] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                               hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1105,9 +1108,8 @@ bool launch_fb_dt(const CeFwdParams& f, const CeBwdParams& b, int64_t N, hipStre
       hipLaunchKernelGGL((ce_fb_kernel<DT, 16, kFwdThreadsShort>), g, blk, 0, stream, f, b);
     return true;
   }
-  const dim3 blk(kFwdThreads);
   if (nvec <= 8 * kFwdThreads)
-    hipLaunchKernelGGL((ce_fb_kernel<DT, 8, kFwdThreads>), g, blk, 0, stream, f, b);
+    launch_fb_split<DT, 8, 8, 6>(f, b, g, nvec, stream);
   else if (nvec <= 16 * kFwdThreads)
     launch_fb_split<DT, 16, 16>(f, b, g, nvec, stream);
   else if (nvec <= kFbVecs * kFwdThreads)
