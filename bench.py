@@ -7,7 +7,9 @@ buffer).  The headline workload is (SQ,B,V) = (2048, 2, 128256) BF16 logits,
 4096 tokens, the shape of the TransformerEngine PR's validation comment.
 Inputs are synthetic and resident in HBM before the timed region.
 
-The K timed steps run back to back with one pair of HIP events around all of
+Each workload first runs untimed for at least 50 ms of GPU time (the clocks
+come back up after the host has spent time building it), then W warmup steps;
+the K timed steps run back to back with one pair of HIP events around all of
 them (nothing recorded in between); each phase is then timed in a loop of its
 own.  Printed: ONE JSON line with throughput (tokens/s), the roofline of the
 dominant kernel (the backward sweep, HBM bound: its algorithmic bytes per
@@ -68,6 +70,30 @@ def _graph_step_ms(step, steps: int, warmup: int) -> float:
     e[1].record()
     torch.cuda.synchronize()
     return e[0].elapsed_time(e[1]) / steps
+
+
+SETTLE_MS = 50.0
+
+
+def _settle(step, min_ms: float = SETTLE_MS) -> None:
+    """Untimed work before a workload's warmup steps: after an idle stretch
+    (the host builds the next workload) the GPU's clocks take ~20 ms of work to
+    come back up -- 4096 x 32000 BF16 steps measured ~155 us in the first 30
+    and ~131 us after 150 -- so each workload first runs its step for at least
+    `min_ms` of GPU time, then the W warmup steps, then the K timed steps."""
+    import torch
+    torch.cuda.synchronize()
+    done = 0.0
+    n = 1
+    while done < min_ms:
+        e = _event_pairs(1)[0]
+        e[0].record()
+        for _ in range(n):
+            step()
+        e[1].record()
+        torch.cuda.synchronize()
+        done += e[0].elapsed_time(e[1])
+        n = min(2 * n, 64)
 
 
 def _loop_ms(fn, steps: int) -> float:
@@ -155,6 +181,7 @@ def bench_logits(case, steps: int, warmup: int):
         fwd()
         bwd()
 
+    _settle(step)
     for _ in range(warmup):
         step()
     # timed region: K whole steps, bracketed by synchronisation, with one pair
@@ -267,6 +294,7 @@ def bench_linear(case, steps: int, warmup: int, f32: bool = False):
         f_step()
         b_step()
 
+    _settle(step)
     for _ in range(warmup):
         step()
     whole = _event_pairs(1)[0]
@@ -315,6 +343,7 @@ def bench_linear(case, steps: int, warmup: int, f32: bool = False):
 
 def _time_steps(step, steps: int, warmup: int):
     import torch
+    _settle(step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
