@@ -1082,15 +1082,13 @@ template <int DT, int NR, int NV, int W = kFwdThreads / 128>
 void launch_fb_split(const CeFwdParams& f, const CeBwdParams& b, dim3 g, int64_t nvec,
                      hipStream_t stream) {
   auto kern = ce_fb_split_kernel<DT, NR, NV, kFwdThreads, W>;
-  static const bool attr = [kern] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (NV - NR) * kFwdThreads * 16);
-    return true;
-  }();
-  (void)attr;
   const int64_t in_lds = (nvec + 63) / 64 * 64 - (int64_t)NR * kFwdThreads;
   const size_t lds = in_lds > 0 ? (size_t)in_lds * 16 : 0;
+  // allow the dynamic LDS on whichever device the call runs (set per call: a
+  // host-side attribute, no stream work, so graph capture is unaffected)
+  if (lds > 0)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   hipLaunchKernelGGL(kern, g, dim3(kFwdThreads), lds, stream, f, b);
 }
 
