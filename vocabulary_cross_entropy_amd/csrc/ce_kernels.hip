@@ -1075,21 +1075,21 @@ namespace {
 // Rows over 48 KB take ce_fb_split_kernel: up to 8 vectors a lane all in
 // VGPRs at 6 waves per SIMD, up to 16 all in VGPRs at 4, beyond that
 // kFbRegVecs in VGPRs and the rest in LDS, sized for the longest row of this
-// V (no head elements).
+// V (no head elements); rows of at most 48 KB see launch_fb_dt.
 constexpr int kFbRegVecs = 22;
 
-template <int DT, int NR, int NV, int W = kFwdThreads / 128>
+template <int DT, int NR, int NV, int W = kFwdThreads / 128, int NT = kFwdThreads>
 void launch_fb_split(const CeFwdParams& f, const CeBwdParams& b, dim3 g, int64_t nvec,
                      hipStream_t stream) {
-  auto kern = ce_fb_split_kernel<DT, NR, NV, kFwdThreads, W>;
-  const int64_t in_lds = (nvec + 63) / 64 * 64 - (int64_t)NR * kFwdThreads;
+  auto kern = ce_fb_split_kernel<DT, NR, NV, NT, W>;
+  const int64_t in_lds = (nvec + 63) / 64 * 64 - (int64_t)NR * NT;
   const size_t lds = in_lds > 0 ? (size_t)in_lds * 16 : 0;
   // allow the dynamic LDS on whichever device the call runs (set per call: a
   // host-side attribute, no stream work, so graph capture is unaffected)
   if (lds > 0)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL(kern, g, dim3(kFwdThreads), lds, stream, f, b);
+  hipLaunchKernelGGL(kern, g, dim3(NT), lds, stream, f, b);
 }
 
 template <int DT>
@@ -1099,11 +1099,16 @@ bool launch_fb_dt(const CeFwdParams& f, const CeBwdParams& b, int64_t N, hipStre
   const int64_t nvec = f.V / Elem<DT>::kVec;
   const dim3 g((unsigned)N);
   if (fwd_short_row(DT, f.V)) {
-    const dim3 blk(kFwdThreadsShort);
+    // rows of at most 48 KB: 256 threads, as the forward; up to 8 vectors a
+    // lane ce_fb_kernel (125 VGPRs, 4 workgroups per CU; the lean kernel at 6
+    // waves per SIMD was 15% slower at 8000 BF16 columns), beyond that the
+    // lean kernel at 4 waves (102 VGPRs where ce_fb_kernel took 173 and two
+    // workgroups per CU: 24000 columns 94-98 -> 87 us)
     if (nvec <= 8 * kFwdThreadsShort)
-      hipLaunchKernelGGL((ce_fb_kernel<DT, 8, kFwdThreadsShort>), g, blk, 0, stream, f, b);
+      hipLaunchKernelGGL((ce_fb_kernel<DT, 8, kFwdThreadsShort>), g, dim3(kFwdThreadsShort), 0,
+                         stream, f, b);
     else
-      hipLaunchKernelGGL((ce_fb_kernel<DT, 16, kFwdThreadsShort>), g, blk, 0, stream, f, b);
+      launch_fb_split<DT, 16, 16, 4, kFwdThreadsShort>(f, b, g, nvec, stream);
     return true;
   }
   if (nvec <= 8 * kFwdThreads)
