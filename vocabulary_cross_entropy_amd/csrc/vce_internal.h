@@ -57,7 +57,7 @@ struct CeBwdParams {
   int reduce_loss;
   int64_t ignore_idx;
   int64_t v0, Vg;  // the row holds columns v0 .. v0 + V - 1 of Vg (0, V unless sharded)
-  int splits;      // workgroups per row (set by the launcher)
+  int splits = 1;  // workgroups per row (set by the launcher)
 };
 
 hipError_t launch_ce_forward(const CeFwdParams& p, int dtype, int64_t N, hipStream_t stream);
