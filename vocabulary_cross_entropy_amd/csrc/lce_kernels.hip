@@ -274,7 +274,7 @@ struct LoopState {
 // 3, behind the barrier).  Waits: the compiler
 // places s_waitcnt vmcnt before each LDS write (its load was issued 32 loads
 // earlier) and lgkmcnt before the MFMAs that use fresh fragments.
-template <int B1, bool PD, bool QD, bool MASK>
+template <int B1, bool PD, bool QD, bool MASK, bool ZERO = false>
 __device__ __forceinline__ void loop_slice(LoopState& S, const SliceLoader<PD>& lp,
                                            const SliceLoader<QD>& lq, uint16_t LDS_AS* sp,
                                            uint16_t LDS_AS* sq, int k, int klast, int wr,
@@ -304,8 +304,10 @@ __device__ __forceinline__ void loop_slice(LoopState& S, const SliceLoader<PD>& 
           __builtin_amdgcn_s_barrier();
           __builtin_amdgcn_sched_barrier(0);
         }
-        S.acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(S.FA[a], S.FB[f][b], S.acc[a][b],
-                                                              0, 0, 0);
+        // ZERO (the tile's first slice): k-step 0 starts from C = 0, an
+        // inline constant of the MFMA, so the accumulators need no clearing
+        const f32x16_t c = (ZERO && ks == 0) ? f32x16_t{} : S.acc[a][b];
+        S.acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(S.FA[a], S.FB[f][b], c, 0, 0, 0);
         // next k-step's Q fragments (at k-step 3: of the next slice, from the
         // stage the barrier has just published)
         if (m == (ks == 3 ? 2 : 1)) {
@@ -365,10 +367,11 @@ struct Segs {
   }
 };
 
-// One operand pair's sum over K added to the accumulators in S: loaders,
-// prologue and main loop, then a drain and a barrier, after which both LDS
-// stages are free again (for the next pair or the epilogue).
-template <bool PD, bool QD, bool MASK>
+// One operand pair's sum over K added to the accumulators in S (ZERO: stored
+// into them, whatever they held): loaders, prologue and main loop, then a
+// drain and a barrier, after which both LDS stages are free again (for the
+// next pair or the epilogue).
+template <bool PD, bool QD, bool MASK, bool ZERO>
 __device__ __forceinline__ void mainloop(LoopState& S, const Operand& P, const Operand& Q,
                                          int64_t K, int64_t i0, int64_t j0, int wave, int lane,
                                          int wr, int wc, uint16_t LDS_AS* sp,
@@ -412,7 +415,20 @@ __device__ __forceinline__ void mainloop(LoopState& S, const Operand& P, const O
   for (int a = 0; a < NA; ++a) S.FA[a] = frag<PD>(sp, wr * WM + 32 * a, 0, lane);
 #pragma unroll
   for (int b = 0; b < NB; ++b) S.FB[0][b] = frag<QD>(sq, wc * WN + 32 * b, 0, lane);
-  for (int k = 0; k < nk; k += 2) {
+  int k = 0;
+  if (ZERO) {
+    if (nk == 0) {  // K = 0: the sum is empty
+#pragma unroll
+      for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) S.acc[a][b] = f32x16_t{};
+    } else {
+      loop_slice<1, PD, QD, MASK, true>(S, lp, lq, sp, sq, 0, klast, wr, wc, lane);
+      loop_slice<0, PD, QD, MASK>(S, lp, lq, sp, sq, 1, klast, wr, wc, lane);
+      k = 2;
+    }
+  }
+  for (; k < nk; k += 2) {
     loop_slice<1, PD, QD, MASK>(S, lp, lq, sp, sq, k, klast, wr, wc, lane);
     loop_slice<0, PD, QD, MASK>(S, lp, lq, sp, sq, k + 1, klast, wr, wc, lane);
   }
@@ -437,17 +453,21 @@ __device__ __forceinline__ void gemm_tile(const Segs<NSEG>& G, int64_t K, int bi
   const int wr = wave / NWC, wc = wave % NWC;
 
   LoopState S;
+  if (NSEG == 1) {
+    // the first k-step writes the accumulators
+    mainloop<PD, QD, MASK, true>(S, G.p(0), G.q(0), K, i0, j0, wave, lane, wr, wc, sp, sq);
+  } else {
 #pragma unroll
-  for (int a = 0; a < NA; ++a)
+    for (int a = 0; a < NA; ++a)
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) S.acc[a][b][r] = 0.0f;
-
-  // one copy of the main loop, run once per pair
+        for (int r = 0; r < 16; ++r) S.acc[a][b][r] = 0.0f;
+    // one copy of the main loop, run once per pair
 #pragma nounroll
-  for (int s = 0; s < NSEG; ++s)
-    mainloop<PD, QD, MASK>(S, G.p(s), G.q(s), K, i0, j0, wave, lane, wr, wc, sp, sq);
+    for (int s = 0; s < NSEG; ++s)
+      mainloop<PD, QD, MASK, false>(S, G.p(s), G.q(s), K, i0, j0, wave, lane, wr, wc, sp, sq);
+  }
   Epi::apply(ep, S.acc, i0, j0, wr, wc, lane, smem);
 }
 
@@ -789,44 +809,53 @@ struct EpiDzT {
       *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{w[0], w[1], w[2], w[3]};
       *reinterpret_cast<u32x4_t*>(dst + 16) = u32x4_t{w[4], w[5], w[6], w[7]};
     };
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const Tok k = token(b);
-      const float goff = k.g * (p.eps / (float)p.Vg);
-      const int tl = target_row(k);
-      uint16_t* const drow = p.dz + (j0 + wc * WN + b * 32 + (lane & 31)) * p.ldz + row0;
-#pragma unroll
-      for (int a = 0; a < NA; ++a) {
-        float val[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x = value(k, goff, acc[a][b][4 * q + e]);
-            val[4 * q + e] = (full || a * 32 + 8 * q + e < lim) ? x : 0.0f;
+    // the per-element row test only where the wave's rows run past the
+    // chunk (a uniform branch: a select per element there, none elsewhere)
+    auto columns = [&](auto masked) {
+      constexpr bool MASKED = decltype(masked)::value;
+  #pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const Tok k = token(b);
+        const float goff = k.g * (p.eps / (float)p.Vg);
+        const int tl = target_row(k);
+        uint16_t* const drow = p.dz + (j0 + wc * WN + b * 32 + (lane & 31)) * p.ldz + row0;
+  #pragma unroll
+        for (int a = 0; a < NA; ++a) {
+          float val[16];
+  #pragma unroll
+          for (int q = 0; q < 4; ++q)
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float x = value(k, goff, acc[a][b][4 * q + e]);
+              val[4 * q + e] = (!MASKED || a * 32 + 8 * q + e < lim) ? x : 0.0f;
+            }
+          // the target's element (rarely in this block): the same value less
+          // (1 - eps) g
+          if (tl >= 0 && (tl >> 5) == a) {
+  #pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (tl == a * 32 + 8 * (r >> 2) + (r & 3))
+                val[r] = value(k, goff, acc[a][b][r]) - k.g * (1.0f - p.eps);
           }
-        // the target's element (rarely in this block): the same value less
-        // (1 - eps) g
-        if (tl >= 0 && (tl >> 5) == a) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (tl == a * 32 + 8 * (r >> 2) + (r & 3))
-              val[r] = value(k, goff, acc[a][b][r]) - k.g * (1.0f - p.eps);
+          uint32_t w[8];
+  #pragma unroll
+          for (int r = 0; r < 8; ++r) w[r] = pack_bf16x2(val[2 * r], val[2 * r + 1]);
+          if constexpr (SPLIT) {
+            // the lo plane: what the BF16 hi value leaves of each FP32 value
+            uint32_t wl[8];
+  #pragma unroll
+            for (int r = 0; r < 8; ++r)
+              wl[r] = pack_bf16x2(val[2 * r] - bf16_lo(w[r]), val[2 * r + 1] - bf16_hi(w[r]));
+            swap_store(wl, drow + p.plane + a * 32);
+          }
+          swap_store(w, drow + a * 32);
         }
-        uint32_t w[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) w[r] = pack_bf16x2(val[2 * r], val[2 * r + 1]);
-        if constexpr (SPLIT) {
-          // the lo plane: what the BF16 hi value leaves of each FP32 value
-          uint32_t wl[8];
-#pragma unroll
-          for (int r = 0; r < 8; ++r)
-            wl[r] = pack_bf16x2(val[2 * r] - bf16_lo(w[r]), val[2 * r + 1] - bf16_hi(w[r]));
-          swap_store(wl, drow + p.plane + a * 32);
-        }
-        swap_store(w, drow + a * 32);
       }
-    }
+    };
+    if (full)
+      columns(std::false_type{});
+    else
+      columns(std::true_type{});
   }
 };
 
