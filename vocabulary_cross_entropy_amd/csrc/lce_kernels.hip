@@ -380,6 +380,12 @@ __device__ __forceinline__ void mainloop(LoopState& S, const Operand& P, const O
   SliceLoader<QD> lq;
   lp.init(P, i0, wave, lane);
   lq.init(Q, j0, wave, lane);
+  // Q's stages start 64 KB into LDS, past the 16-bit offset of an LDS
+  // instruction; with that base opaque to the compiler, each fragment address
+  // of Q is one register for both stages (stage and block go in the offset).
+  // Measured on the one-pair tile only (it gave the three-pair tile more
+  // spills).
+  if (ZERO) asm volatile("" : "+v"(sq));
   // An even number of slices (the loop body runs two); slices at or past K
   // read as zeros and add nothing.
   const int nk = (int)((K + 2 * BK - 1) / (2 * BK)) * 2;
