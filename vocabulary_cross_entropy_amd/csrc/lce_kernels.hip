@@ -455,7 +455,8 @@ __device__ __forceinline__ void gemm_tile(const Segs<NSEG>& G, int64_t K, int bi
   int ti, tj;
   tile_of(bid, n_ti, n_tj, &ti, &tj);
   const int64_t i0 = (int64_t)ti * BM, j0 = (int64_t)tj * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
   const int wr = wave / NWC, wc = wave % NWC;
 
   LoopState S;
@@ -474,7 +475,12 @@ __device__ __forceinline__ void gemm_tile(const Segs<NSEG>& G, int64_t K, int bi
     for (int s = 0; s < NSEG; ++s)
       mainloop<PD, QD, MASK, false>(S, G.p(s), G.q(s), K, i0, j0, wave, lane, wr, wc, sp, sq);
   }
-  Epi::apply(ep, S.acc, i0, j0, wr, wc, lane, smem);
+  // the epilogue's lane index is computed anew after the loop (from a value
+  // the compiler cannot hoist), so no per-lane index lives across the loop
+  unsigned z = 0;
+  asm volatile("" : "+s"(z));
+  const int elane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, z));
+  Epi::apply(ep, S.acc, i0, j0, wr, wc, elane, smem);
 }
 
 template <class Epi, bool PD, bool QD, bool MASK, int NSEG>
