@@ -31,7 +31,8 @@ def _bf16(a):
 
 @pytest.mark.parametrize("p_dim,q_dim", [(False, False), (False, True), (True, False), (True, True)])
 @pytest.mark.parametrize("rows,cols,K", [(300, 520, 200), (512, 768, 4096), (40, 8, 8),
-                                         (776, 1000, 4104), (4096, 256, 64), (264, 256, 333)])
+                                         (776, 1000, 4104), (4096, 256, 64), (264, 256, 333),
+                                         (264, 520, 128), (520, 256, 256), (256, 264, 192)])
 def test_gemm(rows, cols, K, p_dim, q_dim):
     """The GEMM core in each operand layout against an FP64 product of the same
     BF16 values.  Ragged rows, columns and K cover the masked loads; a
@@ -55,6 +56,19 @@ def test_gemm(rows, cols, K, p_dim, q_dim):
     # FP32 accumulation of exact BF16 products: error far below 2^-14 of the
     # sum of |terms|; an indexing mistake gives errors of the order of the terms
     assert np.all(err <= 2.0 ** -14 * scale + 1e-30), float((err / (scale + 1e-30)).max())
+
+
+@pytest.mark.parametrize("p_dim,q_dim", [(False, False), (True, True)])
+def test_gemm_empty_k(p_dim, q_dim):
+    """K = 0: the empty sum writes zeros over whatever C held (the tile's first
+    k-step normally writes the accumulators; with no k-step they are cleared)."""
+    rows, cols = 264, 520
+    P = _bf16(wl.f32_to_bf16_bits(np.ones((8, rows) if p_dim else (rows, 8), np.float32)))
+    Q = _bf16(wl.f32_to_bf16_bits(np.ones((8, cols) if q_dim else (cols, 8), np.float32)))
+    C = torch.full((rows, cols), float("nan"), dtype=torch.float32, device="cuda")
+    vce.gemm_bf16(P, Q, 0, p_dim=p_dim, q_dim=q_dim, out=C)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(C).item() == 0
 
 
 # --- helpers -----------------------------------------------------------------------
