@@ -513,6 +513,30 @@ __global__ __launch_bounds__(NT, 1) void gemm2_kernel(GemmProblem<NSEG> A,
     gemm_tile<EB, PB, QB, MB, NSEG>(B.G, B.K, blockIdx.x - na, B.n_ti, B.n_tj, eb, smem);
 }
 
+// Three independent problems in one grid, in this order: the backward's dX and
+// dW GEMMs of chunk c (both read that chunk's dZ) and the dZ GEMM of chunk
+// c + 1 (written to the other dZ buffer).  The next chunk's short dZ tiles
+// fill the last wave of the long dX and dW tiles, which separate launches
+// leave partly idle.
+template <class EA, bool PA, bool QA, bool MA, class EB, bool PB, bool QB, bool MB, class EC,
+          bool PC, bool QC, bool MC, int NSEG>
+__global__ __launch_bounds__(NT, 1) void gemm3_kernel(GemmProblem<NSEG> A,
+                                                      typename EA::Params ea,
+                                                      GemmProblem<NSEG> B,
+                                                      typename EB::Params eb,
+                                                      GemmProblem<NSEG> C,
+                                                      typename EC::Params ec) {
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[kSmemElems];
+  const int na = A.n_ti * A.n_tj, nb = B.n_ti * B.n_tj;
+  const int bid = blockIdx.x;
+  if (bid < na)
+    gemm_tile<EA, PA, QA, MA, NSEG>(A.G, A.K, bid, A.n_ti, A.n_tj, ea, smem);
+  else if (bid < na + nb)
+    gemm_tile<EB, PB, QB, MB, NSEG>(B.G, B.K, bid - na, B.n_ti, B.n_tj, eb, smem);
+  else
+    gemm_tile<EC, PC, QC, MC, NSEG>(C.G, C.K, bid - na - nb, C.n_ti, C.n_tj, ec, smem);
+}
+
 // ---- epilogues ------------------------------------------------------------------
 
 // Plain FP32 store (the exported building block).
@@ -1095,6 +1119,46 @@ hipError_t run_gemm2(const Segs<NSEG>& GA, int64_t rowsA, int64_t colsA, int64_t
   return launch2<EA, PA, QA, true, EB, PB, QB, true, NSEG>(A, ea, B, eb, n, stream);
 }
 
+template <class EA, bool PA, bool QA, class EB, bool PB, bool QB, bool MB, class EC, bool PC,
+          bool QC, bool MC, int NSEG>
+hipError_t launch3(const GemmProblem<NSEG>& A, const typename EA::Params& ea,
+                   const GemmProblem<NSEG>& B, const typename EB::Params& eb,
+                   const GemmProblem<NSEG>& C, const typename EC::Params& ec, int64_t n,
+                   hipStream_t stream) {
+  hipLaunchKernelGGL((gemm3_kernel<EA, PA, QA, false, EB, PB, QB, MB, EC, PC, QC, MC, NSEG>),
+                     dim3((unsigned)n), dim3(NT), 0, stream, A, ea, B, eb, C, ec);
+  return hipGetLastError();
+}
+
+// Problems A, B and C in one launch, in that order.  A's K must need no mask
+// (the callers pass a whole chunk); B's and C's may.
+template <class EA, bool PA, bool QA, class EB, bool PB, bool QB, class EC, bool PC, bool QC,
+          int NSEG>
+hipError_t run_gemm3(const Segs<NSEG>& GA, int64_t rowsA, int64_t colsA, int64_t KA,
+                     const typename EA::Params& ea, const Segs<NSEG>& GB, int64_t rowsB,
+                     int64_t colsB, int64_t KB, const typename EB::Params& eb,
+                     const Segs<NSEG>& GC, int64_t rowsC, int64_t colsC, int64_t KC,
+                     const typename EC::Params& ec, hipStream_t stream) {
+  GemmProblem<NSEG> A{GA, KA, (int)((rowsA + BM - 1) / BM), (int)((colsA + BN - 1) / BN)};
+  GemmProblem<NSEG> B{GB, KB, (int)((rowsB + BM - 1) / BM), (int)((colsB + BN - 1) / BN)};
+  GemmProblem<NSEG> C{GC, KC, (int)((rowsC + BM - 1) / BM), (int)((colsC + BN - 1) / BN)};
+  const int64_t n = (int64_t)A.n_ti * A.n_tj + (int64_t)B.n_ti * B.n_tj + (int64_t)C.n_ti * C.n_tj;
+  if (n <= 0) return hipSuccess;
+  if (n > INT32_MAX / 2 || needs_mask(KA)) return hipErrorInvalidValue;
+  const bool mb = needs_mask(KB), mc = needs_mask(KC);
+  if (!mb && !mc)
+    return launch3<EA, PA, QA, EB, PB, QB, false, EC, PC, QC, false, NSEG>(A, ea, B, eb, C, ec, n,
+                                                                          stream);
+  if (!mb && mc)
+    return launch3<EA, PA, QA, EB, PB, QB, false, EC, PC, QC, true, NSEG>(A, ea, B, eb, C, ec, n,
+                                                                         stream);
+  if (mb && !mc)
+    return launch3<EA, PA, QA, EB, PB, QB, true, EC, PC, QC, false, NSEG>(A, ea, B, eb, C, ec, n,
+                                                                         stream);
+  return launch3<EA, PA, QA, EB, PB, QB, true, EC, PC, QC, true, NSEG>(A, ea, B, eb, C, ec, n,
+                                                                      stream);
+}
+
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
@@ -1129,9 +1193,13 @@ bool lce_make_plan(int64_t M, int64_t H, int64_t V, LcePlan* plan, bool f32) {
   const size_t dz = align256((size_t)p.Mp * p.chunk * 2);
   p.dzplane = f32 ? (int64_t)(dz / 2) : 0;
   const size_t dx = (!f32 && p.n_chunks > 1) ? align256((size_t)p.Mp * H * 4) : 0;
+  // the BF16 form with several chunks keeps two dZ buffers: chunk c + 1's dZ
+  // is formed in the launch that reads chunk c's
+  const bool two_dz = !f32 && p.n_chunks > 1;
   p.off_part = split;
   p.off_dz = split;
-  p.off_dx = split + (f32 ? 2 : 1) * dz;
+  p.off_dz2 = two_dz ? split + dz : split;
+  p.off_dx = split + (f32 || two_dz ? 2 : 1) * dz;
   const size_t bwd = p.off_dx + dx;
   p.fwd_bytes = fwd;
   p.total = fwd > bwd ? fwd : bwd;
@@ -1302,6 +1370,71 @@ hipError_t backward_f32(const LcePlan& plan, const LceBwdArgs& a, hipStream_t st
   return hipSuccess;
 }
 
+// The BF16 backward, per vocabulary chunk c: dZ_c (vocabulary x tokens, K = H,
+// both operands K-contiguous) into one of two buffers; then dX += dZ_c W_c
+// (hidden x tokens, K = the chunk's vocabulary: W_c read dim-contiguous, dZ
+// K-contiguous) and the chunk's dW rows (hidden x vocabulary, K = tokens: X
+// and dZ both read dim-contiguous) in one launch, dX's longer tiles first, and
+// with them dZ_{c+1} into the other buffer, its short tiles last.
+template <bool ENT>
+hipError_t backward_bf16(const LcePlan& plan, const LceBwdArgs& a, hipStream_t stream) {
+  uint16_t* const dzb[2] = {reinterpret_cast<uint16_t*>(a.ws + plan.off_dz),
+                            reinterpret_cast<uint16_t*>(a.ws + plan.off_dz2)};
+  float* dxacc = reinterpret_cast<float*>(a.ws + plan.off_dx);
+  const uint16_t* X = static_cast<const uint16_t*>(a.X);
+  const uint16_t* W = static_cast<const uint16_t*>(a.W);
+  const int64_t H = plan.H, M = plan.M;
+  auto rows_of = [&](int64_t c) {
+    const int64_t c0 = c * plan.chunk;
+    return (plan.V - c0) < plan.chunk ? (plan.V - c0) : plan.chunk;
+  };
+  auto dz_problem = [&](int64_t c, uint16_t* dz, Segs<1>* G, typename EpiDzT<ENT>::Params* ep) {
+    const int64_t c0 = c * plan.chunk, vc = rows_of(c);
+    *G = Segs<1>{{Operand{W + c0 * H, H, vc, H}}, {Operand{X, H, M, H}}};
+    *ep = typename EpiDzT<ENT>::Params{dz, plan.ldz, c0, vc, a.stats, a.targets, a.grad_output,
+                                       a.n_valid, ENT ? a.entropy : nullptr,
+                                       ENT ? a.grad_entropy : nullptr, a.eps, a.reduce_loss,
+                                       a.ignore_idx, M, plan.V, a.v0, a.Vg};
+  };
+  hipError_t e;
+  {
+    Segs<1> G;
+    typename EpiDzT<ENT>::Params ep;
+    dz_problem(0, dzb[0], &G, &ep);
+    e = run_gemm<EpiDzT<ENT>, false, false, 1>(G, rows_of(0), plan.Mp, H, ep, stream);
+    if (e != hipSuccess) return e;
+  }
+  for (int64_t c = 0; c < plan.n_chunks; ++c) {
+    const int64_t c0 = c * plan.chunk, vc = rows_of(c);
+    uint16_t* dz = dzb[c & 1];
+    const Segs<1> GX{{Operand{W + c0 * H, H, H, vc}}, {Operand{dz, plan.ldz, M, vc}}};
+    const int mode = (c > 0 ? 1 : 0) | (c + 1 == plan.n_chunks ? 2 : 0);
+    const EpiDx::Params ex{dxacc, static_cast<uint16_t*>(a.dX), H, M, mode};
+    const Segs<1> GW{{Operand{X, H, H, M}}, {Operand{dz, plan.ldz, vc, M}}};
+    const EpiDw::Params ew{static_cast<uint16_t*>(a.dW), H, c0, vc};
+    if (c + 1 < plan.n_chunks && plan.off_dz2 != plan.off_dz && !needs_mask(vc)) {
+      Segs<1> GZ;
+      typename EpiDzT<ENT>::Params ez;
+      dz_problem(c + 1, dzb[(c + 1) & 1], &GZ, &ez);
+      e = run_gemm3<EpiDx, true, false, EpiDw, true, true, EpiDzT<ENT>, false, false, 1>(
+          GX, H, M, vc, ex, GW, H, vc, M, ew, GZ, rows_of(c + 1), plan.Mp, H, ez, stream);
+      if (e != hipSuccess) return e;
+    } else {
+      e = run_gemm2<EpiDx, true, false, EpiDw, true, true, 1>(GX, H, M, vc, ex, GW, H, vc, M, ew,
+                                                              stream);
+      if (e != hipSuccess) return e;
+      if (c + 1 < plan.n_chunks) {  // one dZ buffer: the next chunk's dZ after this launch
+        Segs<1> GZ;
+        typename EpiDzT<ENT>::Params ez;
+        dz_problem(c + 1, dzb[(c + 1) & 1], &GZ, &ez);
+        e = run_gemm<EpiDzT<ENT>, false, false, 1>(GZ, rows_of(c + 1), plan.Mp, H, ez, stream);
+        if (e != hipSuccess) return e;
+      }
+    }
+  }
+  return hipSuccess;
+}
+
 }  // namespace
 
 hipError_t launch_lce_backward(const LcePlan& plan, const LceBwdArgs& a, hipStream_t stream) {
@@ -1315,52 +1448,8 @@ hipError_t launch_lce_backward(const LcePlan& plan, const LceBwdArgs& a, hipStre
   if (plan.f32)
     return a.grad_entropy ? backward_f32<true>(plan, a, stream)
                           : backward_f32<false>(plan, a, stream);
-  uint16_t* dz = reinterpret_cast<uint16_t*>(a.ws + plan.off_dz);
-  float* dxacc = reinterpret_cast<float*>(a.ws + plan.off_dx);
-  const uint16_t* X = static_cast<const uint16_t*>(a.X);
-  const uint16_t* W = static_cast<const uint16_t*>(a.W);
-  for (int64_t c = 0; c < plan.n_chunks; ++c) {
-    const int64_t c0 = c * plan.chunk;
-    const int64_t vc = (plan.V - c0) < plan.chunk ? (plan.V - c0) : plan.chunk;
-    const uint16_t* Wc = W + c0 * plan.H;
-    // dZ of the chunk: (vocabulary x tokens), K = H, both operands K-contiguous
-    {
-      Operand P{Wc, plan.H, vc, plan.H};
-      Operand Q{X, plan.H, plan.M, plan.H};
-      hipError_t e;
-      if (a.grad_entropy) {
-        EpiDzT<true>::Params ep{dz, plan.ldz, c0, vc, a.stats, a.targets, a.grad_output,
-                                a.n_valid, a.entropy, a.grad_entropy, a.eps, a.reduce_loss,
-                                a.ignore_idx, plan.M, plan.V, a.v0, a.Vg};
-        e = run_gemm<EpiDzT<true>, false, false>(P, Q, vc, plan.Mp, plan.H, ep, stream);
-      } else {
-        EpiDzT<false>::Params ep{dz, plan.ldz, c0, vc, a.stats, a.targets, a.grad_output,
-                                 a.n_valid, nullptr, nullptr, a.eps, a.reduce_loss,
-                                 a.ignore_idx, plan.M, plan.V, a.v0, a.Vg};
-        e = run_gemm<EpiDzT<false>, false, false>(P, Q, vc, plan.Mp, plan.H, ep, stream);
-      }
-      if (e != hipSuccess) return e;
-    }
-    // dX += dZ_c W_c: (hidden x tokens), K = vocabulary of the chunk; W_c is
-    // read dim-contiguous (h contiguous per vocabulary row), dZ K-contiguous.
-    // dW rows of the chunk: (hidden x vocabulary), K = tokens; X (h contiguous
-    // per token) and dZ (v contiguous per token) are both read dim-contiguous.
-    // One launch, dX's (longer) tiles first.
-    {
-      Operand PX{Wc, plan.H, plan.H, vc};
-      Operand QX{dz, plan.ldz, plan.M, vc};
-      const int mode = (c > 0 ? 1 : 0) | (c + 1 == plan.n_chunks ? 2 : 0);
-      EpiDx::Params ex{dxacc, static_cast<uint16_t*>(a.dX), plan.H, plan.M, mode};
-      Operand PW{X, plan.H, plan.H, plan.M};
-      Operand QW{dz, plan.ldz, vc, plan.M};
-      EpiDw::Params ew{static_cast<uint16_t*>(a.dW), plan.H, c0, vc};
-      hipError_t e = run_gemm2<EpiDx, true, false, EpiDw, true, true, 1>(
-          Segs<1>{{PX}, {QX}}, plan.H, plan.M, vc, ex, Segs<1>{{PW}, {QW}}, plan.H, vc, plan.M,
-          ew, stream);
-      if (e != hipSuccess) return e;
-    }
-  }
-  return hipSuccess;
+  return a.grad_entropy ? backward_bf16<true>(plan, a, stream)
+                        : backward_bf16<false>(plan, a, stream);
 }
 
 hipError_t launch_gemm_bf16(const void* P, int64_t ldp, int p_dim, const void* Q, int64_t ldq,

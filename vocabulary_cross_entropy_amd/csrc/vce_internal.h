@@ -89,6 +89,7 @@ struct LcePlan {
   int64_t ldz;         // row stride (elements) of the dZ chunk buffer
   size_t off_part;     // forward: per-tile partials and target logits
   size_t off_dz, off_dx;  // backward: dZ of one chunk, FP32 dX accumulator
+  size_t off_dz2;         // second dZ buffer (BF16 form, several chunks), else off_dz
   size_t fwd_bytes;       // what the forward alone uses (from offset 0)
   size_t total;
   // FP32 inputs: X and W split into BF16 hi and lo planes in the workspace
