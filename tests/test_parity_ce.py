@@ -183,6 +183,20 @@ def test_ragged_vocab(V, dtype):
     check_backward(case, out)
 
 
+@pytest.mark.parametrize("V,dtype,reduce_loss", [(32000, "bf16", True), (128256, "bf16", False),
+                                               (4099, "fp32", False), (1000, "fp32", True)])
+def test_full_smoothing(V, dtype, reduce_loss):
+    # eps = 1: every class gets 1/V, the target none, so the loss is lse - mean z
+    # whatever the target and the gradient is g (p - 1/V) (the target's (1 - eps)
+    # term vanishes); the oracle states q = (1 - eps) onehot + eps / V directly.
+    case = wl.make_logits(2110 + V, 2, 16, V, dtype=dtype, sigma=3.0, ignore_count=3,
+                          label_smoothing=1.0, reduce_loss=reduce_loss, grad_output="random")
+    _say(f"full smoothing V={V} {dtype} reduce={reduce_loss}")
+    out = run_case(case)
+    check_forward(case, out)
+    check_backward(case, out)
+
+
 def test_fp32_large_vocab():
     case = wl.make_logits(2101, 8, 8, 128256, dtype="fp32", sigma=4.0, ignore_count=3,
                           target_boost=8.0, label_smoothing=0.1, reduce_loss=True)

@@ -56,7 +56,7 @@ def _case(seed, d0, d1, V, dtype, eps, red, layout="B,SQ", n_ign=3, sigma=3.0):
                                      ("bf16", 40000), ("bf16", 90001), ("bf16", 100003),
                                      ("bf16", 128256),
                                      ("fp32", 45000)])
-@pytest.mark.parametrize("eps,red", [(0.0, False), (0.1, True)])
+@pytest.mark.parametrize("eps,red", [(0.0, False), (0.1, True), (1.0, False)])
 @pytest.mark.parametrize("overwrite", [False, True])
 def test_one_pass_equals_two_calls(dtype, V, eps, red, overwrite):
     # 131080 BF16 and 70000 FP32 exceed the on-chip row and take the two sweeps;

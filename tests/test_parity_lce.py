@@ -124,7 +124,7 @@ def full_check(case):
     return out
 
 
-@pytest.mark.parametrize("eps", [0.0, 0.1])
+@pytest.mark.parametrize("eps", [0.0, 0.1, 1.0])
 @pytest.mark.parametrize("reduce_loss", [True, False])
 def test_linear_small(eps, reduce_loss):
     case = wl.make_linear(3001, 300, 264, 1000, ignore_count=7, label_smoothing=eps,
