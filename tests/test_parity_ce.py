@@ -197,6 +197,74 @@ def test_full_smoothing(V, dtype, reduce_loss):
     check_backward(case, out)
 
 
+@pytest.mark.parametrize("kind", ["offset_fp32", "wide_bf16"])
+def test_large_logits(kind):
+    # Logits far from 0: an offset of 1e4 (z - m still exact in FP32) and a
+    # spread of sigma = 100 in BF16 (most exponentials underflow to 0).
+    if kind == "offset_fp32":
+        case = wl.make_logits(2120, 2, 8, 3000, dtype="fp32", sigma=2.0, ignore_count=2,
+                              grad_output="random")
+        case.logits += np.float32(1e4)
+    else:
+        case = wl.make_logits(2121, 2, 8, 32000, dtype="bf16", sigma=100.0, ignore_count=2,
+                              label_smoothing=0.1, reduce_loss=True)
+    _say(f"large logits: {kind}")
+    out = run_case(case)
+    ref_loss, ref_stats, _ = oracle.ce_forward(case.logits, case.targets, case.label_smoothing,
+                                               case.ignore_idx)
+    assert_loss_close(out["loss"], ref_loss)
+    valid = case.targets.reshape(-1) != case.ignore_idx
+    st, rs = out["stats"][valid], ref_stats[valid]
+    np.testing.assert_array_equal(st[:, 0], rs[:, 0].astype(np.float32))
+    np.testing.assert_array_equal(st[:, 2], rs[:, 2].astype(np.float32))
+    np.testing.assert_allclose(st[:, 1], rs[:, 1], rtol=2e-5)
+    # the mean logit is an FP32 sum over the row: its error scales with the
+    # size of the logits (1e4 here), not with the mean
+    size = np.abs(oracle.bf16_to_f64(case.logits) if case.dtype == "bf16" else
+                  case.logits.astype(np.float64)).reshape(case.N, -1).max(axis=1)[valid]
+    assert np.all(np.abs(st[:, 3] - rs[:, 3]) <= 1e-5 + 2e-7 * size)
+    check_backward(case, out)
+
+
+@pytest.mark.parametrize("V,dtype", [(32000, "bf16"), (128256, "bf16"), (4099, "fp32")])
+def test_rows_masked_with_the_most_negative_finite_value(V, dtype):
+    # All but a few logits of each row set to the most negative finite value
+    # (a finite mask instead of -inf): most threads' first chunks then hold
+    # nothing else, and their running maximum lies far below the row's.  Their
+    # terms must vanish in the merge (e^(m_old - m) = 0), not poison d.  The
+    # mean logit overflows FP32 here, so eps = 0 and the saved mean is not
+    # compared.
+    case = wl.make_logits(2130 + V, 2, 8, V, dtype=dtype, sigma=3.0, ignore_count=2,
+                          grad_output="random")
+    rng = np.random.default_rng(V)
+    keep = np.zeros((case.N, V), bool)
+    for r in range(case.N):
+        keep[r, rng.choice(V, 5, replace=False)] = True
+    tf = case.targets.reshape(-1)
+    keep[np.arange(case.N)[tf >= 0], tf[tf >= 0]] = True
+    flat = case.logits.reshape(case.N, V)
+    flat[~keep] = np.uint16(0xFF7F) if dtype == "bf16" else np.float32(-3.4028235e38)
+    _say(f"masked rows V={V} {dtype}")
+    out = run_case(case)
+    ref_loss, ref_stats, _ = oracle.ce_forward(case.logits, case.targets, 0.0, case.ignore_idx)
+    assert_loss_close(out["loss"], ref_loss)
+    valid = tf != case.ignore_idx
+    st, rs = out["stats"][valid], ref_stats[valid]
+    np.testing.assert_array_equal(st[:, 0], rs[:, 0].astype(np.float32))
+    np.testing.assert_array_equal(st[:, 2], rs[:, 2].astype(np.float32))
+    np.testing.assert_allclose(st[:, 1], rs[:, 1], rtol=2e-5)
+    check_backward(case, out)
+    # the one-pass form reduces the same way
+    z = to_device(case.logits, case.dtype)
+    t = torch.from_numpy(case.targets).cuda()
+    go = torch.from_numpy(case.grad_output).cuda()
+    l1, _, s1, _, g1 = vce.ce_forward_backward(z, t, go)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(l1.cpu().numpy(), out["loss"])
+    np.testing.assert_array_equal(s1.cpu().numpy().reshape(-1, 4), out["stats"])
+    np.testing.assert_array_equal(to_host_bits(g1), out["grad"])
+
+
 def test_fp32_large_vocab():
     case = wl.make_logits(2101, 8, 8, 128256, dtype="fp32", sigma=4.0, ignore_count=3,
                           target_boost=8.0, label_smoothing=0.1, reduce_loss=True)

@@ -133,6 +133,39 @@ def test_linear_small(eps, reduce_loss):
     full_check(case)
 
 
+@pytest.mark.parametrize("log2_scale", [14, 22])
+def test_linear_large_logits(log2_scale):
+    # W scaled by 2^k (exact in BF16) puts the logits near 2^k: the exponent
+    # offsets m log2(e) and lse log2(e) then round by up to 2^(k-24), which the
+    # epilogues take back out per token.
+    case = wl.make_linear(3010 + log2_scale, 300, 264, 3000, ignore_count=7,
+                          label_smoothing=0.1, reduce_loss=True,
+                          name=f"large_logits_2^{log2_scale}")
+    w = wl.bf16_bits_to_f32(case.W) * np.float32(2.0 ** log2_scale)
+    case.W = wl.f32_to_bf16_bits(w)
+    assert np.array_equal(wl.bf16_bits_to_f32(case.W), w)
+    out = run_lce(case)
+    ref_loss, ref_stats, _ = linear.forward(case.X, case.W, case.targets, case.label_smoothing,
+                                            case.ignore_idx)
+    lw = check_loss(case, out, ref_loss)
+    # The logits themselves carry the FP32 GEMM's rounding, relative to their
+    # size (here up to about 2^(k+2)), so the row max and the target logit are
+    # compared relative to that size; d = sum exp(z - m) inherits absolute
+    # logit errors of that order and is not compared.
+    valid = case.targets != case.ignore_idx
+    st, rs = out["stats"][valid], ref_stats[valid]
+    size = 2.0 ** (log2_scale + 3)
+    np.testing.assert_allclose(st[:, 0], rs[:, 0], rtol=0, atol=2e-5 * size)
+    np.testing.assert_allclose(st[:, 2], rs[:, 2], rtol=0, atol=2e-5 * size)
+    g = oracle.row_scale(case.grad_output, case.targets, case.reduce_loss, case.ignore_idx)
+    rdX, rdW = linear.backward(case.X, case.W, case.targets, g, case.label_smoothing,
+                               case.ignore_idx)
+    dW = oracle.bf16_to_f64(to_host_bits(out["dW_dev"]))
+    fx, fw = rel_frobenius(out["dX"], rdX), rel_frobenius(dW, rdW)
+    _say(f"{case.name}: loss rel {lw:.2e}, dX frob {fx:.2e}, dW frob {fw:.2e}")
+    assert fx <= LINEAR_FROB_RTOL and fw <= LINEAR_FROB_RTOL
+
+
 def test_linear_multichunk_ragged_vocab():
     # three backward chunks, the last ragged; V not a multiple of any tile
     case = wl.make_linear(3002, 520, 136, 70001, ignore_frac=0.05, label_smoothing=0.1,

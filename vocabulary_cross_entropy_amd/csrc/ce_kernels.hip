@@ -46,6 +46,16 @@ constexpr int kBwdThreadsShort = 512;
 constexpr int64_t kBwdShortRowBytes = 32768;
 constexpr int kFbVecs = 32;  // most 16-byte vectors per thread the one-pass kernel holds
 constexpr int kUnroll = 4;
+// The forward's exponent offset is fl(m log2(e)) for the chunk's running
+// maximum m, its rounding rho taken back out by a factor 2^-rho; |rho| grows
+// to 2^6 at |m| = 2^30, the clamp below.  A chunk whose running maximum lies
+// beyond it (a thread whose logits so far are all masked with a finite value
+// such as -FLT_MAX) gets the offset of the clamped value instead, so its
+// terms underflow to 0 or stay finite and vanish in the later merge with a
+// larger maximum, which rescales them by e^(m_old - m_new) = 0, instead of
+// turning d into inf or NaN.  A row whose final maximum itself exceeds 2^30
+// in magnitude is outside this form.
+constexpr float kFoldMaxM = 0x1p30f;
 
 template <int DT>
 struct Elem;
@@ -140,9 +150,11 @@ __device__ __forceinline__ void fold(S& st, const u32x4_t* w, int nvalid = N) {
   // rounding rho = m log2(e) - mL (exact by an FMA), taken back out of the
   // chunk's sum below; what remains per term is the rounding of the FMA,
   // relative to (z - m) log2(e), so the terms near the maximum, which make
-  // up d, are the most accurate.  A NaN logit makes d NaN.
-  const float mL = mref * kLog2e;
-  const float rho = __builtin_fmaf(mref, kLog2e, -mL);
+  // up d, are the most accurate.  A NaN logit makes d NaN.  The offset is
+  // taken from m clamped to kFoldMaxM (see there).
+  const float mc = fminf(fmaxf(mref, -kFoldMaxM), kFoldMaxM);
+  const float mL = mc * kLog2e;
+  const float rho = __builtin_fmaf(mc, kLog2e, -mL);
   float dpart[N], wpart[N];
 #pragma unroll
   for (int u = 0; u < N; ++u) {
@@ -204,8 +216,9 @@ __device__ __forceinline__ void fold_lean(LseState& st, u32x4_t* w, int nvalid =
   for (int u = 0; u < N; ++u) asm volatile("" : "+v"(w[u]));
   const float m_new = fmaxf(st.m, cm);
   const float mref = (m_new == kNegInf) ? 0.0f : m_new;
-  const float mL = mref * kLog2e;
-  const float rho = __builtin_fmaf(mref, kLog2e, -mL);
+  const float mc = fminf(fmaxf(mref, -kFoldMaxM), kFoldMaxM);
+  const float mL = mc * kLog2e;
+  const float rho = __builtin_fmaf(mc, kLog2e, -mL);
   float dsum = 0.0f;
 #pragma unroll
   for (int u = 0; u < N; ++u) {

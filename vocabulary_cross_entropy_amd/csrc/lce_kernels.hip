@@ -679,6 +679,17 @@ struct EpiLseT {
       d += __shfl_xor(d, 32, 64);
       sz += __shfl_xor(sz, 32, 64);
       if (ENT) w += __shfl_xor(w, 32, 64);
+      // Every term above carries the factor 2^rho of the rounding rho =
+      // m log2(e) - mL (exact by an FMA), and every exponent t the addend rho:
+      // taken back out of the column's sums, d -> 2^-rho d and
+      // w -> 2^-rho (w - rho d), so the error of a term does not grow with |m|
+      // (up to |m| of about 2^29, where 2^rho would leave the FP32 range).
+      {
+        const float rho = __builtin_fmaf((mx == kNegInf) ? 0.0f : mx, kLog2e, -mL);
+        const float corr = fabsf(rho) < 0x1p-10f ? -rho * kLn2 : exp2_hw(-rho) - 1.0f;
+        if (ENT) w = __builtin_fmaf(__builtin_fmaf(-rho, d, w), corr, __builtin_fmaf(-rho, d, w));
+        d = __builtin_fmaf(d, corr, d);
+      }
       // Target logit: only a lane whose token's target lies in this wave's
       // rows (rarely any) picks it.
       const int64_t j = j0 + wc * WN + b * 32 + (lane & 31);
@@ -786,27 +797,37 @@ struct EpiDzT {
     // column) or NaN (target out of range) are folded into the arithmetic:
     // g = 0 or NaN, and an exponent pushed to -inf so that exp() is 0 for
     // every finite logit.
+    // lse2 = fl(lse log2(e)) is the exponent's offset; its rounding, lo =
+    // lse log2(e) - lse2, is taken back out of the factors that multiply the
+    // exponential (ge = 2^-lo g, gHe = 2^-lo gH), so the error of p does not
+    // grow with |m| (up to |m| of about 2^29).
     struct Tok {
       int64_t t;
-      float g, lse2, gH, ez;
+      float g, ge, lse2, gH, gHe, ez;
       bool live;
     };
     auto token = [&](int b) {
       const int64_t j = j0 + wc * WN + b * 32 + (lane & 31);
-      Tok k{-1, 0.0f, 1e30f, 0.0f, 0.0f, false};
+      Tok k{-1, 0.0f, 0.0f, 1e30f, 0.0f, 0.0f, 0.0f, false};
       if (j < p.M) {
         k.t = tg[b];
         if (k.t != p.ignore_idx) {
           if (k.t >= 0 && k.t < p.Vg) {
             k.live = true;
             k.g = p.reduce_loss ? gscale : go[b];
-            k.lse2 = sv[b][0] * kLog2e + log2_hw(sv[b][1]);
+            const float ld = log2_hw(sv[b][1]);
+            k.lse2 = __builtin_fmaf(sv[b][0], kLog2e, ld);
+            const float lo = __builtin_fmaf(sv[b][0], kLog2e, -k.lse2) + ld;
+            const float f = exp2_hw(-lo);
+            k.ge = k.g * f;
             if (ENT) {  // dH/dz_v = p_v (E_p[z] - z_v), E_p[z] = lse - H
               k.gH = gh[b];
+              k.gHe = k.gH * f;
               k.ez = k.lse2 * kLn2 - hv[b];
             }
           } else {
             k.g = __builtin_nanf("");
+            k.ge = k.g;
           }
         }
       }
@@ -814,7 +835,7 @@ struct EpiDzT {
     };
     auto value = [&](const Tok& k, float goff, float z) {
       const float ex = exp2_hw(__builtin_fmaf(z, kLog2e, -k.lse2));
-      return ENT ? ex * __builtin_fmaf(k.gH, k.ez - z, k.g) - goff : ex * k.g - goff;
+      return ENT ? ex * __builtin_fmaf(k.gHe, k.ez - z, k.ge) - goff : ex * k.ge - goff;
     };
     // The target's element also gets -(1 - eps) g: only a lane whose target
     // lies in this wave's rows (rarely any) recomputes that one value.
