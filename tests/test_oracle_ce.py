@@ -174,6 +174,35 @@ def test_negative_infinity_column():
     assert np.all(np.isinf(loss_s))
 
 
+def test_finite_mask_columns():
+    # Columns masked with the most negative finite FP32 value behave like
+    # absent classes when eps = 0: loss and kept gradients equal those of the
+    # row without them (e^(-FLT_MAX - m) is 0 in FP64 too), masked gradients
+    # are 0.  The same with the BF16 pattern 0xFF7F.
+    z = _rand_logits(11, 3, 12, dtype=np.float32)
+    keep = np.array([0, 2, 3, 7, 11])
+    t = np.array([2, 7, 11], np.int64)
+    zm = np.full((3, 12), np.float32(-3.4028235e38), np.float32)
+    zm[:, keep] = z[:, keep]
+    remap = {v: i for i, v in enumerate(keep)}
+    tk = np.array([remap[int(x)] for x in t], np.int64)
+    loss_ref, _, _ = oracle.ce_forward(z[:, keep], tk, 0.0)
+    loss, stats, _ = oracle.ce_forward(zm, t, 0.0)
+    np.testing.assert_allclose(loss, loss_ref, rtol=1e-14)
+    g = np.array([1.0, 0.5, 2.0])
+    grad = oracle.ce_backward(zm, t, g, 0.0)
+    np.testing.assert_allclose(grad[:, keep], oracle.ce_backward(z[:, keep], tk, g, 0.0),
+                               rtol=1e-13, atol=1e-16)
+    mask = np.ones(12, bool)
+    mask[keep] = False
+    assert np.all(grad[:, mask] == 0.0)
+    zb = np.full((3, 12), 0xFF7F, np.uint16)
+    zb[:, keep] = (zm[:, keep].view(np.uint32) >> 16).astype(np.uint16)
+    lb, _, _ = oracle.ce_forward(zb, t, 0.0)
+    lbr, _, _ = oracle.ce_forward(zb[:, keep], tk, 0.0)
+    np.testing.assert_allclose(lb, lbr, rtol=1e-14)
+
+
 # --- finite differences ----------------------------------------------------------
 
 @pytest.mark.parametrize("V", [2, 3, 5, 17])
