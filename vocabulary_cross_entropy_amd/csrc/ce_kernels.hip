@@ -346,32 +346,44 @@ __global__ __launch_bounds__(NT) void ce_fwd_kernel(CeFwdParams p) {
 }
 
 // Averaged loss over non-ignored rows and their count, one workgroup, fixed
-// summation order (bitwise reproducible).
+// summation order (bitwise reproducible): thread i sums rows i, i + 1024, ...
+// in FP64 (the loss is read whatever the target, so both loads of a row go
+// out together; an ignored row adds 0), then a butterfly over each
+// wavefront's lanes (every lane ends with the same bits) and the sixteen
+// wavefront sums in order.
 __global__ __launch_bounds__(1024) void ce_mean_kernel(CeMeanParams p) {
-  __shared__ double ssum[1024];
-  __shared__ int64_t scnt[1024];
+  __shared__ double ssum[16];
+  __shared__ int64_t scnt[16];
   double sum = 0.0;
   int64_t cnt = 0;
+#pragma unroll 4
   for (int64_t r = threadIdx.x; r < p.N; r += 1024) {
     const int64_t i0 = r / p.d1, i1 = r - i0 * p.d1;
-    if (p.targets[i0 * p.ts0 + i1 * p.ts1] != p.ignore_idx) {
-      if (p.loss_tok) sum += (double)p.loss_tok[r];
-      ++cnt;
-    }
+    const bool valid = p.targets[i0 * p.ts0 + i1 * p.ts1] != p.ignore_idx;
+    const double l = p.loss_tok ? (double)p.loss_tok[r] : 0.0;
+    sum += valid ? l : 0.0;
+    cnt += valid ? 1 : 0;
   }
-  ssum[threadIdx.x] = sum;
-  scnt[threadIdx.x] = cnt;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    sum += __shfl_xor(sum, off, 64);
+    cnt += __shfl_xor(cnt, off, 64);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    ssum[wave] = sum;
+    scnt[wave] = cnt;
+  }
   __syncthreads();
-  for (int s = 512; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) {
-      ssum[threadIdx.x] += ssum[threadIdx.x + s];
-      scnt[threadIdx.x] += scnt[threadIdx.x + s];
-    }
-    __syncthreads();
-  }
   if (threadIdx.x == 0) {
-    const int64_t c = scnt[0];
-    if (p.loss_mean) p.loss_mean[0] = (float)(ssum[0] / (double)(c > 0 ? c : 1));
+    double s = ssum[0];
+    int64_t c = scnt[0];
+#pragma unroll
+    for (int w = 1; w < 16; ++w) {
+      s += ssum[w];
+      c += scnt[w];
+    }
+    if (p.loss_mean) p.loss_mean[0] = (float)(s / (double)(c > 0 ? c : 1));
     if (p.n_valid) p.n_valid[0] = (int32_t)c;
   }
 }
