@@ -686,7 +686,12 @@ struct EpiLseT {
       // (up to |m| of about 2^29, where 2^rho would leave the FP32 range).
       {
         const float rho = __builtin_fmaf((mx == kNegInf) ? 0.0f : mx, kLog2e, -mL);
-        const float corr = fabsf(rho) < 0x1p-10f ? -rho * kLn2 : exp2_hw(-rho) - 1.0f;
+        // 2^-rho - 1 = -rho ln 2 to within (rho ln 2)^2 / 2 for |rho| < 2^-10
+        // (|m| < 2^13); beyond, the exponential, on a branch the whole
+        // wavefront skips in the common case
+        float corr = -rho * kLn2;
+        if (__builtin_amdgcn_ballot_w64(!(fabsf(rho) < 0x1p-10f)))
+          corr = fabsf(rho) < 0x1p-10f ? corr : exp2_hw(-rho) - 1.0f;
         if (ENT) w = __builtin_fmaf(__builtin_fmaf(-rho, d, w), corr, __builtin_fmaf(-rho, d, w));
         d = __builtin_fmaf(d, corr, d);
       }
@@ -818,7 +823,9 @@ struct EpiDzT {
             const float ld = log2_hw(sv[b][1]);
             k.lse2 = __builtin_fmaf(sv[b][0], kLog2e, ld);
             const float lo = __builtin_fmaf(sv[b][0], kLog2e, -k.lse2) + ld;
-            const float f = exp2_hw(-lo);
+            // 2^-lo = 1 - lo ln 2 to within (lo ln 2)^2 / 2 for |lo| < 2^-10
+            float f = __builtin_fmaf(-lo, kLn2, 1.0f);
+            if (!(fabsf(lo) < 0x1p-10f)) f = exp2_hw(-lo);
             k.ge = k.g * f;
             if (ENT) {  // dH/dz_v = p_v (E_p[z] - z_v), E_p[z] = lse - H
               k.gH = gh[b];
