@@ -37,6 +37,14 @@
  * Saved statistics: stats is (N, 4) FP32 per row = (m, d, z_t, mean_v z_v),
  * 16 bytes per row.  Rows that are ignored hold zeros there.
  *
+ * Value range: logits are read as IEEE values.  -inf entries (padded
+ * vocabularies) get probability 0, and so do entries masked with a finite
+ * value far below the row's maximum (such as -FLT_MAX); with eps > 0 the
+ * mean logit enters the loss, and it is an FP32 sum that overflows when many
+ * logits lie near +-FLT_MAX.  A row whose largest logit exceeds 2^30 in
+ * magnitude is outside the logits forward's exponent form (its statistics
+ * are not meaningful), as are linear-form logits beyond about 2^29.
+ *
  * Entropy (optional, the "optional entropy" output of the Liger-Kernel PR,
  * Summary): H_r = -sum_v p_v ln p_v of p = softmax(z_r), FP32 per row, 0 for
  * ignored rows (it does not depend on the target otherwise).  Given an
