@@ -314,6 +314,40 @@ int lce_backward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Scaled linear form (the Liger-Kernel PR "Add SM100 tensor-parallel fused
+ * scaled cross entropy", title and Summary: a "fused scaled linear
+ * cross-entropy"; the pages do not say what is scaled).  Read here as the
+ * loss of logits = logit_scale * X W^T, a positive scalar applied to the
+ * logits before the softmax (a logit scale or inverse temperature):
+ *     loss_r = CE(logit_scale * (X W^T)_r, t_r), with eps and ignore_idx as
+ *     in lce_forward;
+ * dX and dW are the gradients of that loss (logit_scale times the gradient
+ * with respect to the scaled logits, pushed through X W^T).  The saved
+ * statistics and the entropy are those of the scaled logits.
+ *
+ *  lce_forward_scaled, lce_backward_scaled: the arguments of lce_forward and
+ *    lce_backward plus logit_scale, which must be finite and > 0
+ *    (VCE_EINVAL otherwise, nothing launched); the same backward must get
+ *    the same logit_scale as its forward.  logit_scale = 1 gives bit for bit
+ *    the results of lce_forward and lce_backward; a power of two 2^k gives
+ *    bit for bit the unscaled results for W * 2^k (dW then 2^k times the
+ *    unscaled dW, as the chain rule says).  The scale is folded into the
+ *    exponent's factor and the gradient's factor, so it costs no work per
+ *    logit.
+ */
+int lce_forward_scaled(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
+                       float logit_scale, const int64_t* targets, float label_smoothing,
+                       int reduce_loss, int64_t ignore_idx, float* loss_tok, float* loss_mean,
+                       float* stats, int32_t* n_valid, float* entropy, void* workspace,
+                       size_t workspace_bytes, void* stream);
+int lce_backward_scaled(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
+                        float logit_scale, const int64_t* targets, const float* stats,
+                        const int32_t* n_valid, const float* grad_output, const float* entropy,
+                        const float* grad_entropy, float label_smoothing, int reduce_loss,
+                        int64_t ignore_idx, void* dX, void* dW, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
  * FP32 inputs to the linear form (the cross-entropy API page, Description:
  * BF16 or FP32 input, FP32 loss and gradient computation).  X (M, H) and W
  * (V, H) are FP32, row-major, contiguous, 16-byte aligned, H a multiple of 8.

@@ -15,6 +15,11 @@ logits, then dX = dZ W and dW = dZ^T X):
          [+ gH_r dH/dZ_r when an entropy gradient is given]
     dX = dZ W,   dW = dZ^T X                  (FP64 matrix products)
 
+The scaled form (``scale`` s, the reading of the Liger-Kernel PR title's
+"scaled" linear cross-entropy as a logit scale) is the same with Z = s X W^T;
+by the chain rule its gradients are dX = s dZ W and dW = s dZ^T X, with dZ
+the gradient with respect to the scaled logits.
+
 Rows (tokens) are independent, so large problems are processed in token
 chunks purely to bound host memory; dW is then the sum over chunks of
 dZ_c^T X_c, which is the same sum over tokens split into consecutive ranges.
@@ -52,7 +57,7 @@ def logits(X_bits: np.ndarray, W_bits: np.ndarray, rows=None) -> np.ndarray:
 
 
 def forward(X_bits, W_bits, targets, label_smoothing=0.0, ignore_idx=-100, rows=None,
-            token_chunk: int | None = None):
+            token_chunk: int | None = None, scale: float = 1.0):
     """Per-token loss, stats (max, denominator, z_target, mean z) and lse.
 
     Returns ``(loss, stats, lse)`` for the selected rows (all by default)."""
@@ -64,7 +69,7 @@ def forward(X_bits, W_bits, targets, label_smoothing=0.0, ignore_idx=-100, rows=
     stats = np.empty((idx.size, 4))
     for s in range(0, idx.size, chunk):
         sel = idx[s:s + chunk]
-        Z = _dec(X_bits[sel]) @ W.T
+        Z = scale * (_dec(X_bits[sel]) @ W.T)
         l, st, _ = ce_forward(Z, t_all[sel], label_smoothing, ignore_idx)
         loss[s:s + chunk] = l
         stats[s:s + chunk] = st
@@ -73,23 +78,25 @@ def forward(X_bits, W_bits, targets, label_smoothing=0.0, ignore_idx=-100, rows=
     return loss, stats, lse
 
 
-def entropy(X_bits, W_bits, targets, ignore_idx=-100, token_chunk: int | None = None):
-    """Per-token entropy of softmax(X W^T) in FP64 (0 for ignored tokens)."""
+def entropy(X_bits, W_bits, targets, ignore_idx=-100, token_chunk: int | None = None,
+            scale: float = 1.0):
+    """Per-token entropy of softmax(scale X W^T) in FP64 (0 for ignored tokens)."""
     t_all = np.asarray(targets, np.int64).reshape(-1)
     W = _dec(W_bits)
     M = t_all.size
     chunk = token_chunk or max(1, M)
     out = np.empty(M)
     for s in range(0, M, chunk):
-        Z = _dec(X_bits[s:s + chunk]) @ W.T
+        Z = scale * (_dec(X_bits[s:s + chunk]) @ W.T)
         out[s:s + chunk] = _entropy(Z, t_all[s:s + chunk], ignore_idx)
     return out
 
 
 def backward(X_bits, W_bits, targets, g, label_smoothing=0.0, ignore_idx=-100,
-             token_chunk: int | None = None, grad_entropy=None):
+             token_chunk: int | None = None, grad_entropy=None, scale: float = 1.0):
     """Full dX (M, H) and dW (V, H) in FP64.  ``g`` is g_r for every token;
-    ``grad_entropy`` (per token, optional) adds the entropy's gradient."""
+    ``grad_entropy`` (per token, optional) adds the entropy's gradient;
+    ``scale``: the logits are scale X W^T."""
     t_all = np.asarray(targets, np.int64).reshape(-1)
     g_all = np.asarray(g, np.float64).reshape(-1)
     M = t_all.size
@@ -99,11 +106,12 @@ def backward(X_bits, W_bits, targets, g, label_smoothing=0.0, ignore_idx=-100,
     chunk = token_chunk or M
     for s in range(0, M, chunk):
         Xc = _dec(X_bits[s:s + chunk])
-        Z = Xc @ W.T
+        Z = scale * (Xc @ W.T)
         dZ = ce_backward(Z, t_all[s:s + chunk], g_all[s:s + chunk], label_smoothing, ignore_idx)
         if grad_entropy is not None:
             gh = np.asarray(grad_entropy, np.float64).reshape(-1)[s:s + chunk]
             add_entropy_grad(dZ, Z, t_all[s:s + chunk], gh, ignore_idx)
+        dZ = scale * dZ  # the gradient with respect to X W^T
         dX[s:s + chunk] = dZ @ W
         dW += dZ.T @ Xc
     return dX, dW

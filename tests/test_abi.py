@@ -388,3 +388,25 @@ def test_lce_forward_noalloc_rejects(L, kw, code):
     # static scratch is not looked up
     assert noalloc(L, **kw) == code
     assert L.vce_strerror(code)
+
+
+@pytest.mark.parametrize("scale,code", [
+    (0.0, 1), (-1.0, 1), (float("nan"), 1), (float("inf"), 1),
+])
+def test_lce_scaled_reject_a_bad_scale(L, scale, code):
+    # logit_scale must be finite and > 0; checked before anything else
+    ws = L.lce_workspace_size(64, 64, 1000)
+    assert L.lce_forward_scaled(A, A, 64, 64, 1000, scale, A, 0.0, 1, -100, A, A, A, A, None, A,
+                                ws, None) == code
+    assert L.lce_backward_scaled(A, A, 64, 64, 1000, scale, A, A, A, A, None, None, 0.0, 1, -100,
+                                 A, A, A, ws, None) == code
+
+
+def test_lce_scaled_share_the_other_checks(L):
+    ws = L.lce_workspace_size(64, 64, 1000)
+    assert L.lce_forward_scaled(A, A, 64, 12, 1000, 0.5, A, 0.0, 1, -100, A, A, A, A, None, A,
+                                ws, None) == 7
+    assert L.lce_forward_scaled(A, A, 64, 64, 1000, 0.5, A, 0.0, 1, -100, A, A, A, A, None, A,
+                                1, None) == 5
+    assert L.lce_backward_scaled(A, A, 64, 64, 1000, 2.0, A, A, A, A, None, None, 0.0, 1, -100,
+                                 None, A, A, ws, None) == 1

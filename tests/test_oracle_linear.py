@@ -194,3 +194,69 @@ def test_f32_inputs_pure_python_tiny():
     loss, _, _ = linear.forward(X, W, t)
     for r in range(3):
         assert loss[r] == pytest.approx(tiny.loss_row(Z[r], int(t[r]), 0.0), rel=1e-13)
+
+
+# --- the scaled form: logits = s X W^T --------------------------------------------
+
+@pytest.mark.parametrize("scale", [0.7, 3.0])
+@pytest.mark.parametrize("eps,reduce_loss", [(0.0, False), (0.1, True)])
+def test_scaled_against_torch_autograd_float64(scale, eps, reduce_loss):
+    # cross_entropy(s X W^T) by torch float64 autograd: loss, dX, dW
+    X, W, t = _case(21, 12, 16, 37, n_ign=2, f64=False)
+    Xt = torch.tensor(oracle.bf16_to_f64(X), requires_grad=True)
+    Wt = torch.tensor(oracle.bf16_to_f64(W), requires_grad=True)
+    red = "mean" if reduce_loss else "none"
+    ref = torch.nn.functional.cross_entropy(scale * (Xt @ Wt.T), torch.tensor(t),
+                                            ignore_index=IGN, label_smoothing=eps, reduction=red)
+    go = np.array([1.5]) if reduce_loss else np.random.default_rng(2).uniform(0.5, 1.5, 12)
+    ref.backward(torch.tensor(go[0] if reduce_loss else go, dtype=torch.float64))
+    loss, _, _ = linear.forward(X, W, t, eps, scale=scale)
+    if reduce_loss:
+        assert oracle.mean_loss(loss, t) == pytest.approx(ref.item(), rel=1e-12)
+    else:
+        np.testing.assert_allclose(loss, ref.detach().numpy(), rtol=1e-12, atol=1e-13)
+    g = oracle.row_scale(go, t, reduce_loss)
+    dX, dW = linear.backward(X, W, t, g, eps, scale=scale)
+    np.testing.assert_allclose(dX, Xt.grad.numpy(), rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(dW, Wt.grad.numpy(), rtol=1e-11, atol=1e-14)
+
+
+def test_scaled_finite_differences_with_entropy_tiny():
+    # J = sum_r g_r loss_r + gH_r H_r at logits s X W^T, central differences
+    X, W, t = _case(22, 3, 4, 7)
+    eps, s = 0.1, 1.7
+    g = np.array([1.0, 0.5, -0.25])
+    gH = np.array([0.8, -1.2, 0.3])
+    dX, dW = linear.backward(X, W, t, g, eps, grad_entropy=gH, scale=s)
+    h = 1e-6
+
+    def total(Xa, Wa):
+        loss, _, _ = linear.forward(Xa, Wa, t, eps, scale=s)
+        return float(np.dot(g, loss) + np.dot(gH, linear.entropy(Xa, Wa, t, scale=s)))
+
+    for i in range(3):
+        for j in range(4):
+            Xp = X.copy(); Xp[i, j] += h
+            Xm = X.copy(); Xm[i, j] -= h
+            assert abs((total(Xp, W) - total(Xm, W)) / (2 * h) - dX[i, j]) < 1e-7
+    for v in range(7):
+        for j in range(4):
+            Wp = W.copy(); Wp[v, j] += h
+            Wm = W.copy(); Wm[v, j] -= h
+            assert abs((total(X, Wp) - total(X, Wm)) / (2 * h) - dW[v, j]) < 1e-7
+
+
+def test_scaled_equals_unscaled_with_scaled_classifier():
+    # s X W^T = X (s W)^T: the same loss and dX; dW_scaled = s dW of the unscaled
+    # problem at W' = s W (chain rule), for any s > 0
+    X, W, t = _case(23, 9, 8, 21, n_ign=1)
+    s, eps = 2.5, 0.05
+    g = np.random.default_rng(3).uniform(0.5, 1.5, 9)
+    l1, st1, _ = linear.forward(X, W, t, eps, scale=s)
+    l2, st2, _ = linear.forward(X, s * W, t, eps)
+    np.testing.assert_allclose(l1, l2, rtol=1e-13)
+    np.testing.assert_allclose(st1, st2, rtol=1e-13)
+    dX1, dW1 = linear.backward(X, W, t, g, eps, scale=s)
+    dX2, dW2 = linear.backward(X, s * W, t, g, eps)
+    np.testing.assert_allclose(dX1, dX2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dW1, s * dW2, rtol=1e-12, atol=1e-13)

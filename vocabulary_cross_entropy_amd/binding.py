@@ -46,6 +46,10 @@ SIGNATURES = {
                                    _VP, _VP, _VP, _VP]),
     "lce_backward": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _F32, _I32,
                             _I64, _VP, _VP, _VP, _SZ, _VP]),
+    "lce_forward_scaled": (_I32, [_VP, _VP, _I64, _I64, _I64, _F32, _VP, _F32, _I32, _I64, _VP,
+                                  _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "lce_backward_scaled": (_I32, [_VP, _VP, _I64, _I64, _I64, _F32, _VP, _VP, _VP, _VP, _VP,
+                                   _VP, _F32, _I32, _I64, _VP, _VP, _VP, _SZ, _VP]),
     "lce_workspace_size_f32": (_SZ, [_I64, _I64, _I64]),
     "lce_forward_f32": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _F32, _I32, _I64, _VP, _VP, _VP,
                                _VP, _VP, _VP, _SZ, _VP]),
@@ -451,11 +455,13 @@ def _check_like(t, name: str, ref: torch.Tensor):
 def lce_forward(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
                 label_smoothing: float = 0.0, reduce_loss: bool = True, ignore_idx: int = -100,
                 *, workspace: torch.Tensor | None = None, stream=None, out=None,
-                with_entropy: bool = False):
+                with_entropy: bool = False, logit_scale: float = 1.0):
     """Fused linear cross-entropy forward, BF16 X and W.  Returns (loss_tok,
-    loss_mean, stats, n_valid), plus the per-token entropy with ``with_entropy``."""
+    loss_mean, stats, n_valid), plus the per-token entropy with ``with_entropy``.
+    ``logit_scale`` (finite, > 0): the loss of logit_scale * X W^T
+    (``lce_forward_scaled``); the backward must get the same value."""
     return _lce_forward(False, X, W, targets, label_smoothing, reduce_loss, ignore_idx,
-                        workspace, stream, out, with_entropy)
+                        workspace, stream, out, with_entropy, logit_scale)
 
 
 def lce_forward_noalloc(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
@@ -501,7 +507,7 @@ def lce_forward_f32(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
 
 
 def _lce_forward(f32, X, W, targets, label_smoothing, reduce_loss, ignore_idx, workspace,
-                 stream, out, with_entropy):
+                 stream, out, with_entropy, logit_scale=1.0):
     _check_linear(X, W, targets, torch.float32 if f32 else torch.bfloat16)
     M, H = X.shape
     V = W.shape[0]
@@ -521,11 +527,20 @@ def _lce_forward(f32, X, W, targets, label_smoothing, reduce_loss, ignore_idx, w
                 entropy=ent)
     _check_buf(workspace, "workspace", workspace.numel(), torch.uint8, like=X)
     _need_cuda(X, W, targets)
-    name = "lce_forward_f32" if f32 else "lce_forward"
-    rc = getattr(lib(), name)(_ptr(X), _ptr(W), M, H, V, _ptr(targets), float(label_smoothing),
-                              int(bool(reduce_loss)), int(ignore_idx), _ptr(loss_tok),
-                              _ptr(loss_mean), _ptr(stats), _ptr(n_valid), _ptr(ent),
-                              _ptr(workspace), workspace.numel(), _stream(stream))
+    if logit_scale != 1.0:
+        name = "lce_forward_scaled"
+        rc = lib().lce_forward_scaled(_ptr(X), _ptr(W), M, H, V, float(logit_scale),
+                                      _ptr(targets), float(label_smoothing),
+                                      int(bool(reduce_loss)), int(ignore_idx), _ptr(loss_tok),
+                                      _ptr(loss_mean), _ptr(stats), _ptr(n_valid), _ptr(ent),
+                                      _ptr(workspace), workspace.numel(), _stream(stream))
+    else:
+        name = "lce_forward_f32" if f32 else "lce_forward"
+        rc = getattr(lib(), name)(_ptr(X), _ptr(W), M, H, V, _ptr(targets),
+                                  float(label_smoothing), int(bool(reduce_loss)),
+                                  int(ignore_idx), _ptr(loss_tok), _ptr(loss_mean), _ptr(stats),
+                                  _ptr(n_valid), _ptr(ent), _ptr(workspace), workspace.numel(),
+                                  _stream(stream))
     _check(name, rc)
     if with_entropy:
         return loss_tok, loss_mean, stats, n_valid, ent
@@ -537,13 +552,13 @@ def lce_backward(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, stats:
                  label_smoothing: float = 0.0, reduce_loss: bool = True, ignore_idx: int = -100,
                  *, workspace: torch.Tensor | None = None, dX: torch.Tensor | None = None,
                  dW: torch.Tensor | None = None, stream=None, entropy: torch.Tensor | None = None,
-                 grad_entropy: torch.Tensor | None = None):
+                 grad_entropy: torch.Tensor | None = None, logit_scale: float = 1.0):
     """Fused linear cross-entropy backward.  Returns (dX, dW), BF16.  With
     ``grad_entropy`` the entropy's gradient is added (``entropy``: the
-    forward's entropy output)."""
+    forward's entropy output).  ``logit_scale``: as given to the forward."""
     return _lce_backward(False, X, W, targets, stats, n_valid, grad_output, label_smoothing,
                          reduce_loss, ignore_idx, workspace, dX, dW, stream, entropy,
-                         grad_entropy)
+                         grad_entropy, logit_scale)
 
 
 def lce_backward_f32(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
@@ -561,7 +576,8 @@ def lce_backward_f32(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor,
 
 
 def _lce_backward(f32, X, W, targets, stats, n_valid, grad_output, label_smoothing,
-                  reduce_loss, ignore_idx, workspace, dX, dW, stream, entropy, grad_entropy):
+                  reduce_loss, ignore_idx, workspace, dX, dW, stream, entropy, grad_entropy,
+                  logit_scale=1.0):
     _check_linear(X, W, targets, torch.float32 if f32 else torch.bfloat16)
     M, H = X.shape
     V = W.shape[0]
@@ -576,12 +592,21 @@ def _lce_backward(f32, X, W, targets, stats, n_valid, grad_output, label_smoothi
     _check_like(dW, "dW", W)
     _check_buf(workspace, "workspace", workspace.numel(), torch.uint8, like=X)
     _need_cuda(X, W, targets, stats, grad_output)
-    name = "lce_backward_f32" if f32 else "lce_backward"
-    rc = getattr(lib(), name)(_ptr(X), _ptr(W), M, H, V, _ptr(targets), _ptr(stats),
-                              _ptr(n_valid), _ptr(grad_output), _ptr(entropy),
-                              _ptr(grad_entropy), float(label_smoothing),
-                              int(bool(reduce_loss)), int(ignore_idx), _ptr(dX), _ptr(dW),
-                              _ptr(workspace), workspace.numel(), _stream(stream))
+    if logit_scale != 1.0:
+        name = "lce_backward_scaled"
+        rc = lib().lce_backward_scaled(_ptr(X), _ptr(W), M, H, V, float(logit_scale),
+                                       _ptr(targets), _ptr(stats), _ptr(n_valid),
+                                       _ptr(grad_output), _ptr(entropy), _ptr(grad_entropy),
+                                       float(label_smoothing), int(bool(reduce_loss)),
+                                       int(ignore_idx), _ptr(dX), _ptr(dW), _ptr(workspace),
+                                       workspace.numel(), _stream(stream))
+    else:
+        name = "lce_backward_f32" if f32 else "lce_backward"
+        rc = getattr(lib(), name)(_ptr(X), _ptr(W), M, H, V, _ptr(targets), _ptr(stats),
+                                  _ptr(n_valid), _ptr(grad_output), _ptr(entropy),
+                                  _ptr(grad_entropy), float(label_smoothing),
+                                  int(bool(reduce_loss)), int(ignore_idx), _ptr(dX), _ptr(dW),
+                                  _ptr(workspace), workspace.numel(), _stream(stream))
     _check(name, rc)
     return dX, dW
 

@@ -605,18 +605,21 @@ struct EpiLseT {
     const int64_t* targets;
     int64_t M, V, Mp, ignore_idx;
     int64_t v0;  // vocabulary index of W's first row (0 unless sharded)
+    float scale;   // logits are scale times the accumulators (1 unscaled)
+    float slog2e;  // fl(scale log2(e)), the exponent's factor
   };
-  // Sum over the block's values of exp(z - m) (as d), z (as s) and, with ENT,
-  // exp(z - m) (z - m) log2(e) (as w), each as a tree; rows at offsets >= lim
-  // left out when MASKED.
+  // Sum over the block's values of exp(z - m) (as d), the accumulators (as
+  // s) and, with ENT, exp(z - m) (z - m) log2(e) (as w), each as a tree; rows
+  // at offsets >= lim left out when MASKED.  z = scale v, so the exponent is
+  // v fl(scale log2(e)) - mL.
   template <bool MASKED>
-  __device__ static void sums(const f32x16_t& v, int a, float mL, int lim, float& d, float& s,
-                              float& w) {
+  __device__ static void sums(const f32x16_t& v, int a, float sl2e, float mL, int lim, float& d,
+                              float& s, float& w) {
     float e[16], t[16], z[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const bool in = !MASKED || a * 32 + 8 * (r >> 2) + (r & 3) < lim;
-      t[r] = __builtin_fmaf(v[r], kLog2e, -mL);
+      t[r] = __builtin_fmaf(v[r], sl2e, -mL);
       e[r] = in ? exp2_hw(t[r]) : 0.0f;
       z[r] = in ? v[r] : 0.0f;
       if (ENT) t[r] = in ? e[r] * t[r] : 0.0f;
@@ -666,14 +669,14 @@ struct EpiLseT {
             if (a * 32 + 8 * (r >> 2) + (r & 3) < lim) mx = fmaxf(mx, acc[a][b][r]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mL = ((mx == kNegInf) ? 0.0f : mx) * kLog2e;
+      const float mL = ((mx == kNegInf) ? 0.0f : mx) * p.slog2e;
       float d = 0.0f, sz = 0.0f, w = 0.0f;
 #pragma unroll
       for (int a = 0; a < NA; ++a) {
         if (full)
-          sums<false>(acc[a][b], a, mL, lim, d, sz, w);
+          sums<false>(acc[a][b], a, p.slog2e, mL, lim, d, sz, w);
         else
-          sums<true>(acc[a][b], a, mL, lim, d, sz, w);
+          sums<true>(acc[a][b], a, p.slog2e, mL, lim, d, sz, w);
         __builtin_amdgcn_sched_barrier(0);  // one block's temporaries at a time
       }
       d += __shfl_xor(d, 32, 64);
@@ -685,7 +688,7 @@ struct EpiLseT {
       // w -> 2^-rho (w - rho d), so the error of a term does not grow with |m|
       // (up to |m| of about 2^29, where 2^rho would leave the FP32 range).
       {
-        const float rho = __builtin_fmaf((mx == kNegInf) ? 0.0f : mx, kLog2e, -mL);
+        const float rho = __builtin_fmaf((mx == kNegInf) ? 0.0f : mx, p.slog2e, -mL);
         // 2^-rho - 1 = -rho ln 2 to within (rho ln 2)^2 / 2 for |rho| < 2^-10
         // (|m| < 2^13); beyond, the exponential, on a branch the whole
         // wavefront skips in the common case
@@ -702,11 +705,13 @@ struct EpiLseT {
         const int64_t t = tg[b];
         const int64_t tl64 = t - p.v0 - vbase;
         const bool inr = t != p.ignore_idx && tl64 >= 0 && tl64 < 128 && ((tl64 >> 2) & 1) == 0;
-        if (inr) p.zt[j] = pick(acc, b, (int)tl64);
+        if (inr) p.zt[j] = p.scale * pick(acc, b, (int)tl64);
       }
       if (lane < 32) {
         float* e = sh + (((wr * NWC + wc) * NB + b) * 32 + lane) * 4;
-        *reinterpret_cast<f32x4_t*>(e) = f32x4_t{mx, d, sz, w};
+        // the maximum and the sum of logits in logit units (scale times the
+        // accumulators; d and w are relative to that maximum already)
+        *reinterpret_cast<f32x4_t*>(e) = f32x4_t{p.scale * mx, d, p.scale * sz, w};
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -768,6 +773,8 @@ struct EpiDzT {
     int reduce_loss;
     int64_t ignore_idx, M, V;
     int64_t v0, Vg;  // W holds vocabulary rows v0 .. v0 + V - 1 of Vg (0, V unless sharded)
+    float scale;     // logits are scale times the accumulators (1 unscaled)
+    float slog2e;    // fl(scale log2(e))
     int64_t plane;   // SPLIT: elements from the hi plane to the lo plane
   };
   __device__ static void apply(const Params& p, f32x16_t (&acc)[NA][NB], int64_t i0, int64_t j0,
@@ -819,7 +826,9 @@ struct EpiDzT {
         if (k.t != p.ignore_idx) {
           if (k.t >= 0 && k.t < p.Vg) {
             k.live = true;
-            k.g = p.reduce_loss ? gscale : go[b];
+            // the gradient with respect to the accumulators: scale times the
+            // one with respect to the logits
+            k.g = p.scale * (p.reduce_loss ? gscale : go[b]);
             const float ld = log2_hw(sv[b][1]);
             k.lse2 = __builtin_fmaf(sv[b][0], kLog2e, ld);
             const float lo = __builtin_fmaf(sv[b][0], kLog2e, -k.lse2) + ld;
@@ -828,7 +837,7 @@ struct EpiDzT {
             if (!(fabsf(lo) < 0x1p-10f)) f = exp2_hw(-lo);
             k.ge = k.g * f;
             if (ENT) {  // dH/dz_v = p_v (E_p[z] - z_v), E_p[z] = lse - H
-              k.gH = gh[b];
+              k.gH = p.scale * gh[b];
               k.gHe = k.gH * f;
               k.ez = k.lse2 * kLn2 - hv[b];
             }
@@ -841,8 +850,9 @@ struct EpiDzT {
       return k;
     };
     auto value = [&](const Tok& k, float goff, float z) {
-      const float ex = exp2_hw(__builtin_fmaf(z, kLog2e, -k.lse2));
-      return ENT ? ex * __builtin_fmaf(k.gHe, k.ez - z, k.ge) - goff : ex * k.ge - goff;
+      const float ex = exp2_hw(__builtin_fmaf(z, p.slog2e, -k.lse2));
+      return ENT ? ex * __builtin_fmaf(k.gHe, __builtin_fmaf(-p.scale, z, k.ez), k.ge) - goff
+                 : ex * k.ge - goff;
     };
     // The target's element also gets -(1 - eps) g: only a lane whose target
     // lies in this wave's rows (rarely any) recomputes that one value.
@@ -1310,9 +1320,9 @@ hipError_t launch_lce_forward(const LcePlan& plan, const LceFwdArgs& a, hipStrea
   // the entropy accumulator: for the entropy output, or a shard's entropy statistic
   const bool ent = a.entropy != nullptr || a.partial_w != nullptr;
   const EpiLseT<true>::Params ept{pm, pd, ps, pw, zt, a.targets, plan.M, plan.V, plan.Mp,
-                                  a.ignore_idx, a.v0};
+                                  a.ignore_idx, a.v0, a.scale, a.scale * kLog2e};
   const EpiLseT<false>::Params epf{pm, pd, ps, pw, zt, a.targets, plan.M, plan.V, plan.Mp,
-                                   a.ignore_idx, a.v0};
+                                   a.ignore_idx, a.v0, a.scale, a.scale * kLog2e};
   if (!plan.f32) {
     const uint16_t* X = static_cast<const uint16_t*>(a.X);
     const uint16_t* W = static_cast<const uint16_t*>(a.W);
@@ -1379,7 +1389,8 @@ hipError_t backward_f32(const LcePlan& plan, const LceBwdArgs& a, hipStream_t st
       typename EpiDzT<ENT, true>::Params ep{dzh, plan.ldz, c0, vc, a.stats, a.targets,
                                             a.grad_output, a.n_valid, a.entropy, a.grad_entropy,
                                             a.eps, a.reduce_loss, a.ignore_idx, M, plan.V,
-                                            a.v0, a.Vg, plan.dzplane};
+                                            a.v0, a.Vg, a.scale, a.scale * kLog2e,
+                                            plan.dzplane};
       e = run_gemm<EpiDzT<ENT, true>, false, false, 3>(G, vc, plan.Mp, H, ep, stream);
       if (e != hipSuccess) return e;
     }
@@ -1422,7 +1433,8 @@ hipError_t backward_bf16(const LcePlan& plan, const LceBwdArgs& a, hipStream_t s
     *ep = typename EpiDzT<ENT>::Params{dz, plan.ldz, c0, vc, a.stats, a.targets, a.grad_output,
                                        a.n_valid, ENT ? a.entropy : nullptr,
                                        ENT ? a.grad_entropy : nullptr, a.eps, a.reduce_loss,
-                                       a.ignore_idx, M, plan.V, a.v0, a.Vg};
+                                       a.ignore_idx, M, plan.V, a.v0, a.Vg, a.scale,
+                                       a.scale * kLog2e};
   };
   hipError_t e;
   {

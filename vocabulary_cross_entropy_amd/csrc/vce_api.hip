@@ -533,7 +533,8 @@ int lce_forward_impl(bool f32, const void* X, const void* W, int64_t M, int64_t 
                      const int64_t* targets, float label_smoothing, int reduce_loss,
                      int64_t ignore_idx, float* loss_tok, float* loss_mean, float* stats,
                      int32_t* n_valid, float* entropy, void* workspace, size_t workspace_bytes,
-                     void* stream, bool static_ws = false) {
+                     void* stream, bool static_ws = false, float scale = 1.0f) {
+  if (!(scale > 0.0f) || !__builtin_isfinite(scale)) return VCE_EINVAL;  // finite, positive
   vce::LcePlan plan;
   int rc = check_lce_common(X, W, M, H, V, targets, label_smoothing, reduce_loss, workspace,
                             workspace_bytes, &plan, f32, static_ws);
@@ -566,6 +567,7 @@ int lce_forward_impl(bool f32, const void* X, const void* W, int64_t M, int64_t 
     a.v0 = 0;
     a.partial = nullptr;
     a.partial_w = nullptr;
+    a.scale = scale;
     rc = launch_status(vce::launch_lce_forward(plan, a, s));
     if (rc != VCE_OK) return rc;
   }
@@ -589,7 +591,9 @@ int lce_backward_impl(bool f32, const void* X, const void* W, int64_t M, int64_t
                       const int64_t* targets, const float* stats, const int32_t* n_valid,
                       const float* grad_output, const float* entropy, const float* grad_entropy,
                       float label_smoothing, int reduce_loss, int64_t ignore_idx, void* dX,
-                      void* dW, void* workspace, size_t workspace_bytes, void* stream) {
+                      void* dW, void* workspace, size_t workspace_bytes, void* stream,
+                      float scale = 1.0f) {
+  if (!(scale > 0.0f) || !__builtin_isfinite(scale)) return VCE_EINVAL;  // finite, positive
   vce::LcePlan plan;
   int rc = check_lce_common(X, W, M, H, V, targets, label_smoothing, reduce_loss, workspace,
                             workspace_bytes, &plan, f32);
@@ -621,6 +625,7 @@ int lce_backward_impl(bool f32, const void* X, const void* W, int64_t M, int64_t
   a.ws = static_cast<char*>(workspace);
   a.v0 = 0;
   a.Vg = V;
+  a.scale = scale;
   return launch_status(vce::launch_lce_backward(plan, a, static_cast<hipStream_t>(stream)));
 }
 
@@ -634,6 +639,16 @@ int lce_forward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
   return lce_forward_impl(false, X, W, M, H, V, targets, label_smoothing, reduce_loss,
                           ignore_idx, loss_tok, loss_mean, stats, n_valid, entropy, workspace,
                           workspace_bytes, stream);
+}
+
+int lce_forward_scaled(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
+                       float logit_scale, const int64_t* targets, float label_smoothing,
+                       int reduce_loss, int64_t ignore_idx, float* loss_tok, float* loss_mean,
+                       float* stats, int32_t* n_valid, float* entropy, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return lce_forward_impl(false, X, W, M, H, V, targets, label_smoothing, reduce_loss,
+                          ignore_idx, loss_tok, loss_mean, stats, n_valid, entropy, workspace,
+                          workspace_bytes, stream, /*static_ws=*/false, logit_scale);
 }
 
 int lce_forward_noalloc(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
@@ -663,6 +678,17 @@ int lce_backward(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
   return lce_backward_impl(false, X, W, M, H, V, targets, stats, n_valid, grad_output, entropy,
                            grad_entropy, label_smoothing, reduce_loss, ignore_idx, dX, dW,
                            workspace, workspace_bytes, stream);
+}
+
+int lce_backward_scaled(const void* X, const void* W, int64_t M, int64_t H, int64_t V,
+                        float logit_scale, const int64_t* targets, const float* stats,
+                        const int32_t* n_valid, const float* grad_output, const float* entropy,
+                        const float* grad_entropy, float label_smoothing, int reduce_loss,
+                        int64_t ignore_idx, void* dX, void* dW, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return lce_backward_impl(false, X, W, M, H, V, targets, stats, n_valid, grad_output, entropy,
+                           grad_entropy, label_smoothing, reduce_loss, ignore_idx, dX, dW,
+                           workspace, workspace_bytes, stream, logit_scale);
 }
 
 int lce_backward_f32(const float* X, const float* W, int64_t M, int64_t H, int64_t V,

@@ -119,6 +119,7 @@ struct LceFwdArgs {
   int64_t v0;      // vocabulary index of W's first row (0 unless sharded)
   float* partial;  // shard mode: (M, 4) local statistics instead of loss/stats
   float* partial_w;  // shard mode, optional: (M) entropy statistic w of the shard
+  float scale = 1.0f;  // logits = scale X W^T (scale > 0)
 };
 
 struct LceBwdArgs {
@@ -137,6 +138,7 @@ struct LceBwdArgs {
   void* dW;
   char* ws;
   int64_t v0, Vg;  // W holds vocabulary rows v0 .. v0 + V - 1 of Vg (0, V unless sharded)
+  float scale = 1.0f;  // logits = scale X W^T (scale > 0)
 };
 
 hipError_t launch_lce_forward(const LcePlan& plan, const LceFwdArgs& a, hipStream_t stream);
