@@ -415,6 +415,35 @@ int lce_backward_shard(const void* X, const void* W, int64_t M, int64_t H, int64
                        size_t workspace_bytes, void* stream);
 
 /*
+ * Tensor-parallel scaled linear cross-entropy, the combination the
+ * Liger-Kernel PR "Add SM100 tensor-parallel fused scaled cross entropy"
+ * names in its title and Summary: the shard forms above for the logits
+ * logit_scale * X W_local^T (the scaled form of lce_forward_scaled).  Every
+ * shard of one problem takes the same logit_scale.  The partials are those of
+ * the scaled logits, so ce_merge_shards merges them unchanged; the backward
+ * takes the merged statistics and the same logit_scale.
+ *
+ *  lce_forward_shard_scaled, lce_backward_shard_scaled: the arguments of
+ *    lce_forward_shard and lce_backward_shard plus logit_scale, finite and
+ *    > 0 (VCE_EINVAL otherwise, nothing launched).  logit_scale = 1 gives bit
+ *    for bit the unscaled shard results; 2^k those of the unscaled shard
+ *    forms for W_local * 2^k.
+ */
+int lce_forward_shard_scaled(const void* X, const void* W, int64_t M, int64_t H,
+                             int64_t V_local, float logit_scale, const int64_t* targets,
+                             int64_t vocab_start, int64_t ignore_idx, float* partial,
+                             float* partial_w, void* workspace, size_t workspace_bytes,
+                             void* stream);
+int lce_backward_shard_scaled(const void* X, const void* W, int64_t M, int64_t H,
+                              int64_t V_local, float logit_scale, const int64_t* targets,
+                              int64_t vocab_start, int64_t V, const float* stats,
+                              const int32_t* n_valid, const float* grad_output,
+                              const float* entropy, const float* grad_entropy,
+                              float label_smoothing, int reduce_loss, int64_t ignore_idx,
+                              void* dX, void* dW, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
  * vce_gemm_bf16: the matrix-core building block of the linear form, exported
  * so it can be checked and timed on its own, as the Liger-Kernel PR "Add SM100
  * tensor-parallel fused scaled cross entropy" validates its classifier GEMM

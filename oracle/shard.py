@@ -183,19 +183,24 @@ def _dec_bf16(a: np.ndarray) -> np.ndarray:
 
 
 def linear_shard_partials(X_bits: np.ndarray, W_shard_bits: np.ndarray, targets: np.ndarray,
-                          vocab_start: int, ignore_idx: int = -100) -> np.ndarray:
-    """Local statistics (M, 4) of Z_k = X W_k^T (see ``shard_partials``)."""
-    Zk = _dec_bf16(X_bits) @ _dec_bf16(W_shard_bits).T
+                          vocab_start: int, ignore_idx: int = -100,
+                          scale: float = 1.0) -> np.ndarray:
+    """Local statistics (M, 4) of Z_k = s X W_k^T (see ``shard_partials``;
+    s = ``scale``, the logit scale of the scaled form, 1 for the plain one)."""
+    Zk = scale * (_dec_bf16(X_bits) @ _dec_bf16(W_shard_bits).T)
     return shard_partials(Zk, targets, vocab_start, ignore_idx)
 
 
 def linear_shard_backward(X_bits: np.ndarray, W_shard_bits: np.ndarray, targets: np.ndarray,
                           vocab_start: int, V: int, stats: np.ndarray, g: np.ndarray,
-                          label_smoothing: float = 0.0, ignore_idx: int = -100):
+                          label_smoothing: float = 0.0, ignore_idx: int = -100,
+                          scale: float = 1.0):
     """(dX_k, dW_k) of one shard from the global statistics: dZ_k from
-    ``shard_backward`` on Z_k, then dX_k = dZ_k W_k and dW_k = dZ_k^T X."""
+    ``shard_backward`` on Z_k = s X W_k^T, the gradient with respect to X W_k^T
+    s dZ_k, then dX_k = s dZ_k W_k and dW_k = s dZ_k^T X."""
     X = _dec_bf16(X_bits)
     Wk = _dec_bf16(W_shard_bits)
-    dZk = shard_backward(X @ Wk.T, targets, vocab_start, V, stats, g, label_smoothing,
-                         ignore_idx)
+    dZk = shard_backward(scale * (X @ Wk.T), targets, vocab_start, V, stats, g,
+                         label_smoothing, ignore_idx)
+    dZk = scale * dZk
     return dZk @ Wk, dZk.T @ X

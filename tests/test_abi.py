@@ -410,3 +410,29 @@ def test_lce_scaled_share_the_other_checks(L):
                                 1, None) == 5
     assert L.lce_backward_scaled(A, A, 64, 64, 1000, 2.0, A, A, A, A, None, None, 0.0, 1, -100,
                                  None, A, A, ws, None) == 1
+
+
+@pytest.mark.parametrize("scale", [0.0, -2.0, float("nan"), float("inf")])
+def test_lce_shard_scaled_reject_a_bad_scale(L, scale):
+    ws = L.lce_workspace_size(64, 64, 1000)
+    assert L.lce_forward_shard_scaled(A, A, 64, 64, 1000, scale, A, 0, -100, A, None, A, ws,
+                                      None) == 1
+    assert L.lce_backward_shard_scaled(A, A, 64, 64, 1000, scale, A, 0, 4000, A, A, A, None,
+                                       None, 0.0, 1, -100, A, A, A, ws, None) == 1
+
+
+def test_lce_shard_scaled_share_the_other_checks(L):
+    ws = L.lce_workspace_size(64, 64, 1000)
+    # H not a multiple of 8
+    assert L.lce_forward_shard_scaled(A, A, 64, 12, 1000, 0.5, A, 0, -100, A, None, A, ws,
+                                      None) == 7
+    # negative vocab_start; shard beyond the full vocabulary
+    assert L.lce_forward_shard_scaled(A, A, 64, 64, 1000, 0.5, A, -1, -100, A, None, A, ws,
+                                      None) == 1
+    assert L.lce_backward_shard_scaled(A, A, 64, 64, 1000, 0.5, A, 3500, 4000, A, A, A, None,
+                                       None, 0.0, 1, -100, A, A, A, ws, None) == 1
+    # workspace too small; no dW
+    assert L.lce_forward_shard_scaled(A, A, 64, 64, 1000, 0.5, A, 0, -100, A, None, A, 1,
+                                      None) == 5
+    assert L.lce_backward_shard_scaled(A, A, 64, 64, 1000, 2.0, A, 0, 4000, A, A, A, None, None,
+                                       0.0, 1, -100, A, None, A, ws, None) == 1

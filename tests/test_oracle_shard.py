@@ -179,6 +179,35 @@ def test_linear_shards_sum_to_the_unsharded_gradients(eps):
     np.testing.assert_allclose(np.concatenate([o[1] for o in outs]), rdW, rtol=1e-10, atol=1e-13)
 
 
+@pytest.mark.parametrize("scale,eps", [(0.7, 0.0), (1.9, 0.1)])
+def test_scaled_linear_shards_against_torch_autograd(scale, eps):
+    # the shards of s X W^T merge to torch's cross-entropy of the scaled logits
+    # (float64, label smoothing over the full vocabulary) and their gradient
+    # pieces add up to its autograd gradients
+    from oracle import linear
+    X, W, t = _linear_case(23, 20, 12, 250, n_ign=2)
+    b = _split(250, 3, 9)
+    parts = [shard.linear_shard_partials(X, W[a:e], t, a, IGN, scale=scale) for a, e in b]
+    loss, st = shard.merge_shards(parts, t, 250, eps, IGN)
+    Xt = torch.tensor(oracle.bf16_to_f64(X), requires_grad=True)
+    Wt = torch.tensor(oracle.bf16_to_f64(W), requires_grad=True)
+    tt = torch.from_numpy(t)
+    ref = torch.nn.functional.cross_entropy(scale * (Xt @ Wt.T), tt, ignore_index=IGN,
+                                            reduction="none", label_smoothing=eps)
+    np.testing.assert_allclose(loss, ref.detach().numpy(), rtol=1e-12, atol=1e-12)
+    g = np.random.default_rng(3).standard_normal(20) * (t != IGN)
+    (ref * torch.from_numpy(g)).sum().backward()
+    outs = [shard.linear_shard_backward(X, W[a:e], t, a, 250, st, g, eps, IGN, scale=scale)
+            for a, e in b]
+    np.testing.assert_allclose(sum(o[0] for o in outs), Xt.grad.numpy(), rtol=1e-10,
+                               atol=1e-13)
+    np.testing.assert_allclose(np.concatenate([o[1] for o in outs]), Wt.grad.numpy(),
+                               rtol=1e-10, atol=1e-13)
+    # and the unsharded scaled oracle
+    rl, _, _ = linear.forward(X, W, t, eps, IGN, scale=scale)
+    np.testing.assert_allclose(loss, rl, rtol=1e-12, atol=1e-12)
+
+
 def test_linear_shard_against_pure_python():
     # tiny: dX_k and dW_k from the pure-Python gradient rows and products
     X, W, t = _linear_case(22, 3, 4, 7)

@@ -134,3 +134,149 @@ def test_scaled_with_entropy_against_the_oracle():
     fw = rel_frobenius(oracle.bf16_to_f64(to_host_bits(out["dW"])), rdW)
     _say(f"entropy rel err {rel:.2e}; dX frob {fx:.2e}, dW frob {fw:.2e}")
     assert fx <= LINEAR_FROB_RTOL and fw <= LINEAR_FROB_RTOL
+
+
+# --- vocabulary shards of the scaled form (tensor-parallel scaled linear CE) ---
+
+from oracle import shard as oshard  # noqa: E402
+
+
+def _run_shards(case, bounds, scale, *, Ws_bits=None, with_entropy=False, gH=None):
+    """Shard forwards, merge, shard backwards through the binding."""
+    X = to_device(case.X, "bf16")
+    t = torch.from_numpy(case.targets).cuda()
+    go = torch.from_numpy(case.grad_output).cuda()
+    if Ws_bits is None:
+        Ws_bits = [np.ascontiguousarray(case.W[a:b]) for a, b in bounds]
+    Ws = [to_device(w, "bf16") for w in Ws_bits]
+    parts = torch.empty((len(bounds), case.M, 4), dtype=torch.float32, device="cuda")
+    pws = torch.empty((len(bounds), case.M), dtype=torch.float32, device="cuda")
+    for k, ((a, b), Wk) in enumerate(zip(bounds, Ws)):
+        vce.lce_forward_shard(X, Wk, t, a, case.ignore_idx, out=parts[k],
+                              with_entropy=with_entropy, out_w=pws[k], logit_scale=scale)
+    m = vce.ce_merge_shards(parts, t, case.V, case.label_smoothing, case.reduce_loss,
+                            case.ignore_idx, partials_w=pws if with_entropy else None)
+    loss, mean, stats, nv = m[:4]
+    ent = m[4] if with_entropy else None
+    gHd = None if gH is None else torch.from_numpy(gH).cuda()
+    outs = [vce.lce_backward_shard(X, Wk, t, a, case.V, stats, nv, go, case.label_smoothing,
+                                   case.reduce_loss, case.ignore_idx, entropy=ent,
+                                   grad_entropy=gHd, logit_scale=scale)
+            for (a, b), Wk in zip(bounds, Ws)]
+    torch.cuda.synchronize()
+    return dict(parts=parts, pws=pws, loss=loss, mean=mean, stats=stats, n_valid=nv,
+                entropy=ent, dX=[o[0] for o in outs], dW=[o[1] for o in outs])
+
+
+SHARD_BOUNDS = [(0, 2000), (2000, 6500), (6500, 9000)]
+
+
+def test_scaled_shards_against_the_oracle():
+    case = wl.make_linear(5140, 700, 264, 9000, ignore_count=20, label_smoothing=0.1,
+                          reduce_loss=True)
+    scale = 0.7
+    out = _run_shards(case, SHARD_BOUNDS, scale)
+    valid = case.targets != case.ignore_idx
+    for k, (a, b) in enumerate(SHARD_BOUNDS):
+        ref = oshard.linear_shard_partials(case.X, case.W[a:b], case.targets, a,
+                                           case.ignore_idx, scale=scale)
+        got = out["parts"][k].cpu().numpy()
+        assert np.all(got[~valid] == 0.0)
+        np.testing.assert_allclose(got[valid, 0], ref[valid, 0], atol=1e-3)
+        np.testing.assert_allclose(got[valid, 1], ref[valid, 1], rtol=2e-3)
+        np.testing.assert_allclose(got[valid, 2], ref[valid, 2], rtol=1e-3, atol=0.05)
+        np.testing.assert_allclose(got[valid, 3], ref[valid, 3], atol=1e-3)
+    ref_loss, ref_stats, _ = linear.forward(case.X, case.W, case.targets, 0.1, case.ignore_idx,
+                                            scale=scale)
+    loss = out["loss"].cpu().numpy().reshape(-1).astype(np.float64)
+    assert np.all(loss[~valid] == 0.0)
+    rel = float(np.max(np.abs(loss[valid] - ref_loss[valid]) / np.abs(ref_loss[valid])))
+    assert rel <= LINEAR_LOSS_RTOL, rel
+    rm = oracle.mean_loss(ref_loss, case.targets, case.ignore_idx)
+    assert abs(out["mean"].item() - rm) <= LINEAR_LOSS_RTOL * abs(rm)
+    g = oracle.row_scale(case.grad_output, case.targets, True, case.ignore_idx)
+    rdX, rdW = linear.backward(case.X, case.W, case.targets, g, 0.1, case.ignore_idx,
+                               scale=scale)
+    for k, (a, b) in enumerate(SHARD_BOUNDS):
+        rdXk, _ = oshard.linear_shard_backward(case.X, case.W[a:b], case.targets, a, case.V,
+                                               ref_stats, g, 0.1, case.ignore_idx, scale=scale)
+        fx = rel_frobenius(oracle.bf16_to_f64(to_host_bits(out["dX"][k])), rdXk)
+        fw = rel_frobenius(oracle.bf16_to_f64(to_host_bits(out["dW"][k])), rdW[a:b])
+        assert fx <= LINEAR_FROB_RTOL and fw <= LINEAR_FROB_RTOL, (k, fx, fw)
+    fsum = rel_frobenius(sum(oracle.bf16_to_f64(to_host_bits(d)) for d in out["dX"]), rdX)
+    _say(f"shards, scale {scale}: loss rel {rel:.2e}, summed dX frob {fsum:.2e}")
+    assert fsum <= LINEAR_FROB_RTOL
+
+
+def test_scaled_shards_with_entropy_against_the_oracle():
+    case = wl.make_linear(5150, 300, 192, 6000, ignore_count=9, label_smoothing=0.1,
+                          reduce_loss=True)
+    bounds = [(0, 2500), (2500, 6000)]
+    scale = 1.6
+    gH = (np.random.default_rng(5151).standard_normal(case.M) * 0.7).astype(np.float32)
+    out = _run_shards(case, bounds, scale, with_entropy=True, gH=gH)
+    valid = case.targets != case.ignore_idx
+    H = out["entropy"].cpu().numpy().reshape(-1).astype(np.float64)
+    ref_H = linear.entropy(case.X, case.W, case.targets, case.ignore_idx, scale=scale)
+    assert np.all(H[~valid] == 0.0)
+    rel = float(np.max(np.abs(H[valid] - ref_H[valid]) / np.abs(ref_H[valid])))
+    assert rel <= LINEAR_LOSS_RTOL, rel
+    g = oracle.row_scale(case.grad_output, case.targets, True, case.ignore_idx)
+    rdX, rdW = linear.backward(case.X, case.W, case.targets, g, 0.1, case.ignore_idx,
+                               grad_entropy=gH.astype(np.float64), scale=scale)
+    dX = sum(oracle.bf16_to_f64(to_host_bits(d)) for d in out["dX"])
+    dW = np.concatenate([oracle.bf16_to_f64(to_host_bits(d)) for d in out["dW"]])
+    fx, fw = rel_frobenius(dX, rdX), rel_frobenius(dW, rdW)
+    _say(f"shards with entropy, scale {scale}: H rel {rel:.2e}, dX frob {fx:.2e}, "
+         f"dW frob {fw:.2e}")
+    assert fx <= LINEAR_FROB_RTOL and fw <= LINEAR_FROB_RTOL
+
+
+def test_power_of_two_scale_shards_are_bitwise_the_scaled_classifier():
+    # as for the unsharded form: s = 2^k on every shard equals the unscaled
+    # shards of W 2^k exactly (partials, merged results and dX shares; dW
+    # shares 2^k times theirs); the second shard spans two backward chunks
+    case = wl.make_linear(5160, 520, 256, 70001, ignore_count=5, label_smoothing=0.1,
+                          reduce_loss=False, grad_output="random")
+    bounds = [(0, 33000), (33000, 70001)]
+    s = 2.0 ** -3
+    w2 = wl.bf16_bits_to_f32(case.W) * np.float32(s)
+    W2 = wl.f32_to_bf16_bits(w2)
+    assert np.array_equal(wl.bf16_bits_to_f32(W2), w2)
+    a = _run_shards(case, bounds, s)
+    b = _run_shards(case, bounds, 1.0, Ws_bits=[np.ascontiguousarray(W2[x:y]) for x, y in bounds])
+    for k in ("parts", "loss", "stats"):
+        assert torch.equal(a[k], b[k]), k
+    for k in range(len(bounds)):
+        assert torch.equal(a["dX"][k], b["dX"][k])
+        assert torch.equal(a["dW"][k].float(), s * b["dW"][k].float())
+    _say("shards, scale 2^-3: bitwise the unscaled shards of W * 2^-3")
+
+
+def test_scale_one_through_the_scaled_shard_entry_points_is_bitwise_the_plain_ones():
+    case = wl.make_linear(5170, 300, 264, 3000, ignore_count=7, label_smoothing=0.1,
+                          reduce_loss=True)
+    a0, a1 = 1000, 3000
+    X = to_device(case.X, "bf16")
+    Wk = to_device(np.ascontiguousarray(case.W[a0:a1]), "bf16")
+    t = torch.from_numpy(case.targets).cuda()
+    go = torch.ones(1, device="cuda")
+    ws = vce.lce_workspace(case.M, case.H, a1 - a0)
+    part, pw = vce.lce_forward_shard(X, Wk, t, a0, -100, workspace=ws, with_entropy=True)
+    stats = torch.rand((case.M, 4), device="cuda") + 1.0  # any merged statistics will do
+    nv = torch.full((), case.M - 7, dtype=torch.int32, device="cuda")
+    dX, dW = vce.lce_backward_shard(X, Wk, t, a0, case.V, stats, nv, go, 0.1, True,
+                                    workspace=ws)
+    L = binding.lib()
+    part1, pw1 = torch.empty_like(part), torch.empty_like(pw)
+    dX1, dW1 = torch.empty_like(dX), torch.empty_like(dW)
+    p = lambda x: ctypes.c_void_p(x.data_ptr())
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert L.lce_forward_shard_scaled(p(X), p(Wk), case.M, case.H, a1 - a0, 1.0, p(t), a0,
+                                      -100, p(part1), p(pw1), p(ws), ws.numel(), s) == 0
+    assert L.lce_backward_shard_scaled(p(X), p(Wk), case.M, case.H, a1 - a0, 1.0, p(t), a0,
+                                       case.V, p(stats), p(nv), p(go), None, None, 0.1, 1,
+                                       -100, p(dX1), p(dW1), p(ws), ws.numel(), s) == 0
+    torch.cuda.synchronize()
+    for x, y in ((part, part1), (pw, pw1), (dX, dX1), (dW, dW1)):
+        assert torch.equal(x, y)

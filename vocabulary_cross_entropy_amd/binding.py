@@ -59,6 +59,11 @@ SIGNATURES = {
                                  _SZ, _VP]),
     "lce_backward_shard": (_I32, [_VP, _VP, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _VP, _VP,
                                   _VP, _VP, _F32, _I32, _I64, _VP, _VP, _VP, _SZ, _VP]),
+    "lce_forward_shard_scaled": (_I32, [_VP, _VP, _I64, _I64, _I64, _F32, _VP, _I64, _I64, _VP,
+                                        _VP, _VP, _SZ, _VP]),
+    "lce_backward_shard_scaled": (_I32, [_VP, _VP, _I64, _I64, _I64, _F32, _VP, _I64, _I64, _VP,
+                                         _VP, _VP, _VP, _VP, _F32, _I32, _I64, _VP, _VP, _VP,
+                                         _SZ, _VP]),
     "vce_gemm_bf16": (_I32, [_VP, _I64, _I32, _VP, _I64, _I32, _I64, _I64, _I64, _VP, _I64, _VP]),
 }
 
@@ -613,10 +618,14 @@ def _lce_backward(f32, X, W, targets, stats, n_valid, grad_output, label_smoothi
 
 def lce_forward_shard(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, vocab_start: int,
                       ignore_idx: int = -100, *, workspace: torch.Tensor | None = None,
-                      stream=None, out=None, with_entropy: bool = False, out_w=None):
+                      stream=None, out=None, with_entropy: bool = False, out_w=None,
+                      logit_scale: float = 1.0):
     """Partial statistics (M, 4) of the vocabulary shard W (V_local, H) holding
     rows vocab_start .. vocab_start + V_local - 1 of the full classifier; with
-    ``with_entropy`` also its entropy statistic (M), returned second."""
+    ``with_entropy`` also its entropy statistic (M), returned second.  With
+    ``logit_scale`` s the shard's logits are s X W^T
+    (``lce_forward_shard_scaled``); every shard and the backward take the
+    same s."""
     _check_linear(X, W, targets)
     M, H = X.shape
     V = W.shape[0]
@@ -629,10 +638,18 @@ def lce_forward_shard(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, v
     _check_buf(part, "partial", 4 * M, like=X)
     _check_buf(pw, "partial_w", M, like=X)
     _need_cuda(X, W, targets)
-    rc = lib().lce_forward_shard(_ptr(X), _ptr(W), M, H, V, _ptr(targets), int(vocab_start),
-                                 int(ignore_idx), _ptr(part), _ptr(pw), _ptr(workspace),
-                                 workspace.numel(), _stream(stream))
-    _check("lce_forward_shard", rc)
+    if logit_scale != 1.0:
+        name = "lce_forward_shard_scaled"
+        rc = lib().lce_forward_shard_scaled(_ptr(X), _ptr(W), M, H, V, float(logit_scale),
+                                            _ptr(targets), int(vocab_start), int(ignore_idx),
+                                            _ptr(part), _ptr(pw), _ptr(workspace),
+                                            workspace.numel(), _stream(stream))
+    else:
+        name = "lce_forward_shard"
+        rc = lib().lce_forward_shard(_ptr(X), _ptr(W), M, H, V, _ptr(targets), int(vocab_start),
+                                     int(ignore_idx), _ptr(part), _ptr(pw), _ptr(workspace),
+                                     workspace.numel(), _stream(stream))
+    _check(name, rc)
     return (part, pw) if with_entropy else part
 
 
@@ -643,10 +660,12 @@ def lce_backward_shard(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, 
                        workspace: torch.Tensor | None = None, dX: torch.Tensor | None = None,
                        dW: torch.Tensor | None = None, stream=None,
                        entropy: torch.Tensor | None = None,
-                       grad_entropy: torch.Tensor | None = None):
+                       grad_entropy: torch.Tensor | None = None,
+                       logit_scale: float = 1.0):
     """(dX share, dW) of one vocabulary shard from the merged ``stats``; the
     shards' dX shares sum to the full dX.  ``entropy``, ``grad_entropy`` as in
-    ``ce_backward_shard``."""
+    ``ce_backward_shard``; ``logit_scale`` as given to ``lce_forward_shard``
+    (``lce_backward_shard_scaled``)."""
     _check_linear(X, W, targets)
     M, H = X.shape
     VL = W.shape[0]
@@ -660,13 +679,24 @@ def lce_backward_shard(X: torch.Tensor, W: torch.Tensor, targets: torch.Tensor, 
     _check_like(dX, "dX", X)
     _check_like(dW, "dW", W)
     _need_cuda(X, W, targets, stats, grad_output)
-    rc = lib().lce_backward_shard(_ptr(X), _ptr(W), M, H, VL, _ptr(targets), int(vocab_start),
-                                  int(V), _ptr(stats), _ptr(n_valid), _ptr(grad_output),
-                                  _ptr(entropy), _ptr(grad_entropy),
-                                  float(label_smoothing), int(bool(reduce_loss)),
-                                  int(ignore_idx), _ptr(dX), _ptr(dW), _ptr(workspace),
-                                  workspace.numel(), _stream(stream))
-    _check("lce_backward_shard", rc)
+    if logit_scale != 1.0:
+        name = "lce_backward_shard_scaled"
+        rc = lib().lce_backward_shard_scaled(_ptr(X), _ptr(W), M, H, VL, float(logit_scale),
+                                             _ptr(targets), int(vocab_start), int(V),
+                                             _ptr(stats), _ptr(n_valid), _ptr(grad_output),
+                                             _ptr(entropy), _ptr(grad_entropy),
+                                             float(label_smoothing), int(bool(reduce_loss)),
+                                             int(ignore_idx), _ptr(dX), _ptr(dW),
+                                             _ptr(workspace), workspace.numel(), _stream(stream))
+    else:
+        name = "lce_backward_shard"
+        rc = lib().lce_backward_shard(_ptr(X), _ptr(W), M, H, VL, _ptr(targets),
+                                      int(vocab_start), int(V), _ptr(stats), _ptr(n_valid),
+                                      _ptr(grad_output), _ptr(entropy), _ptr(grad_entropy),
+                                      float(label_smoothing), int(bool(reduce_loss)),
+                                      int(ignore_idx), _ptr(dX), _ptr(dW), _ptr(workspace),
+                                      workspace.numel(), _stream(stream))
+    _check(name, rc)
     return dX, dW
 
 

@@ -701,10 +701,13 @@ int lce_backward_f32(const float* X, const float* W, int64_t M, int64_t H, int64
                            workspace, workspace_bytes, stream);
 }
 
-int lce_forward_shard(const void* X, const void* W, int64_t M, int64_t H, int64_t V_local,
-                      const int64_t* targets, int64_t vocab_start, int64_t ignore_idx,
-                      float* partial, float* partial_w, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+namespace {
+
+int lce_forward_shard_impl(const void* X, const void* W, int64_t M, int64_t H, int64_t V_local,
+                           float scale, const int64_t* targets, int64_t vocab_start,
+                           int64_t ignore_idx, float* partial, float* partial_w, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!(scale > 0.0f) || !__builtin_isfinite(scale)) return VCE_EINVAL;  // finite, positive
   vce::LcePlan plan;
   int rc = check_lce_common(X, W, M, H, V_local, targets, 0.0f, 0, workspace, workspace_bytes,
                             &plan);
@@ -729,15 +732,17 @@ int lce_forward_shard(const void* X, const void* W, int64_t M, int64_t H, int64_
   a.v0 = vocab_start;
   a.partial = partial;
   a.partial_w = partial_w;
+  a.scale = scale;
   return launch_status(vce::launch_lce_forward(plan, a, static_cast<hipStream_t>(stream)));
 }
 
-int lce_backward_shard(const void* X, const void* W, int64_t M, int64_t H, int64_t V_local,
-                       const int64_t* targets, int64_t vocab_start, int64_t V,
-                       const float* stats, const int32_t* n_valid, const float* grad_output,
-                       const float* entropy, const float* grad_entropy, float label_smoothing,
-                       int reduce_loss, int64_t ignore_idx, void* dX, void* dW, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+int lce_backward_shard_impl(const void* X, const void* W, int64_t M, int64_t H, int64_t V_local,
+                            float scale, const int64_t* targets, int64_t vocab_start, int64_t V,
+                            const float* stats, const int32_t* n_valid, const float* grad_output,
+                            const float* entropy, const float* grad_entropy,
+                            float label_smoothing, int reduce_loss, int64_t ignore_idx, void* dX,
+                            void* dW, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!(scale > 0.0f) || !__builtin_isfinite(scale)) return VCE_EINVAL;  // finite, positive
   vce::LcePlan plan;
   int rc = check_lce_common(X, W, M, H, V_local, targets, label_smoothing, reduce_loss, workspace,
                             workspace_bytes, &plan);
@@ -770,7 +775,54 @@ int lce_backward_shard(const void* X, const void* W, int64_t M, int64_t H, int64
   a.ws = static_cast<char*>(workspace);
   a.v0 = vocab_start;
   a.Vg = V;
+  a.scale = scale;
   return launch_status(vce::launch_lce_backward(plan, a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+int lce_forward_shard(const void* X, const void* W, int64_t M, int64_t H, int64_t V_local,
+                      const int64_t* targets, int64_t vocab_start, int64_t ignore_idx,
+                      float* partial, float* partial_w, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return lce_forward_shard_impl(X, W, M, H, V_local, 1.0f, targets, vocab_start, ignore_idx,
+                                partial, partial_w, workspace, workspace_bytes, stream);
+}
+
+int lce_forward_shard_scaled(const void* X, const void* W, int64_t M, int64_t H,
+                             int64_t V_local, float logit_scale, const int64_t* targets,
+                             int64_t vocab_start, int64_t ignore_idx, float* partial,
+                             float* partial_w, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return lce_forward_shard_impl(X, W, M, H, V_local, logit_scale, targets, vocab_start,
+                                ignore_idx, partial, partial_w, workspace, workspace_bytes,
+                                stream);
+}
+
+int lce_backward_shard(const void* X, const void* W, int64_t M, int64_t H, int64_t V_local,
+                       const int64_t* targets, int64_t vocab_start, int64_t V,
+                       const float* stats, const int32_t* n_valid, const float* grad_output,
+                       const float* entropy, const float* grad_entropy, float label_smoothing,
+                       int reduce_loss, int64_t ignore_idx, void* dX, void* dW, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return lce_backward_shard_impl(X, W, M, H, V_local, 1.0f, targets, vocab_start, V, stats,
+                                 n_valid, grad_output, entropy, grad_entropy, label_smoothing,
+                                 reduce_loss, ignore_idx, dX, dW, workspace, workspace_bytes,
+                                 stream);
+}
+
+int lce_backward_shard_scaled(const void* X, const void* W, int64_t M, int64_t H,
+                              int64_t V_local, float logit_scale, const int64_t* targets,
+                              int64_t vocab_start, int64_t V, const float* stats,
+                              const int32_t* n_valid, const float* grad_output,
+                              const float* entropy, const float* grad_entropy,
+                              float label_smoothing, int reduce_loss, int64_t ignore_idx,
+                              void* dX, void* dW, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return lce_backward_shard_impl(X, W, M, H, V_local, logit_scale, targets, vocab_start, V,
+                                 stats, n_valid, grad_output, entropy, grad_entropy,
+                                 label_smoothing, reduce_loss, ignore_idx, dX, dW, workspace,
+                                 workspace_bytes, stream);
 }
 
 int vce_gemm_bf16(const void* P, int64_t ldp, int p_dim, const void* Q, int64_t ldq, int q_dim,
