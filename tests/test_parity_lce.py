@@ -180,6 +180,29 @@ def test_linear_token_wave_boundaries(M):
     full_check(case)
 
 
+@pytest.mark.parametrize("M,H,V", [(1, 8, 7), (3, 16, 300), (257, 8, 2), (17, 72, 257),
+                                   (40, 8, 65)])
+def test_linear_degenerate_shapes(M, H, V):
+    # one token, the narrowest hidden size (one 8-element chunk of a K slice),
+    # two classes, one row past a token tile, one column past a vocabulary tile
+    case = wl.make_linear(3020 + M + V, M, H, V, ignore_count=0, label_smoothing=0.1,
+                          reduce_loss=M > 2, grad_output="random", name=f"m{M}_h{H}_v{V}")
+    full_check(case)
+
+
+def test_linear_single_class():
+    # V = 1: p = 1 = q for every row, so the loss and both gradients are 0 (to
+    # within the rounding of exp(0) and of the statistics)
+    case = wl.make_linear(3030, 40, 24, 1, ignore_count=3, label_smoothing=0.1,
+                          reduce_loss=False, grad_output="random")
+    out = run_lce(case)
+    ref_loss, _, _ = linear.forward(case.X, case.W, case.targets, 0.1, case.ignore_idx)
+    assert np.all(ref_loss == 0.0)
+    assert np.max(np.abs(out["loss"])) <= 1e-6
+    assert np.max(np.abs(out["dX"])) <= 1e-5
+    assert torch.max(torch.abs(out["dW_dev"].float())).item() <= 1e-5
+
+
 def test_linear_all_ignored():
     case = wl.make_linear(3004, 64, 64, 500, ignore_count=64, reduce_loss=True)
     out = run_lce(case)
