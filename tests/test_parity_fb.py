@@ -48,7 +48,8 @@ def _case(seed, d0, d1, V, dtype, eps, red, layout="B,SQ", n_ign=3, sigma=3.0):
                           layout=layout)
 
 
-@pytest.mark.parametrize("dtype,V", [("fp32", 1000), ("bf16", 7), ("bf16", 1001),
+@pytest.mark.parametrize("dtype,V", [("bf16", 1), ("fp32", 2), ("bf16", 9),
+                                     ("fp32", 1000), ("bf16", 7), ("bf16", 1001),
                                      ("fp32", 4099), ("bf16", 32000), ("bf16", 65537),
                                      ("fp32", 65536), ("bf16", 131072),
                                      ("bf16", 131080), ("fp32", 70000),
