@@ -82,7 +82,7 @@ enum vce_status {
   VCE_EALIAS = 4,       /* overwrite_input set but grad != logits, or buffers overlap */
   VCE_EWORKSPACE = 5,   /* workspace too small (see lce_workspace_size) */
   VCE_EHIP = 6,         /* a kernel launch failed */
-  VCE_EUNSUPPORTED = 7, /* a size this build does not handle (see the entry point) */
+  VCE_EUNSUPPORTED = 7, /* a size the library does not handle (see the entry point) */
   VCE_ESCRATCH = 8      /* beyond the static scratch of lce_forward_noalloc */
 };
 

@@ -77,7 +77,7 @@ const char* vce_strerror(int status) {
     case VCE_EALIAS: return "buffer aliasing violates overwrite_input";
     case VCE_EWORKSPACE: return "workspace too small";
     case VCE_EHIP: return "HIP kernel launch failed";
-    case VCE_EUNSUPPORTED: return "size not supported by this build";
+    case VCE_EUNSUPPORTED: return "size not supported by the library";
     case VCE_ESCRATCH:
       return "problem larger than the static scratch of lce_forward_noalloc "
              "(LCE_NOALLOC_SCRATCH_BYTES)";
